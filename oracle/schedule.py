@@ -1,0 +1,49 @@
+"""Model of the look-ahead block schedule, for checking the kernel's trace.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
+
+The asynchronous-KV-prefetch review (section 3.4, Algorithm 1) gives each of
+w warps of a thread block a block-index range [s, e): a warp walks its blocks
+with stride w, looks up the current block in the block table and loads it,
+and, when block_idx + w is still below e, looks up that block too and starts
+fetching it into the cache before computing Q*K^T on the current one.  The
+third page (section 2.2) assigns warp i the blocks i, i + 4, i + 8, ... of a
+4-warp block, so wave i starts at s + i.
+"""
+from typing import Dict, List, Optional, Tuple
+
+Event = Tuple[int, int, Optional[int]]  # (iteration, computed block, fetched-ahead block)
+
+
+def wave_schedule(s: int, e: int, w: int, wave: int) -> List[Event]:
+    """Events of one wave, in program order."""
+    if w <= 0 or not 0 <= wave < w:
+        raise ValueError("need 0 <= wave < w")
+    events: List[Event] = []
+    block_idx = s + wave
+    it = 0
+    while block_idx < e:
+        ahead = block_idx + w if block_idx + w < e else None
+        events.append((it, block_idx, ahead))
+        block_idx += w
+        it += 1
+    return events
+
+
+def group_schedule(s: int, e: int, w: int) -> Dict[int, List[Event]]:
+    """Events of all w waves of one work-group over [s, e)."""
+    return {wave: wave_schedule(s, e, w, wave) for wave in range(w)}
+
+
+def expected_trace(s: int, e: int, w: int):
+    """Per block j in [s, e): (wave that computes it, its iteration, wave that
+    fetched it ahead or -1).  This is what the kernel's debug trace records."""
+    out = {}
+    for wave, events in group_schedule(s, e, w).items():
+        for it, j, _ in events:
+            out[j] = [wave, it, -1]
+    for wave, events in group_schedule(s, e, w).items():
+        for _, _, ahead in events:
+            if ahead is not None:
+                out[ahead][2] = wave
+    return out

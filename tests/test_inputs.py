@@ -1,0 +1,64 @@
+"""The seeded generator: determinism, layout, poison placement (CPU)."""
+import numpy as np
+import pytest
+
+from paged_kv_cache_226_amd import inputs as gen
+
+
+def test_same_seed_same_bytes_and_digest():
+    a = gen.make_case(3, 8, 2, [40, 64, 17], seed=5, extra_pool_blocks=3)
+    b = gen.make_case(3, 8, 2, [40, 64, 17], seed=5, extra_pool_blocks=3)
+    assert gen.digests(a) == gen.digests(b)
+    c = gen.make_case(3, 8, 2, [40, 64, 17], seed=6, extra_pool_blocks=3)
+    assert gen.digests(a)["k_cache"] != gen.digests(c)["k_cache"]
+
+
+def test_chunking_does_not_change_the_stream(monkeypatch):
+    a = gen.make_case(2, 4, 4, [100, 37], seed=7)
+    monkeypatch.setattr(gen, "_CHUNK", 1000)
+    b = gen.make_case(2, 4, 4, [100, 37], seed=7)
+    assert gen.digests(a) == gen.digests(b)
+
+
+def test_tiny_workload_layout():
+    x = gen.make_inputs("tiny")
+    assert x.q.shape == (2, 4, 128) and x.k_cache.shape == (64, 4, 16, 128)
+    assert list(x.context_lens) == [256, 200]
+    assert x.block_tables.shape == (2, 16)
+    assert (x.block_tables[0] >= 0).all()
+    assert (x.block_tables[1, :13] >= 0).all() and (x.block_tables[1, 13:] == -1).all()
+    used = np.concatenate([x.block_tables[0], x.block_tables[1, :13]])
+    assert len(set(used.tolist())) == 29 and used.max() < 64
+    assert x.scale == np.float32(1 / np.sqrt(128))
+
+
+@pytest.mark.parametrize("name", ["llama2_7b", "llama3_8b", "qwen25_7b", "qwen25_14b"])
+def test_workload_shapes(name):
+    w = gen.WORKLOADS[name]
+    assert w.num_q_heads % w.num_kv_heads == 0
+    assert w.head_dim == 128 and w.block_size == 16
+
+
+def test_ragged_lengths_in_range_and_pool_exact():
+    x = gen.make_case(64, 8, 2, (), seed=2, ctx_range=(512, 8192),
+                      max_blocks_per_seq=512, head_dim=16)
+    c = x.context_lens
+    assert c.min() >= 512 and c.max() <= 8192 and len(set(c.tolist())) > 30
+    nb = -(-c // 16)
+    assert x.k_cache.shape[0] == nb.sum()
+    ids = np.concatenate([x.block_tables[b, :n] for b, n in enumerate(nb)])
+    assert np.array_equal(np.sort(ids), np.arange(nb.sum()))
+    for b, n in enumerate(nb):
+        assert (x.block_tables[b, n:] == -1).all()
+
+
+def test_poison_covers_exactly_the_unread_bytes():
+    x = gen.make_case(2, 2, 2, [20, 32], seed=8, extra_pool_blocks=2)
+    gen.apply_poison(x)
+    k = np.isnan(x.k_cache.astype(np.float32))
+    read = np.zeros_like(k)
+    for b, L in enumerate(x.context_lens):
+        for t in range(L):
+            read[x.block_tables[b, t // 16], :, t % 16, :] = True
+    assert np.array_equal(k, ~read)
+    assert np.array_equal(np.isnan(x.v_cache.astype(np.float32)), ~read)

@@ -1,0 +1,301 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+- a library routine: torch's scaled_dot_product_attention in float64 on
+  contiguous K/V that the test scatters into a shuffled pool itself;
+- closed forms: equal V rows, ctx = 1, Q = 0 / scale = 0, a one-hot key;
+- invariances: block placement, GQA vs MHA with repeated KV heads;
+- the oracle's fp16 decoder against numpy over all 65536 bit patterns;
+- planted mistakes: copies of the oracle with one plausible bug each must
+  fail at least one of these pins.
+"""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import oracle as orc
+from paged_kv_cache_226_amd import inputs as gen
+
+D, T = 128, 16
+
+
+def scatter_case(seed, B, Hq, Hkv, lens, d=D, t=T, extra=3):
+    """Draw contiguous per-sequence K/V [Hkv][L][d] and scatter them into a
+    NaN-filled pool of shuffled blocks (test-side code, independent of the
+    oracle's gather)."""
+    rng = np.random.default_rng(seed)
+    nbs = [-(-L // t) for L in lens]
+    NB = sum(nbs) + extra
+    perm = rng.permutation(NB)
+    MB = max(nbs + [1])
+    bt = np.full((B, MB), -1, np.int32)
+    kpool = np.full((NB, Hkv, t, d), np.nan, np.float16)
+    vpool = np.full((NB, Hkv, t, d), np.nan, np.float16)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float16)
+    kc, vc = [], []
+    off = 0
+    for b, L in enumerate(lens):
+        K = rng.standard_normal((Hkv, L, d)).astype(np.float16)
+        V = rng.standard_normal((Hkv, L, d)).astype(np.float16)
+        kc.append(K)
+        vc.append(V)
+        for j in range(nbs[b]):
+            p = perm[off + j]
+            bt[b, j] = p
+            n = min(t, L - j * t)
+            for h in range(Hkv):
+                kpool[p, h, :n] = K[h, j * t:j * t + n]
+                vpool[p, h, :n] = V[h, j * t:j * t + n]
+        off += nbs[b]
+    ctx = np.asarray(lens, np.int32)
+    return q, kpool, vpool, bt, ctx, kc, vc
+
+
+def sdpa_ref(q, kc, vc, scale):
+    """torch SDPA in float64 per sequence, GQA by contiguous head groups."""
+    out = []
+    for b in range(q.shape[0]):
+        qq = torch.from_numpy(q[b].astype(np.float64))[None, :, None, :]
+        kk = torch.from_numpy(kc[b].astype(np.float64))[None]
+        vv = torch.from_numpy(vc[b].astype(np.float64))[None]
+        o = F.scaled_dot_product_attention(qq, kk, vv, scale=float(scale),
+                                           enable_gqa=True)
+        out.append(o[0, :, 0, :].numpy())
+    return np.stack(out)
+
+
+SCALE = float(np.float32(1 / np.sqrt(D)))
+
+
+@pytest.mark.parametrize("seed,B,Hq,Hkv,lens", [
+    (10, 1, 1, 1, [1]),
+    (11, 2, 4, 4, [17, 50]),
+    (12, 3, 4, 2, [33, 15, 16]),
+    (13, 2, 4, 1, [31, 49]),
+    (14, 3, 10, 2, [7, 45, 29]),
+    (15, 2, 7, 1, [47, 18]),
+    (16, 1, 16, 2, [300]),
+])
+def test_matches_sdpa_on_scattered_pool(seed, B, Hq, Hkv, lens):
+    q, kp, vp, bt, ctx, kc, vc = scatter_case(seed, B, Hq, Hkv, lens)
+    got = orc.paged_attention_f64(q, kp, vp, bt, ctx, SCALE)
+    ref = sdpa_ref(q, kc, vc, SCALE)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_small_head_dim_and_block_size():
+    """The definition does not depend on D = 128, T = 16."""
+    q, kp, vp, bt, ctx, kc, vc = scatter_case(20, 2, 6, 3, [9, 23], d=8, t=4)
+    got = orc.paged_attention_f64(q, kp, vp, bt, ctx, 0.3)
+    ref = sdpa_ref(q, kc, vc, float(np.float32(0.3)))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_tiny_workload_matches_sdpa():
+    x = gen.make_inputs("tiny")
+    got = orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                  x.context_lens, x.scale)
+    kc, vc = [], []
+    for b, L in enumerate(x.context_lens):
+        idx = np.arange(L)
+        phys = x.block_tables[b, idx // T]
+        kc.append(np.transpose(x.k_cache[phys, :, idx % T, :], (1, 0, 2)))
+        vc.append(np.transpose(x.v_cache[phys, :, idx % T, :], (1, 0, 2)))
+    np.testing.assert_allclose(got, sdpa_ref(x.q, kc, vc, x.scale), rtol=0, atol=1e-12)
+
+
+def test_block_placement_invariance_bitwise():
+    x = gen.make_case(3, 8, 2, [40, 64, 17], seed=21, extra_pool_blocks=5)
+    a = orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                x.context_lens, x.scale)
+    rng = np.random.default_rng(99)
+    NB = x.k_cache.shape[0]
+    pi = rng.permutation(NB)
+    k2 = np.empty_like(x.k_cache)
+    v2 = np.empty_like(x.v_cache)
+    k2[pi] = x.k_cache
+    v2[pi] = x.v_cache
+    bt2 = np.where(x.block_tables >= 0, pi[np.maximum(x.block_tables, 0)], -1).astype(np.int32)
+    b = orc.paged_attention_f64(x.q, k2, v2, bt2, x.context_lens, x.scale)
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
+def test_equal_v_rows_give_that_row():
+    x = gen.make_case(2, 4, 2, [37, 80], seed=22)
+    c = np.random.default_rng(1).standard_normal(D).astype(np.float16)
+    x.v_cache[:] = c
+    got = orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                  x.context_lens, x.scale)
+    np.testing.assert_allclose(got, np.broadcast_to(c.astype(np.float64), got.shape),
+                               rtol=1e-14, atol=0)
+
+
+def test_context_one_gives_first_v_row_exactly():
+    x = gen.make_case(3, 6, 3, [1, 1, 1], seed=23, extra_pool_blocks=4)
+    got = orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                  x.context_lens, x.scale)
+    for b in range(3):
+        for h in range(6):
+            v0 = x.v_cache[x.block_tables[b, 0], h // 2, 0].astype(np.float64)
+            assert np.array_equal(got[b, h], v0)
+
+
+@pytest.mark.parametrize("mode", ["zero_q", "zero_scale"])
+def test_uniform_weights_give_mean_of_v(mode):
+    x = gen.make_case(2, 4, 4, [45, 16], seed=24)
+    scale = x.scale
+    if mode == "zero_q":
+        x.q[:] = 0
+    else:
+        scale = 0.0
+    got = orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                  x.context_lens, scale)
+    for b, L in enumerate(x.context_lens):
+        idx = np.arange(L)
+        rows = x.v_cache[x.block_tables[b, idx // T], :, idx % T, :].astype(np.float64)
+        np.testing.assert_allclose(got[b], rows.mean(axis=0), rtol=0, atol=1e-13)
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads_bitwise():
+    g = 5
+    x = gen.make_case(2, 10, 2, [33, 70], seed=25, extra_pool_blocks=2)
+    a = orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                x.context_lens, x.scale)
+    k_rep = np.repeat(x.k_cache, g, axis=1)
+    v_rep = np.repeat(x.v_cache, g, axis=1)
+    b = orc.paged_attention_f64(x.q, k_rep, v_rep, x.block_tables, x.context_lens,
+                                x.scale)
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
+def test_one_hot_key_closed_form():
+    """k_{t*} = lam * q and every other key 0: weight e^a on t*, 1 elsewhere,
+    with a = scale * lam * |q|^2."""
+    L, tstar, lam = 37, 21, 0.75
+    x = gen.make_case(1, 1, 1, [L], seed=26)
+    q = x.q[0, 0].astype(np.float64)
+    x.k_cache[:] = 0
+    kst = (lam * q).astype(np.float16)
+    p = x.block_tables[0, tstar // T]
+    x.k_cache[p, 0, tstar % T] = kst
+    got = orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                  x.context_lens, x.scale)[0, 0]
+    a = float(x.scale) * float(np.dot(q, kst.astype(np.float64)))
+    idx = np.arange(L)
+    rows = x.v_cache[x.block_tables[0, idx // T], 0, idx % T].astype(np.float64)
+    wts = np.ones(L)
+    wts[tstar] = np.exp(a)
+    ref = (wts[:, None] * rows).sum(0) / wts.sum()
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-15)
+    assert a > 5  # the key really dominates
+
+
+def test_context_zero_gives_zeros():
+    x = gen.make_case(2, 4, 2, [0, 20], seed=27, extra_pool_blocks=1)
+    got = orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                  x.context_lens, x.scale)
+    assert np.all(got[0] == 0) and np.all(np.isfinite(got[1]))
+
+
+def test_never_reads_poisoned_bytes():
+    x = gen.make_case(3, 4, 2, [40, 16, 3], seed=28, extra_pool_blocks=6)
+    clean = orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                    x.context_lens, x.scale)
+    gen.apply_poison(x)
+    assert np.isnan(x.k_cache.astype(np.float32)).any()
+    dirty = orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                    x.context_lens, x.scale)
+    assert np.array_equal(clean.view(np.uint64), dirty.view(np.uint64))
+
+
+def test_rows_variant_equals_full():
+    x = gen.make_case(3, 8, 2, [40, 64, 17], seed=29)
+    full = orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                   x.context_lens, x.scale)
+    rows = np.array([[2, 7], [0, 0], [1, 3]])
+    part = orc.paged_attention_rows_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                        x.context_lens, x.scale, rows)
+    for i, (b, h) in enumerate(rows):
+        assert np.array_equal(part[i], full[b, h])
+
+
+def test_bad_inputs_are_errors():
+    x = gen.make_case(1, 2, 2, [20], seed=30)
+    bt = x.block_tables.copy()
+    bt[0, 1] = x.k_cache.shape[0]
+    with pytest.raises(RuntimeError, match="outside the pool"):
+        orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, bt, x.context_lens, x.scale)
+    with pytest.raises(RuntimeError, match="exceeds"):
+        orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                np.array([10_000], np.int32), x.scale)
+
+
+def test_fp16_decoder_all_bit_patterns():
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([orc.half_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint64), ref[~nan].view(np.uint64))
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each mutation of the oracle source must break a pin.
+
+MUTATIONS = {
+    "slot_index": ("t % T) * D", "(t + 1) % T) * D"),
+    "kv_head_map": ("const int kvh = h / g;", "const int kvh = h % Hkv;"),
+    "exp_sign": ("s[t] = exp(s[t] - m);", "s[t] = exp(m - s[t]);"),
+    "no_normalise": ("out_row[d] /= Z;", "out_row[d] /= 1.0;"),
+    "dropped_last_token": ("for (t = 0; t < L; ++t) {\n        s[t] = exp",
+                           "for (t = 0; t < L - 1; ++t) {\n        s[t] = exp"),
+    "scale_dropped": ("s[t] = scale * dot;", "s[t] = dot;"),
+    "q_head_row": ("((int64_t)b * Hq + h) * D", "((int64_t)b * Hq + kvh) * D"),
+}
+
+
+def _pins_pass(lib_path):
+    """Run the SDPA and closed-form pins against a given oracle build."""
+    saved = orc._lib
+    try:
+        orc._lib = None
+        import oracle.build as ob
+        real = ob.LIB
+        ob.LIB = lib_path
+        try:
+            test_matches_sdpa_on_scattered_pool(14, 3, 10, 2, [7, 45, 29])
+            test_context_one_gives_first_v_row_exactly()
+            test_uniform_weights_give_mean_of_v("zero_q")
+            test_gqa_equals_mha_with_repeated_kv_heads_bitwise()
+            test_small_head_dim_and_block_size()
+        finally:
+            ob.LIB = real
+    except (AssertionError, RuntimeError):
+        return False
+    finally:
+        orc._lib = saved
+    return True
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name):
+    src_path = os.path.join(os.path.dirname(orc.__file__), "pa_oracle.c")
+    src = open(src_path).read()
+    old, new = MUTATIONS[name]
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    mutated = src.replace(old, new)
+    tmp = tempfile.mkdtemp(prefix="oracle_mut_")
+    try:
+        c = os.path.join(tmp, "m.c")
+        so = os.path.join(tmp, "libm.so")
+        open(c, "w").write(mutated)
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                        "-ffp-contract=off", c, "-o", so, "-lm"], check=True)
+        assert not _pins_pass(so), f"no pin caught the planted mistake {name}"
+    finally:
+        shutil.rmtree(tmp)
