@@ -1,0 +1,155 @@
+/*
+ * paged_attn.h -- C ABI of the MI355X (gfx950) paged decode-attention library.
+ *
+ * The operation (asynchronous-KV-prefetch review, sections 3.2-3.4 and 4.1;
+ * PagedAttention answer, section 3): one decode step of attention for a batch
+ * of sequences whose keys and values live in fixed-size blocks of a shared
+ * physical pool.  For sequence b and query head h (kv head h / (Hq / Hkv)),
+ * every token t < context_lens[b] sits in block block_tables[b][t / 16] at
+ * slot t % 16, and
+ *     out[b][h] = softmax_t(scale * q[b][h] . K_t) . V_t
+ * computed with an fp32 online softmax and fp32 accumulation, rounded once to
+ * fp16 (round to nearest even).
+ *
+ * How the blocks are walked (review, section 3.4, Algorithm 1): a work-group
+ * owns a block range [s, e) of one (sequence, KV head); its w wavefronts take
+ * blocks s + wave, s + wave + w, ...  Before computing block j a wavefront
+ * issues the fetch of block j + w (when j + w < e) so that its memory latency
+ * overlaps the compute of block j.  `pa_options.prefetch` chooses how that
+ * fetch is made; results are bitwise identical in every mode.
+ *
+ * Conventions
+ *  - Tensor pointers are DEVICE pointers, owned by the caller; the library
+ *    keeps no reference after a call returns and allocates nothing.
+ *  - fp16 means IEEE binary16 bits.  Layouts are row-major:
+ *        q, out       [num_seqs][num_q_heads][128]
+ *        k_cache      [num_blocks][num_kv_heads][16][128]   (token-major)
+ *        v_cache      [num_blocks][num_kv_heads][16][128]   (token-major)
+ *        block_tables [num_seqs][max_blocks_per_seq]  int32 physical block ids
+ *        context_lens [num_seqs]                      int32 tokens to attend
+ *    Each (block, kv head) slice is one contiguous 4 KiB piece.
+ *  - All pointers must be 16-byte aligned; out must not alias an input.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Argument checks are host-only and never read device memory.
+ *    Faults during execution surface at the caller's next synchronisation.
+ *  - Data-dependent preconditions cannot be checked on the host:
+ *        0 <= block_tables[b][j] < num_blocks   for j < ceil(ctx_b / 16)
+ *        context_lens[b] <= max_blocks_per_seq * 16
+ *    Violating the first is undefined behaviour unless a debug error word is
+ *    given (then the kernel flags it and reads block 0 instead).  Context
+ *    lengths beyond the table are clamped to it (flagged in debug mode).
+ *    context_lens[b] <= 0 yields an all-zero output row.
+ *  - Return values are PA_* status codes; nothing is printed, nothing aborts,
+ *    no C++ exception crosses this boundary.
+ *  - Calls are reentrant for distinct out / workspace / debug buffers.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+#define PA_HEAD_DIM 128
+#define PA_BLOCK_SIZE 16
+#define PA_G_MAX 16      /* query heads per KV head */
+#define PA_WAVES_MAX 8   /* wavefronts per work-group */
+
+enum pa_status {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1, /* null pointer, bad count, misaligned pointer */
+    PA_ERR_UNSUPPORTED = 2, /* head_dim != 128, block_size != 16, g > PA_G_MAX */
+    PA_ERR_WORKSPACE = 3,   /* plan needs a workspace that is missing or too small */
+    PA_ERR_HIP = 4          /* a kernel launch failed (hipGetLastError) */
+};
+
+/* How block j + w is fetched while block j is computed. */
+enum pa_prefetch {
+    PA_PREFETCH_OFF = 0,  /* load block j, wait, compute: no look-ahead */
+    PA_PREFETCH_L2 = 1,   /* touch every 128 B line of block j + w so it is
+                             brought into L2 / Infinity Cache; data discarded */
+    PA_PREFETCH_REG = 2,  /* load block j + w into a second register buffer */
+    PA_PREFETCH_BOTH = 3  /* REG for block j + w, plus an L2 touch of j + 2w */
+};
+
+typedef struct pa_shape {
+    int32_t num_seqs;           /* B >= 1 */
+    int32_t num_q_heads;        /* Hq >= 1 */
+    int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv <= PA_G_MAX */
+    int32_t head_dim;           /* must be 128 */
+    int32_t block_size;         /* must be 16 */
+    int32_t max_blocks_per_seq; /* row stride of block_tables, >= 1 */
+    int64_t num_blocks;         /* pool size, >= 1 */
+} pa_shape;
+
+typedef struct pa_options {
+    int32_t prefetch;          /* enum pa_prefetch; negative = library default */
+    int32_t partition_blocks;  /* blocks per split-context partition; 0 = auto */
+    int32_t waves_per_wg;      /* w in {1, 2, 4, 8}; 0 = auto */
+    int32_t reserved;          /* must be 0 */
+    void *workspace;           /* device scratch for partition partials; may be
+                                  NULL when the plan has one partition */
+    size_t workspace_bytes;
+    /* Debug outputs (all NULL in normal use; any non-NULL selects the
+       checked kernel variant, which computes bitwise the same result):
+       debug_gather_k  fp16 [B][Hkv][max_blocks_per_seq*16][128]: the K rows
+                       each wavefront actually loaded for the compute step;
+       debug_trace     int32 [B][Hkv][max_blocks_per_seq][2]: per block, the
+                       (wave << 16 | iteration) that computed it and the wave
+                       that fetched it ahead (entries never visited keep the
+                       caller's fill value);
+       debug_error_word int32: bit 0 set if a block id was outside the pool,
+                       bit 1 if a context length exceeded the table. */
+    void *debug_gather_k;
+    int32_t *debug_trace;
+    int32_t *debug_error_word;
+} pa_options;
+
+/* The plan a call would use, for logging and tests. */
+typedef struct pa_plan_info {
+    int32_t prefetch;
+    int32_t waves_per_wg;
+    int32_t partition_blocks;
+    int32_t num_partitions;    /* partitions of the longest possible sequence */
+    int64_t workgroups;        /* decode-kernel grid size */
+    size_t workspace_bytes;    /* 0 when num_partitions == 1 */
+} pa_plan_info;
+
+/* Fill *opts with the defaults (prefetch = library default, auto sizes). */
+void paged_attn_default_options(pa_options *opts);
+
+/* One decode step; see the conventions above.  shape must be non-NULL; opts
+   may be NULL (defaults).  stream is a hipStream_t or NULL. */
+int paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, const int32_t *context_lens,
+                      float scale, void *out, const pa_shape *shape,
+                      const pa_options *opts, void *stream);
+
+/* Plan for (shape, opts) without launching.  Host-only. */
+int paged_attn_plan(const pa_shape *shape, const pa_options *opts,
+                    pa_plan_info *info);
+
+/* Workspace bytes paged_attn_decode needs for (shape, opts); 0 if none or if
+   the arguments are invalid.  Host-only. */
+size_t paged_attn_workspace_size(const pa_shape *shape, const pa_options *opts);
+
+/* Streaming-read ceiling: reads `bytes` (a multiple of 16, 16-byte aligned)
+   from device buffer `buf` once with the same 128-bit loads the decode kernel
+   uses and writes one 16-byte value per work-group into `sink` (device, at
+   least paged_attn_stream_read_sink_bytes(bytes) bytes). */
+int paged_attn_stream_read(const void *buf, size_t bytes, void *sink,
+                           void *stream);
+size_t paged_attn_stream_read_sink_bytes(size_t bytes);
+
+const char *paged_attn_error_string(int status);
+int paged_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,213 @@
+// C ABI of the paged decode-attention library: argument checks, the launch
+// plan (work-group size, split-context partitions, workspace) and dispatch.
+// Everything here is host code; it never reads device memory.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/paged_attn.h"
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int kDefaultPrefetch = PA_PREFETCH_REG;
+constexpr int kDefaultWaves = 4;
+constexpr int kMaxPartitionBlocks = 1024;  // LDS slice of the block table: 4 KiB
+// Work-groups the auto plan aims for before it splits contexts: four
+// work-groups of four wavefronts per compute unit on 256 CUs.
+constexpr int64_t kTargetWorkgroups = 1024;
+
+struct Plan {
+  int pf, waves, PB, P;
+  int64_t wgs;
+  size_t ws_bytes;
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(const pa_shape* sh) {
+  if (!sh) return PA_ERR_INVALID_ARG;
+  if (sh->num_seqs < 1 || sh->num_q_heads < 1 || sh->num_kv_heads < 1 ||
+      sh->max_blocks_per_seq < 1 || sh->num_blocks < 1)
+    return PA_ERR_INVALID_ARG;
+  if (sh->num_q_heads % sh->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (sh->head_dim != PA_HEAD_DIM || sh->block_size != PA_BLOCK_SIZE)
+    return PA_ERR_UNSUPPORTED;
+  const int g = sh->num_q_heads / sh->num_kv_heads;
+  if (g > PA_G_MAX) return PA_ERR_UNSUPPORTED;
+  // grid.y = Hkv and grid.z = B must fit the launch limits.
+  if (sh->num_kv_heads > 65535 || sh->num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+  // Byte offsets of the pool must fit int64.
+  if (sh->num_blocks > (INT64_MAX / 8192) / sh->num_kv_heads) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
+  int rc = check_shape(sh);
+  if (rc) return rc;
+  pa_options d;
+  paged_attn_default_options(&d);
+  if (!o) o = &d;
+  if (o->reserved != 0) return PA_ERR_INVALID_ARG;
+  const int g = sh->num_q_heads / sh->num_kv_heads;
+
+  int pf = o->prefetch < 0 ? kDefaultPrefetch : o->prefetch;
+  if (pf > PA_PREFETCH_BOTH) return PA_ERR_INVALID_ARG;
+
+  int waves = o->waves_per_wg == 0 ? kDefaultWaves : o->waves_per_wg;
+  if (waves != 1 && waves != 2 && waves != 4 && waves != 8) return PA_ERR_INVALID_ARG;
+  if (g > 8 && waves > 4) return PA_ERR_UNSUPPORTED;  // register budget
+
+  const int MB = sh->max_blocks_per_seq;
+  int PB;
+  if (o->partition_blocks < 0) return PA_ERR_INVALID_ARG;
+  if (o->partition_blocks > 0) {
+    if (o->partition_blocks > kMaxPartitionBlocks) return PA_ERR_UNSUPPORTED;
+    PB = o->partition_blocks < MB ? o->partition_blocks : MB;
+  } else {
+    const int64_t units = (int64_t)sh->num_seqs * sh->num_kv_heads;
+    int64_t want = (kTargetWorkgroups + units - 1) / units;
+    if (want < 1) want = 1;
+    int64_t pb = (MB + want - 1) / want;
+    pb = (pb + waves - 1) / waves * waves;       // whole rounds of the W waves
+    if (pb < 2 * waves) pb = 2 * waves;           // at least two blocks per wave
+    if (pb > kMaxPartitionBlocks) pb = kMaxPartitionBlocks;
+    if (pb > MB) pb = MB;
+    PB = (int)pb;
+  }
+  const int P = (MB + PB - 1) / PB;
+  pl->pf = pf;
+  pl->waves = waves;
+  pl->PB = PB;
+  pl->P = P;
+  pl->wgs = (int64_t)P * sh->num_kv_heads * sh->num_seqs;
+  pl->ws_bytes = P > 1 ? (size_t)sh->num_seqs * sh->num_q_heads * P * (2 + PA_HEAD_DIM) *
+                             sizeof(float)
+                       : 0;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void paged_attn_default_options(pa_options* o) {
+  if (!o) return;
+  memset(o, 0, sizeof(*o));
+  o->prefetch = -1;
+}
+
+int paged_attn_plan(const pa_shape* sh, const pa_options* o, pa_plan_info* info) {
+  if (!info) return PA_ERR_INVALID_ARG;
+  Plan pl;
+  int rc = make_plan(sh, o, &pl);
+  if (rc) return rc;
+  info->prefetch = pl.pf;
+  info->waves_per_wg = pl.waves;
+  info->partition_blocks = pl.PB;
+  info->num_partitions = pl.P;
+  info->workgroups = pl.wgs;
+  info->workspace_bytes = pl.ws_bytes;
+  return PA_OK;
+}
+
+size_t paged_attn_workspace_size(const pa_shape* sh, const pa_options* o) {
+  Plan pl;
+  if (make_plan(sh, o, &pl)) return 0;
+  return pl.ws_bytes;
+}
+
+int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      float scale, void* out, const pa_shape* sh, const pa_options* o,
+                      void* stream) {
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
+      (reinterpret_cast<uintptr_t>(context_lens) & 3u))
+    return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  Plan pl;
+  int rc = make_plan(sh, o, &pl);
+  if (rc) return rc;
+  pa_options d;
+  paged_attn_default_options(&d);
+  if (!o) o = &d;
+  if (pl.P > 1) {
+    if (!o->workspace || o->workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE;
+    if (!aligned16(o->workspace)) return PA_ERR_INVALID_ARG;
+  }
+  if ((o->debug_gather_k && !aligned16(o->debug_gather_k)) ||
+      (o->debug_trace && (reinterpret_cast<uintptr_t>(o->debug_trace) & 3u)) ||
+      (o->debug_error_word && (reinterpret_cast<uintptr_t>(o->debug_error_word) & 3u)))
+    return PA_ERR_INVALID_ARG;
+
+  const int g = sh->num_q_heads / sh->num_kv_heads;
+  pa::DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.bt = block_tables;
+  a.ctx = context_lens;
+  a.out = static_cast<uint16_t*>(out);
+  if (pl.P > 1) {
+    float* ws = static_cast<float*>(o->workspace);
+    const size_t rows = (size_t)sh->num_seqs * sh->num_q_heads * pl.P;
+    a.ws_ml = ws;
+    a.ws_o = ws + rows * 2;
+  }
+  a.dbg_k = static_cast<uint16_t*>(o->debug_gather_k);
+  a.dbg_trace = o->debug_trace;
+  a.dbg_err = o->debug_error_word;
+  a.sink = nullptr;
+  a.sink_enable = 0;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.B = sh->num_seqs;
+  a.Hq = sh->num_q_heads;
+  a.Hkv = sh->num_kv_heads;
+  a.MB = sh->max_blocks_per_seq;
+  a.P = pl.P;
+  a.PB = pl.PB;
+  a.NB = sh->num_blocks;
+  a.blk_bytes = (int64_t)sh->num_kv_heads * PA_BLOCK_SIZE * PA_HEAD_DIM * 2;
+  a.lds_bt_bytes = pa::lds_bt_bytes_for(pl.PB);
+  const bool dbg = o->debug_gather_k || o->debug_trace || o->debug_error_word;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (pa::launch_decode(a, g, pl.pf, dbg, pl.waves, st) != hipSuccess) return PA_ERR_HIP;
+  if (pl.P > 1 && pa::launch_reduce(a, st) != hipSuccess) return PA_ERR_HIP;
+  return PA_OK;
+}
+
+size_t paged_attn_stream_read_sink_bytes(size_t bytes) {
+  (void)bytes;
+  return 16 * 4096;
+}
+
+int paged_attn_stream_read(const void* buf, size_t bytes, void* sink, void* stream) {
+  if (!buf || !sink || bytes == 0 || (bytes & 15u) || !aligned16(buf) || !aligned16(sink))
+    return PA_ERR_INVALID_ARG;
+  // 16 work-groups of 256 threads per CU on 256 CUs.
+  if (pa::launch_stream_read(buf, bytes, sink, 4096, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return PA_ERR_HIP;
+  return PA_OK;
+}
+
+const char* paged_attn_error_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int paged_attn_abi_version(void) { return PA_ABI_VERSION; }
+
+}  // extern "C"

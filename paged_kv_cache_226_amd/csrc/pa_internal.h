@@ -1,0 +1,46 @@
+// Internal interface between the C ABI (pa_api.cpp) and the kernels
+// (pa_kernels.hip).  Not installed; the public interface is paged_attn.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Everything a decode launch needs, passed by value as the kernel argument.
+struct DecodeArgs {
+  const uint16_t* q;     // [B][Hq][128] fp16
+  const uint16_t* k;     // [NB][Hkv][16][128] fp16
+  const uint16_t* v;     // [NB][Hkv][16][128] fp16
+  const int32_t* bt;     // [B][MB]
+  const int32_t* ctx;    // [B]
+  uint16_t* out;         // [B][Hq][128] fp16
+  float* ws_ml;          // [B][Hq][P][2]   (max in log2 units, sum)
+  float* ws_o;           // [B][Hq][P][128] unnormalised output
+  uint16_t* dbg_k;       // see pa_options.debug_gather_k
+  int32_t* dbg_trace;    // see pa_options.debug_trace
+  int32_t* dbg_err;      // see pa_options.debug_error_word
+  int32_t* sink;         // never written while sink_enable == 0
+  float scale_log2;      // scale * log2(e)
+  int B, Hq, Hkv, MB;
+  int P;                 // partitions in the grid
+  int PB;                // blocks per partition
+  int64_t NB;            // pool blocks
+  int64_t blk_bytes;     // bytes from one physical block to the next (Hkv * 4096)
+  int lds_bt_bytes;      // LDS bytes reserved for the block-table slice
+  int sink_enable;
+};
+
+inline int lds_bt_bytes_for(int PB) { return ((PB * 4) + 15) / 16 * 16; }
+
+inline size_t decode_lds_bytes(int PB, int g, int waves) {
+  return (size_t)lds_bt_bytes_for(PB) + (size_t)waves * g * (128 + 2) * 4;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int g, int pf, bool dbg, int waves,
+                         hipStream_t st);
+hipError_t launch_reduce(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_stream_read(const void* buf, size_t bytes, void* sink, int groups,
+                              hipStream_t st);
+
+}  // namespace pa

@@ -1,0 +1,135 @@
+"""PyTorch-facing binding of the paged decode-attention library.
+
+Argument marshalling only: shapes, dtypes and devices are checked, device
+pointers and the current HIP stream are handed to libpaged_attn.so, and every
+step of the computation runs in the HIP kernels.  torch supplies device
+memory (including the partition workspace) and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _native as nat
+
+
+def _stream_handle(stream: Optional[torch.cuda.Stream]) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+
+
+def shape_of(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor) -> nat.PaShape:
+    B, Hq, D = q.shape
+    NB, Hkv, T, Dk = k_cache.shape
+    return nat.make_shape(B, Hq, Hkv, block_tables.shape[1], NB, head_dim=D, block_size=T)
+
+
+def options(prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0) -> nat.PaOptions:
+    o = nat.default_options()
+    o.prefetch = int(prefetch)
+    o.partition_blocks = int(partition_blocks)
+    o.waves_per_wg = int(waves_per_wg)
+    return o
+
+
+def plan(q, k_cache, block_tables, **kw) -> dict:
+    return nat.plan(shape_of(q, k_cache, block_tables), options(**kw))
+
+
+def workspace_bytes(q, k_cache, block_tables, **kw) -> int:
+    sh = shape_of(q, k_cache, block_tables)
+    return int(nat.lib().paged_attn_workspace_size(ctypes.byref(sh), ctypes.byref(options(**kw))))
+
+
+def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor,
+                      scale: Optional[float] = None, out: Optional[torch.Tensor] = None, *,
+                      prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0,
+                      workspace: Optional[torch.Tensor] = None,
+                      debug_gather_k: Optional[torch.Tensor] = None,
+                      debug_trace: Optional[torch.Tensor] = None,
+                      debug_error_word: Optional[torch.Tensor] = None,
+                      stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """One decode step of paged attention; returns out (fp16 [B, Hq, 128]).
+
+    q [B, Hq, 128] fp16; k_cache, v_cache [NB, Hkv, 16, 128] fp16; block_tables
+    [B, MB] int32; context_lens [B] int32; scale defaults to 1/sqrt(128).
+    """
+    _check(q, "q", torch.float16, 3)
+    _check(k_cache, "k_cache", torch.float16, 4)
+    _check(v_cache, "v_cache", torch.float16, 4)
+    _check(block_tables, "block_tables", torch.int32, 2)
+    _check(context_lens, "context_lens", torch.int32, 1)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    B, Hq, D = q.shape
+    if block_tables.shape[0] != B or context_lens.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("inconsistent shapes")
+    if scale is None:
+        scale = D ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.float16, 3)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    sh = shape_of(q, k_cache, block_tables)
+    o = options(prefetch, partition_blocks, waves_per_wg)
+    need = int(nat.lib().paged_attn_workspace_size(ctypes.byref(sh), ctypes.byref(o)))
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace needs {need} bytes")
+        o.workspace = workspace.data_ptr()
+        o.workspace_bytes = workspace.numel() * workspace.element_size()
+    if debug_gather_k is not None:
+        _check(debug_gather_k, "debug_gather_k", torch.float16, 4)
+        o.debug_gather_k = debug_gather_k.data_ptr()
+    if debug_trace is not None:
+        _check(debug_trace, "debug_trace", torch.int32, 4)
+        o.debug_trace = debug_trace.data_ptr()
+    if debug_error_word is not None:
+        _check(debug_error_word, "debug_error_word", torch.int32, 1)
+        o.debug_error_word = debug_error_word.data_ptr()
+    rc = nat.lib().paged_attn_decode(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
+        ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(block_tables.data_ptr()),
+        ctypes.c_void_p(context_lens.data_ptr()), ctypes.c_float(scale),
+        ctypes.c_void_p(out.data_ptr()), ctypes.byref(sh), ctypes.byref(o),
+        _stream_handle(stream))
+    if rc != nat.PA_OK:
+        raise RuntimeError(f"paged_attn_decode: {nat.error_string(rc)} ({rc})")
+    return out
+
+
+def stream_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Read every byte of buf once (the streaming-read ceiling kernel).
+    Returns the sink: one 16-byte XOR per work-group."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    sink_bytes = int(nat.lib().paged_attn_stream_read_sink_bytes(nbytes))
+    if sink is None:
+        sink = torch.zeros(sink_bytes // 4, dtype=torch.int32, device=buf.device)
+    rc = nat.lib().paged_attn_stream_read(ctypes.c_void_p(buf.data_ptr()),
+                                          ctypes.c_size_t(nbytes),
+                                          ctypes.c_void_p(sink.data_ptr()),
+                                          _stream_handle(stream))
+    if rc != nat.PA_OK:
+        raise RuntimeError(f"paged_attn_stream_read: {nat.error_string(rc)} ({rc})")
+    return sink

@@ -8,3 +8,17 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+import pytest  # noqa: E402
+
+
+@pytest.fixture(scope="session")
+def native_lib():
+    """The built HIP library (built here only if nothing is built yet)."""
+    from paged_kv_cache_226_amd import _native as nat
+    import os as _os
+    if not _os.path.exists(nat.LIB_PATH):
+        from paged_kv_cache_226_amd import build as _b
+        _b.build()
+    return nat.lib()

@@ -1,0 +1,60 @@
+"""Full-size workloads on the GPU: sampled rows against the oracle (MI355X).
+
+The decode call uses the default options, i.e. the launch configuration the
+bench times; every prefetch mode must give the same bits on the whole output.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from paged_kv_cache_226_amd import inputs as gen
+from paged_kv_cache_226_amd import ops
+
+from parity import assert_close, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu(native_lib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def sample_rows(x, n, seed):
+    B, Hq, _ = x.q.shape
+    rng = np.random.default_rng(seed)
+    rows = {(0, 0), (B - 1, Hq - 1)}
+    c = x.context_lens
+    rows.add((int(np.argmax(c)), 0))
+    rows.add((int(np.argmin(c)), Hq - 1))
+    while len(rows) < n:
+        rows.add((int(rng.integers(B)), int(rng.integers(Hq))))
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["llama2_7b", "llama3_8b", "qwen25_7b", "qwen25_14b"])
+def test_workload_sampled_rows(name):
+    print(f"[workload] {name}: generating", flush=True)
+    x = gen.make_inputs(name)
+    dev = to_device(x)
+    print(f"[workload] {name}: decode", flush=True)
+    out = ops.paged_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                dev["context_lens"], x.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    for pf in (0, 1, 2, 3):
+        o2 = ops.paged_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"],
+                                   dev["block_tables"], dev["context_lens"], x.scale,
+                                   prefetch=pf)
+        torch.cuda.synchronize()
+        assert torch.equal(o2.view(torch.int16), out.view(torch.int16)), f"mode {pf}"
+    got = out.cpu().numpy()
+    del dev, out
+    rows = sample_rows(x, 48, seed=len(name))
+    print(f"[workload] {name}: oracle on {len(rows)} rows", flush=True)
+    ref = orc.paged_attention_rows_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                       x.context_lens, x.scale, rows)
+    e = assert_close(got[rows[:, 0], rows[:, 1]], ref, name)
+    print(f"[workload] {name}: {e}", flush=True)
