@@ -1,0 +1,254 @@
+"""Benchmark: paged decode attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--prefetch MODE]
+
+A step is one paged_attn_decode call over the whole batch (the decode kernel,
+plus the cross-partition reduce when the plan splits contexts), i.e. one
+layer's decode attention, with every input already resident in HBM.  The
+printed JSON line reports effective KV GB/s (algorithmic KV bytes / time)
+as `value`, µs/step, the fraction of the 8 TB/s HBM peak, the roofline of
+the decode kernel, per-prefetch-mode timings, the streaming-read ceiling
+measured in the same run, and the fp64 CPU oracle timed on the host cores
+(plus the parity of the GPU output against it).
+
+Inputs are synthetic (seeded N(0,1) Q/K/V, shuffled block tables) with the
+shapes of the workload; see paged_kv_cache_226_amd/inputs.py.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attention µs/step + effective KV GB/s (% of HBM peak), 1 GPU"
+KERNEL_SOURCES = ["paged_kv_cache_226_amd/csrc/pa_kernels.hip",
+                  "paged_kv_cache_226_amd/csrc/pa_api.cpp",
+                  "paged_kv_cache_226_amd/csrc/pa_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, mode_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"pa_decode_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    key = f"hbm_bytes_per_launch_{mode_name}"
+    return float(kv[key]) if key in kv else None
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama2_7b")
+    ap.add_argument("--prefetch", type=int, default=-1, help="-1 = library default")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU time budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="short run for rocprofv3: every prefetch mode, no CPU leg")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this bench runs on exactly one GPU; the decode kernel "
+                                   "is a single-GPU path (no collectives). Use --gpus 1."}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_226_amd import accounting as acc
+    from paged_kv_cache_226_amd import inputs as gen
+    from paged_kv_cache_226_amd import ops
+    from paged_kv_cache_226_amd import _native as nat
+
+    nat.lib()  # fail loudly if the HIP library is not built
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(3)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = gen.WORKLOADS[args.workload]
+    t0 = time.time()
+    x = gen.make_inputs(w)
+    print(f"[bench] generated {args.workload} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    d = {k: torch.from_numpy(getattr(x, k)).to(dev)
+         for k in ("q", "v_cache", "block_tables", "context_lens")}
+    d["k_cache"] = torch.from_numpy(gen.pack_k(x.k_cache)).to(dev)
+    out = torch.empty_like(d["q"])
+    Hkv = x.k_cache.shape[1]
+    kv_bytes = acc.step_kv_bytes(Hkv, 128, x.context_lens)
+    other_bytes = acc.step_other_bytes(w.num_seqs, w.num_q_heads, 128, x.context_lens)
+    flops = acc.step_flops(w.num_q_heads, 128, x.context_lens)
+    plan = ops.plan(d["q"], d["k_cache"], d["block_tables"], prefetch=args.prefetch)
+    ws_bytes = plan["workspace_bytes"]
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(pf):
+        ops.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                              d["context_lens"], x.scale, out, prefetch=pf, workspace=ws)
+
+    def timed(pf, steps, warmup):
+        for _ in range(warmup):
+            step(pf)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            step(pf)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / steps  # µs per step
+
+    def per_launch(pf, steps):
+        """Average single-launch duration: an event pair around each call."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            a.record(stream)
+            step(pf)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        return sum(ts) / len(ts), ts[len(ts) // 2]
+
+    mode = plan["prefetch"]
+    mode_names = nat.PREFETCH_NAMES
+    if args.profile:
+        for pf in (0, 1, 2, 3):
+            timed(pf, args.steps, args.warmup)
+        # Calibration kernels of known size for the HBM byte counters: a 1 GiB
+        # streaming read (reads 2^30 B) and a 1 GiB fp16 elementwise copy
+        # (reads and writes 2^30 B each).
+        src = torch.empty(1 << 29, dtype=torch.float16, device=dev).normal_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            ops.stream_read(src)
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_run": args.workload, "steps": args.steps,
+                          "calibration": {"stream_read_bytes": 1 << 30,
+                                          "copy_read_bytes": 1 << 30,
+                                          "copy_write_bytes": 1 << 30}}), flush=True)
+        return
+
+    us = timed(mode, args.steps, args.warmup)
+    launch_avg, launch_med = per_launch(mode, args.steps)
+    modes = {}
+    for pf in (0, 1, 2, 3):
+        u = timed(pf, max(20, args.steps // 4), 5)
+        modes[mode_names[pf]] = {"us_per_step": round(u, 2), "GBps": round(kv_bytes / u / 1e3, 1)}
+
+    # streaming-read ceiling over a buffer larger than every cache
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    sink = ops.stream_read(buf)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(10):
+        ops.stream_read(buf, sink)
+    b.record(stream)
+    torch.cuda.synchronize()
+    stream_gbps = (4 << 30) / (a.elapsed_time(b) * 1e3 / 10) / 1e3
+    del buf
+
+    # the decode kernel is the dominant (with one partition, the only) kernel
+    decode_only = plan["num_partitions"] == 1
+    achieved = kv_bytes / launch_avg / 1e3
+    traffic = read_traffic(args.workload, mode_names[mode])
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": acc.HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / acc.HBM_PEAK_GBPS, 4),
+                "traffic": traffic, "kernel": "pa_decode_kernel" + ("" if decode_only else
+                                                                    " + pa_reduce_kernel"),
+                "launch_us_avg": round(launch_avg, 2), "launch_us_median": round(launch_med, 2)}
+
+    result = {
+        "metric": METRIC,
+        "value": round(kv_bytes / us / 1e3, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5),
+        "us_per_step": round(us, 2),
+        "pct_hbm_peak": round(100 * kv_bytes / us / 1e3 / acc.HBM_PEAK_GBPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 in, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": w.num_seqs, "q_heads": w.num_q_heads,
+                   "kv_heads": w.num_kv_heads, "head_dim": 128, "block_size": 16,
+                   "context_sum": int(np.maximum(x.context_lens, 0).sum()),
+                   "context_min": int(x.context_lens.min()),
+                   "context_max": int(x.context_lens.max()),
+                   "prefetch": mode_names[mode], "waves_per_wg": plan["waves_per_wg"],
+                   "partition_blocks": plan["partition_blocks"],
+                   "num_partitions": plan["num_partitions"], "parallelism": "single GPU"},
+        "kv_bytes_per_step": kv_bytes,
+        "other_bytes_per_step": other_bytes,
+        "flops_per_step": flops,
+        "prefetch_modes": modes,
+        "stream_read_ceiling_GBps": round(stream_gbps, 1),
+        "pct_of_stream_ceiling": round(100 * kv_bytes / us / 1e3 / stream_gbps, 1),
+        "roofline": roofline,
+        "kernel_source_hash": kernel_source_hash(),
+        "inputs_sha256": {k: v[:16] for k, v in gen.digests(x).items()},
+    }
+
+    if not args.no_cpu_baseline:
+        from oracle import oracle as orc
+        got = out.cpu().numpy().astype(np.float64)
+        ref = None
+        runs = []
+        deadline = time.time() + args.cpu_seconds
+        while True:
+            t1 = time.perf_counter()
+            ref = orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                          x.context_lens, x.scale)
+            runs.append(time.perf_counter() - t1)
+            if time.time() > deadline or len(runs) >= 5:
+                break
+        t_cpu = sorted(runs)[len(runs) // 2]
+        diff = np.abs(got - ref)
+        result["cpu_baseline"] = {
+            "value": round(kv_bytes / t_cpu / 1e9, 3), "unit": "GB/s",
+            "us_per_step": round(t_cpu * 1e6, 1), "cores": orc.max_threads(), "kind": "oracle",
+            "sample": f"the whole {args.workload} step (all {w.num_seqs * w.num_q_heads} "
+                      f"(sequence, head) rows), fp64, median of {len(runs)} run(s)"}
+        result["parity"] = {"abs": float(diff.max()),
+                            "rel": float((diff / np.maximum(np.abs(ref), 1e-3)).max()),
+                            "rows_checked": int(w.num_seqs * w.num_q_heads)}
+        result["gpu_speedup_vs_cpu_oracle"] = round(t_cpu * 1e6 / us, 1)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

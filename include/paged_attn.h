@@ -23,11 +23,17 @@
  *    keeps no reference after a call returns and allocates nothing.
  *  - fp16 means IEEE binary16 bits.  Layouts are row-major:
  *        q, out       [num_seqs][num_q_heads][128]
- *        k_cache      [num_blocks][num_kv_heads][16][128]   (token-major)
- *        v_cache      [num_blocks][num_kv_heads][16][128]   (token-major)
+ *        k_cache      [num_blocks][num_kv_heads][16][16][8]
+ *                     (dim group g, token t, dim 8g+i): the 16 bytes of one
+ *                     token's dims 8g..8g+7 are one piece, and the 16 tokens'
+ *                     pieces of a group are 256 contiguous bytes
+ *        v_cache      [num_blocks][num_kv_heads][16][128]   (token, dim)
  *        block_tables [num_seqs][max_blocks_per_seq]  int32 physical block ids
  *        context_lens [num_seqs]                      int32 tokens to attend
- *    Each (block, kv head) slice is one contiguous 4 KiB piece.
+ *    Each (block, kv head) slice of K and of V is one contiguous 4 KiB piece.
+ *    K's grouping lets one 128-bit load per lane deliver an MFMA operand
+ *    (token on the lane's column, 8 dims in the lane) while every load
+ *    instruction still reads 1 KiB of contiguous memory.
  *  - All pointers must be 16-byte aligned; out must not alias an input.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream).  Argument checks are host-only and never read device memory.

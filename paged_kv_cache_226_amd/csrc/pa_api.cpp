@@ -50,14 +50,12 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   paged_attn_default_options(&d);
   if (!o) o = &d;
   if (o->reserved != 0) return PA_ERR_INVALID_ARG;
-  const int g = sh->num_q_heads / sh->num_kv_heads;
 
   int pf = o->prefetch < 0 ? kDefaultPrefetch : o->prefetch;
   if (pf > PA_PREFETCH_BOTH) return PA_ERR_INVALID_ARG;
 
   int waves = o->waves_per_wg == 0 ? kDefaultWaves : o->waves_per_wg;
   if (waves != 1 && waves != 2 && waves != 4 && waves != 8) return PA_ERR_INVALID_ARG;
-  if (g > 8 && waves > 4) return PA_ERR_UNSUPPORTED;  // register budget
 
   const int MB = sh->max_blocks_per_seq;
   int PB;
@@ -168,6 +166,7 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
   a.B = sh->num_seqs;
   a.Hq = sh->num_q_heads;
   a.Hkv = sh->num_kv_heads;
+  a.G = g;
   a.MB = sh->max_blocks_per_seq;
   a.P = pl.P;
   a.PB = pl.PB;
@@ -177,7 +176,7 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
   const bool dbg = o->debug_gather_k || o->debug_trace || o->debug_error_word;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (pa::launch_decode(a, g, pl.pf, dbg, pl.waves, st) != hipSuccess) return PA_ERR_HIP;
+  if (pa::launch_decode(a, pl.pf, dbg, pl.waves, st) != hipSuccess) return PA_ERR_HIP;
   if (pl.P > 1 && pa::launch_reduce(a, st) != hipSuccess) return PA_ERR_HIP;
   return PA_OK;
 }

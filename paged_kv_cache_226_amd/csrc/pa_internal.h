@@ -10,7 +10,7 @@ namespace pa {
 // Everything a decode launch needs, passed by value as the kernel argument.
 struct DecodeArgs {
   const uint16_t* q;     // [B][Hq][128] fp16
-  const uint16_t* k;     // [NB][Hkv][16][128] fp16
+  const uint16_t* k;     // [NB][Hkv][16 dim groups][16 tokens][8] fp16
   const uint16_t* v;     // [NB][Hkv][16][128] fp16
   const int32_t* bt;     // [B][MB]
   const int32_t* ctx;    // [B]
@@ -23,6 +23,7 @@ struct DecodeArgs {
   int32_t* sink;         // never written while sink_enable == 0
   float scale_log2;      // scale * log2(e)
   int B, Hq, Hkv, MB;
+  int G;                 // query heads per KV head, 1..16
   int P;                 // partitions in the grid
   int PB;                // blocks per partition
   int64_t NB;            // pool blocks
@@ -37,8 +38,7 @@ inline size_t decode_lds_bytes(int PB, int g, int waves) {
   return (size_t)lds_bt_bytes_for(PB) + (size_t)waves * g * (128 + 2) * 4;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int g, int pf, bool dbg, int waves,
-                         hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, int waves, hipStream_t st);
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_stream_read(const void* buf, size_t bytes, void* sink, int groups,
                               hipStream_t st);

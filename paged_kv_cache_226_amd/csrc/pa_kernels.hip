@@ -1,4 +1,4 @@
-// Paged decode attention kernels for gfx950 (CDNA4, wave64).
+// Paged decode attention kernels for gfx950 (CDNA4, wave64, MFMA).
 //
 // Method (asynchronous-KV-prefetch review, sections 3.2-3.4 and 4.1): a
 // work-group owns the block range [s, e) of one (sequence, KV head); its W
@@ -6,18 +6,31 @@
 // KV-cache-prefetching article, section 2.2, gives the same assignment for a
 // 4-warp block).  Before computing block j a wavefront issues the fetch of
 // block j+W, so the memory latency of the next block overlaps the compute of
-// the current one.  Q*K^T is computed per block against the Q heads held in
-// registers, then logits times V.
+// the current one.  Q*K^T is computed per block against Q held in registers,
+// then logits times V.
 //
-// Lane layout for one 16-token x 128-dim fp16 block (4 KiB, contiguous):
-//   lane l = 16 r + c  (row r = 0..3, column c = 0..15)
-//   load i (0..3) reads token 4i + r, dims 8c..8c+7: 16 bytes at byte offset
-//   1024 i + 16 l, so every load instruction covers 1 KiB of whole 128 B lines.
-// Q.K: each lane does 4 v_dot2_f32_f16 over its 8 dims; a 16-lane DPP
-// butterfly leaves the token's full dot product in every lane of the row.
-// Each row keeps its own online-softmax state (m, l, acc[8 dims per lane])
-// over the tokens 4i + r it owns, so the hot loop needs no cross-row traffic.
-// The 4 rows and then the W waves are merged once at the end.
+// One wavefront serves every query head of its KV head (GQA group g <= 16):
+// the heads are the 16 columns of the MFMA tiles, so the per-block cost does
+// not grow with g.  Lane l = 16*G + c (lane group G = 0..3, column c = 0..15)
+// holds head c.
+//
+// K block (layout [16 dim groups][16 tokens][8 dims], 4 KiB):
+//   Q.K^T = 4 x v_mfma_f32_16x16x32_f16, A = K (16 token rows), B = Q^T.
+//   For chunk ch, lane (G, c) loads the 16 bytes of dims 32ch+8G.. of token
+//   pi(c) = 4(c%4) + c/4: 1 KiB contiguous per load instruction.  The token
+//   permutation pi puts token 4q+G in output row 4G+q, i.e. lane (G, c) ends
+//   with the scores of tokens {4q + G : q = 0..3} for head c.
+// V block (layout [16 tokens][128 dims], 4 KiB):
+//   lane (G, c) loads tokens 4i+G (i = 0..3), dims 8c..8c+7: 1 KiB contiguous
+//   per load, and exactly the tokens whose probabilities it holds.
+//   O^T += V^T P^T as 8 dim tiles x v_mfma_f32_16x16x16f16; tile t takes dims
+//   {8c + t}.  P is split into fp16 hi + lo parts (two MFMAs per tile), so the
+//   weights enter with ~22 significant bits; products accumulate in fp32.
+//   Lane (G, c) ends with head c, dims 32G..32G+31.
+// Softmax: fp32 online softmax per head; the block maximum is shared by the
+// four lanes of a column (two cross-lane steps); the accumulator is rescaled
+// only when some head's running maximum changed (rescaling by 1 is exact, so
+// skipping it changes no bits).
 //
 // Look-ahead modes (PF): 0 none; 1 an L2 / Infinity-Cache touch of every
 // 128 B line of block j+W (one dword per lane, value discarded); 2 block j+W
@@ -31,55 +44,38 @@
 
 namespace pa {
 
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;
 constexpr int kT = 16;
 constexpr int kWave = 64;
 constexpr int kBlockHeadBytes = kD * kT * 2;  // 4096
-
-// DPP controls (gfx9 encoding).
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141; // row_half_mirror
-constexpr int kDppMirror = 0x140;     // row_mirror
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float x) {
-  return __int_as_float(
-      __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over the 16 lanes of a DPP row; every lane of the row gets the same bits
-// (each step adds two operands that are the same pair on both partners).
-__device__ __forceinline__ float row_sum16(float x) {
-  x += dpp_f32<kDppXor1>(x);
-  x += dpp_f32<kDppXor2>(x);
-  x += dpp_f32<kDppHalfMirror>(x);
-  x += dpp_f32<kDppMirror>(x);
-  return x;
-}
+constexpr int kRec = kD + 2;                  // merge record: m, l, o[128]
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ half2_t as_h2(uint32_t u) {
-  return __builtin_bit_cast(half2_t, u);
-}
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
+// Two fp16 values, one from each source dword: half h (0 = low, 1 = high) of
+// `lo` into the low half of the result, half h of `hi` into the high half.
+__device__ __forceinline__ uint32_t pick_halves(uint32_t lo, uint32_t hi, int h) {
+  return __builtin_amdgcn_perm(hi, lo, h ? 0x07060302u : 0x05040100u);
+}
+
 struct BlockBuf {
-  u32x4 k[4];
-  u32x4 v[4];
+  u32x4 k[4];  // chunk ch: token pi(c), dims 32ch+8G .. +7
+  u32x4 v[4];  // i: token 4i+G, dims 8c .. 8c+7
 };
 
 // ---------------------------------------------------------------------------
-template <int G, int PF, bool DBG>
-__global__ void __launch_bounds__(G <= 8 ? 512 : 256)
-pa_decode_kernel(const DecodeArgs a) {
+template <int PF, bool DBG>
+__global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   int32_t* bt_s = reinterpret_cast<int32_t*>(smem_raw);
   float* merge_s = reinterpret_cast<float*>(smem_raw + a.lds_bt_bytes);
@@ -87,12 +83,14 @@ pa_decode_kernel(const DecodeArgs a) {
   const int p = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
+  const int G = a.G;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int W = blockDim.x / kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int r = lane >> 4;
-  const int c = lane & 15;
+  const int lg = lane >> 4;                    // lane group 0..3
+  const int c = lane & 15;                     // column: head c of the group
+  const int pic = ((c & 3) << 2) | (c >> 2);   // token held in K row c
 
   int ctx = a.ctx[b];
   const int tab_tokens = a.MB * kT;
@@ -106,7 +104,7 @@ pa_decode_kernel(const DecodeArgs a) {
 
   if (s >= e) {
     // Nothing to attend in this partition.  With one partition the output
-    // row is written here (context <= 0 gives zeros); otherwise the reduce
+    // rows are written here (context <= 0 gives zeros); otherwise the reduce
     // kernel only reads partitions that hold blocks.
     if (a.P == 1) {
       for (int idx = tid; idx < G * kD; idx += blockDim.x) {
@@ -121,37 +119,37 @@ pa_decode_kernel(const DecodeArgs a) {
   const int32_t* bt_row = a.bt + (int64_t)b * a.MB;
   for (int i = tid; i < e - s; i += blockDim.x) bt_s[i] = bt_row[s + i];
 
-  // Q heads of this KV head: 8 dims (16 B) per lane per head.
-  half2_t qv[G][4];
+  // Q^T operand: lane (lg, c), chunk ch = dims 32ch+8lg .. +7 of head c
+  // (zero for the padding columns c >= G).
+  half8_t qb[4];
+  {
+    const int hc = c < G ? c : 0;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + kvh * G + hc) * kD + 8 * lg;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const u32x4 w4 = *reinterpret_cast<const u32x4*>(
-        a.q + ((int64_t)b * a.Hq + kvh * G + h) * kD + 8 * c);
-    qv[h][0] = as_h2(w4.x);
-    qv[h][1] = as_h2(w4.y);
-    qv[h][2] = as_h2(w4.z);
-    qv[h][3] = as_h2(w4.w);
+    for (int ch = 0; ch < 4; ++ch) {
+      u32x4 w4 = {0u, 0u, 0u, 0u};
+      if (c < G) w4 = *reinterpret_cast<const u32x4*>(qrow + 32 * ch);
+      qb[ch] = __builtin_bit_cast(half8_t, w4);
+    }
   }
   __syncthreads();
 
-  float m[G], l[G], acc[G][8];
+  float m = -INFINITY;  // running max of head c (log2 units), same in the 4 lanes
+  float l = 0.f;        // this lane's share of the softmax denominator
+  f32x4 acc[8];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) acc[h][d] = 0.f;
-  }
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const unsigned char* kbase =
       reinterpret_cast<const unsigned char*>(a.k) + (int64_t)kvh * kBlockHeadBytes;
   const unsigned char* vbase =
       reinterpret_cast<const unsigned char*>(a.v) + (int64_t)kvh * kBlockHeadBytes;
-  const int lane_off = lane * 16;
+  const int k_off = (lg * kT + pic) * 16;
+  const int v_off = lane * 16;
 
   auto load_block = [&](BlockBuf& buf, int64_t ph) {
-    const unsigned char* kb = kbase + ph * a.blk_bytes + lane_off;
-    const unsigned char* vb = vbase + ph * a.blk_bytes + lane_off;
+    const unsigned char* kb = kbase + ph * a.blk_bytes + k_off;
+    const unsigned char* vb = vbase + ph * a.blk_bytes + v_off;
 #pragma unroll
     for (int i = 0; i < 4; ++i) buf.k[i] = *reinterpret_cast<const u32x4*>(kb + 1024 * i);
 #pragma unroll
@@ -173,61 +171,61 @@ pa_decode_kernel(const DecodeArgs a) {
   auto compute = [&](BlockBuf& buf, int j) {
     if (DBG && a.dbg_k) {
       unsigned char* dst = reinterpret_cast<unsigned char*>(a.dbg_k) +
-                           ((((int64_t)b * a.Hkv + kvh) * a.MB + j) * kT) * kD * 2 +
-                           lane_off;
+                           ((((int64_t)b * a.Hkv + kvh) * a.MB + j) * kT + pic) * kD * 2 +
+                           lg * 16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + 1024 * i) = buf.k[i];
+      for (int ch = 0; ch < 4; ++ch) *reinterpret_cast<u32x4*>(dst + 64 * ch) = buf.k[ch];
     }
-    const int tok0 = j * kT + r;  // this row's token for i = 0; +4 per i
-    const bool tail = j * kT + kT > ctx;
+    const int rem = ctx - j * kT;  // valid tokens in this block, >= 1
+    const bool tail = rem < kT;
     if (tail) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (tok0 + 4 * i >= ctx) buf.v[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int i = 0; i < 4; ++i)
+        if (4 * i + lg >= rem) buf.v[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+    // scores of tokens 4q+lg for head c
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, buf.k[ch]),
+                                                     qb[ch], sacc, 0, 0, 0);
+    float sc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sc[q] = sacc[q] * a.scale_log2;
+    if (tail) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (4 * q + lg >= rem) sc[q] = -INFINITY;
+    }
+    float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float m_new = fmaxf(m, bm);  // finite: every block has a valid token
+    const float alpha = fast_exp2(m - m_new);
+    float pr[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pr[q] = fast_exp2(sc[q] - m_new);
+    l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m = m_new;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+    }
+    half4_t phi, plo;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      phi[q] = (_Float16)pr[q];
+      plo[q] = (_Float16)(pr[q] - (float)phi[q]);
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float sc[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float d = 0.f;
-        d = __builtin_amdgcn_fdot2(qv[h][0], as_h2(buf.k[i].x), d, false);
-        d = __builtin_amdgcn_fdot2(qv[h][1], as_h2(buf.k[i].y), d, false);
-        d = __builtin_amdgcn_fdot2(qv[h][2], as_h2(buf.k[i].z), d, false);
-        d = __builtin_amdgcn_fdot2(qv[h][3], as_h2(buf.k[i].w), d, false);
-        sc[i] = row_sum16(d) * a.scale_log2;
-      }
-      float m_use;
-      float m_new;
-      if (tail) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (tok0 + 4 * i >= ctx) sc[i] = -INFINITY;
-        m_new = fmaxf(m[h], fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-        m_use = m_new == -INFINITY ? 0.f : m_new;
-      } else {
-        m_new = fmaxf(m[h], fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-        m_use = m_new;
-      }
-      const float alpha = fast_exp2(m[h] - m_use);
-      float pr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(sc[i] - m_use);
-      l[h] = l[h] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-      m[h] = m_new;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) acc[h][d] *= alpha;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t vw[4] = {buf.v[i].x, buf.v[i].y, buf.v[i].z, buf.v[i].w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const half2_t hv = as_h2(vw[u]);
-          acc[h][2 * u] = __builtin_fmaf(pr[i], (float)hv.x, acc[h][2 * u]);
-          acc[h][2 * u + 1] = __builtin_fmaf(pr[i], (float)hv.y, acc[h][2 * u + 1]);
-        }
-      }
+    for (int t = 0; t < 8; ++t) {
+      const int u = t >> 1, h = t & 1;
+      u32x2 vt;
+      vt.x = pick_halves(buf.v[0][u], buf.v[1][u], h);
+      vt.y = pick_halves(buf.v[2][u], buf.v[3][u], h);
+      const half4_t av = __builtin_bit_cast(half4_t, vt);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, phi, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, plo, acc[t], 0, 0, 0);
     }
   };
 
@@ -345,40 +343,19 @@ pa_decode_kernel(const DecodeArgs a) {
   // storing (a.sink_enable is 0 in every call).
   if (a.sink_enable && sink == 0x9E3779B9u && lane == 0) a.sink[0] = (int32_t)sink;
 
-  // ---- merge the 4 rows of each wave (lanes l, l^16, l^32, l^48) ----------
-#pragma unroll
-  for (int step = 16; step <= 32; step *= 2) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], step);
-      const float lo = __shfl_xor(l[h], step);
-      const float M = fmaxf(m[h], mo);
-      const float Mu = M == -INFINITY ? 0.f : M;
-      const float as = fast_exp2(m[h] - Mu);
-      const float ao = fast_exp2(mo - Mu);
-      l[h] = l[h] * as + lo * ao;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const float oo = __shfl_xor(acc[h][d], step);
-        acc[h][d] = acc[h][d] * as + oo * ao;
-      }
-      m[h] = M;
+  // ---- merge: the 4 lanes of a column, then the W waves through LDS -------
+  float lt = l + __shfl_xor(l, 16);
+  lt += __shfl_xor(lt, 32);
+  if (c < G) {
+    float* rec = merge_s + (wave * G + c) * kRec;
+    if (lg == 0) {
+      rec[0] = m;
+      rec[1] = lt;
     }
-  }
-
-  // ---- merge the W waves through LDS --------------------------------------
-  constexpr int kRec = kD + 2;  // m, l, o[128]
-  if (r == 0) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float* rec = merge_s + (wave * G + h) * kRec;
-      if (c == 0) {
-        rec[0] = m[h];
-        rec[1] = l[h];
-      }
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int d = 0; d < 8; ++d) rec[2 + 8 * c + d] = acc[h][d];
-    }
+      for (int t = 0; t < 8; ++t) rec[2 + 32 * lg + 8 * q + t] = acc[t][q];
   }
   __syncthreads();
 
@@ -436,20 +413,21 @@ __global__ void __launch_bounds__(128) pa_reduce_kernel(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Streaming-read ceiling: every 16-byte word of buf read once.
+// Streaming-read ceiling: every 16-byte word of buf read once, eight loads in
+// flight per lane, non-temporal.
 __global__ void __launch_bounds__(256) stream_read_kernel(const u32x4* __restrict__ buf,
                                                           int64_t n16, u32x4* sink) {
   const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   u32x4 x = {0u, 0u, 0u, 0u};
-  for (; i + 3 * nthreads < n16; i += 4 * nthreads) {
-    const u32x4 a0 = buf[i];
-    const u32x4 a1 = buf[i + nthreads];
-    const u32x4 a2 = buf[i + 2 * nthreads];
-    const u32x4 a3 = buf[i + 3 * nthreads];
-    x ^= a0 ^ a1 ^ a2 ^ a3;
+  for (; i + 7 * nthreads < n16; i += 8 * nthreads) {
+    u32x4 r[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r[k] = __builtin_nontemporal_load(buf + i + k * nthreads);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x ^= r[k];
   }
-  for (; i < n16; i += nthreads) x ^= buf[i];
+  for (; i < n16; i += nthreads) x ^= __builtin_nontemporal_load(buf + i);
   // reduce within the work-group so only one value per group is stored
   __shared__ u32x4 red[256];
   red[threadIdx.x] = x;
@@ -464,59 +442,23 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const u32x4* __restric
 // ---------------------------------------------------------------------------
 // Launchers.
 
-template <int G, int PF, bool DBG>
-static hipError_t launch_decode_t(const DecodeArgs& a, dim3 grid, dim3 block,
-                                  size_t lds, hipStream_t st) {
-  hipLaunchKernelGGL((pa_decode_kernel<G, PF, DBG>), grid, block, lds, st, a);
+template <int PF, bool DBG>
+static hipError_t launch_decode_t(const DecodeArgs& a, dim3 grid, dim3 block, size_t lds,
+                                  hipStream_t st) {
+  hipLaunchKernelGGL((pa_decode_kernel<PF, DBG>), grid, block, lds, st, a);
   return hipGetLastError();
 }
 
-typedef hipError_t (*decode_fn)(const DecodeArgs&, dim3, dim3, size_t, hipStream_t);
-
-template <int G>
-static decode_fn pick_pf(int pf, bool dbg) {
-  switch (pf * 2 + (dbg ? 1 : 0)) {
-    case 0: return launch_decode_t<G, 0, false>;
-    case 1: return launch_decode_t<G, 0, true>;
-    case 2: return launch_decode_t<G, 1, false>;
-    case 3: return launch_decode_t<G, 1, true>;
-    case 4: return launch_decode_t<G, 2, false>;
-    case 5: return launch_decode_t<G, 2, true>;
-    case 6: return launch_decode_t<G, 3, false>;
-    case 7: return launch_decode_t<G, 3, true>;
-  }
-  return nullptr;
-}
-
-static decode_fn pick(int g, int pf, bool dbg) {
-  switch (g) {
-    case 1: return pick_pf<1>(pf, dbg);
-    case 2: return pick_pf<2>(pf, dbg);
-    case 3: return pick_pf<3>(pf, dbg);
-    case 4: return pick_pf<4>(pf, dbg);
-    case 5: return pick_pf<5>(pf, dbg);
-    case 6: return pick_pf<6>(pf, dbg);
-    case 7: return pick_pf<7>(pf, dbg);
-    case 8: return pick_pf<8>(pf, dbg);
-    case 9: return pick_pf<9>(pf, dbg);
-    case 10: return pick_pf<10>(pf, dbg);
-    case 11: return pick_pf<11>(pf, dbg);
-    case 12: return pick_pf<12>(pf, dbg);
-    case 13: return pick_pf<13>(pf, dbg);
-    case 14: return pick_pf<14>(pf, dbg);
-    case 15: return pick_pf<15>(pf, dbg);
-    case 16: return pick_pf<16>(pf, dbg);
-  }
-  return nullptr;
-}
-
-hipError_t launch_decode(const DecodeArgs& a, int g, int pf, bool dbg, int waves,
-                         hipStream_t st) {
-  decode_fn fn = pick(g, pf, dbg);
-  if (!fn) return hipErrorInvalidValue;
+hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, int waves, hipStream_t st) {
+  typedef hipError_t (*fn_t)(const DecodeArgs&, dim3, dim3, size_t, hipStream_t);
+  static const fn_t table[8] = {
+      launch_decode_t<0, false>, launch_decode_t<0, true>, launch_decode_t<1, false>,
+      launch_decode_t<1, true>,  launch_decode_t<2, false>, launch_decode_t<2, true>,
+      launch_decode_t<3, false>, launch_decode_t<3, true>};
+  if (pf < 0 || pf > 3) return hipErrorInvalidValue;
   const dim3 grid(a.P, a.Hkv, a.B);
   const dim3 block(kWave * waves);
-  return fn(a, grid, block, decode_lds_bytes(a.PB, g, waves), st);
+  return table[pf * 2 + (dbg ? 1 : 0)](a, grid, block, decode_lds_bytes(a.PB, a.G, waves), st);
 }
 
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t st) {

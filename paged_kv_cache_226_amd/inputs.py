@@ -193,6 +193,22 @@ def apply_poison(x: PagedInputs) -> None:
     x.v_cache[~used] = nan
 
 
+def pack_k(k_cache: np.ndarray) -> np.ndarray:
+    """K pool in the kernel's layout [NB][Hkv][D/8][T][8]: inside a 4 KiB
+    (block, head) slice, the 16 tokens' values of dims 8g..8g+7 are 256
+    contiguous bytes (group g), so one 16-byte piece holds 8 dims of one
+    token.  A pure reindexing: unpack_k(pack_k(k)) == k bit for bit."""
+    NB, H, T, D = k_cache.shape
+    return np.ascontiguousarray(
+        k_cache.reshape(NB, H, T, D // 8, 8).transpose(0, 1, 3, 2, 4))
+
+
+def unpack_k(k_packed: np.ndarray) -> np.ndarray:
+    """Inverse of pack_k: back to token-major [NB][Hkv][T][D]."""
+    NB, H, G8, T, X = k_packed.shape
+    return np.ascontiguousarray(k_packed.transpose(0, 1, 3, 2, 4).reshape(NB, H, T, G8 * X))
+
+
 def digests(x: PagedInputs) -> Dict[str, str]:
     """SHA-256 of every array, to log which exact inputs a result came from."""
     out = {}

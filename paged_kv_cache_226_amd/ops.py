@@ -33,8 +33,8 @@ def _check(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int):
 
 def shape_of(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor) -> nat.PaShape:
     B, Hq, D = q.shape
-    NB, Hkv, T, Dk = k_cache.shape
-    return nat.make_shape(B, Hq, Hkv, block_tables.shape[1], NB, head_dim=D, block_size=T)
+    NB, Hkv, G8, T, X = k_cache.shape
+    return nat.make_shape(B, Hq, Hkv, block_tables.shape[1], NB, head_dim=G8 * X, block_size=T)
 
 
 def options(prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0) -> nat.PaOptions:
@@ -65,18 +65,20 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
     """One decode step of paged attention; returns out (fp16 [B, Hq, 128]).
 
-    q [B, Hq, 128] fp16; k_cache, v_cache [NB, Hkv, 16, 128] fp16; block_tables
-    [B, MB] int32; context_lens [B] int32; scale defaults to 1/sqrt(128).
+    q [B, Hq, 128] fp16; k_cache [NB, Hkv, 16, 16, 8] fp16 (dim group, token, 8
+    dims); v_cache [NB, Hkv, 16, 128] fp16 (token, dim); block_tables [B, MB]
+    int32; context_lens [B] int32; scale defaults to 1/sqrt(128).
     """
     _check(q, "q", torch.float16, 3)
-    _check(k_cache, "k_cache", torch.float16, 4)
+    _check(k_cache, "k_cache", torch.float16, 5)
     _check(v_cache, "v_cache", torch.float16, 4)
     _check(block_tables, "block_tables", torch.int32, 2)
     _check(context_lens, "context_lens", torch.int32, 1)
-    if v_cache.shape != k_cache.shape:
-        raise ValueError("k_cache and v_cache shapes differ")
+    NB, Hkv, G8, T, X = k_cache.shape
     B, Hq, D = q.shape
-    if block_tables.shape[0] != B or context_lens.shape[0] != B or k_cache.shape[3] != D:
+    if tuple(v_cache.shape) != (NB, Hkv, T, G8 * X) or G8 * X != D:
+        raise ValueError("k_cache must be [NB, Hkv, D/8, T, 8] and v_cache [NB, Hkv, T, D]")
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("inconsistent shapes")
     if scale is None:
         scale = D ** -0.5

@@ -12,6 +12,7 @@ import numpy as np
 import torch
 
 from oracle import oracle as orc
+from paged_kv_cache_226_amd import inputs as gen
 from paged_kv_cache_226_amd import ops
 
 ABS_TOL = 2e-3
@@ -21,7 +22,7 @@ REL_FLOOR = 1e-3
 
 def to_device(x, device="cuda"):
     return dict(q=torch.from_numpy(x.q).to(device),
-                k_cache=torch.from_numpy(x.k_cache).to(device),
+                k_cache=torch.from_numpy(gen.pack_k(x.k_cache)).to(device),
                 v_cache=torch.from_numpy(x.v_cache).to(device),
                 block_tables=torch.from_numpy(x.block_tables).to(device),
                 context_lens=torch.from_numpy(x.context_lens).to(device))

@@ -83,8 +83,6 @@ def good_shape(**kw):
     (dict(opts=dict(reserved=1)), nat.PA_ERR_INVALID_ARG),
     (dict(opts=dict(partition_blocks=-1)), nat.PA_ERR_INVALID_ARG),
     (dict(opts=dict(partition_blocks=2048)), nat.PA_ERR_UNSUPPORTED),
-    (dict(shape=dict(num_q_heads=32, num_kv_heads=2), opts=dict(waves_per_wg=8)),
-     nat.PA_ERR_UNSUPPORTED),
     # 4096 blocks per sequence need several partitions: no workspace given
     (dict(), nat.PA_ERR_WORKSPACE),
     (dict(opts=dict(workspace=FAKE, workspace_bytes=16)), nat.PA_ERR_WORKSPACE),

@@ -62,3 +62,15 @@ def test_poison_covers_exactly_the_unread_bytes():
             read[x.block_tables[b, t // 16], :, t % 16, :] = True
     assert np.array_equal(k, ~read)
     assert np.array_equal(np.isnan(x.v_cache.astype(np.float32)), ~read)
+
+
+def test_pack_k_is_a_bijective_reindexing():
+    x = gen.make_case(2, 4, 2, [40, 17], seed=9, extra_pool_blocks=1)
+    kp = gen.pack_k(x.k_cache)
+    NB, H = x.k_cache.shape[:2]
+    assert kp.shape == (NB, H, 16, 16, 8)
+    assert np.array_equal(gen.unpack_k(kp).view(np.uint16), x.k_cache.view(np.uint16))
+    # piece (group g, token t) holds dims 8g..8g+7 of token t
+    for (p, h, g, t) in [(0, 0, 0, 0), (3, 1, 15, 15), (5, 0, 7, 2)]:
+        assert np.array_equal(kp[p, h, g, t].view(np.uint16),
+                              x.k_cache[p, h, t, 8 * g:8 * g + 8].view(np.uint16))
