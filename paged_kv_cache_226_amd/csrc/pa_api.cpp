@@ -14,9 +14,11 @@ namespace {
 constexpr int kDefaultPrefetch = PA_PREFETCH_REG;
 constexpr int kDefaultWaves = 4;
 constexpr int kMaxPartitionBlocks = 1024;  // LDS slice of the block table: 4 KiB
-// Work-groups the auto plan aims for before it splits contexts: four
-// work-groups of four wavefronts per compute unit on 256 CUs.
+// The auto plan: at least this many work-groups (four per compute unit on
+// 256 CUs) and at most kAutoPartitionBlocks blocks (1 MiB of K and V) per
+// work-group, so ragged batches split into similar-sized pieces.
 constexpr int64_t kTargetWorkgroups = 1024;
+constexpr int kAutoPartitionBlocks = 128;
 
 struct Plan {
   int pf, waves, PB, P;
@@ -36,7 +38,7 @@ int check_shape(const pa_shape* sh) {
     return PA_ERR_UNSUPPORTED;
   const int g = sh->num_q_heads / sh->num_kv_heads;
   if (g > PA_G_MAX) return PA_ERR_UNSUPPORTED;
-  // grid.y = Hkv and grid.z = B must fit the launch limits.
+  // grid.x = Hkv and grid.y = B must fit the launch limits.
   if (sh->num_kv_heads > 65535 || sh->num_seqs > 65535) return PA_ERR_UNSUPPORTED;
   // Byte offsets of the pool must fit int64.
   if (sh->num_blocks > (INT64_MAX / 8192) / sh->num_kv_heads) return PA_ERR_UNSUPPORTED;
@@ -68,6 +70,7 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
     int64_t want = (kTargetWorkgroups + units - 1) / units;
     if (want < 1) want = 1;
     int64_t pb = (MB + want - 1) / want;
+    if (pb > kAutoPartitionBlocks) pb = kAutoPartitionBlocks;
     pb = (pb + waves - 1) / waves * waves;       // whole rounds of the W waves
     if (pb < 2 * waves) pb = 2 * waves;           // at least two blocks per wave
     if (pb > kMaxPartitionBlocks) pb = kMaxPartitionBlocks;
@@ -75,6 +78,7 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
     PB = (int)pb;
   }
   const int P = (MB + PB - 1) / PB;
+  if (P > 65535) return PA_ERR_UNSUPPORTED;  // grid.z
   pl->pf = pf;
   pl->waves = waves;
   pl->PB = PB;

@@ -80,9 +80,12 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
   int32_t* bt_s = reinterpret_cast<int32_t*>(smem_raw);
   float* merge_s = reinterpret_cast<float*>(smem_raw + a.lds_bt_bytes);
 
-  const int p = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  // Partition index slowest: every sequence's first partition is dispatched
+  // before any second one, so the large work-groups of a ragged batch start
+  // first and the short tail partitions fill in behind them.
+  const int kvh = blockIdx.x;
+  const int b = blockIdx.y;
+  const int p = blockIdx.z;
   const int G = a.G;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -147,13 +150,17 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
   const int k_off = (lg * kT + pic) * 16;
   const int v_off = lane * 16;
 
+  // K/V are streamed: every byte is used once, by this wave, so the loads
+  // are non-temporal (they do not displace lines that will be reused).  The
+  // L2 touch of the look-ahead modes is an ordinary load: it is meant to
+  // leave its lines in the cache.
   auto load_block = [&](BlockBuf& buf, int64_t ph) {
     const unsigned char* kb = kbase + ph * a.blk_bytes + k_off;
     const unsigned char* vb = vbase + ph * a.blk_bytes + v_off;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) buf.k[i] = *reinterpret_cast<const u32x4*>(kb + 1024 * i);
+    for (int i = 0; i < 4; ++i) buf.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + 1024 * i));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) buf.v[i] = *reinterpret_cast<const u32x4*>(vb + 1024 * i);
+    for (int i = 0; i < 4; ++i) buf.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + 1024 * i));
   };
 
   // One dword per lane: lanes 0-31 cover the 32 lines of the K block, lanes
@@ -456,7 +463,7 @@ hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, int waves, hipSt
       launch_decode_t<1, true>,  launch_decode_t<2, false>, launch_decode_t<2, true>,
       launch_decode_t<3, false>, launch_decode_t<3, true>};
   if (pf < 0 || pf > 3) return hipErrorInvalidValue;
-  const dim3 grid(a.P, a.Hkv, a.B);
+  const dim3 grid(a.Hkv, a.B, a.P);
   const dim3 block(kWave * waves);
   return table[pf * 2 + (dbg ? 1 : 0)](a, grid, block, decode_lds_bytes(a.PB, a.G, waves), st);
 }

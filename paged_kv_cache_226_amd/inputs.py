@@ -176,6 +176,17 @@ def make_inputs(workload, *, poison: bool = False) -> PagedInputs:
                      poison=poison, name=w.name)
 
 
+def workload_context_lens(workload) -> np.ndarray:
+    """The context lengths make_inputs(workload) draws, without drawing the
+    pools (the lengths are the first draw of the seeded stream)."""
+    w = WORKLOADS[workload] if isinstance(workload, str) else workload
+    if w.ctx_range is not None:
+        rng = np.random.default_rng(w.seed)
+        lo, hi = w.ctx_range
+        return rng.integers(lo, hi + 1, size=w.num_seqs).astype(np.int32)
+    return np.asarray(w.context_lens, dtype=np.int32)
+
+
 def apply_poison(x: PagedInputs) -> None:
     """NaN into every pool byte that no (sequence, token < ctx) refers to."""
     T = x.k_cache.shape[2]

@@ -1,0 +1,175 @@
+"""Summarise rocprofv3 CSV output of bench.py into short text reports.
+
+    python -m paged_kv_cache_226_amd.rocprof_summary --workload llama2_7b \
+        --kernel-trace DIR [--fetch DIR --write DIR --tcc DIR --sq DIR] \
+        --command "..." --out-dir profiles
+
+Inputs are the directories rocprofv3 wrote with `--output-format csv`
+(`*_kernel_stats.csv`, `*_counter_collection.csv`).  Writes:
+  pa_decode_<workload>_kernel_trace.md   per-kernel durations
+  pa_decode_<workload>_counters.md       per prefetch mode: HBM bytes, L2 hit
+                                         rate, stall share, instructions
+  pa_decode_<workload>_traffic.txt       HBM bytes per launch, read by bench.py
+                                         while the kernel sources are unchanged
+
+FETCH_SIZE and WRITE_SIZE are scaled by what the same counters read for
+kernels of known size in the same process (bench.py --profile runs a 1 GiB
+streaming read and a 1 GiB fp16 elementwise copy).
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import os
+import re
+import sys
+
+MODE_NAMES = {0: "off", 1: "l2", 2: "reg", 3: "both"}
+DECODE_RE = re.compile(r"pa_decode_kernel<(\d), (true|false)>")
+
+
+def _rows(d, suffix):
+    out = []
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def counters(d):
+    """{(kernel name, counter): [values per dispatch]}"""
+    agg = collections.defaultdict(list)
+    for r in _rows(d, "_counter_collection.csv"):
+        agg[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+    return agg
+
+
+def mean(v):
+    return sum(v) / len(v) if v else float("nan")
+
+
+def decode_mode(name):
+    m = DECODE_RE.search(name)
+    if not m or m.group(2) != "false":
+        return None
+    return int(m.group(1))
+
+
+def per_mode(agg, counter):
+    out = {}
+    for (k, c), v in agg.items():
+        if c == counter and decode_mode(k) is not None:
+            out[decode_mode(k)] = mean(v)
+    return out
+
+
+def calibration(agg, counter, kind):
+    """Known bytes / counter bytes for a calibration kernel."""
+    best = None
+    for (k, c), v in agg.items():
+        if c != counter:
+            continue
+        if kind == "stream" and "stream_read_kernel" in k:
+            best = mean(v)
+        if kind == "copy" and "elementwise_kernel" in k:
+            val = mean(v)
+            if best is None or val > best:
+                best = val
+    if not best:
+        return None
+    return (1 << 30) / (best * 1024.0)
+
+
+def kernel_stats(d):
+    rows = _rows(d, "_kernel_stats.csv")
+    return [(r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+             float(r["MaxNs"]) / 1e3, float(r["Percentage"])) for r in rows]
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--kernel-trace")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--tcc")
+    ap.add_argument("--sq")
+    ap.add_argument("--command", default="", help="the command lines that produced the inputs")
+    ap.add_argument("--source-hash", default="")
+    ap.add_argument("--out-dir", default="profiles")
+    a = ap.parse_args(argv)
+
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from paged_kv_cache_226_amd import accounting as acc
+    from paged_kv_cache_226_amd import inputs as gen
+
+    w = gen.WORKLOADS[a.workload]
+    ctx = gen.workload_context_lens(w)
+    kv = acc.step_kv_bytes(w.num_kv_heads, 128, ctx)
+    other = acc.step_other_bytes(w.num_seqs, w.num_q_heads, 128, ctx)
+    os.makedirs(a.out_dir, exist_ok=True)
+    head = [f"workload: {a.workload} ({w.description})",
+            f"algorithmic KV bytes per launch: {kv}  (Q, output, block tables: {other})",
+            "command:", *["    " + c for c in a.command.split(" ;; ") if c]]
+
+    if a.kernel_trace:
+        lines = ["# pa_decode kernel trace: " + a.workload, "", "```", *head, "```", "",
+                 "| kernel | calls | avg us | min us | max us | % time | effective KV GB/s |",
+                 "|---|---|---|---|---|---|---|"]
+        for name, calls, avg, mn, mx, pct in sorted(kernel_stats(a.kernel_trace),
+                                                     key=lambda r: -r[5]):
+            gbps = f"{kv / avg / 1e3:.0f}" if decode_mode(name) is not None else ""
+            lines.append(f"| `{name[:70]}` | {calls} | {avg:.2f} | {mn:.2f} | {mx:.2f} | "
+                         f"{pct:.1f} | {gbps} |")
+        with open(os.path.join(a.out_dir, f"pa_decode_{a.workload}_kernel_trace.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+
+    if a.fetch and a.write:
+        fa, wa = counters(a.fetch), counters(a.write)
+        fk_stream = calibration(fa, "FETCH_SIZE", "stream")
+        fk_copy = calibration(fa, "FETCH_SIZE", "copy")
+        wk_copy = calibration(wa, "WRITE_SIZE", "copy")
+        fk = fk_stream or fk_copy
+        fetch = per_mode(fa, "FETCH_SIZE")
+        write = per_mode(wa, "WRITE_SIZE")
+        tcc = counters(a.tcc) if a.tcc else {}
+        hit, miss = per_mode(tcc, "TCC_HIT"), per_mode(tcc, "TCC_MISS")
+        sq = counters(a.sq) if a.sq else {}
+        wait, wcyc = per_mode(sq, "SQ_WAIT_INST_ANY"), per_mode(sq, "SQ_WAVE_CYCLES")
+        valu, waves = per_mode(sq, "SQ_INSTS_VALU"), per_mode(sq, "SQ_WAVES")
+        vmem = per_mode(sq, "SQ_INSTS_VMEM_RD")
+        lines = ["# pa_decode counters per look-ahead mode: " + a.workload, "", "```", *head,
+                 f"FETCH_SIZE scale: {fk_stream} (1 GiB streaming read), {fk_copy} (1 GiB copy)",
+                 f"WRITE_SIZE scale: {wk_copy} (1 GiB copy)", "```", "",
+                 "| mode | HBM read bytes | read / algorithmic | HBM write bytes | L2 hit rate |"
+                 " stall share (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES) | VALU insts / wave |"
+                 " VMEM reads / wave |",
+                 "|---|---|---|---|---|---|---|---|"]
+        traffic = {}
+        for m in sorted(fetch):
+            rb = fetch[m] * 1024 * fk if fk else float("nan")
+            wb = write.get(m, float("nan")) * 1024 * (wk_copy or 1.0)
+            traffic[m] = rb + wb
+            hr = hit[m] / (hit[m] + miss[m]) if m in hit and (hit[m] + miss[m]) else float("nan")
+            st = wait[m] / wcyc[m] if m in wait and wcyc.get(m) else float("nan")
+            vw = valu[m] / waves[m] if m in valu and waves.get(m) else float("nan")
+            mw = vmem[m] / waves[m] if m in vmem and waves.get(m) else float("nan")
+            lines.append(f"| {MODE_NAMES[m]} | {rb:.4g} | {rb / kv:.4f} | {wb:.4g} | "
+                         f"{100 * hr:.2f} % | {100 * st:.1f} % | {vw:.0f} | {mw:.0f} |")
+        with open(os.path.join(a.out_dir, f"pa_decode_{a.workload}_counters.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        with open(os.path.join(a.out_dir, f"pa_decode_{a.workload}_traffic.txt"), "w") as f:
+            f.write("# HBM bytes per decode-kernel launch (FETCH_SIZE + WRITE_SIZE, scaled)\n")
+            f.write(f"# workload: {a.workload}\n")
+            f.write(f"kernel_source_hash: {a.source_hash}\n")
+            f.write(f"fetch_scale: {fk}\nwrite_scale: {wk_copy}\n")
+            f.write(f"algorithmic_kv_bytes: {kv}\n")
+            for m, v in sorted(traffic.items()):
+                f.write(f"hbm_bytes_per_launch_{MODE_NAMES[m]}: {v:.0f}\n")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -74,3 +74,13 @@ def test_pack_k_is_a_bijective_reindexing():
     for (p, h, g, t) in [(0, 0, 0, 0), (3, 1, 15, 15), (5, 0, 7, 2)]:
         assert np.array_equal(kp[p, h, g, t].view(np.uint16),
                               x.k_cache[p, h, t, 8 * g:8 * g + 8].view(np.uint16))
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama3_8b"])
+def test_workload_context_lens_matches_generation(name):
+    w = gen.WORKLOADS[name]
+    if name == "llama3_8b":  # same draw order at a small head_dim
+        import dataclasses
+        w = dataclasses.replace(w, head_dim=8)
+    x = gen.make_inputs(w)
+    assert np.array_equal(gen.workload_context_lens(w), x.context_lens)
