@@ -106,8 +106,7 @@ def main():
     other_bytes = acc.step_other_bytes(w.num_seqs, w.num_q_heads, 128, x.context_lens)
     flops = acc.step_flops(w.num_q_heads, 128, x.context_lens)
     plan = ops.plan(d["q"], d["k_cache"], d["block_tables"], prefetch=args.prefetch)
-    ws_bytes = plan["workspace_bytes"]
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws = ops.new_workspace(d["q"], d["k_cache"], d["block_tables"], prefetch=args.prefetch)
     stream = torch.cuda.current_stream()
 
     def step(pf):

@@ -17,6 +17,14 @@
  * issues the fetch of block j + w (when j + w < e) so that its memory latency
  * overlaps the compute of block j.  `pa_options.prefetch` chooses how that
  * fetch is made; results are bitwise identical in every mode.
+
+ *
+ * Ranges are split-context partitions of partition_blocks blocks, one
+ * work-group each (grid: KV head x sequence x partition); when a sequence
+ * has several, a second kernel merges their partial softmax states (the
+ * answer's "reduce output" step).  Results are deterministic for a given
+ * plan; different partition sizes or wave counts round differently (all
+ * within the fp32 accumulation error).
  *
  * Conventions
  *  - Tensor pointers are DEVICE pointers, owned by the caller; the library
@@ -47,7 +55,12 @@
  *    context_lens[b] <= 0 yields an all-zero output row.
  *  - Return values are PA_* status codes; nothing is printed, nothing aborts,
  *    no C++ exception crosses this boundary.
- *  - Calls are reentrant for distinct out / workspace / debug buffers.
+ *  - Calls are reentrant for distinct out / workspace / debug buffers.  Two
+ *    calls that overlap in time must not share a workspace.
+ *  - Workspace (when the plan has several partitions, see
+ *    paged_attn_workspace_size): device memory owned by the caller, 16-byte
+ *    aligned, any contents; it holds fp32 partial states between the two
+ *    kernels of one call.
  */
 #ifndef PAGED_ATTN_H
 #define PAGED_ATTN_H
@@ -94,7 +107,10 @@ typedef struct pa_shape {
 
 typedef struct pa_options {
     int32_t prefetch;          /* enum pa_prefetch; negative = library default */
-    int32_t partition_blocks;  /* blocks per split-context partition; 0 = auto */
+    int32_t partition_blocks;  /* blocks per split-context partition; 0 = auto:
+                                  one partition per sequence when the batch has
+                                  at least 1024 (sequence, KV head) pairs, else
+                                  partitions of at most 128 blocks */
     int32_t waves_per_wg;      /* w in {1, 2, 4, 8}; 0 = auto */
     int32_t reserved;          /* must be 0 */
     void *workspace;           /* device scratch for partition partials; may be
@@ -144,9 +160,10 @@ int paged_attn_plan(const pa_shape *shape, const pa_options *opts,
 size_t paged_attn_workspace_size(const pa_shape *shape, const pa_options *opts);
 
 /* Streaming-read ceiling: reads `bytes` (a multiple of 16, 16-byte aligned)
-   from device buffer `buf` once with the same 128-bit loads the decode kernel
-   uses and writes one 16-byte value per work-group into `sink` (device, at
-   least paged_attn_stream_read_sink_bytes(bytes) bytes). */
+   from device buffer `buf` once, in 8 KiB chunks per wavefront of the same
+   non-temporal 128-bit loads the decode kernel uses, and writes one 16-byte
+   XOR per work-group into `sink` (device, at least
+   paged_attn_stream_read_sink_bytes(bytes) bytes). */
 int paged_attn_stream_read(const void *buf, size_t bytes, void *sink,
                            void *stream);
 size_t paged_attn_stream_read_sink_bytes(size_t bytes);

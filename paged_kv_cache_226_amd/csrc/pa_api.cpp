@@ -1,5 +1,5 @@
 // C ABI of the paged decode-attention library: argument checks, the launch
-// plan (work-group size, split-context partitions, workspace) and dispatch.
+// plan (scheduling mode, work-group size, workspace) and dispatch.
 // Everything here is host code; it never reads device memory.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -14,9 +14,12 @@ namespace {
 constexpr int kDefaultPrefetch = PA_PREFETCH_REG;
 constexpr int kDefaultWaves = 4;
 constexpr int kMaxPartitionBlocks = 1024;  // LDS slice of the block table: 4 KiB
-// The auto plan: at least this many work-groups (four per compute unit on
-// 256 CUs) and at most kAutoPartitionBlocks blocks (1 MiB of K and V) per
-// work-group, so ragged batches split into similar-sized pieces.
+constexpr size_t kMaxLdsBytes = 65536;     // dynamic LDS per work-group
+// Auto partition size.  When the batch alone gives at least
+// kTargetWorkgroups work-groups (four per CU on 256 CUs), every (sequence,
+// KV head) is one work-group: no split, no reduce.  Otherwise contexts are
+// split into partitions of at most kAutoPartitionBlocks blocks (1 MiB of K
+// and V), which also keeps the pieces of a ragged batch similar in size.
 constexpr int64_t kTargetWorkgroups = 1024;
 constexpr int kAutoPartitionBlocks = 128;
 
@@ -40,8 +43,9 @@ int check_shape(const pa_shape* sh) {
   if (g > PA_G_MAX) return PA_ERR_UNSUPPORTED;
   // grid.x = Hkv and grid.y = B must fit the launch limits.
   if (sh->num_kv_heads > 65535 || sh->num_seqs > 65535) return PA_ERR_UNSUPPORTED;
-  // Byte offsets of the pool must fit int64.
+  // Byte offsets of the pool and token counts must fit their types.
   if (sh->num_blocks > (INT64_MAX / 8192) / sh->num_kv_heads) return PA_ERR_UNSUPPORTED;
+  if (sh->max_blocks_per_seq > INT32_MAX / PA_BLOCK_SIZE) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
 
@@ -52,6 +56,7 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   paged_attn_default_options(&d);
   if (!o) o = &d;
   if (o->reserved != 0) return PA_ERR_INVALID_ARG;
+  const int g = sh->num_q_heads / sh->num_kv_heads;
 
   int pf = o->prefetch < 0 ? kDefaultPrefetch : o->prefetch;
   if (pf > PA_PREFETCH_BOTH) return PA_ERR_INVALID_ARG;
@@ -59,18 +64,19 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   int waves = o->waves_per_wg == 0 ? kDefaultWaves : o->waves_per_wg;
   if (waves != 1 && waves != 2 && waves != 4 && waves != 8) return PA_ERR_INVALID_ARG;
 
+  const int B = sh->num_seqs, Hkv = sh->num_kv_heads;
   const int MB = sh->max_blocks_per_seq;
-  int PB;
   if (o->partition_blocks < 0) return PA_ERR_INVALID_ARG;
+  int PB;
   if (o->partition_blocks > 0) {
     if (o->partition_blocks > kMaxPartitionBlocks) return PA_ERR_UNSUPPORTED;
     PB = o->partition_blocks < MB ? o->partition_blocks : MB;
   } else {
-    const int64_t units = (int64_t)sh->num_seqs * sh->num_kv_heads;
+    const int64_t units = (int64_t)B * Hkv;
     int64_t want = (kTargetWorkgroups + units - 1) / units;
     if (want < 1) want = 1;
     int64_t pb = (MB + want - 1) / want;
-    if (pb > kAutoPartitionBlocks) pb = kAutoPartitionBlocks;
+    if (want > 1 && pb > kAutoPartitionBlocks) pb = kAutoPartitionBlocks;
     pb = (pb + waves - 1) / waves * waves;       // whole rounds of the W waves
     if (pb < 2 * waves) pb = 2 * waves;           // at least two blocks per wave
     if (pb > kMaxPartitionBlocks) pb = kMaxPartitionBlocks;
@@ -79,14 +85,14 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   }
   const int P = (MB + PB - 1) / PB;
   if (P > 65535) return PA_ERR_UNSUPPORTED;  // grid.z
+  if (pa::decode_lds_bytes(PB, g, waves) > kMaxLdsBytes) return PA_ERR_UNSUPPORTED;
+  memset(pl, 0, sizeof(*pl));
   pl->pf = pf;
   pl->waves = waves;
   pl->PB = PB;
   pl->P = P;
-  pl->wgs = (int64_t)P * sh->num_kv_heads * sh->num_seqs;
-  pl->ws_bytes = P > 1 ? (size_t)sh->num_seqs * sh->num_q_heads * P * (2 + PA_HEAD_DIM) *
-                             sizeof(float)
-                       : 0;
+  pl->wgs = (int64_t)P * Hkv * B;
+  pl->ws_bytes = P > 1 ? (size_t)B * sh->num_q_heads * P * (2 + PA_HEAD_DIM) * sizeof(float) : 0;
   return PA_OK;
 }
 
@@ -105,6 +111,7 @@ int paged_attn_plan(const pa_shape* sh, const pa_options* o, pa_plan_info* info)
   Plan pl;
   int rc = make_plan(sh, o, &pl);
   if (rc) return rc;
+  memset(info, 0, sizeof(*info));
   info->prefetch = pl.pf;
   info->waves_per_wg = pl.waves;
   info->partition_blocks = pl.PB;
@@ -137,7 +144,7 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
   pa_options d;
   paged_attn_default_options(&d);
   if (!o) o = &d;
-  if (pl.P > 1) {
+  if (pl.ws_bytes > 0) {
     if (!o->workspace || o->workspace_bytes < pl.ws_bytes) return PA_ERR_WORKSPACE;
     if (!aligned16(o->workspace)) return PA_ERR_INVALID_ARG;
   }
@@ -155,12 +162,6 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
   a.bt = block_tables;
   a.ctx = context_lens;
   a.out = static_cast<uint16_t*>(out);
-  if (pl.P > 1) {
-    float* ws = static_cast<float*>(o->workspace);
-    const size_t rows = (size_t)sh->num_seqs * sh->num_q_heads * pl.P;
-    a.ws_ml = ws;
-    a.ws_o = ws + rows * 2;
-  }
   a.dbg_k = static_cast<uint16_t*>(o->debug_gather_k);
   a.dbg_trace = o->debug_trace;
   a.dbg_err = o->debug_error_word;
@@ -178,23 +179,32 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
   a.blk_bytes = (int64_t)sh->num_kv_heads * PA_BLOCK_SIZE * PA_HEAD_DIM * 2;
   a.lds_bt_bytes = pa::lds_bt_bytes_for(pl.PB);
   const bool dbg = o->debug_gather_k || o->debug_trace || o->debug_error_word;
-
   hipStream_t st = static_cast<hipStream_t>(stream);
+
+  if (pl.P > 1) {
+    float* ws = static_cast<float*>(o->workspace);
+    const size_t rows = (size_t)sh->num_seqs * sh->num_q_heads * pl.P;
+    a.ws_ml = ws;
+    a.ws_o = ws + rows * 2;
+  }
   if (pa::launch_decode(a, pl.pf, dbg, pl.waves, st) != hipSuccess) return PA_ERR_HIP;
   if (pl.P > 1 && pa::launch_reduce(a, st) != hipSuccess) return PA_ERR_HIP;
   return PA_OK;
 }
 
+// Streaming-read grid: 2048 work-groups of 256 threads (8 per CU on 256
+// CUs), the best of the shapes measured for this read pattern.
+constexpr int kStreamGroups = 2048;
+
 size_t paged_attn_stream_read_sink_bytes(size_t bytes) {
   (void)bytes;
-  return 16 * 4096;
+  return 16 * (size_t)kStreamGroups;
 }
 
 int paged_attn_stream_read(const void* buf, size_t bytes, void* sink, void* stream) {
   if (!buf || !sink || bytes == 0 || (bytes & 15u) || !aligned16(buf) || !aligned16(sink))
     return PA_ERR_INVALID_ARG;
-  // 16 work-groups of 256 threads per CU on 256 CUs.
-  if (pa::launch_stream_read(buf, bytes, sink, 4096, static_cast<hipStream_t>(stream)) !=
+  if (pa::launch_stream_read(buf, bytes, sink, kStreamGroups, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return PA_ERR_HIP;
   return PA_OK;

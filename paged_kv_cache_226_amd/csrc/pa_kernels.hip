@@ -74,18 +74,14 @@ struct BlockBuf {
 };
 
 // ---------------------------------------------------------------------------
+// Walks blocks [s, e) of (sequence b, KV head kvh) with the W waves of the
+// work-group (wave w takes s+w, s+w+W, ...) and leaves one record
+// (m, l, o[128]) per wave and query head in merge_s.  Every thread of the
+// work-group calls it; it synchronises the work-group.
 template <int PF, bool DBG>
-__global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  int32_t* bt_s = reinterpret_cast<int32_t*>(smem_raw);
-  float* merge_s = reinterpret_cast<float*>(smem_raw + a.lds_bt_bytes);
-
-  // Partition index slowest: every sequence's first partition is dispatched
-  // before any second one, so the large work-groups of a ragged batch start
-  // first and the short tail partitions fill in behind them.
-  const int kvh = blockIdx.x;
-  const int b = blockIdx.y;
-  const int p = blockIdx.z;
+__device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, const int kvh,
+                                           const int ctx, const int s, const int e,
+                                           int32_t* bt_s, float* merge_s) {
   const int G = a.G;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -95,30 +91,7 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
   const int c = lane & 15;                     // column: head c of the group
   const int pic = ((c & 3) << 2) | (c >> 2);   // token held in K row c
 
-  int ctx = a.ctx[b];
-  const int tab_tokens = a.MB * kT;
-  if (ctx > tab_tokens) {
-    if (DBG && tid == 0 && a.dbg_err) atomicOr(a.dbg_err, 2);
-    ctx = tab_tokens;
-  }
-  const int nb = ctx > 0 ? (ctx + kT - 1) / kT : 0;
-  const int s = p * a.PB;
-  const int e = min(nb, s + a.PB);
-
-  if (s >= e) {
-    // Nothing to attend in this partition.  With one partition the output
-    // rows are written here (context <= 0 gives zeros); otherwise the reduce
-    // kernel only reads partitions that hold blocks.
-    if (a.P == 1) {
-      for (int idx = tid; idx < G * kD; idx += blockDim.x) {
-        const int h = idx / kD, d = idx % kD;
-        a.out[((int64_t)b * a.Hq + kvh * G + h) * kD + d] = 0;
-      }
-    }
-    return;
-  }
-
-  // Stage this partition's block-table slice in LDS.
+  // Stage the range's block-table slice in LDS.
   const int32_t* bt_row = a.bt + (int64_t)b * a.MB;
   for (int i = tid; i < e - s; i += blockDim.x) bt_s[i] = bt_row[s + i];
 
@@ -365,19 +338,71 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
       for (int t = 0; t < 8; ++t) rec[2 + 32 * lg + 8 * q + t] = acc[t][q];
   }
   __syncthreads();
+}
+
+// Softmax-merge of the W wave records of head h: running max M (log2 units),
+// denominator L and unnormalised output O for dim d.
+__device__ __forceinline__ void combine_waves(const float* merge_s, int W, int G, int h, int d,
+                                              float& M, float& L, float& O) {
+  M = -INFINITY;
+  for (int w = 0; w < W; ++w) M = fmaxf(M, merge_s[(w * G + h) * kRec]);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  L = 0.f;
+  O = 0.f;
+  for (int w = 0; w < W; ++w) {
+    const float* rec = merge_s + (w * G + h) * kRec;
+    const float al = fast_exp2(rec[0] - Mu);
+    L += al * rec[1];
+    O += al * rec[2 + d];
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int PF, bool DBG>
+__global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  int32_t* bt_s = reinterpret_cast<int32_t*>(smem_raw);
+  float* merge_s = reinterpret_cast<float*>(smem_raw + a.lds_bt_bytes);
+
+  // Partition index slowest: every sequence's first partition is dispatched
+  // before any second one, so the large work-groups of a ragged batch start
+  // first and the short tail partitions fill in behind them.
+  const int kvh = blockIdx.x;
+  const int b = blockIdx.y;
+  const int p = blockIdx.z;
+  const int G = a.G;
+  const int tid = threadIdx.x;
+  const int W = blockDim.x / kWave;
+
+  int ctx = a.ctx[b];
+  const int tab_tokens = a.MB * kT;
+  if (ctx > tab_tokens) {
+    if (DBG && tid == 0 && a.dbg_err) atomicOr(a.dbg_err, 2);
+    ctx = tab_tokens;
+  }
+  const int nb = ctx > 0 ? (ctx + kT - 1) / kT : 0;
+  const int s = p * a.PB;
+  const int e = min(nb, s + a.PB);
+
+  if (s >= e) {
+    // Nothing to attend in this partition.  With one partition the output
+    // rows are written here (context <= 0 gives zeros); otherwise the reduce
+    // kernel only reads partitions that hold blocks.
+    if (a.P == 1) {
+      for (int idx = tid; idx < G * kD; idx += blockDim.x) {
+        const int h = idx / kD, d = idx % kD;
+        a.out[((int64_t)b * a.Hq + kvh * G + h) * kD + d] = 0;
+      }
+    }
+    return;
+  }
+
+  walk_range<PF, DBG>(a, b, kvh, ctx, s, e, bt_s, merge_s);
 
   for (int idx = tid; idx < G * kD; idx += blockDim.x) {
     const int h = idx / kD, d = idx % kD;
-    float M = -INFINITY;
-    for (int w = 0; w < W; ++w) M = fmaxf(M, merge_s[(w * G + h) * kRec]);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    float L = 0.f, O = 0.f;
-    for (int w = 0; w < W; ++w) {
-      const float* rec = merge_s + (w * G + h) * kRec;
-      const float al = fast_exp2(rec[0] - Mu);
-      L += al * rec[1];
-      O += al * rec[2 + d];
-    }
+    float M, L, O;
+    combine_waves(merge_s, W, G, h, d, M, L, O);
     const int64_t row = (int64_t)b * a.Hq + kvh * G + h;
     if (a.P == 1) {
       a.out[row * kD + d] = f32_to_f16_bits(O / L);
@@ -420,21 +445,31 @@ __global__ void __launch_bounds__(128) pa_reduce_kernel(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Streaming-read ceiling: every 16-byte word of buf read once, eight loads in
-// flight per lane, non-temporal.
+// Streaming-read ceiling: every 16-byte word of buf read once.  Each wave
+// reads whole 8 KiB chunks (8 non-temporal 128-bit loads per lane, 1 KiB
+// contiguous per instruction, the decode kernel's access granularity), the
+// chunks dealt round-robin over all waves; a ragged tail is read word by
+// word.  One XOR per work-group goes to sink so no load is dead.
 __global__ void __launch_bounds__(256) stream_read_kernel(const u32x4* __restrict__ buf,
                                                           int64_t n16, u32x4* sink) {
-  const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  constexpr int kChunkWords = 512;  // 8 KiB
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  const int64_t nchunks = n16 / kChunkWords;
   u32x4 x = {0u, 0u, 0u, 0u};
-  for (; i + 7 * nthreads < n16; i += 8 * nthreads) {
+  for (int64_t ch = wave_id; ch < nchunks; ch += nwaves) {
+    const u32x4* p = buf + ch * kChunkWords + lane;
     u32x4 r[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) r[k] = __builtin_nontemporal_load(buf + i + k * nthreads);
+    for (int k = 0; k < 8; ++k) r[k] = __builtin_nontemporal_load(p + kWave * k);
 #pragma unroll
     for (int k = 0; k < 8; ++k) x ^= r[k];
   }
-  for (; i < n16; i += nthreads) x ^= __builtin_nontemporal_load(buf + i);
+  const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = nchunks * kChunkWords + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+       i < n16; i += nthreads)
+    x ^= __builtin_nontemporal_load(buf + i);
   // reduce within the work-group so only one value per group is stored
   __shared__ u32x4 red[256];
   red[threadIdx.x] = x;

@@ -37,16 +37,37 @@ def shape_of(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor)
     return nat.make_shape(B, Hq, Hkv, block_tables.shape[1], NB, head_dim=G8 * X, block_size=T)
 
 
-def options(prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0) -> nat.PaOptions:
+def options(prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0,
+            debug_gather_k: Optional[torch.Tensor] = None,
+            debug_trace: Optional[torch.Tensor] = None,
+            debug_error_word: Optional[torch.Tensor] = None) -> nat.PaOptions:
+    """pa_options for these settings (any debug tensor selects the checked
+    kernel variant)."""
     o = nat.default_options()
     o.prefetch = int(prefetch)
     o.partition_blocks = int(partition_blocks)
     o.waves_per_wg = int(waves_per_wg)
+    if debug_gather_k is not None:
+        _check(debug_gather_k, "debug_gather_k", torch.float16, 4)
+        o.debug_gather_k = debug_gather_k.data_ptr()
+    if debug_trace is not None:
+        _check(debug_trace, "debug_trace", torch.int32, 4)
+        o.debug_trace = debug_trace.data_ptr()
+    if debug_error_word is not None:
+        _check(debug_error_word, "debug_error_word", torch.int32, 1)
+        o.debug_error_word = debug_error_word.data_ptr()
     return o
 
 
 def plan(q, k_cache, block_tables, **kw) -> dict:
     return nat.plan(shape_of(q, k_cache, block_tables), options(**kw))
+
+
+def new_workspace(q, k_cache, block_tables, **kw) -> torch.Tensor:
+    """A workspace for this shape and these options (reusable by every later
+    call with the same plan; calls must not overlap on it)."""
+    n = workspace_bytes(q, k_cache, block_tables, **kw)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
 
 
 def workspace_bytes(q, k_cache, block_tables, **kw) -> int:
@@ -89,7 +110,8 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
     sh = shape_of(q, k_cache, block_tables)
-    o = options(prefetch, partition_blocks, waves_per_wg)
+    o = options(prefetch, partition_blocks, waves_per_wg, debug_gather_k, debug_trace,
+                debug_error_word)
     need = int(nat.lib().paged_attn_workspace_size(ctypes.byref(sh), ctypes.byref(o)))
     if need:
         if workspace is None:
@@ -98,15 +120,6 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
             raise ValueError(f"workspace needs {need} bytes")
         o.workspace = workspace.data_ptr()
         o.workspace_bytes = workspace.numel() * workspace.element_size()
-    if debug_gather_k is not None:
-        _check(debug_gather_k, "debug_gather_k", torch.float16, 4)
-        o.debug_gather_k = debug_gather_k.data_ptr()
-    if debug_trace is not None:
-        _check(debug_trace, "debug_trace", torch.int32, 4)
-        o.debug_trace = debug_trace.data_ptr()
-    if debug_error_word is not None:
-        _check(debug_error_word, "debug_error_word", torch.int32, 1)
-        o.debug_error_word = debug_error_word.data_ptr()
     rc = nat.lib().paged_attn_decode(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
         ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(block_tables.data_ptr()),

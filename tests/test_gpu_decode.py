@@ -86,29 +86,33 @@ def test_debug_gather_is_bitwise_the_block_table_gather():
 
 
 @pytest.mark.parametrize("pf", MODES)
-@pytest.mark.parametrize("waves,pb", [(4, 0), (4, 8), (2, 5), (8, 16), (1, 3)])
+@pytest.mark.parametrize("waves,pb", [(4, 0), (2, 0), (4, 8), (2, 5), (8, 16), (1, 3)])
 def test_trace_follows_the_lookahead_schedule(pf, waves, pb):
-    x = gen.make_case(2, 4, 2, [400, 90], seed=140, extra_pool_blocks=2)
+    x = gen.make_case(3, 4, 2, [400, 90, 2000], seed=140, extra_pool_blocks=2)
     dev = to_device(x)
     B, MB = x.block_tables.shape
     Hkv = x.k_cache.shape[1]
     trace = torch.full((B, Hkv, MB, 2), -1, dtype=torch.int32, device="cuda")
-    run(x, dev, prefetch=pf, waves_per_wg=waves, partition_blocks=pb, debug_trace=trace)
+    kw = dict(prefetch=pf, waves_per_wg=waves, partition_blocks=pb)
+    run(x, dev, debug_trace=trace, **kw)
     tr = trace.cpu().numpy()
-    plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], prefetch=pf,
-                    waves_per_wg=waves, partition_blocks=pb)
-    PB, W = plan["partition_blocks"], plan["waves_per_wg"]
+    plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], **kw)
+    W, PB = plan["waves_per_wg"], plan["partition_blocks"]
+    ranges = [(b, h, s, min(-(-int(L) // 16), s + PB))
+              for b, L in enumerate(x.context_lens) for h in range(Hkv)
+              for s in range(0, -(-int(L) // 16), PB)]
+    seen = np.zeros((B, Hkv, MB), dtype=bool)
+    for b, h, s, e in ranges:
+        exp = sch.expected_trace(s, e, W)
+        for j in range(s, e):
+            wave, it, fetcher = exp[j]
+            assert tr[b, h, j, 0] == (wave << 16 | it), (b, h, j)
+            assert tr[b, h, j, 1] == (-1 if pf == 0 else fetcher), (b, h, j, pf)
+            assert not seen[b, h, j]
+            seen[b, h, j] = True
     for b, L in enumerate(x.context_lens):
         nb = -(-int(L) // 16)
-        for s in range(0, nb, PB):
-            e = min(nb, s + PB)
-            exp = sch.expected_trace(s, e, W)
-            for j in range(s, e):
-                wave, it, fetcher = exp[j]
-                for h in range(Hkv):
-                    assert tr[b, h, j, 0] == (wave << 16 | it), (b, j)
-                    want_f = -1 if pf == 0 else fetcher
-                    assert tr[b, h, j, 1] == want_f, (b, j, pf)
+        assert seen[b, :, :nb].all()
         assert (tr[b, :, nb:, :] == -1).all()
 
 
@@ -201,3 +205,16 @@ def test_stream_read_touches_every_word():
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32).reshape(-1, 4), axis=0)
     want = np.bitwise_xor.reduce(host.reshape(-1, 4), axis=0)
     assert np.array_equal(got, want)
+
+
+def test_debug_variant_computes_the_same_bits():
+    x = gen.make_case(4, 16, 4, [900, 33, 2100, 129], seed=157)
+    dev = to_device(x)
+    B, MB = x.block_tables.shape
+    for pb in (0, 16):
+        plain = run(x, dev, partition_blocks=pb)
+        trace = torch.full((B, 4, MB, 2), -1, dtype=torch.int32, device="cuda")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        dbg = run(x, dev, partition_blocks=pb, debug_trace=trace, debug_error_word=err)
+        assert np.array_equal(bits(plain), bits(dbg)), pb
+        assert int(err.item()) == 0
