@@ -62,12 +62,83 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama2_7b")
     ap.add_argument("--prefetch", type=int, default=-1, help="-1 = library default")
+    ap.add_argument("--prefetch-distance", type=int, default=0,
+                    help="L2-touch distance k in wave iterations (modes 1, 3); 0 = 1")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3: every prefetch mode, no CPU leg")
+    ap.add_argument("--sweep", action="store_true",
+                    help="batch x context sweep of one workload's head shape: one JSON "
+                         "line per point (look-ahead off vs on, sampled parity)")
+    ap.add_argument("--sweep-batches", default="8,16,32,64,128,256")
+    ap.add_argument("--sweep-contexts", default="1024,2048,4096,8192,16384,32768")
+    ap.add_argument("--sweep-max-gb", type=float, default=16.0,
+                    help="skip points whose K+V pool exceeds this many GB")
     return ap.parse_args()
+
+
+def run_sweep(args):
+    """Batch x context sweep (the review's section 5.4 figure, at kernel level):
+    for each point, µs/step and KV GB/s with the look-ahead off and with the
+    default look-ahead, and the oracle on two sampled sequences."""
+    import numpy as np
+    import torch
+
+    from oracle import oracle as orc
+    from paged_kv_cache_226_amd import accounting as acc
+    from paged_kv_cache_226_amd import inputs as gen
+    from paged_kv_cache_226_amd import ops
+
+    w = gen.WORKLOADS[args.workload]
+    batches = [int(v) for v in args.sweep_batches.split(",")]
+    contexts = [int(v) for v in args.sweep_contexts.split(",")]
+    stream = torch.cuda.current_stream()
+    for bi, B in enumerate(batches):
+        for ci, ctx in enumerate(contexts):
+            kv_bytes = acc.step_kv_bytes(w.num_kv_heads, 128, [ctx] * B)
+            if kv_bytes > args.sweep_max_gb * 1e9:
+                continue
+            d = gen.make_case_device(B, w.num_q_heads, w.num_kv_heads, ctx,
+                                     seed=10_000 + 100 * bi + ci)
+            out = torch.empty_like(d["q"])
+            ws = ops.new_workspace(d["q"], d["k_cache"], d["block_tables"])
+            plan = ops.plan(d["q"], d["k_cache"], d["block_tables"])
+            times = {}
+            for pf in (0, plan["prefetch"]):
+                f = lambda: ops.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"],
+                                                  d["block_tables"], d["context_lens"],
+                                                  d["scale"], out, prefetch=pf, workspace=ws)
+                for _ in range(3):
+                    f()
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(args.steps):
+                    f()
+                b.record(stream)
+                torch.cuda.synchronize()
+                times[pf] = a.elapsed_time(b) * 1e3 / args.steps
+            seqs = [0, B - 1]
+            x = gen.host_subset(d, seqs)
+            rows = np.array([[i, h] for i in range(len(seqs)) for h in range(w.num_q_heads)])
+            ref = orc.paged_attention_rows_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                               x.context_lens, x.scale, rows)
+            got = out[seqs].float().cpu().numpy().reshape(-1, 128).astype(np.float64)
+            diff = np.abs(got - ref)
+            on = times[plan["prefetch"]]
+            print(json.dumps({
+                "sweep": args.workload, "batch": B, "context": ctx, "kv_bytes": kv_bytes,
+                "partitions": plan["num_partitions"],
+                "us_off": round(times[0], 2), "us_on": round(on, 2),
+                "GBps_on": round(kv_bytes / on / 1e3, 1),
+                "pct_hbm_peak_on": round(100 * kv_bytes / on / 1e3 / acc.HBM_PEAK_GBPS, 2),
+                "speedup_on_vs_off": round(times[0] / on, 4),
+                "parity_abs": float(diff.max()),
+                "parity_rel": float((diff / np.maximum(np.abs(ref), 1e-3)).max())}), flush=True)
+            del d, out, ws
+            torch.cuda.empty_cache()
 
 
 def main():
@@ -92,6 +163,9 @@ def main():
         sys.exit(3)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sweep:
+        run_sweep(args)
+        return
 
     w = gen.WORKLOADS[args.workload]
     t0 = time.time()
@@ -111,7 +185,8 @@ def main():
 
     def step(pf):
         ops.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
-                              d["context_lens"], x.scale, out, prefetch=pf, workspace=ws)
+                              d["context_lens"], x.scale, out, prefetch=pf, workspace=ws,
+                              prefetch_distance=args.prefetch_distance)
 
     def timed(pf, steps, warmup):
         for _ in range(warmup):
@@ -212,7 +287,9 @@ def main():
                    "context_sum": int(np.maximum(x.context_lens, 0).sum()),
                    "context_min": int(x.context_lens.min()),
                    "context_max": int(x.context_lens.max()),
-                   "prefetch": mode_names[mode], "waves_per_wg": plan["waves_per_wg"],
+                   "prefetch": mode_names[mode],
+                   "prefetch_distance": max(1, args.prefetch_distance),
+                   "waves_per_wg": plan["waves_per_wg"],
                    "partition_blocks": plan["partition_blocks"],
                    "num_partitions": plan["num_partitions"], "parallelism": "single GPU"},
         "kv_bytes_per_step": kv_bytes,

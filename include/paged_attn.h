@@ -89,10 +89,11 @@ enum pa_status {
 /* How block j + w is fetched while block j is computed. */
 enum pa_prefetch {
     PA_PREFETCH_OFF = 0,  /* load block j, wait, compute: no look-ahead */
-    PA_PREFETCH_L2 = 1,   /* touch every 128 B line of block j + w so it is
+    PA_PREFETCH_L2 = 1,   /* touch every 128 B line of block j + k*w so it is
                              brought into L2 / Infinity Cache; data discarded */
     PA_PREFETCH_REG = 2,  /* load block j + w into a second register buffer */
-    PA_PREFETCH_BOTH = 3  /* REG for block j + w, plus an L2 touch of j + 2w */
+    PA_PREFETCH_BOTH = 3  /* REG for block j + w, plus an L2 touch of
+                             block j + (1 + k)*w */
 };
 
 typedef struct pa_shape {
@@ -112,7 +113,8 @@ typedef struct pa_options {
                                   at least 1024 (sequence, KV head) pairs, else
                                   partitions of at most 128 blocks */
     int32_t waves_per_wg;      /* w in {1, 2, 4, 8}; 0 = auto */
-    int32_t reserved;          /* must be 0 */
+    int32_t prefetch_distance; /* k, the L2 touch's distance in iterations of
+                                  a wave (modes 1 and 3); 0 = 1, at most 63 */
     void *workspace;           /* device scratch for partition partials; may be
                                   NULL when the plan has one partition */
     size_t workspace_bytes;

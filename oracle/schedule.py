@@ -15,34 +15,36 @@ from typing import Dict, List, Optional, Tuple
 Event = Tuple[int, int, Optional[int]]  # (iteration, computed block, fetched-ahead block)
 
 
-def wave_schedule(s: int, e: int, w: int, wave: int) -> List[Event]:
-    """Events of one wave, in program order."""
-    if w <= 0 or not 0 <= wave < w:
-        raise ValueError("need 0 <= wave < w")
+def wave_schedule(s: int, e: int, w: int, wave: int, distance: int = 1) -> List[Event]:
+    """Events of one wave, in program order.  `distance` generalises the
+    look-ahead to block_idx + distance * w (Algorithm 1 is distance 1)."""
+    if w <= 0 or not 0 <= wave < w or distance < 1:
+        raise ValueError("need 0 <= wave < w and distance >= 1")
     events: List[Event] = []
     block_idx = s + wave
     it = 0
     while block_idx < e:
-        ahead = block_idx + w if block_idx + w < e else None
+        tgt = block_idx + distance * w
+        ahead = tgt if tgt < e else None
         events.append((it, block_idx, ahead))
         block_idx += w
         it += 1
     return events
 
 
-def group_schedule(s: int, e: int, w: int) -> Dict[int, List[Event]]:
+def group_schedule(s: int, e: int, w: int, distance: int = 1) -> Dict[int, List[Event]]:
     """Events of all w waves of one work-group over [s, e)."""
-    return {wave: wave_schedule(s, e, w, wave) for wave in range(w)}
+    return {wave: wave_schedule(s, e, w, wave, distance) for wave in range(w)}
 
 
-def expected_trace(s: int, e: int, w: int):
+def expected_trace(s: int, e: int, w: int, distance: int = 1):
     """Per block j in [s, e): (wave that computes it, its iteration, wave that
     fetched it ahead or -1).  This is what the kernel's debug trace records."""
     out = {}
-    for wave, events in group_schedule(s, e, w).items():
+    for wave, events in group_schedule(s, e, w, distance).items():
         for it, j, _ in events:
             out[j] = [wave, it, -1]
-    for wave, events in group_schedule(s, e, w).items():
+    for wave, events in group_schedule(s, e, w, distance).items():
         for _, _, ahead in events:
             if ahead is not None:
                 out[ahead][2] = wave

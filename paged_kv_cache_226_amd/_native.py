@@ -28,7 +28,7 @@ class PaShape(ctypes.Structure):
 
 class PaOptions(ctypes.Structure):
     _fields_ = [("prefetch", ctypes.c_int32), ("partition_blocks", ctypes.c_int32),
-                ("waves_per_wg", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("waves_per_wg", ctypes.c_int32), ("prefetch_distance", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("debug_gather_k", ctypes.c_void_p), ("debug_trace", ctypes.c_void_p),
                 ("debug_error_word", ctypes.c_void_p)]

@@ -55,7 +55,7 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   pa_options d;
   paged_attn_default_options(&d);
   if (!o) o = &d;
-  if (o->reserved != 0) return PA_ERR_INVALID_ARG;
+  if (o->prefetch_distance < 0 || o->prefetch_distance > 63) return PA_ERR_INVALID_ARG;
   const int g = sh->num_q_heads / sh->num_kv_heads;
 
   int pf = o->prefetch < 0 ? kDefaultPrefetch : o->prefetch;
@@ -178,6 +178,7 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
   a.NB = sh->num_blocks;
   a.blk_bytes = (int64_t)sh->num_kv_heads * PA_BLOCK_SIZE * PA_HEAD_DIM * 2;
   a.lds_bt_bytes = pa::lds_bt_bytes_for(pl.PB);
+  a.pf_dist = o->prefetch_distance > 0 ? o->prefetch_distance : 1;
   const bool dbg = o->debug_gather_k || o->debug_trace || o->debug_error_word;
   hipStream_t st = static_cast<hipStream_t>(stream);
 

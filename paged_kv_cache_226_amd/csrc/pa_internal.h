@@ -29,6 +29,7 @@ struct DecodeArgs {
   int64_t NB;            // pool blocks
   int64_t blk_bytes;     // bytes from one physical block to the next (Hkv * 4096)
   int lds_bt_bytes;      // LDS bytes reserved for the block-table slice
+  int pf_dist;           // L2-touch distance in iterations of a wave, 1..63
   int sink_enable;
 };
 

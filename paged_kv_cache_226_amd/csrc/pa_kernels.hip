@@ -33,10 +33,12 @@
 // skipping it changes no bits).
 //
 // Look-ahead modes (PF): 0 none; 1 an L2 / Infinity-Cache touch of every
-// 128 B line of block j+W (one dword per lane, value discarded); 2 block j+W
+// 128 B line of block j+kW (one dword per lane, value discarded); 2 block j+W
 // loaded into a second register buffer before block j is computed; 3 both,
-// with the touch moved to block j+2W.  The arithmetic is the same code in
-// every mode, so results are bitwise identical.
+// with the touch moved to block j+(1+k)W.  k (a.pf_dist, 1..63) is the
+// touch distance in iterations; the pages' Algorithm 1 is k = 1.  The
+// arithmetic is the same code in every mode, so results are bitwise
+// identical.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -257,9 +259,9 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
       BlockBuf buf;
       load_block(buf, phys_it(it));
       uint32_t got = 0;
-      if (PF == 1) {
-        got = touch_block(phys_it(it + 1));
-        trace_put(j + W, 1, wave);
+      if (PF == 1 && it + a.pf_dist < n_it) {
+        got = touch_block(phys_it(it + a.pf_dist));
+        trace_put(j + a.pf_dist * W, 1, wave);
       }
       trace_put(j, 0, (wave << 16) | it);
       compute(buf, j);
@@ -285,7 +287,7 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
       load_block(nxt, phys_it(it + 1));
       trace_put(j + W, 1, wave);
       uint32_t got = 0;
-      if (PF == 3) got = touch_block(phys_it(it + 2));
+      if (PF == 3 && it + 1 + a.pf_dist < n_it) got = touch_block(phys_it(it + 1 + a.pf_dist));
       trace_put(j, 0, (wave << 16) | it);
       compute(cur, j);
       if (PF == 3) {
@@ -307,7 +309,7 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
         trace_put(j + W, 1, wave);
       }
       uint32_t got = 0;
-      if (PF == 3 && it + 2 < n_it) got = touch_block(phys_it(it + 2));
+      if (PF == 3 && it + 1 + a.pf_dist < n_it) got = touch_block(phys_it(it + 1 + a.pf_dist));
       trace_put(j, 0, (wave << 16) | it);
       compute(bufA, j);
       if (PF == 3) {

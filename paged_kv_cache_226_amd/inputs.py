@@ -82,6 +82,18 @@ WORKLOADS: Dict[str, Workload] = {
     ]
 }
 
+# One GPU's share of a tensor-parallel layer (the review's section 5.5 runs
+# Llama3-8B and Qwen2.5-14B at TP 2, 4 and 8): the KV heads, their query
+# heads and their pool are split evenly, the batch and the contexts are not.
+# Same seeds as the full layer, so the context lengths match it.
+for _base, _tp in [(b, t) for b in ("llama3_8b", "qwen25_14b") for t in (2, 4, 8)]:
+    _w = WORKLOADS[_base]
+    WORKLOADS[f"{_base}_tp{_tp}"] = dataclasses.replace(
+        _w, name=f"{_base}_tp{_tp}", num_q_heads=_w.num_q_heads // _tp,
+        num_kv_heads=_w.num_kv_heads // _tp,
+        description=f"one GPU of {_base} at tensor parallelism {_tp}: "
+                    f"{_w.num_q_heads // _tp} Q / {_w.num_kv_heads // _tp} KV heads")
+
 
 @dataclasses.dataclass
 class PagedInputs:
@@ -226,3 +238,55 @@ def digests(x: PagedInputs) -> Dict[str, str]:
     for k in ("q", "k_cache", "v_cache", "block_tables", "context_lens"):
         out[k] = hashlib.sha256(np.ascontiguousarray(getattr(x, k)).tobytes()).hexdigest()
     return out
+
+
+def make_case_device(num_seqs: int, num_q_heads: int, num_kv_heads: int, context_len: int,
+                     seed: int, device="cuda", head_dim: int = HEAD_DIM,
+                     block_size: int = BLOCK_SIZE) -> Dict[str, object]:
+    """Large inputs drawn directly in device memory (torch's seeded generator
+    on the device), for sweeps whose pools are too big to draw on the host.
+    Every sequence has `context_len` tokens; the pool holds exactly the
+    blocks in use, shuffled.  K is drawn in the kernel's grouped layout
+    (pack_k's layout; the values are i.i.d., so drawing them grouped is the
+    same distribution).  Draw order: permutation, Q, K pool, V pool."""
+    import torch
+
+    nb = blocks_for(context_len, block_size)
+    NB = num_seqs * nb
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    perm = torch.randperm(NB, generator=g, device=device, dtype=torch.int64)
+    bt = perm.to(torch.int32).reshape(num_seqs, nb).contiguous()
+    ctx = torch.full((num_seqs,), context_len, dtype=torch.int32, device=device)
+
+    def normal(shape):
+        out = torch.empty(shape, dtype=torch.float16, device=device)
+        flat = out.view(-1)
+        for i in range(0, flat.numel(), _CHUNK):
+            n = min(_CHUNK, flat.numel() - i)
+            flat[i:i + n] = torch.randn(n, generator=g, device=device, dtype=torch.float32)
+        return out
+
+    q = normal((num_seqs, num_q_heads, head_dim))
+    k = normal((NB, num_kv_heads, head_dim // 8, block_size, 8))
+    v = normal((NB, num_kv_heads, block_size, head_dim))
+    scale = float(np.float32(1.0 / np.sqrt(head_dim)))
+    return dict(q=q, k_cache=k, v_cache=v, block_tables=bt, context_lens=ctx, scale=scale)
+
+
+def host_subset(dev_case: Dict[str, object], seqs: Sequence[int]) -> PagedInputs:
+    """Copy the given sequences of a device case back to the host as a small
+    PagedInputs (their blocks only, renumbered, K unpacked to token-major),
+    so the CPU oracle can check those rows."""
+    import torch
+
+    bt = dev_case["block_tables"][list(seqs)].cpu().numpy()
+    ctx = dev_case["context_lens"][list(seqs)].cpu().numpy().astype(np.int32)
+    used = sorted(set(int(v) for v in bt[bt >= 0].ravel()))
+    remap = {p: i for i, p in enumerate(used)}
+    idx = torch.tensor(used, dtype=torch.int64, device=dev_case["k_cache"].device)
+    kp = dev_case["k_cache"].index_select(0, idx).cpu().numpy()
+    v = dev_case["v_cache"].index_select(0, idx).cpu().numpy()
+    bt2 = np.vectorize(lambda p: remap.get(int(p), -1))(bt).astype(np.int32)
+    q = dev_case["q"][list(seqs)].cpu().numpy()
+    return PagedInputs(q, unpack_k(kp), v, bt2, ctx, dev_case["scale"], "subset")

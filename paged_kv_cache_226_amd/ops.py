@@ -38,6 +38,7 @@ def shape_of(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor)
 
 
 def options(prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0,
+            prefetch_distance: int = 0,
             debug_gather_k: Optional[torch.Tensor] = None,
             debug_trace: Optional[torch.Tensor] = None,
             debug_error_word: Optional[torch.Tensor] = None) -> nat.PaOptions:
@@ -47,6 +48,7 @@ def options(prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0
     o.prefetch = int(prefetch)
     o.partition_blocks = int(partition_blocks)
     o.waves_per_wg = int(waves_per_wg)
+    o.prefetch_distance = int(prefetch_distance)
     if debug_gather_k is not None:
         _check(debug_gather_k, "debug_gather_k", torch.float16, 4)
         o.debug_gather_k = debug_gather_k.data_ptr()
@@ -79,6 +81,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       block_tables: torch.Tensor, context_lens: torch.Tensor,
                       scale: Optional[float] = None, out: Optional[torch.Tensor] = None, *,
                       prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0,
+                      prefetch_distance: int = 0,
                       workspace: Optional[torch.Tensor] = None,
                       debug_gather_k: Optional[torch.Tensor] = None,
                       debug_trace: Optional[torch.Tensor] = None,
@@ -110,8 +113,8 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
     sh = shape_of(q, k_cache, block_tables)
-    o = options(prefetch, partition_blocks, waves_per_wg, debug_gather_k, debug_trace,
-                debug_error_word)
+    o = options(prefetch, partition_blocks, waves_per_wg, prefetch_distance, debug_gather_k,
+                debug_trace, debug_error_word)
     need = int(nat.lib().paged_attn_workspace_size(ctypes.byref(sh), ctypes.byref(o)))
     if need:
         if workspace is None:

@@ -57,6 +57,15 @@ def test_random_shapes(seed, B, Hq, Hkv, lens, pf):
     assert_close(run(x, prefetch=pf), oracle(x), f"{seed} pf={pf}")
 
 
+@pytest.mark.parametrize("dist", [1, 2, 4, 8, 63])
+def test_touch_distance_changes_no_bits(dist):
+    x = gen.make_case(3, 8, 2, [700, 2000, 95], seed=112, extra_pool_blocks=3)
+    dev = to_device(x)
+    base = run(x, dev, prefetch=0)
+    for pf in (1, 3):
+        assert np.array_equal(bits(run(x, dev, prefetch=pf, prefetch_distance=dist)), bits(base))
+
+
 @pytest.mark.parametrize("waves", [1, 2, 4, 8])
 @pytest.mark.parametrize("pb", [0, 1, 3, 8, 1024])
 def test_waves_and_partitions(waves, pb):
@@ -86,24 +95,28 @@ def test_debug_gather_is_bitwise_the_block_table_gather():
 
 
 @pytest.mark.parametrize("pf", MODES)
-@pytest.mark.parametrize("waves,pb", [(4, 0), (2, 0), (4, 8), (2, 5), (8, 16), (1, 3)])
-def test_trace_follows_the_lookahead_schedule(pf, waves, pb):
+@pytest.mark.parametrize("waves,pb,dist", [(4, 0, 1), (2, 0, 1), (4, 8, 1), (2, 5, 1), (8, 16, 1),
+                                           (1, 3, 1), (4, 0, 2), (2, 0, 5), (4, 32, 3)])
+def test_trace_follows_the_lookahead_schedule(pf, waves, pb, dist):
     x = gen.make_case(3, 4, 2, [400, 90, 2000], seed=140, extra_pool_blocks=2)
     dev = to_device(x)
     B, MB = x.block_tables.shape
     Hkv = x.k_cache.shape[1]
     trace = torch.full((B, Hkv, MB, 2), -1, dtype=torch.int32, device="cuda")
-    kw = dict(prefetch=pf, waves_per_wg=waves, partition_blocks=pb)
+    kw = dict(prefetch=pf, waves_per_wg=waves, partition_blocks=pb, prefetch_distance=dist)
     run(x, dev, debug_trace=trace, **kw)
     tr = trace.cpu().numpy()
-    plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], **kw)
+    plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], prefetch=pf,
+                    waves_per_wg=waves, partition_blocks=pb)
     W, PB = plan["waves_per_wg"], plan["partition_blocks"]
     ranges = [(b, h, s, min(-(-int(L) // 16), s + PB))
               for b, L in enumerate(x.context_lens) for h in range(Hkv)
               for s in range(0, -(-int(L) // 16), PB)]
     seen = np.zeros((B, Hkv, MB), dtype=bool)
     for b, h, s, e in ranges:
-        exp = sch.expected_trace(s, e, W)
+        # slot 1 holds the L2 touch in mode 1 (distance dist) and the
+        # register fetch of block j + W in modes 2 and 3
+        exp = sch.expected_trace(s, e, W, dist if pf == 1 else 1)
         for j in range(s, e):
             wave, it, fetcher = exp[j]
             assert tr[b, h, j, 0] == (wave << 16 | it), (b, h, j)

@@ -23,6 +23,7 @@ def _need_gpu(native_lib):
 
 
 def sample_rows(x, n, seed):
+    """Corner rows, the longest and shortest sequence, then random rows."""
     B, Hq, _ = x.q.shape
     rng = np.random.default_rng(seed)
     rows = {(0, 0), (B - 1, Hq - 1)}
@@ -34,7 +35,9 @@ def sample_rows(x, n, seed):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name", ["llama2_7b", "llama3_8b", "qwen25_7b", "qwen25_14b"])
+@pytest.mark.parametrize("name", ["llama2_7b", "llama3_8b", "qwen25_7b", "qwen25_14b",
+                                  "llama3_8b_tp2", "llama3_8b_tp4", "llama3_8b_tp8",
+                                  "qwen25_14b_tp2", "qwen25_14b_tp4", "qwen25_14b_tp8"])
 def test_workload_sampled_rows(name):
     print(f"[workload] {name}: generating", flush=True)
     x = gen.make_inputs(name)
@@ -58,3 +61,15 @@ def test_workload_sampled_rows(name):
                                        x.context_lens, x.scale, rows)
     e = assert_close(got[rows[:, 0], rows[:, 1]], ref, name)
     print(f"[workload] {name}: {e}", flush=True)
+
+
+def test_device_generated_case_against_the_oracle():
+    """The sweep's device-side inputs: two sequences copied back and checked."""
+    d = gen.make_case_device(6, 8, 2, 1000, seed=77)
+    out = ops.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                d["context_lens"], d["scale"])
+    torch.cuda.synchronize()
+    x = gen.host_subset(d, [1, 5])
+    ref = orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables, x.context_lens,
+                                  x.scale)
+    assert_close(out[[1, 5]].cpu().numpy(), ref, "device case")

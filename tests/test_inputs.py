@@ -32,11 +32,19 @@ def test_tiny_workload_layout():
     assert x.scale == np.float32(1 / np.sqrt(128))
 
 
-@pytest.mark.parametrize("name", ["llama2_7b", "llama3_8b", "qwen25_7b", "qwen25_14b"])
+@pytest.mark.parametrize("name", sorted(gen.WORKLOADS))
 def test_workload_shapes(name):
     w = gen.WORKLOADS[name]
     assert w.num_q_heads % w.num_kv_heads == 0
     assert w.head_dim == 128 and w.block_size == 16
+
+
+@pytest.mark.parametrize("base,tp", [(b, t) for b in ("llama3_8b", "qwen25_14b") for t in (2, 4, 8)])
+def test_tensor_parallel_shards_keep_the_group_and_contexts(base, tp):
+    full, shard = gen.WORKLOADS[base], gen.WORKLOADS[f"{base}_tp{tp}"]
+    assert shard.num_kv_heads * tp == full.num_kv_heads
+    assert shard.group == full.group and shard.num_seqs == full.num_seqs
+    assert np.array_equal(gen.workload_context_lens(shard), gen.workload_context_lens(full))
 
 
 def test_ragged_lengths_in_range_and_pool_exact():

@@ -28,3 +28,17 @@ def test_four_warp_example():
     assert ev == [(0, 0, 4), (1, 4, 8), (2, 8, None)]
     tr = sch.expected_trace(0, 12, 4)
     assert tr[0] == [0, 0, -1] and tr[4] == [0, 1, 0] and tr[9] == [1, 2, 1]
+
+
+@pytest.mark.parametrize("w,k", [(1, 2), (4, 2), (4, 3), (2, 8)])
+def test_longer_lookahead_targets_the_same_wave_k_iterations_later(w, k):
+    s, e = 5, 5 + 61
+    for wave, ev in sch.group_schedule(s, e, w, k).items():
+        for n, (it, j, ahead) in enumerate(ev):
+            if n + k < len(ev):
+                assert ahead == ev[n + k][1] == j + k * w
+            else:
+                assert ahead is None
+    tr = sch.expected_trace(s, e, w, k)
+    fetched = [j for j in range(s, e) if tr[j][2] >= 0]
+    assert fetched == list(range(s + k * w, e))
