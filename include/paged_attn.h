@@ -153,6 +153,24 @@ int paged_attn_decode(const void *q, const void *k_cache, const void *v_cache,
                       float scale, void *out, const pa_shape *shape,
                       const pa_options *opts, void *stream);
 
+/* One decode step over an FP8 KV cache (answer section 4: FP8 to shrink the
+   KV footprint).  K and V hold OCP FP8 E4M3 bytes (1 sign, 4 exponent bits
+   with bias 7, 3 fraction bits, no infinities, 0x7f / 0xff are NaN); a
+   cached value means byte_value * k_scale (K) or * v_scale (V), both finite
+   and > 0.  Layouts, one byte per value, 2 KiB per (block, KV head):
+       k_cache  [num_blocks][num_kv_heads][8][16][16]
+                (dim group g, token t, dim 16g+i)
+       v_cache  [num_blocks][num_kv_heads][16][128]   (token, dim)
+   q and out stay fp16.  The kernel widens E4M3 to fp16 exactly, applies
+   k_scale to the scores and v_scale to the output, and otherwise computes
+   exactly as paged_attn_decode does.  Everything else -- shape, options,
+   workspace, debug outputs, status codes -- is as for paged_attn_decode;
+   debug_gather_k receives the widened K bytes before k_scale. */
+int paged_attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache,
+                          const int32_t *block_tables, const int32_t *context_lens,
+                          float scale, float k_scale, float v_scale, void *out,
+                          const pa_shape *shape, const pa_options *opts, void *stream);
+
 /* Plan for (shape, opts) without launching.  Host-only. */
 int paged_attn_plan(const pa_shape *shape, const pa_options *opts,
                     pa_plan_info *info);

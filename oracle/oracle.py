@@ -47,6 +47,15 @@ def _load():
     lib.pao_decode_rows_f64.restype = ctypes.c_int
     lib.pao_half_to_double.argtypes = [ctypes.c_uint16]
     lib.pao_half_to_double.restype = ctypes.c_double
+    lib.pao_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    lib.pao_e4m3_to_double.restype = ctypes.c_double
+    f = ctypes.c_float
+    lib.pao_decode_fp8_f64.argtypes = [p, p, p, p, p, f, f, f, i32, i32, i32, i32, i32, i32,
+                                       i64, p, i32]
+    lib.pao_decode_fp8_f64.restype = ctypes.c_int
+    lib.pao_decode_fp8_rows_f64.argtypes = [p, p, p, p, p, f, f, f, i32, i32, i32, i32, i32,
+                                            i32, i64, p, p, i64, p, i32]
+    lib.pao_decode_fp8_rows_f64.restype = ctypes.c_int
     lib.pao_max_threads.argtypes = []
     lib.pao_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -63,10 +72,15 @@ def half_to_double(bits: int) -> float:
     return float(_load().pao_half_to_double(int(bits) & 0xFFFF))
 
 
-def _prep(q, k_cache, v_cache, block_tables, context_lens):
+def e4m3_to_double(bits: int) -> float:
+    """The oracle's own OCP FP8 E4M3 decoder, exposed so tests can pin it."""
+    return float(_load().pao_e4m3_to_double(int(bits) & 0xFF))
+
+
+def _prep(q, k_cache, v_cache, block_tables, context_lens, kv_dtype=np.float16):
     q = np.ascontiguousarray(q, dtype=np.float16)
-    k_cache = np.ascontiguousarray(k_cache, dtype=np.float16)
-    v_cache = np.ascontiguousarray(v_cache, dtype=np.float16)
+    k_cache = np.ascontiguousarray(k_cache, dtype=kv_dtype)
+    v_cache = np.ascontiguousarray(v_cache, dtype=kv_dtype)
     bt = np.ascontiguousarray(block_tables, dtype=np.int32)
     ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
     if q.ndim != 3 or k_cache.ndim != 4 or v_cache.shape != k_cache.shape:
@@ -114,5 +128,38 @@ def paged_attention_rows_f64(q, k_cache, v_cache, block_tables, context_lens,
                                      _ptr(ctx), float(np.float32(scale)), B, Hq,
                                      Hkv, D, T, MB, NB, _ptr(rb), _ptr(rh),
                                      rows.shape[0], _ptr(out), int(threads))
+    _check(rc)
+    return out
+
+
+def paged_attention_fp8_f64(q, k8, v8, block_tables, context_lens, scale, k_scale, v_scale,
+                            threads: int = 0) -> np.ndarray:
+    """E4M3 caches (uint8 [NB, Hkv, T, D], token-major), values byte * scale.
+    All (b, h) rows; float64 [B, Hq, D]."""
+    q, k, v, bt, ctx, (B, Hq, Hkv, D, T, MB, NB) = _prep(
+        q, k8, v8, block_tables, context_lens, np.uint8)
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    rc = _load().pao_decode_fp8_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(bt), _ptr(ctx),
+                                    float(np.float32(scale)), float(np.float32(k_scale)),
+                                    float(np.float32(v_scale)), B, Hq, Hkv, D, T, MB, NB,
+                                    _ptr(out), int(threads))
+    _check(rc)
+    return out
+
+
+def paged_attention_fp8_rows_f64(q, k8, v8, block_tables, context_lens, scale, k_scale,
+                                 v_scale, rows, threads: int = 0) -> np.ndarray:
+    """The listed (b, h) rows of paged_attention_fp8_f64; returns [n, D]."""
+    q, k, v, bt, ctx, (B, Hq, Hkv, D, T, MB, NB) = _prep(
+        q, k8, v8, block_tables, context_lens, np.uint8)
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 2)
+    rb = np.ascontiguousarray(rows[:, 0], dtype=np.int32)
+    rh = np.ascontiguousarray(rows[:, 1], dtype=np.int32)
+    out = np.zeros((rows.shape[0], D), dtype=np.float64)
+    rc = _load().pao_decode_fp8_rows_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(bt), _ptr(ctx),
+                                         float(np.float32(scale)), float(np.float32(k_scale)),
+                                         float(np.float32(v_scale)), B, Hq, Hkv, D, T, MB, NB,
+                                         _ptr(rb), _ptr(rh), rows.shape[0], _ptr(out),
+                                         int(threads))
     _check(rc)
     return out

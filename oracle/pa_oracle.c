@@ -38,6 +38,11 @@
  *   out     [B][Hq][D]           double
  * ctx[b] <= 0 gives an all-zero row.  Tokens t >= ctx[b], block-table
  * padding and unused pool blocks are never read.
+ *
+ * FP8 caches (the PagedAttention answer, section 4, names FP8 KV storage):
+ * the same layouts with one OCP E4M3 byte per value; a cached value means
+ * decode(byte) * k_scale for K and decode(byte) * v_scale for V, and the
+ * attention is the same definition applied to those values.
  */
 #include <math.h>
 #include <stdint.h>
@@ -71,12 +76,42 @@ double pao_half_to_double(uint16_t h) {
     return sign ? -mag : mag;
 }
 
+/* OCP FP8 E4M3 -> double, exact.  1 sign bit, 4 exponent bits (bias 7),
+ * 3 fraction bits; exponent 0 is subnormal; no infinities; exponent 15 with
+ * fraction 7 (0x7f, 0xff) is NaN, every other exponent-15 code is a normal
+ * number (the largest is 448). */
+double pao_e4m3_to_double(uint8_t x) {
+    const int sign = (x >> 7) & 1;
+    const int expo = (x >> 3) & 0xf;
+    const int frac = x & 0x7;
+    double mag;
+    if (expo == 0xf && frac == 0x7) {
+        mag = NAN;
+    } else if (expo == 0) {
+        mag = ldexp((double)frac, -9);
+    } else {
+        mag = ldexp((double)(8 + frac), expo - 10);
+    }
+    return sign ? -mag : mag;
+}
+
+/* Element idx of a K or V pool: fp16 bits, or E4M3 bytes times their scale. */
+typedef struct {
+    const void *data;
+    int fp8;
+    double scale;
+} pao_pool;
+
+static double pao_at(pao_pool p, int64_t idx) {
+    if (p.fp8) return pao_e4m3_to_double(((const uint8_t *)p.data)[idx]) * p.scale;
+    return pao_half_to_double(((const uint16_t *)p.data)[idx]);
+}
+
 /* One (b, h) output row.  Returns a PAO_* code. */
-static int pao_row(const uint16_t *q, const uint16_t *k_cache,
-                   const uint16_t *v_cache, const int32_t *bt,
-                   const int32_t *ctx, double scale, int b, int h, int Hq,
-                   int Hkv, int D, int T, int MB, int64_t NB, double *out_row,
-                   double *s /* scratch, >= MB*T */) {
+static int pao_row(const uint16_t *q, pao_pool k_cache, pao_pool v_cache,
+                   const int32_t *bt, const int32_t *ctx, double scale, int b,
+                   int h, int Hq, int Hkv, int D, int T, int MB, int64_t NB,
+                   double *out_row, double *s /* scratch, >= MB*T */) {
     const int g = Hq / Hkv;
     const int kvh = h / g;
     const int L = ctx[b];
@@ -92,10 +127,10 @@ static int pao_row(const uint16_t *q, const uint16_t *k_cache,
     for (t = 0; t < L; ++t) {
         const int32_t p = bt[(int64_t)b * MB + t / T];
         if (p < 0 || (int64_t)p >= NB) return PAO_ERR_BLOCK_ID;
-        const uint16_t *krow = k_cache + (((int64_t)p * Hkv + kvh) * T + t % T) * D;
+        const int64_t krow = (((int64_t)p * Hkv + kvh) * T + t % T) * D;
         double dot = 0.0;
         for (d = 0; d < D; ++d)
-            dot += pao_half_to_double(qrow[d]) * pao_half_to_double(krow[d]);
+            dot += pao_half_to_double(qrow[d]) * pao_at(k_cache, krow + d);
         s[t] = scale * dot;
         if (s[t] > m) m = s[t];
     }
@@ -110,8 +145,8 @@ static int pao_row(const uint16_t *q, const uint16_t *k_cache,
     /* weighted sum of V rows */
     for (t = 0; t < L; ++t) {
         const int32_t p = bt[(int64_t)b * MB + t / T];
-        const uint16_t *vrow = v_cache + (((int64_t)p * Hkv + kvh) * T + t % T) * D;
-        for (d = 0; d < D; ++d) out_row[d] += s[t] * pao_half_to_double(vrow[d]);
+        const int64_t vrow = (((int64_t)p * Hkv + kvh) * T + t % T) * D;
+        for (d = 0; d < D; ++d) out_row[d] += s[t] * pao_at(v_cache, vrow + d);
     }
     for (d = 0; d < D; ++d) out_row[d] /= Z;
     return PAO_OK;
@@ -124,16 +159,14 @@ static int pao_check_shape(int B, int Hq, int Hkv, int D, int T, int MB, int64_t
     return PAO_OK;
 }
 
-/* Rows listed in (rows_b[i], rows_h[i]) for i < nrows; out is [nrows][D]. */
-int pao_decode_rows_f64(const uint16_t *q, const uint16_t *k_cache,
-                        const uint16_t *v_cache, const int32_t *bt,
-                        const int32_t *ctx, float scale, int B, int Hq, int Hkv,
-                        int D, int T, int MB, int64_t NB, const int32_t *rows_b,
-                        const int32_t *rows_h, int64_t nrows, double *out,
-                        int nthreads) {
+static int pao_rows(const uint16_t *q, pao_pool k_cache, pao_pool v_cache,
+                    const int32_t *bt, const int32_t *ctx, float scale, int B,
+                    int Hq, int Hkv, int D, int T, int MB, int64_t NB,
+                    const int32_t *rows_b, const int32_t *rows_h, int64_t nrows,
+                    double *out, int nthreads) {
     int rc = pao_check_shape(B, Hq, Hkv, D, T, MB, NB);
     if (rc) return rc;
-    if (!q || !k_cache || !v_cache || !bt || !ctx || !rows_b || !rows_h || !out)
+    if (!q || !k_cache.data || !v_cache.data || !bt || !ctx || !rows_b || !rows_h || !out)
         return nrows == 0 ? PAO_OK : PAO_ERR_ARG;
     for (int64_t i = 0; i < nrows; ++i)
         if (rows_b[i] < 0 || rows_b[i] >= B || rows_h[i] < 0 || rows_h[i] >= Hq)
@@ -169,10 +202,10 @@ int pao_decode_rows_f64(const uint16_t *q, const uint16_t *k_cache,
 }
 
 /* Every (b, h); out is [B][Hq][D]. */
-int pao_decode_f64(const uint16_t *q, const uint16_t *k_cache,
-                   const uint16_t *v_cache, const int32_t *bt,
-                   const int32_t *ctx, float scale, int B, int Hq, int Hkv,
-                   int D, int T, int MB, int64_t NB, double *out, int nthreads) {
+static int pao_all(const uint16_t *q, pao_pool k_cache, pao_pool v_cache,
+                   const int32_t *bt, const int32_t *ctx, float scale, int B,
+                   int Hq, int Hkv, int D, int T, int MB, int64_t NB, double *out,
+                   int nthreads) {
     int rc = pao_check_shape(B, Hq, Hkv, D, T, MB, NB);
     if (rc) return rc;
     const int64_t n = (int64_t)B * Hq;
@@ -187,11 +220,54 @@ int pao_decode_f64(const uint16_t *q, const uint16_t *k_cache,
         rb[i] = (int32_t)(i / Hq);
         rh[i] = (int32_t)(i % Hq);
     }
-    rc = pao_decode_rows_f64(q, k_cache, v_cache, bt, ctx, scale, B, Hq, Hkv, D,
-                             T, MB, NB, rb, rh, n, out, nthreads);
+    rc = pao_rows(q, k_cache, v_cache, bt, ctx, scale, B, Hq, Hkv, D, T, MB, NB,
+                  rb, rh, n, out, nthreads);
     free(rb);
     free(rh);
     return rc;
+}
+
+/* fp16 caches. */
+int pao_decode_f64(const uint16_t *q, const uint16_t *k_cache,
+                   const uint16_t *v_cache, const int32_t *bt,
+                   const int32_t *ctx, float scale, int B, int Hq, int Hkv,
+                   int D, int T, int MB, int64_t NB, double *out, int nthreads) {
+    pao_pool k = {k_cache, 0, 1.0}, v = {v_cache, 0, 1.0};
+    return pao_all(q, k, v, bt, ctx, scale, B, Hq, Hkv, D, T, MB, NB, out, nthreads);
+}
+
+/* Rows listed in (rows_b[i], rows_h[i]) for i < nrows; out is [nrows][D]. */
+int pao_decode_rows_f64(const uint16_t *q, const uint16_t *k_cache,
+                        const uint16_t *v_cache, const int32_t *bt,
+                        const int32_t *ctx, float scale, int B, int Hq, int Hkv,
+                        int D, int T, int MB, int64_t NB, const int32_t *rows_b,
+                        const int32_t *rows_h, int64_t nrows, double *out,
+                        int nthreads) {
+    pao_pool k = {k_cache, 0, 1.0}, v = {v_cache, 0, 1.0};
+    return pao_rows(q, k, v, bt, ctx, scale, B, Hq, Hkv, D, T, MB, NB, rows_b,
+                    rows_h, nrows, out, nthreads);
+}
+
+/* E4M3 caches with per-tensor scales (applied in double). */
+int pao_decode_fp8_f64(const uint16_t *q, const uint8_t *k_cache,
+                       const uint8_t *v_cache, const int32_t *bt,
+                       const int32_t *ctx, float scale, float k_scale,
+                       float v_scale, int B, int Hq, int Hkv, int D, int T,
+                       int MB, int64_t NB, double *out, int nthreads) {
+    pao_pool k = {k_cache, 1, (double)k_scale}, v = {v_cache, 1, (double)v_scale};
+    return pao_all(q, k, v, bt, ctx, scale, B, Hq, Hkv, D, T, MB, NB, out, nthreads);
+}
+
+int pao_decode_fp8_rows_f64(const uint16_t *q, const uint8_t *k_cache,
+                            const uint8_t *v_cache, const int32_t *bt,
+                            const int32_t *ctx, float scale, float k_scale,
+                            float v_scale, int B, int Hq, int Hkv, int D, int T,
+                            int MB, int64_t NB, const int32_t *rows_b,
+                            const int32_t *rows_h, int64_t nrows, double *out,
+                            int nthreads) {
+    pao_pool k = {k_cache, 1, (double)k_scale}, v = {v_cache, 1, (double)v_scale};
+    return pao_rows(q, k, v, bt, ctx, scale, B, Hq, Hkv, D, T, MB, NB, rows_b,
+                    rows_h, nrows, out, nthreads);
 }
 
 int pao_max_threads(void) {

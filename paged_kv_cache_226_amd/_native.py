@@ -62,6 +62,10 @@ def lib():
     L.paged_attn_decode.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                     ctypes.POINTER(PaShape), ctypes.POINTER(PaOptions), vp]
     L.paged_attn_decode.restype = ctypes.c_int
+    f32 = ctypes.c_float
+    L.paged_attn_decode_fp8.argtypes = [vp, vp, vp, vp, vp, f32, f32, f32, vp,
+                                        ctypes.POINTER(PaShape), ctypes.POINTER(PaOptions), vp]
+    L.paged_attn_decode_fp8.restype = ctypes.c_int
     L.paged_attn_plan.argtypes = [ctypes.POINTER(PaShape), ctypes.POINTER(PaOptions),
                                   ctypes.POINTER(PaPlanInfo)]
     L.paged_attn_plan.restype = ctypes.c_int

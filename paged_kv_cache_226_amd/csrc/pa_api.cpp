@@ -127,10 +127,15 @@ size_t paged_attn_workspace_size(const pa_shape* sh, const pa_options* o) {
   return pl.ws_bytes;
 }
 
-int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* block_tables, const int32_t* context_lens,
-                      float scale, void* out, const pa_shape* sh, const pa_options* o,
-                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by the fp16 and the E4M3 entry points.
+int decode_impl(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens, float scale,
+                bool kv8, float k_scale, float v_scale, void* out, const pa_shape* sh,
+                const pa_options* o, void* stream) {
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return PA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
@@ -138,6 +143,8 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
       (reinterpret_cast<uintptr_t>(context_lens) & 3u))
     return PA_ERR_INVALID_ARG;
   if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (!isfinite(k_scale) || !isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f))
+    return PA_ERR_INVALID_ARG;
   Plan pl;
   int rc = make_plan(sh, o, &pl);
   if (rc) return rc;
@@ -157,8 +164,8 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
   pa::DecodeArgs a;
   memset(&a, 0, sizeof(a));
   a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k_cache);
-  a.v = static_cast<const uint16_t*>(v_cache);
+  a.k = k_cache;
+  a.v = v_cache;
   a.bt = block_tables;
   a.ctx = context_lens;
   a.out = static_cast<uint16_t*>(out);
@@ -167,7 +174,8 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
   a.dbg_err = o->debug_error_word;
   a.sink = nullptr;
   a.sink_enable = 0;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.scale_log2 = (float)((double)scale * (double)k_scale * 1.4426950408889634);
+  a.v_scale = v_scale;
   a.B = sh->num_seqs;
   a.Hq = sh->num_q_heads;
   a.Hkv = sh->num_kv_heads;
@@ -176,7 +184,7 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
   a.P = pl.P;
   a.PB = pl.PB;
   a.NB = sh->num_blocks;
-  a.blk_bytes = (int64_t)sh->num_kv_heads * PA_BLOCK_SIZE * PA_HEAD_DIM * 2;
+  a.blk_bytes = (int64_t)sh->num_kv_heads * PA_BLOCK_SIZE * PA_HEAD_DIM * (kv8 ? 1 : 2);
   a.lds_bt_bytes = pa::lds_bt_bytes_for(pl.PB);
   a.pf_dist = o->prefetch_distance > 0 ? o->prefetch_distance : 1;
   const bool dbg = o->debug_gather_k || o->debug_trace || o->debug_error_word;
@@ -188,9 +196,29 @@ int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
     a.ws_ml = ws;
     a.ws_o = ws + rows * 2;
   }
-  if (pa::launch_decode(a, pl.pf, dbg, pl.waves, st) != hipSuccess) return PA_ERR_HIP;
+  if (pa::launch_decode(a, pl.pf, dbg, kv8, pl.waves, st) != hipSuccess) return PA_ERR_HIP;
   if (pl.P > 1 && pa::launch_reduce(a, st) != hipSuccess) return PA_ERR_HIP;
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      float scale, void* out, const pa_shape* sh, const pa_options* o,
+                      void* stream) {
+  return decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, false, 1.f, 1.f,
+                     out, sh, o, stream);
+}
+
+int paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          float scale, float k_scale, float v_scale, void* out,
+                          const pa_shape* sh, const pa_options* o, void* stream) {
+  return decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, true, k_scale,
+                     v_scale, out, sh, o, stream);
 }
 
 // Streaming-read grid: 2048 work-groups of 256 threads (8 per CU on 256

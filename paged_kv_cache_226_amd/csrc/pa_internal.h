@@ -10,8 +10,9 @@ namespace pa {
 // Everything a decode launch needs, passed by value as the kernel argument.
 struct DecodeArgs {
   const uint16_t* q;     // [B][Hq][128] fp16
-  const uint16_t* k;     // [NB][Hkv][16 dim groups][16 tokens][8] fp16
-  const uint16_t* v;     // [NB][Hkv][16][128] fp16
+  const void* k;         // fp16 [NB][Hkv][16 dim groups][16 tokens][8], or
+                         // E4M3 [NB][Hkv][8 dim groups][16 tokens][16]
+  const void* v;         // fp16 or E4M3 [NB][Hkv][16 tokens][128]
   const int32_t* bt;     // [B][MB]
   const int32_t* ctx;    // [B]
   uint16_t* out;         // [B][Hq][128] fp16
@@ -21,7 +22,8 @@ struct DecodeArgs {
   int32_t* dbg_trace;    // see pa_options.debug_trace
   int32_t* dbg_err;      // see pa_options.debug_error_word
   int32_t* sink;         // never written while sink_enable == 0
-  float scale_log2;      // scale * log2(e)
+  float scale_log2;      // scale * log2(e) (times the K scale for E4M3 caches)
+  float v_scale;         // 1, or the V scale of an E4M3 cache
   int B, Hq, Hkv, MB;
   int G;                 // query heads per KV head, 1..16
   int P;                 // partitions in the grid
@@ -39,7 +41,8 @@ inline size_t decode_lds_bytes(int PB, int g, int waves) {
   return (size_t)lds_bt_bytes_for(PB) + (size_t)waves * g * (128 + 2) * 4;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, int waves, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int waves,
+                         hipStream_t st);
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_stream_read(const void* buf, size_t bytes, void* sink, int groups,
                               hipStream_t st);

@@ -70,17 +70,47 @@ __device__ __forceinline__ uint32_t pick_halves(uint32_t lo, uint32_t hi, int h)
   return __builtin_amdgcn_perm(hi, lo, h ? 0x07060302u : 0x05040100u);
 }
 
+// One block as loaded by a lane.  fp16 cache: k[ch] = token pi(c), dims
+// 32ch+8G..+7 and v[i] = token 4i+G, dims 8c..8c+7.  FP8 (E4M3) cache:
+// k[m] = token pi(c), dims 64m+16G..+15 and v[i] = token 4i+G, dims
+// 8c..8c+7, one byte each.
+template <bool KV8>
 struct BlockBuf {
-  u32x4 k[4];  // chunk ch: token pi(c), dims 32ch+8G .. +7
-  u32x4 v[4];  // i: token 4i+G, dims 8c .. 8c+7
+  u32x4 k[4];
+  u32x4 v[4];
 };
+template <>
+struct BlockBuf<true> {
+  u32x4 k[2];
+  u32x2 v[4];
+};
+
+// Eight E4M3 values (two dwords, lowest byte first) widened to fp16.  Every
+// E4M3 value is exactly representable in fp16, and the conversion scale is
+// 1, so this step is exact; the cache scales are applied to the scores and
+// to the output instead.
+__device__ __forceinline__ u32x4 widen_fp8x8(uint32_t w0, uint32_t w1) {
+  return u32x4{
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true))};
+}
+
+// First of the 8 dims that MFMA chunk ch of Q.K^T covers in lane group lg.
+// The dot product sums over dims, so K and Q only need the same mapping;
+// each cache layout uses the one that its 128-bit loads deliver.
+template <bool KV8>
+__device__ __forceinline__ int chunk_dim(int ch, int lg) {
+  return KV8 ? 64 * (ch >> 1) + 16 * lg + 8 * (ch & 1) : 32 * ch + 8 * lg;
+}
 
 // ---------------------------------------------------------------------------
 // Walks blocks [s, e) of (sequence b, KV head kvh) with the W waves of the
 // work-group (wave w takes s+w, s+w+W, ...) and leaves one record
 // (m, l, o[128]) per wave and query head in merge_s.  Every thread of the
 // work-group calls it; it synchronises the work-group.
-template <int PF, bool DBG>
+template <int PF, bool DBG, bool KV8>
 __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, const int kvh,
                                            const int ctx, const int s, const int e,
                                            int32_t* bt_s, float* merge_s) {
@@ -97,16 +127,16 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
   const int32_t* bt_row = a.bt + (int64_t)b * a.MB;
   for (int i = tid; i < e - s; i += blockDim.x) bt_s[i] = bt_row[s + i];
 
-  // Q^T operand: lane (lg, c), chunk ch = dims 32ch+8lg .. +7 of head c
-  // (zero for the padding columns c >= G).
+  // Q^T operand: lane (lg, c), chunk ch = 8 dims of head c starting at
+  // chunk_dim(ch, lg) (zero for the padding columns c >= G).
   half8_t qb[4];
   {
     const int hc = c < G ? c : 0;
-    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + kvh * G + hc) * kD + 8 * lg;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + kvh * G + hc) * kD;
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
       u32x4 w4 = {0u, 0u, 0u, 0u};
-      if (c < G) w4 = *reinterpret_cast<const u32x4*>(qrow + 32 * ch);
+      if (c < G) w4 = *reinterpret_cast<const u32x4*>(qrow + chunk_dim<KV8>(ch, lg));
       qb[ch] = __builtin_bit_cast(half8_t, w4);
     }
   }
@@ -118,31 +148,47 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  constexpr int kHeadBytes = KV8 ? kBlockHeadBytes / 2 : kBlockHeadBytes;
   const unsigned char* kbase =
-      reinterpret_cast<const unsigned char*>(a.k) + (int64_t)kvh * kBlockHeadBytes;
+      reinterpret_cast<const unsigned char*>(a.k) + (int64_t)kvh * kHeadBytes;
   const unsigned char* vbase =
-      reinterpret_cast<const unsigned char*>(a.v) + (int64_t)kvh * kBlockHeadBytes;
-  const int k_off = (lg * kT + pic) * 16;
-  const int v_off = lane * 16;
+      reinterpret_cast<const unsigned char*>(a.v) + (int64_t)kvh * kHeadBytes;
+  const int k_off = (lg * kT + pic) * 16;      // the 16-byte piece of K row pic
+  const int v_off = lane * (KV8 ? 8 : 16);     // token lg, dims 8c..8c+7
+  typedef BlockBuf<KV8> Buf;
 
   // K/V are streamed: every byte is used once, by this wave, so the loads
   // are non-temporal (they do not displace lines that will be reused).  The
   // L2 touch of the look-ahead modes is an ordinary load: it is meant to
   // leave its lines in the cache.
-  auto load_block = [&](BlockBuf& buf, int64_t ph) {
+  // Every load instruction reads 1 KiB (fp16) or 512 B / 1 KiB (FP8 V / K)
+  // of contiguous memory.
+  auto load_block = [&](Buf& buf, int64_t ph) {
     const unsigned char* kb = kbase + ph * a.blk_bytes + k_off;
     const unsigned char* vb = vbase + ph * a.blk_bytes + v_off;
+    if constexpr (KV8) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) buf.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + 1024 * i));
+      for (int i = 0; i < 2; ++i)
+        buf.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + 1024 * i));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) buf.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + 1024 * i));
+      for (int i = 0; i < 4; ++i)
+        buf.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vb + 512 * i));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        buf.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + 1024 * i));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        buf.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + 1024 * i));
+    }
   };
 
-  // One dword per lane: lanes 0-31 cover the 32 lines of the K block, lanes
-  // 32-63 those of the V block.
+  // One dword per lane: lanes 0-31 cover the 128 B lines of the K block
+  // (32 fp16 / 16 FP8), lanes 32-63 those of the V block.
   auto touch_block = [&](int64_t ph) -> uint32_t {
+    constexpr int kLines = kHeadBytes / 128;
     const unsigned char* base = (lane < 32 ? kbase : vbase) + ph * a.blk_bytes;
-    return *reinterpret_cast<const uint32_t*>(base + (lane & 31) * 128);
+    return *reinterpret_cast<const uint32_t*>(base + (lane & (kLines - 1)) * 128);
   };
 
   auto trace_put = [&](int j, int slot, int value) {
@@ -150,26 +196,41 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
       a.dbg_trace[(((int64_t)b * a.Hkv + kvh) * a.MB + j) * 2 + slot] = value;
   };
 
-  auto compute = [&](BlockBuf& buf, int j) {
+  auto compute = [&](Buf& buf, int j) {
+    // fp16 operands: K chunks and V rows
+    u32x4 kh[4], vh[4];
+    if constexpr (KV8) {
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch)
+        kh[ch] = widen_fp8x8(buf.k[ch >> 1][2 * (ch & 1)], buf.k[ch >> 1][2 * (ch & 1) + 1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vh[i] = widen_fp8x8(buf.v[i].x, buf.v[i].y);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kh[i] = buf.k[i];
+        vh[i] = buf.v[i];
+      }
+    }
     if (DBG && a.dbg_k) {
       unsigned char* dst = reinterpret_cast<unsigned char*>(a.dbg_k) +
-                           ((((int64_t)b * a.Hkv + kvh) * a.MB + j) * kT + pic) * kD * 2 +
-                           lg * 16;
+                           ((((int64_t)b * a.Hkv + kvh) * a.MB + j) * kT + pic) * kD * 2;
 #pragma unroll
-      for (int ch = 0; ch < 4; ++ch) *reinterpret_cast<u32x4*>(dst + 64 * ch) = buf.k[ch];
+      for (int ch = 0; ch < 4; ++ch)
+        *reinterpret_cast<u32x4*>(dst + 2 * chunk_dim<KV8>(ch, lg)) = kh[ch];
     }
     const int rem = ctx - j * kT;  // valid tokens in this block, >= 1
     const bool tail = rem < kT;
     if (tail) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (4 * i + lg >= rem) buf.v[i] = u32x4{0u, 0u, 0u, 0u};
+        if (4 * i + lg >= rem) vh[i] = u32x4{0u, 0u, 0u, 0u};
     }
     // scores of tokens 4q+lg for head c
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, buf.k[ch]),
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, kh[ch]),
                                                      qb[ch], sacc, 0, 0, 0);
     float sc[4];
 #pragma unroll
@@ -203,8 +264,8 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
     for (int t = 0; t < 8; ++t) {
       const int u = t >> 1, h = t & 1;
       u32x2 vt;
-      vt.x = pick_halves(buf.v[0][u], buf.v[1][u], h);
-      vt.y = pick_halves(buf.v[2][u], buf.v[3][u], h);
+      vt.x = pick_halves(vh[0][u], vh[1][u], h);
+      vt.y = pick_halves(vh[2][u], vh[3][u], h);
       const half4_t av = __builtin_bit_cast(half4_t, vt);
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, phi, acc[t], 0, 0, 0);
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, plo, acc[t], 0, 0, 0);
@@ -256,7 +317,7 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
     int it = 0;
     for (; it + 1 < n_it; ++it) {  // block j+W exists
       const int j = j0 + it * W;
-      BlockBuf buf;
+      Buf buf;
       load_block(buf, phys_it(it));
       uint32_t got = 0;
       if (PF == 1 && it + a.pf_dist < n_it) {
@@ -273,16 +334,16 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
     }
     if (it < n_it) {  // this wave's last block: nothing left to fetch ahead
       const int j = j0 + it * W;
-      BlockBuf buf;
+      Buf buf;
       load_block(buf, phys_it(it));
       trace_put(j, 0, (wave << 16) | it);
       compute(buf, j);
     }
     sink ^= pend;
   } else {
-    BlockBuf bufA, bufB;
+    Buf bufA, bufB;
     uint32_t pend = 0;
-    auto step = [&](BlockBuf& cur, BlockBuf& nxt, int it) {
+    auto step = [&](Buf& cur, Buf& nxt, int it) {
       const int j = j0 + it * W;
       load_block(nxt, phys_it(it + 1));
       trace_put(j + W, 1, wave);
@@ -360,7 +421,7 @@ __device__ __forceinline__ void combine_waves(const float* merge_s, int W, int G
 }
 
 // ---------------------------------------------------------------------------
-template <int PF, bool DBG>
+template <int PF, bool DBG, bool KV8>
 __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   int32_t* bt_s = reinterpret_cast<int32_t*>(smem_raw);
@@ -399,7 +460,7 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
     return;
   }
 
-  walk_range<PF, DBG>(a, b, kvh, ctx, s, e, bt_s, merge_s);
+  walk_range<PF, DBG, KV8>(a, b, kvh, ctx, s, e, bt_s, merge_s);
 
   for (int idx = tid; idx < G * kD; idx += blockDim.x) {
     const int h = idx / kD, d = idx % kD;
@@ -407,7 +468,7 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
     combine_waves(merge_s, W, G, h, d, M, L, O);
     const int64_t row = (int64_t)b * a.Hq + kvh * G + h;
     if (a.P == 1) {
-      a.out[row * kD + d] = f32_to_f16_bits(O / L);
+      a.out[row * kD + d] = f32_to_f16_bits(O * a.v_scale / L);
     } else {
       const int64_t pr = row * a.P + p;
       if (d == 0) {
@@ -443,7 +504,7 @@ __global__ void __launch_bounds__(128) pa_reduce_kernel(const DecodeArgs a) {
     L += al * ml[2 * q + 1];
     O += al * o[(int64_t)q * kD + d];
   }
-  a.out[(int64_t)row * kD + d] = f32_to_f16_bits(O / L);
+  a.out[(int64_t)row * kD + d] = f32_to_f16_bits(O * a.v_scale / L);
 }
 
 // ---------------------------------------------------------------------------
@@ -486,23 +547,30 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const u32x4* __restric
 // ---------------------------------------------------------------------------
 // Launchers.
 
-template <int PF, bool DBG>
+template <int PF, bool DBG, bool KV8>
 static hipError_t launch_decode_t(const DecodeArgs& a, dim3 grid, dim3 block, size_t lds,
                                   hipStream_t st) {
-  hipLaunchKernelGGL((pa_decode_kernel<PF, DBG>), grid, block, lds, st, a);
+  hipLaunchKernelGGL((pa_decode_kernel<PF, DBG, KV8>), grid, block, lds, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, int waves, hipStream_t st) {
+hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int waves,
+                         hipStream_t st) {
   typedef hipError_t (*fn_t)(const DecodeArgs&, dim3, dim3, size_t, hipStream_t);
-  static const fn_t table[8] = {
-      launch_decode_t<0, false>, launch_decode_t<0, true>, launch_decode_t<1, false>,
-      launch_decode_t<1, true>,  launch_decode_t<2, false>, launch_decode_t<2, true>,
-      launch_decode_t<3, false>, launch_decode_t<3, true>};
+  static const fn_t table[16] = {
+      launch_decode_t<0, false, false>, launch_decode_t<0, true, false>,
+      launch_decode_t<1, false, false>, launch_decode_t<1, true, false>,
+      launch_decode_t<2, false, false>, launch_decode_t<2, true, false>,
+      launch_decode_t<3, false, false>, launch_decode_t<3, true, false>,
+      launch_decode_t<0, false, true>,  launch_decode_t<0, true, true>,
+      launch_decode_t<1, false, true>,  launch_decode_t<1, true, true>,
+      launch_decode_t<2, false, true>,  launch_decode_t<2, true, true>,
+      launch_decode_t<3, false, true>,  launch_decode_t<3, true, true>};
   if (pf < 0 || pf > 3) return hipErrorInvalidValue;
   const dim3 grid(a.Hkv, a.B, a.P);
   const dim3 block(kWave * waves);
-  return table[pf * 2 + (dbg ? 1 : 0)](a, grid, block, decode_lds_bytes(a.PB, a.G, waves), st);
+  return table[(kv8 ? 8 : 0) + pf * 2 + (dbg ? 1 : 0)](a, grid, block,
+                                                      decode_lds_bytes(a.PB, a.G, waves), st);
 }
 
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t st) {

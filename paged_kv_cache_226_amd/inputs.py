@@ -178,6 +178,68 @@ def make_case(num_seqs: int, num_q_heads: int, num_kv_heads: int,
     return out
 
 
+@dataclasses.dataclass
+class PagedInputsFP8:
+    q: np.ndarray             # fp16 [B, Hq, D]
+    k8: np.ndarray            # uint8 E4M3 [NB, Hkv, T, D] (token-major, logical)
+    v8: np.ndarray            # uint8 E4M3 [NB, Hkv, T, D]
+    block_tables: np.ndarray  # int32 [B, MB]
+    context_lens: np.ndarray  # int32 [B]
+    scale: float
+    k_scale: float            # a cached K value is decode(byte) * k_scale
+    v_scale: float
+    name: str = "case_fp8"
+
+
+# Per-tensor scales of the synthetic FP8 caches: powers of two, so a value
+# N(0, 1) / scale stays below E4M3's 448 with a wide margin and every
+# dequantized value is exact in fp16.
+FP8_K_SCALE = 2.0 ** -5
+FP8_V_SCALE = 2.0 ** -5
+FP8_NAN_BYTE = 0x7F
+
+
+def quantize_e4m3(x: np.ndarray, scale: float) -> np.ndarray:
+    """x / scale rounded to OCP FP8 E4M3 (torch's float8_e4m3fn conversion,
+    round to nearest even), returned as uint8 codes."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32) / np.float32(scale))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def dequantize_e4m3_fp16(codes: np.ndarray) -> np.ndarray:
+    """E4M3 codes to fp16 (exact: E4M3 is a subset of fp16), before scaling."""
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(
+        torch.float8_e4m3fn).to(torch.float16).numpy()
+
+
+def to_fp8(x: PagedInputs, k_scale: float = FP8_K_SCALE,
+           v_scale: float = FP8_V_SCALE) -> PagedInputsFP8:
+    """The same draw as an E4M3 cache: K and V quantized with the scales (NaN
+    fp16 poison becomes the E4M3 NaN code)."""
+    k8 = quantize_e4m3(x.k_cache.astype(np.float32), k_scale)
+    v8 = quantize_e4m3(x.v_cache.astype(np.float32), v_scale)
+    k8[np.isnan(x.k_cache)] = FP8_NAN_BYTE
+    v8[np.isnan(x.v_cache)] = FP8_NAN_BYTE
+    return PagedInputsFP8(x.q, k8, v8, x.block_tables, x.context_lens, x.scale,
+                          float(k_scale), float(v_scale), x.name + "_fp8")
+
+
+def pack_k_fp8(k8: np.ndarray) -> np.ndarray:
+    """E4M3 K pool in the kernel's layout [NB][Hkv][D/16][T][16]: a 16-byte
+    piece holds dims 16g..16g+15 of one token; pure reindexing."""
+    NB, H, T, D = k8.shape
+    return np.ascontiguousarray(k8.reshape(NB, H, T, D // 16, 16).transpose(0, 1, 3, 2, 4))
+
+
+def unpack_k_fp8(kp: np.ndarray) -> np.ndarray:
+    NB, H, G16, T, X = kp.shape
+    return np.ascontiguousarray(kp.transpose(0, 1, 3, 2, 4).reshape(NB, H, T, G16 * X))
+
+
 def make_inputs(workload, *, poison: bool = False) -> PagedInputs:
     """Inputs of a named workload (a key of WORKLOADS or a Workload)."""
     w = WORKLOADS[workload] if isinstance(workload, str) else workload

@@ -77,31 +77,26 @@ def workspace_bytes(q, k_cache, block_tables, **kw) -> int:
     return int(nat.lib().paged_attn_workspace_size(ctypes.byref(sh), ctypes.byref(options(**kw))))
 
 
-def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                      block_tables: torch.Tensor, context_lens: torch.Tensor,
-                      scale: Optional[float] = None, out: Optional[torch.Tensor] = None, *,
-                      prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0,
-                      prefetch_distance: int = 0,
-                      workspace: Optional[torch.Tensor] = None,
-                      debug_gather_k: Optional[torch.Tensor] = None,
-                      debug_trace: Optional[torch.Tensor] = None,
-                      debug_error_word: Optional[torch.Tensor] = None,
-                      stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """One decode step of paged attention; returns out (fp16 [B, Hq, 128]).
+def _check_kv(t: torch.Tensor, name: str, fp8: bool, ndim: int):
+    if fp8 and isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    _check(t, name, torch.uint8 if fp8 else torch.float16, ndim)
 
-    q [B, Hq, 128] fp16; k_cache [NB, Hkv, 16, 16, 8] fp16 (dim group, token, 8
-    dims); v_cache [NB, Hkv, 16, 128] fp16 (token, dim); block_tables [B, MB]
-    int32; context_lens [B] int32; scale defaults to 1/sqrt(128).
-    """
+
+def _decode(fp8: bool, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+            v_scale, out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
+            workspace, debug_gather_k, debug_trace, debug_error_word, stream):
+    name = "paged_attn_decode_fp8" if fp8 else "paged_attn_decode"
     _check(q, "q", torch.float16, 3)
-    _check(k_cache, "k_cache", torch.float16, 5)
-    _check(v_cache, "v_cache", torch.float16, 4)
+    _check_kv(k_cache, "k_cache", fp8, 5)
+    _check_kv(v_cache, "v_cache", fp8, 4)
     _check(block_tables, "block_tables", torch.int32, 2)
     _check(context_lens, "context_lens", torch.int32, 1)
-    NB, Hkv, G8, T, X = k_cache.shape
+    NB, Hkv, NG, T, X = k_cache.shape
     B, Hq, D = q.shape
-    if tuple(v_cache.shape) != (NB, Hkv, T, G8 * X) or G8 * X != D:
-        raise ValueError("k_cache must be [NB, Hkv, D/8, T, 8] and v_cache [NB, Hkv, T, D]")
+    if tuple(v_cache.shape) != (NB, Hkv, T, NG * X) or NG * X != D or X != (16 if fp8 else 8):
+        raise ValueError("k_cache must be [NB, Hkv, D/%d, T, %d] and v_cache [NB, Hkv, T, D]"
+                         % ((16, 16) if fp8 else (8, 8)))
     if block_tables.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("inconsistent shapes")
     if scale is None:
@@ -123,15 +118,68 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
             raise ValueError(f"workspace needs {need} bytes")
         o.workspace = workspace.data_ptr()
         o.workspace_bytes = workspace.numel() * workspace.element_size()
-    rc = nat.lib().paged_attn_decode(
-        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k_cache.data_ptr()),
-        ctypes.c_void_p(v_cache.data_ptr()), ctypes.c_void_p(block_tables.data_ptr()),
-        ctypes.c_void_p(context_lens.data_ptr()), ctypes.c_float(scale),
-        ctypes.c_void_p(out.data_ptr()), ctypes.byref(sh), ctypes.byref(o),
-        _stream_handle(stream))
+    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (q, k_cache, v_cache, block_tables,
+                                                      context_lens)]
+    if fp8:
+        rc = nat.lib().paged_attn_decode_fp8(
+            *ptrs, ctypes.c_float(scale), ctypes.c_float(k_scale), ctypes.c_float(v_scale),
+            ctypes.c_void_p(out.data_ptr()), ctypes.byref(sh), ctypes.byref(o),
+            _stream_handle(stream))
+    else:
+        rc = nat.lib().paged_attn_decode(
+            *ptrs, ctypes.c_float(scale), ctypes.c_void_p(out.data_ptr()), ctypes.byref(sh),
+            ctypes.byref(o), _stream_handle(stream))
     if rc != nat.PA_OK:
-        raise RuntimeError(f"paged_attn_decode: {nat.error_string(rc)} ({rc})")
+        raise RuntimeError(f"{name}: {nat.error_string(rc)} ({rc})")
     return out
+
+
+def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_tables: torch.Tensor, context_lens: torch.Tensor,
+                      scale: Optional[float] = None, out: Optional[torch.Tensor] = None, *,
+                      prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0,
+                      prefetch_distance: int = 0,
+                      workspace: Optional[torch.Tensor] = None,
+                      debug_gather_k: Optional[torch.Tensor] = None,
+                      debug_trace: Optional[torch.Tensor] = None,
+                      debug_error_word: Optional[torch.Tensor] = None,
+                      stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """One decode step of paged attention; returns out (fp16 [B, Hq, 128]).
+
+    q [B, Hq, 128] fp16; k_cache [NB, Hkv, 16, 16, 8] fp16 (dim group, token, 8
+    dims); v_cache [NB, Hkv, 16, 128] fp16 (token, dim); block_tables [B, MB]
+    int32; context_lens [B] int32; scale defaults to 1/sqrt(128).
+    """
+    return _decode(False, q, k_cache, v_cache, block_tables, context_lens, scale, 1.0, 1.0,
+                   out, prefetch, partition_blocks, waves_per_wg, prefetch_distance, workspace,
+                   debug_gather_k, debug_trace, debug_error_word, stream)
+
+
+def paged_attn_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          block_tables: torch.Tensor, context_lens: torch.Tensor,
+                          scale: Optional[float] = None, k_scale: float = 1.0,
+                          v_scale: float = 1.0, out: Optional[torch.Tensor] = None, *,
+                          prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0,
+                          prefetch_distance: int = 0,
+                          workspace: Optional[torch.Tensor] = None,
+                          debug_gather_k: Optional[torch.Tensor] = None,
+                          debug_trace: Optional[torch.Tensor] = None,
+                          debug_error_word: Optional[torch.Tensor] = None,
+                          stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Decode over an OCP E4M3 cache (uint8 or float8_e4m3fn); a cached value
+    is decode(byte) * k_scale (K) or * v_scale (V).
+
+    k_cache [NB, Hkv, 8, 16, 16] (16-dim group, token, 16 dims); v_cache
+    [NB, Hkv, 16, 128] (token, dim); the rest as paged_attn_decode.
+    debug_gather_k receives the widened K values before k_scale (fp16).
+    """
+    if k_cache.dtype == torch.float8_e4m3fn:
+        k_cache = k_cache.view(torch.uint8)
+    if v_cache.dtype == torch.float8_e4m3fn:
+        v_cache = v_cache.view(torch.uint8)
+    return _decode(True, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+                   v_scale, out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
+                   workspace, debug_gather_k, debug_trace, debug_error_word, stream)
 
 
 def stream_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None,

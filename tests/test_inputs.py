@@ -92,3 +92,18 @@ def test_workload_context_lens_matches_generation(name):
         w = dataclasses.replace(w, head_dim=8)
     x = gen.make_inputs(w)
     assert np.array_equal(gen.workload_context_lens(w), x.context_lens)
+
+
+def test_fp8_pack_and_quantize():
+    x = gen.make_case(2, 4, 2, [40, 17], seed=10, extra_pool_blocks=1)
+    x8 = gen.to_fp8(x)
+    assert x8.k8.dtype == np.uint8 and x8.k8.shape == x.k_cache.shape
+    kp = gen.pack_k_fp8(x8.k8)
+    assert kp.shape == (x.k_cache.shape[0], 2, 8, 16, 16)
+    assert np.array_equal(gen.unpack_k_fp8(kp), x8.k8)
+    assert np.array_equal(kp[3, 1, 5, 7], x8.k8[3, 1, 7, 80:96])
+    # quantization error of E4M3 round-to-nearest: at most half a step (2^-4 relative)
+    deq = gen.dequantize_e4m3_fp16(x8.k8).astype(np.float64) * x8.k_scale
+    ref = x.k_cache.astype(np.float64)
+    big = np.abs(ref) > 2.0 ** -6 * x8.k_scale * 8
+    assert (np.abs(deq - ref)[big] <= np.abs(ref)[big] * 2.0 ** -4 + 1e-12).all()

@@ -299,3 +299,58 @@ def test_planted_mistake_is_caught(name):
         assert not _pins_pass(so), f"no pin caught the planted mistake {name}"
     finally:
         shutil.rmtree(tmp)
+
+
+# ---------------------------------------------------------------------------
+# E4M3 (FP8) caches.
+
+def test_e4m3_decoder_all_bit_patterns():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([orc.e4m3_to_double(int(c)) for c in codes])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+    assert np.array_equal(got[~nan].view(np.uint64), ref[~nan].view(np.uint64))
+    assert np.nanmax(got) == 448.0 and got[1] == 2.0 ** -9 and got[0x80] == 0.0
+
+
+@pytest.mark.parametrize("seed,B,Hq,Hkv,lens", [(40, 2, 4, 4, [17, 50]), (41, 3, 10, 2, [7, 45, 29]),
+                                                (42, 1, 16, 2, [300])])
+def test_fp8_oracle_equals_fp16_oracle_on_dequantized_values(seed, B, Hq, Hkv, lens):
+    """With power-of-two scales every dequantized value is exact in fp16, so
+    the E4M3 oracle must give the fp16 oracle's bits on those fp16 values."""
+    x = gen.make_case(B, Hq, Hkv, lens, seed=seed, extra_pool_blocks=3)
+    x8 = gen.to_fp8(x)
+    a = orc.paged_attention_fp8_f64(x8.q, x8.k8, x8.v8, x8.block_tables, x8.context_lens,
+                                    x8.scale, x8.k_scale, x8.v_scale)
+    kd = (gen.dequantize_e4m3_fp16(x8.k8).astype(np.float64) * x8.k_scale).astype(np.float16)
+    vd = (gen.dequantize_e4m3_fp16(x8.v8).astype(np.float64) * x8.v_scale).astype(np.float16)
+    assert np.array_equal(kd.astype(np.float64),
+                          gen.dequantize_e4m3_fp16(x8.k8).astype(np.float64) * x8.k_scale)
+    b = orc.paged_attention_f64(x8.q, kd, vd, x8.block_tables, x8.context_lens, x8.scale)
+    assert np.array_equal(a.view(np.uint64), b.view(np.uint64))
+
+
+def test_fp8_oracle_matches_sdpa():
+    q, kp, vp, bt, ctx, kc, vc = scatter_case(43, 2, 8, 2, [33, 61])
+    k8 = gen.quantize_e4m3(kp.astype(np.float32), 0.125)
+    v8 = gen.quantize_e4m3(vp.astype(np.float32), 0.0625)
+    got = orc.paged_attention_fp8_f64(q, k8, v8, bt, ctx, SCALE, 0.125, 0.0625)
+    kcq = [gen.dequantize_e4m3_fp16(gen.quantize_e4m3(K.astype(np.float32), 0.125))
+           .astype(np.float64) * 0.125 for K in kc]
+    vcq = [gen.dequantize_e4m3_fp16(gen.quantize_e4m3(V.astype(np.float32), 0.0625))
+           .astype(np.float64) * 0.0625 for V in vc]
+    np.testing.assert_allclose(got, sdpa_ref(q, kcq, vcq, SCALE), rtol=0, atol=1e-12)
+
+
+def test_fp8_poison_is_never_read():
+    x = gen.make_case(3, 4, 2, [40, 16, 3], seed=44, extra_pool_blocks=6)
+    x8 = gen.to_fp8(x)
+    clean = orc.paged_attention_fp8_f64(x8.q, x8.k8, x8.v8, x8.block_tables, x8.context_lens,
+                                        x8.scale, x8.k_scale, x8.v_scale)
+    gen.apply_poison(x)
+    p8 = gen.to_fp8(x)
+    assert (p8.k8 == gen.FP8_NAN_BYTE).any()
+    dirty = orc.paged_attention_fp8_f64(p8.q, p8.k8, p8.v8, p8.block_tables, p8.context_lens,
+                                        p8.scale, p8.k_scale, p8.v_scale)
+    assert np.array_equal(clean.view(np.uint64), dirty.view(np.uint64))
