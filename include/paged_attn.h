@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 #define PA_HEAD_DIM 128
 #define PA_BLOCK_SIZE 16
 #define PA_G_MAX 16      /* query heads per KV head */
@@ -96,6 +96,19 @@ enum pa_prefetch {
                              block j + (1 + k)*w */
 };
 
+/* Which sequence each row of the launch grid takes.  Work-groups start in
+   grid order, so starting the longest sequences first shortens the tail of a
+   ragged batch.  The result does not depend on the order. */
+enum pa_seq_order {
+    PA_ORDER_AUTO = 0,          /* LONGEST_FIRST when 2 <= num_seqs <=
+                                   PA_RANK_MAX_SEQS, else NATURAL */
+    PA_ORDER_NATURAL = 1,       /* row r takes sequence r */
+    PA_ORDER_LONGEST_FIRST = 2  /* row r takes the sequence with the r-th most
+                                   blocks, ties by index; each work-group
+                                   ranks the context lengths on the device */
+};
+#define PA_RANK_MAX_SEQS 256
+
 typedef struct pa_shape {
     int32_t num_seqs;           /* B >= 1 */
     int32_t num_q_heads;        /* Hq >= 1 */
@@ -108,13 +121,19 @@ typedef struct pa_shape {
 
 typedef struct pa_options {
     int32_t prefetch;          /* enum pa_prefetch; negative = library default */
-    int32_t partition_blocks;  /* blocks per split-context partition; 0 = auto:
-                                  one partition per sequence when the batch has
-                                  at least 1024 (sequence, KV head) pairs, else
-                                  partitions of at most 128 blocks */
-    int32_t waves_per_wg;      /* w in {1, 2, 4, 8}; 0 = auto */
+    int32_t partition_blocks;  /* blocks per split-context partition, at most
+                                  1024; 0 = auto: one partition per sequence
+                                  when the batch has at least 256 (sequence,
+                                  KV head) pairs, else about 256 / pairs
+                                  partitions of 64..256 blocks */
+    int32_t waves_per_wg;      /* w in {1, 2, 4, 8}; 0 = auto: 8 for unsplit
+                                  batches of 256..767 pairs whose block table
+                                  is 512..1024 blocks wide, else 4 */
     int32_t prefetch_distance; /* k, the L2 touch's distance in iterations of
                                   a wave (modes 1 and 3); 0 = 1, at most 63 */
+    int32_t seq_order;         /* enum pa_seq_order; LONGEST_FIRST needs
+                                  num_seqs <= PA_RANK_MAX_SEQS */
+    int32_t reserved;          /* must be 0 */
     void *workspace;           /* device scratch for partition partials; may be
                                   NULL when the plan has one partition */
     size_t workspace_bytes;
@@ -141,6 +160,8 @@ typedef struct pa_plan_info {
     int32_t num_partitions;    /* partitions of the longest possible sequence */
     int64_t workgroups;        /* decode-kernel grid size */
     size_t workspace_bytes;    /* 0 when num_partitions == 1 */
+    int32_t seq_order;         /* PA_ORDER_NATURAL or PA_ORDER_LONGEST_FIRST */
+    int32_t reserved;
 } pa_plan_info;
 
 /* Fill *opts with the defaults (prefetch = library default, auto sizes). */

@@ -12,19 +12,30 @@
 namespace {
 
 constexpr int kDefaultPrefetch = PA_PREFETCH_REG;
-constexpr int kDefaultWaves = 4;
 constexpr int kMaxPartitionBlocks = 1024;  // LDS slice of the block table: 4 KiB
 constexpr size_t kMaxLdsBytes = 65536;     // dynamic LDS per work-group
-// Auto partition size.  When the batch alone gives at least
-// kTargetWorkgroups work-groups (four per CU on 256 CUs), every (sequence,
-// KV head) is one work-group: no split, no reduce.  Otherwise contexts are
-// split into partitions of at most kAutoPartitionBlocks blocks (1 MiB of K
-// and V), which also keeps the pieces of a ragged batch similar in size.
-constexpr int64_t kTargetWorkgroups = 1024;
-constexpr int kAutoPartitionBlocks = 128;
+// Auto plan, from measurements over the model shapes, their tensor-parallel
+// shards and a batch x context grid (U = sequences x KV heads):
+//  * U >= kOnePartitionUnits (one work-group per CU on 256 CUs): no split, so
+//    no partials and no reduce launch.  Splitting further only added
+//    per-partition overhead, even for ragged batches once the longest
+//    sequences are dispatched first.
+//  * Such work-groups get 8 waves while U < kFourWaveUnits and the table is
+//    at least kLongTableBlocks wide: with under three work-groups per CU the
+//    long sequences then finish on twice the waves (up to 9 % on a ragged
+//    batch, within 2 % either way on uniform ones).  Otherwise 4 waves: at 3
+//    resident waves per SIMD a CU holds three 4-wave work-groups but only one
+//    8-wave one.
+//  * U < kOnePartitionUnits: about kOnePartitionUnits / U partitions of
+//    kMinAutoPartition..kMaxAutoPartition blocks, 4 waves.
+constexpr int64_t kOnePartitionUnits = 256;
+constexpr int64_t kFourWaveUnits = 768;
+constexpr int kLongTableBlocks = 512;
+constexpr int kMinAutoPartition = 64;
+constexpr int kMaxAutoPartition = 256;
 
 struct Plan {
-  int pf, waves, PB, P;
+  int pf, waves, PB, P, order;
   int64_t wgs;
   size_t ws_bytes;
 };
@@ -56,37 +67,59 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   paged_attn_default_options(&d);
   if (!o) o = &d;
   if (o->prefetch_distance < 0 || o->prefetch_distance > 63) return PA_ERR_INVALID_ARG;
+  if (o->reserved != 0) return PA_ERR_INVALID_ARG;
+  int order = o->seq_order;
+  if (order < PA_ORDER_AUTO || order > PA_ORDER_LONGEST_FIRST) return PA_ERR_INVALID_ARG;
+  if (order == PA_ORDER_AUTO)
+    order = sh->num_seqs >= 2 && sh->num_seqs <= PA_RANK_MAX_SEQS ? PA_ORDER_LONGEST_FIRST
+                                                                  : PA_ORDER_NATURAL;
+  if (order == PA_ORDER_LONGEST_FIRST && sh->num_seqs > PA_RANK_MAX_SEQS)
+    return PA_ERR_UNSUPPORTED;
   const int g = sh->num_q_heads / sh->num_kv_heads;
 
   int pf = o->prefetch < 0 ? kDefaultPrefetch : o->prefetch;
   if (pf > PA_PREFETCH_BOTH) return PA_ERR_INVALID_ARG;
 
-  int waves = o->waves_per_wg == 0 ? kDefaultWaves : o->waves_per_wg;
-  if (waves != 1 && waves != 2 && waves != 4 && waves != 8) return PA_ERR_INVALID_ARG;
-
   const int B = sh->num_seqs, Hkv = sh->num_kv_heads;
   const int MB = sh->max_blocks_per_seq;
+  const int64_t units = (int64_t)B * Hkv;
+  const bool rank = order == PA_ORDER_LONGEST_FIRST;
+  if (o->waves_per_wg != 0 && o->waves_per_wg != 1 && o->waves_per_wg != 2 &&
+      o->waves_per_wg != 4 && o->waves_per_wg != 8)
+    return PA_ERR_INVALID_ARG;
   if (o->partition_blocks < 0) return PA_ERR_INVALID_ARG;
+  if (o->partition_blocks > kMaxPartitionBlocks) return PA_ERR_UNSUPPORTED;
+
+  int waves = o->waves_per_wg;
+  if (waves == 0) {
+    const bool whole = o->partition_blocks == 0 ? units >= kOnePartitionUnits
+                                                : o->partition_blocks >= MB;
+    waves = 4;
+    if (whole && units < kFourWaveUnits && MB >= kLongTableBlocks && MB <= kMaxPartitionBlocks &&
+        pa::decode_lds_bytes(MB, g, 8, B, rank) <= kMaxLdsBytes)
+      waves = 8;
+  }
+
   int PB;
   if (o->partition_blocks > 0) {
-    if (o->partition_blocks > kMaxPartitionBlocks) return PA_ERR_UNSUPPORTED;
     PB = o->partition_blocks < MB ? o->partition_blocks : MB;
+  } else if (units >= kOnePartitionUnits) {
+    PB = MB < kMaxPartitionBlocks ? MB : kMaxPartitionBlocks;
   } else {
-    const int64_t units = (int64_t)B * Hkv;
-    int64_t want = (kTargetWorkgroups + units - 1) / units;
-    if (want < 1) want = 1;
+    const int64_t want = (kOnePartitionUnits + units - 1) / units;
     int64_t pb = (MB + want - 1) / want;
-    if (want > 1 && pb > kAutoPartitionBlocks) pb = kAutoPartitionBlocks;
-    pb = (pb + waves - 1) / waves * waves;       // whole rounds of the W waves
-    if (pb < 2 * waves) pb = 2 * waves;           // at least two blocks per wave
-    if (pb > kMaxPartitionBlocks) pb = kMaxPartitionBlocks;
+    pb = (pb + waves - 1) / waves * waves;  // whole rounds of the W waves
+    if (pb < kMinAutoPartition) pb = kMinAutoPartition;
+    if (pb > kMaxAutoPartition) pb = kMaxAutoPartition;
     if (pb > MB) pb = MB;
     PB = (int)pb;
   }
   const int P = (MB + PB - 1) / PB;
   if (P > 65535) return PA_ERR_UNSUPPORTED;  // grid.z
-  if (pa::decode_lds_bytes(PB, g, waves) > kMaxLdsBytes) return PA_ERR_UNSUPPORTED;
+  if (pa::decode_lds_bytes(PB, g, waves, B, rank) > kMaxLdsBytes)
+    return PA_ERR_UNSUPPORTED;
   memset(pl, 0, sizeof(*pl));
+  pl->order = order;
   pl->pf = pf;
   pl->waves = waves;
   pl->PB = PB;
@@ -118,6 +151,7 @@ int paged_attn_plan(const pa_shape* sh, const pa_options* o, pa_plan_info* info)
   info->num_partitions = pl.P;
   info->workgroups = pl.wgs;
   info->workspace_bytes = pl.ws_bytes;
+  info->seq_order = pl.order;
   return PA_OK;
 }
 
@@ -174,6 +208,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.dbg_err = o->debug_error_word;
   a.sink = nullptr;
   a.sink_enable = 0;
+  a.rank_seqs = pl.order == PA_ORDER_LONGEST_FIRST ? 1 : 0;
   a.scale_log2 = (float)((double)scale * (double)k_scale * 1.4426950408889634);
   a.v_scale = v_scale;
   a.B = sh->num_seqs;

@@ -33,12 +33,20 @@ struct DecodeArgs {
   int lds_bt_bytes;      // LDS bytes reserved for the block-table slice
   int pf_dist;           // L2-touch distance in iterations of a wave, 1..63
   int sink_enable;
+  int rank_seqs;         // 1: grid row r takes the sequence of rank r (most blocks first)
 };
 
 inline int lds_bt_bytes_for(int PB) { return ((PB * 4) + 15) / 16 * 16; }
 
-inline size_t decode_lds_bytes(int PB, int g, int waves) {
-  return (size_t)lds_bt_bytes_for(PB) + (size_t)waves * g * (128 + 2) * 4;
+// LDS of the sequence ranking: B block counts padded to a multiple of 4,
+// then the selected sequence.  It overlays the block-table slice and the
+// merge area, which are written only after the ranking is done.
+inline size_t rank_lds_bytes(int B) { return (size_t)((B + 3) / 4 * 4) * 4 + 16; }
+
+inline size_t decode_lds_bytes(int PB, int g, int waves, int B, bool rank) {
+  const size_t main = (size_t)lds_bt_bytes_for(PB) + (size_t)waves * g * (128 + 2) * 4;
+  const size_t r = rank ? rank_lds_bytes(B) : 0;
+  return main > r ? main : r;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int waves,

@@ -421,6 +421,42 @@ __device__ __forceinline__ void combine_waves(const float* merge_s, int W, int G
 }
 
 // ---------------------------------------------------------------------------
+// Longest-first dispatch.  Work-groups start in grid order, so grid row r
+// takes the sequence with the r-th most blocks (ties by index): the longest
+// sequences start first and the short ones fill in behind them, which
+// shortens the tail of a ragged batch.  Every work-group ranks the B block
+// counts itself (B <= 256, so at most 64 16-byte LDS reads per thread); the
+// ranks are a permutation of 0..B-1, so exactly one sequence matches r.
+__device__ __forceinline__ int ranked_sequence(const DecodeArgs& a, int r, int tab_tokens,
+                                            unsigned char* smem) {
+  int* nb_s = reinterpret_cast<int*>(smem);
+  const int Bp = (a.B + 3) / 4 * 4;
+  int* sel_s = nb_s + Bp;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < Bp; i += blockDim.x) {
+    int c = i < a.B ? a.ctx[i] : 0;
+    c = c < 0 ? 0 : (c > tab_tokens ? tab_tokens : c);
+    nb_s[i] = i < a.B ? (c + kT - 1) / kT : -1;  // padding never outranks
+  }
+  __syncthreads();
+  for (int i = tid; i < a.B; i += blockDim.x) {
+    const int ki = nb_s[i];
+    int rank = 0;
+    for (int j = 0; j < Bp; j += 4) {
+      const int4 k4 = *reinterpret_cast<const int4*>(nb_s + j);
+      rank += (k4.x > ki) | ((k4.x == ki) & (j < i));
+      rank += (k4.y > ki) | ((k4.y == ki) & (j + 1 < i));
+      rank += (k4.z > ki) | ((k4.z == ki) & (j + 2 < i));
+      rank += (k4.w > ki) | ((k4.w == ki) & (j + 3 < i));
+    }
+    if (rank == r) *sel_s = i;
+  }
+  __syncthreads();
+  const int b = *sel_s;
+  __syncthreads();  // the LDS is reused by the block walk
+  return b;
+}
+
 template <int PF, bool DBG, bool KV8>
 __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -431,14 +467,14 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
   // before any second one, so the large work-groups of a ragged batch start
   // first and the short tail partitions fill in behind them.
   const int kvh = blockIdx.x;
-  const int b = blockIdx.y;
   const int p = blockIdx.z;
   const int G = a.G;
   const int tid = threadIdx.x;
   const int W = blockDim.x / kWave;
+  const int tab_tokens = a.MB * kT;
+  const int b = a.rank_seqs ? ranked_sequence(a, blockIdx.y, tab_tokens, smem_raw) : blockIdx.y;
 
   int ctx = a.ctx[b];
-  const int tab_tokens = a.MB * kT;
   if (ctx > tab_tokens) {
     if (DBG && tid == 0 && a.dbg_err) atomicOr(a.dbg_err, 2);
     ctx = tab_tokens;
@@ -569,8 +605,8 @@ hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int wa
   if (pf < 0 || pf > 3) return hipErrorInvalidValue;
   const dim3 grid(a.Hkv, a.B, a.P);
   const dim3 block(kWave * waves);
-  return table[(kv8 ? 8 : 0) + pf * 2 + (dbg ? 1 : 0)](a, grid, block,
-                                                      decode_lds_bytes(a.PB, a.G, waves), st);
+  return table[(kv8 ? 8 : 0) + pf * 2 + (dbg ? 1 : 0)](
+      a, grid, block, decode_lds_bytes(a.PB, a.G, waves, a.B, a.rank_seqs != 0), st);
 }
 
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t st) {

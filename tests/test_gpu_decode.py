@@ -231,3 +231,19 @@ def test_debug_variant_computes_the_same_bits():
         dbg = run(x, dev, partition_blocks=pb, debug_trace=trace, debug_error_word=err)
         assert np.array_equal(bits(plain), bits(dbg)), pb
         assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("pb,waves", [(0, 4), (0, 8), (8, 4), (32, 2), (1024, 8)])
+def test_longest_first_order_changes_no_bits(pb, waves):
+    """Ragged batch with ties and an empty context: the dispatch order changes
+    which work-group takes which sequence, never a bit of the result."""
+    lens = [33, 700, 1, 0, 2100, 129, 700, 16, 2100]
+    x = gen.make_case(len(lens), 8, 2, lens, seed=158, extra_pool_blocks=4)
+    dev = to_device(x)
+    nat_ = run(x, dev, partition_blocks=pb, waves_per_wg=waves, seq_order=1)
+    lpt = run(x, dev, partition_blocks=pb, waves_per_wg=waves, seq_order=2)
+    assert np.array_equal(bits(lpt), bits(nat_))
+    assert not lpt[3].any()
+    assert_close(lpt, oracle(x), f"pb={pb} w={waves}")
+    p = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], seq_order=0)
+    assert p["seq_order"] == 2

@@ -229,3 +229,13 @@ def test_fp8_workload_sampled_rows(name):
                                            rows)
     e = assert_close(got[rows[:, 0], rows[:, 1]], ref, name)
     print(f"[fp8 workload] {name}: {e}", flush=True)
+
+
+def test_fp8_longest_first_order_changes_no_bits():
+    lens = [33, 700, 1, 0, 2100, 129, 700]
+    x8 = case8(len(lens), 8, 2, lens, seed=295)
+    dev = to_device8(x8)
+    a = run8(x8, dev, seq_order=1)
+    b = run8(x8, dev, seq_order=2)
+    assert np.array_equal(bits(a), bits(b))
+    assert_close(b, oracle8(x8), "fp8 order")

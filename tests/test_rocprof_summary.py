@@ -1,0 +1,17 @@
+"""Kernel-name matching of the rocprofv3 summariser (CPU)."""
+from paged_kv_cache_226_amd import rocprof_summary as rs
+
+
+def test_decode_mode_selects_the_cache_type_and_skips_debug_instances():
+    names = {n: f"void pa::pa_decode_kernel<{n[0]}, {n[1]}, {n[2]}>(pa::DecodeArgs)"
+             for n in [(m, d, k) for m in range(4) for d in ("false", "true")
+                       for k in ("false", "true")]}
+    try:
+        for kv8 in (False, True):
+            rs.KV8 = kv8
+            for (m, d, k), name in names.items():
+                want = m if d == "false" and (k == "true") == kv8 else None
+                assert rs.decode_mode(name) == want, (name, kv8)
+        assert rs.decode_mode("void pa::pa_reduce_kernel(pa::DecodeArgs)") is None
+    finally:
+        rs.KV8 = False
