@@ -91,7 +91,8 @@ enum pa_prefetch {
     PA_PREFETCH_OFF = 0,  /* load block j, wait, compute: no look-ahead */
     PA_PREFETCH_L2 = 1,   /* touch every 128 B line of block j + k*w so it is
                              brought into L2 / Infinity Cache; data discarded */
-    PA_PREFETCH_REG = 2,  /* load block j + w into a second register buffer */
+    PA_PREFETCH_REG = 2,  /* load block j + k*w into registers (k = 1 or 2
+                             buffers ahead) */
     PA_PREFETCH_BOTH = 3  /* REG for block j + w, plus an L2 touch of
                              block j + (1 + k)*w */
 };
@@ -129,8 +130,13 @@ typedef struct pa_options {
     int32_t waves_per_wg;      /* w in {1, 2, 4, 8}; 0 = auto: 8 for unsplit
                                   batches of 256..767 pairs whose block table
                                   is 512..1024 blocks wide, else 4 */
-    int32_t prefetch_distance; /* k, the L2 touch's distance in iterations of
-                                  a wave (modes 1 and 3); 0 = 1, at most 63 */
+    int32_t prefetch_distance; /* k, the look-ahead distance in iterations of
+                                  a wave (0 = 1, or 2 for mode 2 over an E4M3
+                                  cache): mode 1 touches block j+k*w
+                                  (k <= 63); mode 2 fetches block j+k*w into
+                                  registers (k <= 2, else PA_ERR_UNSUPPORTED);
+                                  mode 3 fetches j+w into registers and
+                                  touches j+(1+k)*w (k <= 63) */
     int32_t seq_order;         /* enum pa_seq_order; LONGEST_FIRST needs
                                   num_seqs <= PA_RANK_MAX_SEQS */
     int32_t reserved;          /* must be 0 */

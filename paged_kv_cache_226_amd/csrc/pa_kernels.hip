@@ -97,6 +97,15 @@ __device__ __forceinline__ u32x4 widen_fp8x8(uint32_t w0, uint32_t w1) {
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true))};
 }
 
+// Compile-time flags for the block compute: may the block be a sequence's
+// partial last block?
+template <bool V>
+struct Flag {
+  static constexpr bool value = V;
+};
+constexpr Flag<false> kNoTail{};
+constexpr Flag<true> kMayTail{};
+
 // First of the 8 dims that MFMA chunk ch of Q.K^T covers in lane group lg.
 // The dot product sums over dims, so K and Q only need the same mapping;
 // each cache layout uses the one that its 128-bit loads deliver.
@@ -196,7 +205,13 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
       a.dbg_trace[(((int64_t)b * a.Hkv + kvh) * a.MB + j) * 2 + slot] = value;
   };
 
-  auto compute = [&](Buf& buf, int j) {
+  // `MayTail` is false wherever the block cannot be the sequence's last one
+  // (every steady-state iteration: those always leave blocks for later
+  // iterations of the same wave).  Without the masking branch there the
+  // loaded registers are used as they are, and the compiler has no reason to
+  // copy a look-ahead buffer, a copy that would wait for its loads early.
+  auto compute = [&](Buf& buf, int j, auto may_tail) {
+    constexpr bool MayTail = decltype(may_tail)::value;
     // fp16 operands: K chunks and V rows
     u32x4 kh[4], vh[4];
     if constexpr (KV8) {
@@ -220,7 +235,7 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
         *reinterpret_cast<u32x4*>(dst + 2 * chunk_dim<KV8>(ch, lg)) = kh[ch];
     }
     const int rem = ctx - j * kT;  // valid tokens in this block, >= 1
-    const bool tail = rem < kT;
+    const bool tail = MayTail && rem < kT;
     if (tail) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -318,14 +333,19 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
     for (; it + 1 < n_it; ++it) {  // block j+W exists
       const int j = j0 + it * W;
       Buf buf;
+      // All of block j's loads (and the touch) are issued before its compute
+      // starts; unfenced, the compiler issues the V loads only after the
+      // first K load has arrived, which serialises two latencies.
+      __builtin_amdgcn_sched_barrier(0);
       load_block(buf, phys_it(it));
       uint32_t got = 0;
       if (PF == 1 && it + a.pf_dist < n_it) {
         got = touch_block(phys_it(it + a.pf_dist));
         trace_put(j + a.pf_dist * W, 1, wave);
       }
+      __builtin_amdgcn_sched_barrier(0);
       trace_put(j, 0, (wave << 16) | it);
-      compute(buf, j);
+      compute(buf, j, kNoTail);
       if (PF == 1) {
         sink ^= pend;
         pend = got;
@@ -337,48 +357,63 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
       Buf buf;
       load_block(buf, phys_it(it));
       trace_put(j, 0, (wave << 16) | it);
-      compute(buf, j);
+      compute(buf, j, kMayTail);
     }
     sink ^= pend;
   } else {
-    Buf bufA, bufB;
+    // Register look-ahead of depth D: block j + D*W is fetched into a ring of
+    // D+1 buffers while block j is computed.  The steady loop is unrolled
+    // D+1 times so every buffer index is a compile-time constant.
+    constexpr int D = PF == 4 ? 2 : 1;
+    Buf bufs[D + 1];
     uint32_t pend = 0;
-    auto step = [&](Buf& cur, Buf& nxt, int it) {
+    auto step = [&](Buf& cur, Buf& ahead, int it) {  // block it+D exists
       const int j = j0 + it * W;
-      load_block(nxt, phys_it(it + 1));
-      trace_put(j + W, 1, wave);
+      // Scheduling fences: the compiler does not model HBM latency.  Without
+      // them it starts the next block's Q.K^T right after that block's loads
+      // are issued (waiting on the very data the look-ahead is meant to
+      // overlap), and issues the look-ahead loads only after the current
+      // block has arrived.
+      __builtin_amdgcn_sched_barrier(0);
+      load_block(ahead, phys_it(it + D));
+      __builtin_amdgcn_sched_barrier(0);
+      trace_put(j + D * W, 1, wave);
       uint32_t got = 0;
-      if (PF == 3 && it + 1 + a.pf_dist < n_it) got = touch_block(phys_it(it + 1 + a.pf_dist));
+      if (PF == 3 && it + D + a.pf_dist < n_it) got = touch_block(phys_it(it + D + a.pf_dist));
       trace_put(j, 0, (wave << 16) | it);
-      compute(cur, j);
+      compute(cur, j, kNoTail);
       if (PF == 3) {
         sink ^= pend;
         pend = got;
       }
       advance(it);
+      __builtin_amdgcn_sched_barrier(0);
     };
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+      if (u < n_it) load_block(bufs[u], phys_it(u));
     int it = 0;
-    if (n_it > 0) load_block(bufA, phys_it(0));
-    for (; it + 3 < n_it; it += 2) {  // blocks it+1 .. it+3 exist
-      step(bufA, bufB, it);
-      step(bufB, bufA, it + 1);
+    for (; it + 2 * D < n_it; it += D + 1) {  // iterations it..it+D all fetch ahead
+#pragma unroll
+      for (int u = 0; u <= D; ++u) step(bufs[u], bufs[(u + D) % (D + 1)], it + u);
     }
-    for (; it < n_it; ++it) {  // at most 3 left; bufA holds block `it`
+    for (; it < n_it; ++it) {  // bufs[0..D-1] hold blocks it..it+D-1
       const int j = j0 + it * W;
-      if (it + 1 < n_it) {
-        load_block(bufB, phys_it(it + 1));
-        trace_put(j + W, 1, wave);
+      if (it + D < n_it) {
+        load_block(bufs[D], phys_it(it + D));
+        trace_put(j + D * W, 1, wave);
       }
       uint32_t got = 0;
-      if (PF == 3 && it + 1 + a.pf_dist < n_it) got = touch_block(phys_it(it + 1 + a.pf_dist));
+      if (PF == 3 && it + D + a.pf_dist < n_it) got = touch_block(phys_it(it + D + a.pf_dist));
       trace_put(j, 0, (wave << 16) | it);
-      compute(bufA, j);
+      compute(bufs[0], j, kMayTail);
       if (PF == 3) {
         sink ^= pend;
         pend = got;
       }
       advance(it);
-      bufA = bufB;
+#pragma unroll
+      for (int u = 0; u < D; ++u) bufs[u] = bufs[u + 1];
     }
     sink ^= pend;
   }
@@ -593,19 +628,22 @@ static hipError_t launch_decode_t(const DecodeArgs& a, dim3 grid, dim3 block, si
 hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int waves,
                          hipStream_t st) {
   typedef hipError_t (*fn_t)(const DecodeArgs&, dim3, dim3, size_t, hipStream_t);
-  static const fn_t table[16] = {
+  // pf 0..3 are the look-ahead modes; 4 is the register look-ahead of depth 2
+  static const fn_t table[20] = {
       launch_decode_t<0, false, false>, launch_decode_t<0, true, false>,
       launch_decode_t<1, false, false>, launch_decode_t<1, true, false>,
       launch_decode_t<2, false, false>, launch_decode_t<2, true, false>,
       launch_decode_t<3, false, false>, launch_decode_t<3, true, false>,
+      launch_decode_t<4, false, false>, launch_decode_t<4, true, false>,
       launch_decode_t<0, false, true>,  launch_decode_t<0, true, true>,
       launch_decode_t<1, false, true>,  launch_decode_t<1, true, true>,
       launch_decode_t<2, false, true>,  launch_decode_t<2, true, true>,
-      launch_decode_t<3, false, true>,  launch_decode_t<3, true, true>};
-  if (pf < 0 || pf > 3) return hipErrorInvalidValue;
+      launch_decode_t<3, false, true>,  launch_decode_t<3, true, true>,
+      launch_decode_t<4, false, true>,  launch_decode_t<4, true, true>};
+  if (pf < 0 || pf > 4) return hipErrorInvalidValue;
   const dim3 grid(a.Hkv, a.B, a.P);
   const dim3 block(kWave * waves);
-  return table[(kv8 ? 8 : 0) + pf * 2 + (dbg ? 1 : 0)](
+  return table[(kv8 ? 10 : 0) + pf * 2 + (dbg ? 1 : 0)](
       a, grid, block, decode_lds_bytes(a.PB, a.G, waves, a.B, a.rank_seqs != 0), st);
 }
 

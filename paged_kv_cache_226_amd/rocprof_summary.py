@@ -28,7 +28,7 @@ import os
 import re
 import sys
 
-MODE_NAMES = {0: "off", 1: "l2", 2: "reg", 3: "both"}
+MODE_NAMES = {0: "off", 1: "l2", 2: "reg", 3: "both", 4: "reg2"}
 DECODE_RE = re.compile(r"pa_decode_kernel<(\d), (true|false), (true|false)>")
 KV8 = False  # which cache type's kernels the summary counts (set by main)
 

@@ -103,6 +103,7 @@ def good_shape(**kw):
     (dict(opts=dict(waves_per_wg=3)), nat.PA_ERR_INVALID_ARG),
     (dict(opts=dict(prefetch_distance=64)), nat.PA_ERR_INVALID_ARG),
     (dict(opts=dict(prefetch_distance=-1)), nat.PA_ERR_INVALID_ARG),
+    (dict(opts=dict(prefetch=2, prefetch_distance=3)), nat.PA_ERR_UNSUPPORTED),
     (dict(opts=dict(partition_blocks=-1)), nat.PA_ERR_INVALID_ARG),
     (dict(opts=dict(partition_blocks=2048)), nat.PA_ERR_UNSUPPORTED),
     (dict(opts=dict(seq_order=3)), nat.PA_ERR_INVALID_ARG),

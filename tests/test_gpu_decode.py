@@ -96,7 +96,8 @@ def test_debug_gather_is_bitwise_the_block_table_gather():
 
 @pytest.mark.parametrize("pf", MODES)
 @pytest.mark.parametrize("waves,pb,dist", [(4, 0, 1), (2, 0, 1), (4, 8, 1), (2, 5, 1), (8, 16, 1),
-                                           (1, 3, 1), (4, 0, 2), (2, 0, 5), (4, 32, 3)])
+                                           (1, 3, 1), (4, 0, 2), (2, 0, 5), (4, 32, 3),
+                                           (2, 5, 2), (1, 3, 2), (8, 0, 2)])
 def test_trace_follows_the_lookahead_schedule(pf, waves, pb, dist):
     x = gen.make_case(3, 4, 2, [400, 90, 2000], seed=140, extra_pool_blocks=2)
     dev = to_device(x)
@@ -104,6 +105,10 @@ def test_trace_follows_the_lookahead_schedule(pf, waves, pb, dist):
     Hkv = x.k_cache.shape[1]
     trace = torch.full((B, Hkv, MB, 2), -1, dtype=torch.int32, device="cuda")
     kw = dict(prefetch=pf, waves_per_wg=waves, partition_blocks=pb, prefetch_distance=dist)
+    if pf == 2 and dist > 2:  # registers hold at most two blocks ahead
+        with pytest.raises(RuntimeError, match="unsupported"):
+            run(x, dev, debug_trace=trace, **kw)
+        return
     run(x, dev, debug_trace=trace, **kw)
     tr = trace.cpu().numpy()
     plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], prefetch=pf,
@@ -114,9 +119,9 @@ def test_trace_follows_the_lookahead_schedule(pf, waves, pb, dist):
               for s in range(0, -(-int(L) // 16), PB)]
     seen = np.zeros((B, Hkv, MB), dtype=bool)
     for b, h, s, e in ranges:
-        # slot 1 holds the L2 touch in mode 1 (distance dist) and the
-        # register fetch of block j + W in modes 2 and 3
-        exp = sch.expected_trace(s, e, W, dist if pf == 1 else 1)
+        # slot 1 holds the L2 touch in mode 1 and the register fetch in mode
+        # 2 (distance dist), the register fetch of block j + W in mode 3
+        exp = sch.expected_trace(s, e, W, 1 if pf == 3 else dist)
         for j in range(s, e):
             wave, it, fetcher = exp[j]
             assert tr[b, h, j, 0] == (wave << 16 | it), (b, h, j)
@@ -247,3 +252,16 @@ def test_longest_first_order_changes_no_bits(pb, waves):
     assert_close(lpt, oracle(x), f"pb={pb} w={waves}")
     p = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], seq_order=0)
     assert p["seq_order"] == 2
+
+
+@pytest.mark.parametrize("waves,pb", [(1, 0), (2, 3), (4, 0), (4, 5), (8, 0), (4, 1024)])
+def test_register_depth_two_changes_no_bits(waves, pb):
+    """Depth-2 register look-ahead against the plain walk, with walks of 1 to
+    many iterations per wave (every tail path of the unrolled loop)."""
+    lens = [1, 17, 33, 49, 65, 81, 97, 113, 129, 300, 2100]
+    x = gen.make_case(len(lens), 8, 2, lens, seed=159, extra_pool_blocks=3)
+    dev = to_device(x)
+    base = run(x, dev, prefetch=0, waves_per_wg=waves, partition_blocks=pb)
+    d2 = run(x, dev, prefetch=2, prefetch_distance=2, waves_per_wg=waves, partition_blocks=pb)
+    assert np.array_equal(bits(d2), bits(base))
+    assert_close(d2, oracle(x), f"depth 2 w={waves} pb={pb}")

@@ -71,6 +71,7 @@ def test_fp8_random_shapes_all_modes(seed, B, Hq, Hkv, lens):
     ref = oracle8(x8)
     dev = to_device8(x8)
     outs = {pf: run8(x8, dev, prefetch=pf) for pf in MODES}
+    outs["reg2"] = run8(x8, dev, prefetch=2, prefetch_distance=2)
     for pf, o in outs.items():
         assert_close(o, ref, f"fp8 {seed} pf={pf}")
         assert np.array_equal(bits(o), bits(outs[0])), f"mode {pf} differs from mode 0"
@@ -165,7 +166,8 @@ def test_fp8_trace_follows_the_lookahead_schedule(pf):
         nb = -(-int(L) // 16)
         for h in range(Hkv):
             for s in range(0, nb, PB):
-                exp = sch.expected_trace(s, min(nb, s + PB), W)
+                # the register look-ahead over E4M3 runs two blocks ahead by default
+                exp = sch.expected_trace(s, min(nb, s + PB), W, 2 if pf == 2 else 1)
                 for j, (wave, it, fetcher) in exp.items():
                     assert tr[b, h, j, 0] == (wave << 16 | it), (b, h, j)
                     assert tr[b, h, j, 1] == (-1 if pf == 0 else fetcher), (b, h, j, pf)
@@ -214,10 +216,11 @@ def test_fp8_workload_sampled_rows(name):
                                     dev["block_tables"], dev["context_lens"], x8.scale,
                                     x8.k_scale, x8.v_scale)
     torch.cuda.synchronize()
-    for pf in (0, 1, 3):
+    for pf, dist in ((0, 0), (1, 0), (3, 0), (2, 2)):
         o2 = ops.paged_attn_decode_fp8(dev["q"], dev["k_cache"], dev["v_cache"],
                                        dev["block_tables"], dev["context_lens"], x8.scale,
-                                       x8.k_scale, x8.v_scale, prefetch=pf)
+                                       x8.k_scale, x8.v_scale, prefetch=pf,
+                                       prefetch_distance=dist)
         torch.cuda.synchronize()
         assert torch.equal(o2.view(torch.int16), out.view(torch.int16)), f"mode {pf}"
     got = out.cpu().numpy()

@@ -47,10 +47,10 @@ def test_workload_sampled_rows(name):
                                 dev["context_lens"], x.scale)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
-    for pf in (0, 1, 2, 3):
+    for pf, dist in ((0, 0), (1, 0), (2, 0), (3, 0), (2, 2)):
         o2 = ops.paged_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"],
                                    dev["block_tables"], dev["context_lens"], x.scale,
-                                   prefetch=pf)
+                                   prefetch=pf, prefetch_distance=dist)
         torch.cuda.synchronize()
         assert torch.equal(o2.view(torch.int16), out.view(torch.int16)), f"mode {pf}"
     got = out.cpu().numpy()
