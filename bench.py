@@ -70,8 +70,9 @@ def read_traffic(workload: str, mode_name: str):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps before the timed region (and at least 250 ms of them)")
     ap.add_argument("--workload", default="llama2_7b")
     ap.add_argument("--prefetch", type=int, default=-1, help="-1 = library default")
     ap.add_argument("--kv-dtype", choices=("fp16", "fp8"), default="fp16",
@@ -214,9 +215,17 @@ def main():
                                   d["context_lens"], x.scale, out, prefetch=pf, workspace=ws,
                                   prefetch_distance=dist)
 
-    def timed(pf, steps, warmup, dist=None):
-        for _ in range(warmup):
-            step(pf, dist)
+    def timed(pf, steps, warmup, dist=None, min_warm_s=0.0):
+        # Warm-up: `warmup` steps, and at least `min_warm_s` seconds of them.
+        # Coming out of idle (e.g. after the host built the inputs) the first
+        # tens of milliseconds of GPU work run measurably slower.
+        t_end = time.perf_counter() + min_warm_s
+        done = 0
+        while done < warmup or time.perf_counter() < t_end:
+            for _ in range(max(1, min(warmup - done, 50)) if done < warmup else 50):
+                step(pf, dist)
+                done += 1
+            torch.cuda.synchronize()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -262,7 +271,7 @@ def main():
                                           "copy_write_bytes": 1 << 30}}), flush=True)
         return
 
-    us = timed(mode, args.steps, args.warmup)
+    us = timed(mode, args.steps, args.warmup, min_warm_s=0.25)
     launch_avg, launch_med = per_launch(mode, args.steps)
     modes = {}
     for pf, dist in MODE_RUNS:
