@@ -33,9 +33,11 @@ KERNEL_SOURCES = ["paged_kv_cache_226_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_226_amd/csrc/pa_internal.h"]
 
 
-# (mode, distance) of the per-mode timings: the four modes at distance 1, and
-# the register look-ahead two blocks ahead
-MODE_RUNS = [(0, 1), (1, 1), (2, 1), (3, 1), (2, 2)]
+# (mode, distance, structure) of the per-mode timings: the four modes at
+# distance 1, the register look-ahead two blocks ahead, and (fp16 only) the
+# four modes of the two-loop structure
+MODE_RUNS = [(0, 1, 0), (1, 1, 0), (2, 1, 0), (3, 1, 0), (2, 2, 0),
+             (0, 1, 1), (1, 1, 1), (2, 1, 1), (3, 1, 1)]
 
 
 def kernel_source_hash() -> str:
@@ -204,7 +206,10 @@ def main():
     ws = ops.new_workspace(d["q"], d["k_cache"], d["block_tables"], prefetch=args.prefetch)
     stream = torch.cuda.current_stream()
 
-    def step(pf, dist=None):
+    ws_two = None if fp8 else ops.new_workspace(d["q"], d["k_cache"], d["block_tables"],
+                                                structure=1)
+
+    def step(pf, dist=None, structure=0):
         dist = args.prefetch_distance if dist is None else dist
         if fp8:
             ops.paged_attn_decode_fp8(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
@@ -212,10 +217,11 @@ def main():
                                       prefetch=pf, workspace=ws, prefetch_distance=dist)
         else:
             ops.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
-                                  d["context_lens"], x.scale, out, prefetch=pf, workspace=ws,
-                                  prefetch_distance=dist)
+                                  d["context_lens"], x.scale, out, prefetch=pf,
+                                  workspace=ws_two if structure else ws,
+                                  prefetch_distance=dist, structure=structure)
 
-    def timed(pf, steps, warmup, dist=None, min_warm_s=0.0):
+    def timed(pf, steps, warmup, dist=None, min_warm_s=0.0, structure=0):
         # Warm-up: `warmup` steps, and at least `min_warm_s` seconds of them.
         # Coming out of idle (e.g. after the host built the inputs) the first
         # tens of milliseconds of GPU work run measurably slower.
@@ -223,14 +229,14 @@ def main():
         done = 0
         while done < warmup or time.perf_counter() < t_end:
             for _ in range(max(1, min(warmup - done, 50)) if done < warmup else 50):
-                step(pf, dist)
+                step(pf, dist, structure)
                 done += 1
             torch.cuda.synchronize()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for _ in range(steps):
-            step(pf, dist)
+            step(pf, dist, structure)
         b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / steps  # µs per step
@@ -253,8 +259,9 @@ def main():
     dist = args.prefetch_distance or (2 if fp8 and mode == nat.PREFETCH_REG else 1)
     mode_label = mode_names[mode] + ("2" if mode == nat.PREFETCH_REG and dist == 2 else "")
     if args.profile:
-        for pf, dist in MODE_RUNS:
-            timed(pf, args.steps, args.warmup, dist)
+        for pf, dist, structure in MODE_RUNS:
+            if not (fp8 and structure):
+                timed(pf, args.steps, args.warmup, dist, structure=structure)
         # Calibration kernels of known size for the HBM byte counters: a 1 GiB
         # streaming read (reads 2^30 B) and a 1 GiB fp16 elementwise copy
         # (reads and writes 2^30 B each).
@@ -274,9 +281,11 @@ def main():
     us = timed(mode, args.steps, args.warmup, min_warm_s=0.25)
     launch_avg, launch_med = per_launch(mode, args.steps)
     modes = {}
-    for pf, dist in MODE_RUNS:
-        u = timed(pf, max(20, args.steps // 4), 5, dist)
-        name = mode_names[pf] + ("2" if dist == 2 else "")
+    for pf, dist, structure in MODE_RUNS:
+        if fp8 and structure:
+            continue
+        u = timed(pf, max(20, args.steps // 4), 5, dist, structure=structure)
+        name = ("two_loop_" if structure else "") + mode_names[pf] + ("2" if dist == 2 else "")
         modes[name] = {"us_per_step": round(u, 2), "GBps": round(kv_bytes / u / 1e3, 1)}
 
     # streaming-read ceiling over a buffer larger than every cache

@@ -110,6 +110,20 @@ enum pa_seq_order {
 };
 #define PA_RANK_MAX_SEQS 256
 
+/* How one work-group walks its blocks. */
+enum pa_structure {
+    PA_STRUCTURE_FUSED = 0,    /* one pass: Q.K^T, online softmax and P.V per
+                                  block, with the look-ahead of whole (K, V)
+                                  blocks (the default) */
+    PA_STRUCTURE_TWO_LOOP = 1  /* the review's two loops (sections 3.4, 4.1):
+                                  all Q.K^T with a K look-ahead, the range
+                                  maximum, then all P.V with a V look-ahead.
+                                  A comparison: fp16 caches only, no debug
+                                  outputs, look-ahead distance 1, partitions
+                                  of at most 32 blocks by default (their
+                                  scores are kept in LDS) */
+};
+
 typedef struct pa_shape {
     int32_t num_seqs;           /* B >= 1 */
     int32_t num_q_heads;        /* Hq >= 1 */
@@ -139,7 +153,7 @@ typedef struct pa_options {
                                   touches j+(1+k)*w (k <= 63) */
     int32_t seq_order;         /* enum pa_seq_order; LONGEST_FIRST needs
                                   num_seqs <= PA_RANK_MAX_SEQS */
-    int32_t reserved;          /* must be 0 */
+    int32_t structure;         /* enum pa_structure */
     void *workspace;           /* device scratch for partition partials; may be
                                   NULL when the plan has one partition */
     size_t workspace_bytes;
@@ -167,7 +181,7 @@ typedef struct pa_plan_info {
     int64_t workgroups;        /* decode-kernel grid size */
     size_t workspace_bytes;    /* 0 when num_partitions == 1 */
     int32_t seq_order;         /* PA_ORDER_NATURAL or PA_ORDER_LONGEST_FIRST */
-    int32_t reserved;
+    int32_t structure;         /* enum pa_structure */
 } pa_plan_info;
 
 /* Fill *opts with the defaults (prefetch = library default, auto sizes). */

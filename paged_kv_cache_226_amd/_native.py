@@ -20,6 +20,7 @@ PREFETCH_NAMES = {0: "off", 1: "l2", 2: "reg", 3: "both"}
 ORDER_AUTO, ORDER_NATURAL, ORDER_LONGEST_FIRST = 0, 1, 2
 ORDER_NAMES = {1: "natural", 2: "longest_first"}
 RANK_MAX_SEQS = 256
+STRUCTURE_FUSED, STRUCTURE_TWO_LOOP = 0, 1
 
 
 class PaShape(ctypes.Structure):
@@ -32,7 +33,7 @@ class PaShape(ctypes.Structure):
 class PaOptions(ctypes.Structure):
     _fields_ = [("prefetch", ctypes.c_int32), ("partition_blocks", ctypes.c_int32),
                 ("waves_per_wg", ctypes.c_int32), ("prefetch_distance", ctypes.c_int32),
-                ("seq_order", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("seq_order", ctypes.c_int32), ("structure", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("debug_gather_k", ctypes.c_void_p), ("debug_trace", ctypes.c_void_p),
                 ("debug_error_word", ctypes.c_void_p)]
@@ -42,7 +43,7 @@ class PaPlanInfo(ctypes.Structure):
     _fields_ = [("prefetch", ctypes.c_int32), ("waves_per_wg", ctypes.c_int32),
                 ("partition_blocks", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
                 ("workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
-                ("seq_order", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("seq_order", ctypes.c_int32), ("structure", ctypes.c_int32)]
 
 
 _lib = None

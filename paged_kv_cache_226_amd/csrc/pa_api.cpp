@@ -33,9 +33,10 @@ constexpr int64_t kFourWaveUnits = 768;
 constexpr int kLongTableBlocks = 512;
 constexpr int kMinAutoPartition = 64;
 constexpr int kMaxAutoPartition = 256;
+constexpr int kTwoLoopPartitionBlocks = 32;
 
 struct Plan {
-  int pf, waves, PB, P, order;
+  int pf, waves, PB, P, order, two;
   int64_t wgs;
   size_t ws_bytes;
 };
@@ -67,7 +68,10 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   paged_attn_default_options(&d);
   if (!o) o = &d;
   if (o->prefetch_distance < 0 || o->prefetch_distance > 63) return PA_ERR_INVALID_ARG;
-  if (o->reserved != 0) return PA_ERR_INVALID_ARG;
+  if (o->structure != PA_STRUCTURE_FUSED && o->structure != PA_STRUCTURE_TWO_LOOP)
+    return PA_ERR_INVALID_ARG;
+  const bool two = o->structure == PA_STRUCTURE_TWO_LOOP;
+  if (two && o->prefetch_distance > 1) return PA_ERR_UNSUPPORTED;
   int order = o->seq_order;
   if (order < PA_ORDER_AUTO || order > PA_ORDER_LONGEST_FIRST) return PA_ERR_INVALID_ARG;
   if (order == PA_ORDER_AUTO)
@@ -93,6 +97,7 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   if (o->partition_blocks > kMaxPartitionBlocks) return PA_ERR_UNSUPPORTED;
 
   int waves = o->waves_per_wg;
+  if (waves == 0 && two) waves = 4;
   if (waves == 0) {
     const bool whole = o->partition_blocks == 0 ? units >= kOnePartitionUnits
                                                 : o->partition_blocks >= MB;
@@ -105,6 +110,10 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   int PB;
   if (o->partition_blocks > 0) {
     PB = o->partition_blocks < MB ? o->partition_blocks : MB;
+  } else if (two) {
+    // 512-token partitions, halved until the scores fit in LDS
+    PB = kTwoLoopPartitionBlocks < MB ? kTwoLoopPartitionBlocks : MB;
+    while (PB > 1 && pa::two_loop_lds_bytes(PB, g, waves, B, rank) > kMaxLdsBytes) PB /= 2;
   } else if (units >= kOnePartitionUnits) {
     PB = MB < kMaxPartitionBlocks ? MB : kMaxPartitionBlocks;
   } else {
@@ -118,10 +127,12 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   }
   const int P = (MB + PB - 1) / PB;
   if (P > 65535) return PA_ERR_UNSUPPORTED;  // grid.z
-  if (pa::decode_lds_bytes(PB, g, waves, B, rank) > kMaxLdsBytes)
-    return PA_ERR_UNSUPPORTED;
+  const size_t lds = two ? pa::two_loop_lds_bytes(PB, g, waves, B, rank)
+                         : pa::decode_lds_bytes(PB, g, waves, B, rank);
+  if (lds > kMaxLdsBytes) return PA_ERR_UNSUPPORTED;
   memset(pl, 0, sizeof(*pl));
   pl->order = order;
+  pl->two = two ? 1 : 0;
   pl->pf = pf;
   pl->waves = waves;
   pl->PB = PB;
@@ -154,6 +165,7 @@ int paged_attn_plan(const pa_shape* sh, const pa_options* o, pa_plan_info* info)
   info->workgroups = pl.wgs;
   info->workspace_bytes = pl.ws_bytes;
   info->seq_order = pl.order;
+  info->structure = pl.two;
   return PA_OK;
 }
 
@@ -229,6 +241,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.pf_dist = o->prefetch_distance > 0 ? o->prefetch_distance
                                        : (kv8 && pl.pf == PA_PREFETCH_REG ? 2 : 1);
   const bool dbg = o->debug_gather_k || o->debug_trace || o->debug_error_word;
+  if (pl.two && (kv8 || dbg)) return PA_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   if (pl.P > 1) {
@@ -237,9 +250,13 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
     a.ws_ml = ws;
     a.ws_o = ws + rows * 2;
   }
-  // the register look-ahead at distance 2 is its own kernel instance
-  const int variant = pl.pf == PA_PREFETCH_REG && a.pf_dist == 2 ? 4 : pl.pf;
-  if (pa::launch_decode(a, variant, dbg, kv8, pl.waves, st) != hipSuccess) return PA_ERR_HIP;
+  if (pl.two) {
+    if (pa::launch_decode_two_loop(a, pl.pf, pl.waves, st) != hipSuccess) return PA_ERR_HIP;
+  } else {
+    // the register look-ahead at distance 2 is its own kernel instance
+    const int variant = pl.pf == PA_PREFETCH_REG && a.pf_dist == 2 ? 4 : pl.pf;
+    if (pa::launch_decode(a, variant, dbg, kv8, pl.waves, st) != hipSuccess) return PA_ERR_HIP;
+  }
   if (pl.P > 1 && pa::launch_reduce(a, st) != hipSuccess) return PA_ERR_HIP;
   return PA_OK;
 }

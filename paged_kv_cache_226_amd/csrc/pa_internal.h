@@ -49,6 +49,16 @@ inline size_t decode_lds_bytes(int PB, int g, int waves, int B, bool rank) {
   return main > r ? main : r;
 }
 
+// The two-loop walk adds the range's scores (PB*16*g fp32) and one maximum
+// per wave and head after the merge records.
+inline size_t two_loop_lds_bytes(int PB, int g, int waves, int B, bool rank) {
+  const size_t main = decode_lds_bytes(PB, g, waves, B, false) + (size_t)PB * 16 * g * 4 +
+                      (size_t)waves * g * 4;
+  const size_t r = rank ? rank_lds_bytes(B) : 0;
+  return main > r ? main : r;
+}
+
+hipError_t launch_decode_two_loop(const DecodeArgs& a, int pf, int waves, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int waves,
                          hipStream_t st);
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t st);

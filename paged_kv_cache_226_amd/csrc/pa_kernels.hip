@@ -438,6 +438,212 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
   __syncthreads();
 }
 
+
+// ---------------------------------------------------------------------------
+// The pages' two-loop structure, kept as a comparison for the fused walk
+// above (fp16 caches, no debug outputs).  Loop 1 walks the range with a K
+// look-ahead and writes the scaled scores of every token to LDS; the
+// per-head maximum M of the range is taken between the loops; loop 2 walks
+// the range again with a V look-ahead and accumulates exp2(s - M) * V.  Each
+// wave leaves the same (m, l, o[128]) record as walk_range, with m = M.
+// PF: 0 no look-ahead, 1 L2 touch of the next K (loop 1) / V (loop 2) block,
+// 2 register double buffer of the next K / V block, 3 both.
+template <int PF>
+__device__ __forceinline__ void walk_two_loop(const DecodeArgs& a, const int b, const int kvh,
+                                              const int ctx, const int s, const int e,
+                                              int32_t* bt_s, float* merge_s, float* logit_s,
+                                              float* wmax_s) {
+  const int G = a.G;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int W = blockDim.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lg = lane >> 4;
+  const int c = lane & 15;
+  const int pic = ((c & 3) << 2) | (c >> 2);
+
+  const int32_t* bt_row = a.bt + (int64_t)b * a.MB;
+  for (int i = tid; i < e - s; i += blockDim.x) bt_s[i] = bt_row[s + i];
+  half8_t qb[4];
+  {
+    const int hc = c < G ? c : 0;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + kvh * G + hc) * kD;
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      u32x4 w4 = {0u, 0u, 0u, 0u};
+      if (c < G) w4 = *reinterpret_cast<const u32x4*>(qrow + chunk_dim<false>(ch, lg));
+      qb[ch] = __builtin_bit_cast(half8_t, w4);
+    }
+  }
+  __syncthreads();
+
+  const unsigned char* kbase =
+      reinterpret_cast<const unsigned char*>(a.k) + (int64_t)kvh * kBlockHeadBytes;
+  const unsigned char* vbase =
+      reinterpret_cast<const unsigned char*>(a.v) + (int64_t)kvh * kBlockHeadBytes;
+  const int k_off = (lg * kT + pic) * 16;
+  const int v_off = lane * 16;
+  const int j0 = s + wave;
+  const int n_it = j0 < e ? (e - j0 + W - 1) / W : 0;
+  // table entry of iteration it (the range's slice is in LDS)
+  auto phys_it = [&](int it) -> int64_t { return (int64_t)bt_s[wave + it * W]; };
+  auto load4 = [&](u32x4* r, const unsigned char* base, int64_t ph, int off) {
+    const unsigned char* p = base + ph * a.blk_bytes + off;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 1024 * i));
+  };
+  // one dword of each 128 B line of a 4 KiB K or V block
+  auto touch = [&](const unsigned char* base, int64_t ph) -> uint32_t {
+    return *reinterpret_cast<const uint32_t*>(base + ph * a.blk_bytes + (lane & 31) * 128);
+  };
+  uint32_t sink = 0;
+
+  // ---- loop 1: scores ------------------------------------------------------
+  float m = -INFINITY;
+  auto scores = [&](const u32x4* kh, int j) {
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, kh[ch]), qb[ch],
+                                                     sacc, 0, 0, 0);
+    const int rem = ctx - j * kT;
+    float bm = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float sc = 4 * q + lg < rem ? sacc[q] * a.scale_log2 : -INFINITY;
+      bm = fmaxf(bm, sc);
+      if (c < G) logit_s[((j - s) * kT + 4 * q + lg) * G + c] = sc;
+    }
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    m = fmaxf(m, bm);
+  };
+  if constexpr (PF >= 2) {
+    u32x4 ka[4], kb[4];
+    if (n_it > 0) load4(ka, kbase, phys_it(0), k_off);
+    int it = 0;
+    for (; it + 2 < n_it; it += 2) {
+      __builtin_amdgcn_sched_barrier(0);
+      load4(kb, kbase, phys_it(it + 1), k_off);
+      if (PF == 3 && it + 2 < n_it) sink ^= touch(kbase, phys_it(it + 2));
+      __builtin_amdgcn_sched_barrier(0);
+      scores(ka, j0 + it * W);
+      __builtin_amdgcn_sched_barrier(0);
+      load4(ka, kbase, phys_it(it + 2), k_off);
+      if (PF == 3 && it + 3 < n_it) sink ^= touch(kbase, phys_it(it + 3));
+      __builtin_amdgcn_sched_barrier(0);
+      scores(kb, j0 + (it + 1) * W);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (; it < n_it; ++it) {
+      if (it + 1 < n_it) load4(kb, kbase, phys_it(it + 1), k_off);
+      scores(ka, j0 + it * W);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ka[i] = kb[i];
+    }
+  } else {
+    for (int it = 0; it < n_it; ++it) {
+      u32x4 kh[4];
+      __builtin_amdgcn_sched_barrier(0);
+      load4(kh, kbase, phys_it(it), k_off);
+      if (PF == 1 && it + 1 < n_it) sink ^= touch(kbase, phys_it(it + 1));
+      __builtin_amdgcn_sched_barrier(0);
+      scores(kh, j0 + it * W);
+    }
+  }
+
+  // ---- the range maximum of each head -------------------------------------
+  if (lg == 0 && c < G) wmax_s[wave * G + c] = m;
+  __syncthreads();
+  float M = -INFINITY;
+  for (int w = 0; w < W; ++w) M = fmaxf(M, wmax_s[w * G + (c < G ? c : 0)]);
+  // M is finite: the range holds at least one valid token
+
+  // ---- loop 2: weights times V ---------------------------------------------
+  float l = 0.f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto weigh = [&](u32x4* vh, int j) {
+    const int rem = ctx - j * kT;
+    half4_t phi, plo;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float pr = 0.f;
+      if (c < G) pr = fast_exp2(logit_s[((j - s) * kT + 4 * q + lg) * G + c] - M);
+      l += pr;
+      phi[q] = (_Float16)pr;
+      plo[q] = (_Float16)(pr - (float)phi[q]);
+    }
+    if (rem < kT) {  // a partial last block: its unused V slots may hold anything
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * i + lg >= rem) vh[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int u = t >> 1, h = t & 1;
+      u32x2 vt;
+      vt.x = pick_halves(vh[0][u], vh[1][u], h);
+      vt.y = pick_halves(vh[2][u], vh[3][u], h);
+      const half4_t av = __builtin_bit_cast(half4_t, vt);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, phi, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, plo, acc[t], 0, 0, 0);
+    }
+  };
+  if constexpr (PF >= 2) {
+    u32x4 va[4], vb[4];
+    if (n_it > 0) load4(va, vbase, phys_it(0), v_off);
+    int it = 0;
+    for (; it + 2 < n_it; it += 2) {
+      __builtin_amdgcn_sched_barrier(0);
+      load4(vb, vbase, phys_it(it + 1), v_off);
+      if (PF == 3 && it + 2 < n_it) sink ^= touch(vbase, phys_it(it + 2));
+      __builtin_amdgcn_sched_barrier(0);
+      weigh(va, j0 + it * W);
+      __builtin_amdgcn_sched_barrier(0);
+      load4(va, vbase, phys_it(it + 2), v_off);
+      if (PF == 3 && it + 3 < n_it) sink ^= touch(vbase, phys_it(it + 3));
+      __builtin_amdgcn_sched_barrier(0);
+      weigh(vb, j0 + (it + 1) * W);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (; it < n_it; ++it) {
+      if (it + 1 < n_it) load4(vb, vbase, phys_it(it + 1), v_off);
+      weigh(va, j0 + it * W);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) va[i] = vb[i];
+    }
+  } else {
+    for (int it = 0; it < n_it; ++it) {
+      u32x4 vh[4];
+      __builtin_amdgcn_sched_barrier(0);
+      load4(vh, vbase, phys_it(it), v_off);
+      if (PF == 1 && it + 1 < n_it) sink ^= touch(vbase, phys_it(it + 1));
+      __builtin_amdgcn_sched_barrier(0);
+      weigh(vh, j0 + it * W);
+    }
+  }
+  if (a.sink_enable && sink == 0x9E3779B9u && lane == 0) a.sink[0] = (int32_t)sink;
+
+  // ---- records: the same layout as walk_range ------------------------------
+  float lt = l + __shfl_xor(l, 16);
+  lt += __shfl_xor(lt, 32);
+  if (c < G) {
+    float* rec = merge_s + (wave * G + c) * kRec;
+    if (lg == 0) {
+      rec[0] = M;
+      rec[1] = lt;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) rec[2 + 32 * lg + 8 * q + t] = acc[t][q];
+  }
+  __syncthreads();
+}
+
 // Softmax-merge of the W wave records of head h: running max M (log2 units),
 // denominator L and unnormalised output O for dim d.
 __device__ __forceinline__ void combine_waves(const float* merge_s, int W, int G, int h, int d,
@@ -492,7 +698,8 @@ __device__ __forceinline__ int ranked_sequence(const DecodeArgs& a, int r, int t
   return b;
 }
 
-template <int PF, bool DBG, bool KV8>
+// TWO selects the two-loop walk (fp16, no debug outputs).
+template <int PF, bool DBG, bool KV8, bool TWO = false>
 __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   int32_t* bt_s = reinterpret_cast<int32_t*>(smem_raw);
@@ -531,7 +738,12 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
     return;
   }
 
-  walk_range<PF, DBG, KV8>(a, b, kvh, ctx, s, e, bt_s, merge_s);
+  if constexpr (TWO) {
+    float* logit_s = merge_s + W * G * kRec;
+    walk_two_loop<PF>(a, b, kvh, ctx, s, e, bt_s, merge_s, logit_s, logit_s + a.PB * kT * G);
+  } else {
+    walk_range<PF, DBG, KV8>(a, b, kvh, ctx, s, e, bt_s, merge_s);
+  }
 
   for (int idx = tid; idx < G * kD; idx += blockDim.x) {
     const int h = idx / kD, d = idx % kD;
@@ -618,10 +830,10 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const u32x4* __restric
 // ---------------------------------------------------------------------------
 // Launchers.
 
-template <int PF, bool DBG, bool KV8>
+template <int PF, bool DBG, bool KV8, bool TWO = false>
 static hipError_t launch_decode_t(const DecodeArgs& a, dim3 grid, dim3 block, size_t lds,
                                   hipStream_t st) {
-  hipLaunchKernelGGL((pa_decode_kernel<PF, DBG, KV8>), grid, block, lds, st, a);
+  hipLaunchKernelGGL((pa_decode_kernel<PF, DBG, KV8, TWO>), grid, block, lds, st, a);
   return hipGetLastError();
 }
 
@@ -645,6 +857,18 @@ hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int wa
   const dim3 block(kWave * waves);
   return table[(kv8 ? 10 : 0) + pf * 2 + (dbg ? 1 : 0)](
       a, grid, block, decode_lds_bytes(a.PB, a.G, waves, a.B, a.rank_seqs != 0), st);
+}
+
+hipError_t launch_decode_two_loop(const DecodeArgs& a, int pf, int waves, hipStream_t st) {
+  typedef hipError_t (*fn_t)(const DecodeArgs&, dim3, dim3, size_t, hipStream_t);
+  static const fn_t table[4] = {
+      launch_decode_t<0, false, false, true>, launch_decode_t<1, false, false, true>,
+      launch_decode_t<2, false, false, true>, launch_decode_t<3, false, false, true>};
+  if (pf < 0 || pf > 3) return hipErrorInvalidValue;
+  const dim3 grid(a.Hkv, a.B, a.P);
+  const dim3 block(kWave * waves);
+  return table[pf](a, grid, block, two_loop_lds_bytes(a.PB, a.G, waves, a.B, a.rank_seqs != 0),
+                   st);
 }
 
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t st) {

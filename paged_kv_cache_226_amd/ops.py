@@ -38,7 +38,7 @@ def shape_of(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor)
 
 
 def options(prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0,
-            prefetch_distance: int = 0, seq_order: int = 0,
+            prefetch_distance: int = 0, seq_order: int = 0, structure: int = 0,
             debug_gather_k: Optional[torch.Tensor] = None,
             debug_trace: Optional[torch.Tensor] = None,
             debug_error_word: Optional[torch.Tensor] = None) -> nat.PaOptions:
@@ -50,6 +50,7 @@ def options(prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0
     o.waves_per_wg = int(waves_per_wg)
     o.prefetch_distance = int(prefetch_distance)
     o.seq_order = int(seq_order)
+    o.structure = int(structure)
     if debug_gather_k is not None:
         _check(debug_gather_k, "debug_gather_k", torch.float16, 4)
         o.debug_gather_k = debug_gather_k.data_ptr()
@@ -86,7 +87,8 @@ def _check_kv(t: torch.Tensor, name: str, fp8: bool, ndim: int):
 
 def _decode(fp8: bool, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
             v_scale, out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
-            seq_order, workspace, debug_gather_k, debug_trace, debug_error_word, stream):
+            seq_order, structure, workspace, debug_gather_k, debug_trace, debug_error_word,
+            stream):
     name = "paged_attn_decode_fp8" if fp8 else "paged_attn_decode"
     _check(q, "q", torch.float16, 3)
     _check_kv(k_cache, "k_cache", fp8, 5)
@@ -110,7 +112,7 @@ def _decode(fp8: bool, q, k_cache, v_cache, block_tables, context_lens, scale, k
             raise ValueError("out must have q's shape")
     sh = shape_of(q, k_cache, block_tables)
     o = options(prefetch, partition_blocks, waves_per_wg, prefetch_distance, seq_order,
-                debug_gather_k, debug_trace, debug_error_word)
+                structure, debug_gather_k, debug_trace, debug_error_word)
     need = int(nat.lib().paged_attn_workspace_size(ctypes.byref(sh), ctypes.byref(o)))
     if need:
         if workspace is None:
@@ -139,7 +141,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       block_tables: torch.Tensor, context_lens: torch.Tensor,
                       scale: Optional[float] = None, out: Optional[torch.Tensor] = None, *,
                       prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0,
-                      prefetch_distance: int = 0, seq_order: int = 0,
+                      prefetch_distance: int = 0, seq_order: int = 0, structure: int = 0,
                       workspace: Optional[torch.Tensor] = None,
                       debug_gather_k: Optional[torch.Tensor] = None,
                       debug_trace: Optional[torch.Tensor] = None,
@@ -153,7 +155,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     """
     return _decode(False, q, k_cache, v_cache, block_tables, context_lens, scale, 1.0, 1.0,
                    out, prefetch, partition_blocks, waves_per_wg, prefetch_distance, seq_order,
-                   workspace, debug_gather_k, debug_trace, debug_error_word, stream)
+                   structure, workspace, debug_gather_k, debug_trace, debug_error_word, stream)
 
 
 def paged_attn_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -162,6 +164,7 @@ def paged_attn_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                           v_scale: float = 1.0, out: Optional[torch.Tensor] = None, *,
                           prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0,
                           prefetch_distance: int = 0, seq_order: int = 0,
+                          structure: int = 0,
                           workspace: Optional[torch.Tensor] = None,
                           debug_gather_k: Optional[torch.Tensor] = None,
                           debug_trace: Optional[torch.Tensor] = None,
@@ -180,7 +183,8 @@ def paged_attn_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
         v_cache = v_cache.view(torch.uint8)
     return _decode(True, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
                    v_scale, out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
-                   seq_order, workspace, debug_gather_k, debug_trace, debug_error_word, stream)
+                   seq_order, structure, workspace, debug_gather_k, debug_trace,
+                   debug_error_word, stream)
 
 
 def stream_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None,

@@ -28,8 +28,10 @@ import os
 import re
 import sys
 
-MODE_NAMES = {0: "off", 1: "l2", 2: "reg", 3: "both", 4: "reg2"}
-DECODE_RE = re.compile(r"pa_decode_kernel<(\d), (true|false), (true|false)>")
+MODE_NAMES = {0: "off", 1: "l2", 2: "reg", 3: "both", 4: "reg2",
+              10: "two_loop_off", 11: "two_loop_l2", 12: "two_loop_reg", 13: "two_loop_both"}
+# pa_decode_kernel<PF, DBG, KV8, TWO>; the two-loop instances count as modes 10 + PF
+DECODE_RE = re.compile(r"pa_decode_kernel<(\d), (true|false), (true|false)(?:, (true|false))?>")
 KV8 = False  # which cache type's kernels the summary counts (set by main)
 
 
@@ -57,7 +59,7 @@ def decode_mode(name):
     m = DECODE_RE.search(name)
     if not m or m.group(2) != "false" or (m.group(3) == "true") != KV8:
         return None
-    return int(m.group(1))
+    return int(m.group(1)) + (10 if m.group(4) == "true" else 0)
 
 
 def per_mode(agg, counter):

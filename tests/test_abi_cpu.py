@@ -64,7 +64,7 @@ def test_struct_layouts_match_header(native_lib, tmp_path):
         assert int(value) == want, line
     o = nat.default_options()
     assert o.prefetch == -1 and o.partition_blocks == 0 and o.waves_per_wg == 0
-    assert o.prefetch_distance == 0 and o.seq_order == 0 and o.reserved == 0
+    assert o.prefetch_distance == 0 and o.seq_order == 0 and o.structure == 0
     assert o.workspace is None and o.debug_gather_k is None
 
 
@@ -108,7 +108,8 @@ def good_shape(**kw):
     (dict(opts=dict(partition_blocks=2048)), nat.PA_ERR_UNSUPPORTED),
     (dict(opts=dict(seq_order=3)), nat.PA_ERR_INVALID_ARG),
     (dict(opts=dict(seq_order=-1)), nat.PA_ERR_INVALID_ARG),
-    (dict(opts=dict(reserved=1)), nat.PA_ERR_INVALID_ARG),
+    (dict(opts=dict(structure=2)), nat.PA_ERR_INVALID_ARG),
+    (dict(opts=dict(structure=1, prefetch_distance=2)), nat.PA_ERR_UNSUPPORTED),
     (dict(shape=dict(num_seqs=257), opts=dict(seq_order=2)), nat.PA_ERR_UNSUPPORTED),
     # too much LDS: 8 waves x 16 heads of merge records
     (dict(shape=dict(num_q_heads=32, num_kv_heads=2), opts=dict(waves_per_wg=8)),
@@ -185,3 +186,24 @@ def test_sequence_order_of_the_plan(native_lib, B, order, want):
 def test_auto_plan_rule(native_lib, B, Hkv, MB, waves, P, PB):
     p = nat.plan(nat.make_shape(B, Hkv * 4, Hkv, MB, 1000))
     assert (p["waves_per_wg"], p["num_partitions"], p["partition_blocks"]) == (waves, P, PB)
+
+
+@pytest.mark.parametrize("g,PB", [(1, 32), (4, 32), (8, 32), (16, 16)])
+def test_two_loop_plan_keeps_the_scores_in_lds(native_lib, g, PB):
+    o = nat.default_options()
+    o.structure = nat.STRUCTURE_TWO_LOOP
+    p = nat.plan(nat.make_shape(4, 2 * g, 2, 512, 100), o)
+    assert (p["structure"], p["waves_per_wg"], p["partition_blocks"]) == (1, 4, PB)
+    assert p["num_partitions"] == -(-512 // PB)
+
+
+def test_two_loop_rejects_e4m3_and_debug_outputs(native_lib):
+    o = nat.default_options()
+    o.structure = nat.STRUCTURE_TWO_LOOP
+    sh = good_shape(max_blocks_per_seq=16)
+    f = nat.lib().paged_attn_decode_fp8
+    rc = f(*[ctypes.c_void_p(FAKE)] * 5, ctypes.c_float(0.1), ctypes.c_float(1.0),
+           ctypes.c_float(1.0), ctypes.c_void_p(FAKE), ctypes.byref(sh), ctypes.byref(o), None)
+    assert rc == nat.PA_ERR_UNSUPPORTED
+    o.debug_error_word = FAKE
+    assert call(sh, o) == nat.PA_ERR_UNSUPPORTED

@@ -13,5 +13,11 @@ def test_decode_mode_selects_the_cache_type_and_skips_debug_instances():
                 want = m if d == "false" and (k == "true") == kv8 else None
                 assert rs.decode_mode(name) == want, (name, kv8)
         assert rs.decode_mode("void pa::pa_reduce_kernel(pa::DecodeArgs)") is None
+        rs.KV8 = False
+        for m in range(4):
+            assert rs.decode_mode(f"void pa::pa_decode_kernel<{m}, false, false, false>(x)") == m
+            assert rs.decode_mode(f"void pa::pa_decode_kernel<{m}, false, false, true>(x)") \
+                == 10 + m
+            assert rs.MODE_NAMES[10 + m].startswith("two_loop_")
     finally:
         rs.KV8 = False
