@@ -299,6 +299,15 @@ def main():
     b.record(stream)
     torch.cuda.synchronize()
     stream_gbps = (4 << 30) / (a.elapsed_time(b) * 1e3 / 10) / 1e3
+    # the same read over exactly this step's KV bytes: the ramp-up and drain
+    # of a launch weigh more on a shorter read
+    n_same = min(kv_bytes, 4 << 30) // 16 * 16
+    a.record(stream)
+    for _ in range(10):
+        ops.stream_read(buf[:n_same], sink)
+    b.record(stream)
+    torch.cuda.synchronize()
+    stream_same_gbps = n_same / (a.elapsed_time(b) * 1e3 / 10) / 1e3
     del buf
 
     # The decode kernel is the dominant kernel.  With one partition it is the
@@ -348,6 +357,8 @@ def main():
         "prefetch_modes": modes,
         "stream_read_ceiling_GBps": round(stream_gbps, 1),
         "pct_of_stream_ceiling": round(100 * kv_bytes / us / 1e3 / stream_gbps, 1),
+        "stream_read_same_size_GBps": round(stream_same_gbps, 1),
+        "pct_of_same_size_stream": round(100 * kv_bytes / us / 1e3 / stream_same_gbps, 1),
         "roofline": roofline,
         "kernel_source_hash": kernel_source_hash(),
         "inputs_sha256": {k: v[:16] for k, v in gen.digests(x).items()},

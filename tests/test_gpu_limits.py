@@ -1,0 +1,87 @@
+"""Limits of the launch and of the address arithmetic (MI355X): the largest
+batch the grid allows, a 64K-token context split into as many as 4096
+partitions, and pools whose byte offsets pass 4 GiB."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from paged_kv_cache_226_amd import inputs as gen
+from paged_kv_cache_226_amd import ops
+
+from parity import assert_close, bits, oracle, run, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu(native_lib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def test_batch_at_the_grid_limit():
+    """65535 sequences (grid.y's limit) of 0..16 tokens; natural order."""
+    B = 65535
+    rng = np.random.default_rng(400)
+    lens = rng.integers(0, 17, size=B)
+    x = gen.make_case(B, 2, 1, lens, seed=400, extra_pool_blocks=1)
+    print(f"[limits] B={B}, pool {x.k_cache.shape[0]} blocks", flush=True)
+    out = run(x)
+    assert not out[lens == 0].any()
+    rows = np.array([(b, h) for b in rng.choice(B, 200, replace=False) for h in range(2)])
+    ref = orc.paged_attention_rows_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                       x.context_lens, x.scale, rows)
+    assert_close(out[rows[:, 0], rows[:, 1]], ref, "B=65535")
+
+
+@pytest.mark.parametrize("pb,waves", [(0, 0), (1, 4), (1, 8), (7, 2), (1024, 1)])
+def test_context_of_64k_tokens(pb, waves):
+    x = gen.make_case(1, 8, 2, [65536], seed=401)
+    dev = to_device(x)
+    p = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], partition_blocks=pb,
+                 waves_per_wg=waves)
+    print(f"[limits] 64K tokens: {p}", flush=True)
+    if pb == 1:
+        assert p["num_partitions"] == 4096
+    assert_close(run(x, dev, partition_blocks=pb, waves_per_wg=waves), oracle(x),
+                 f"64K pb={pb} w={waves}")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_pool_offsets_beyond_4_gib(fp8):
+    """The used blocks sit at the top of a 140000-block pool (K alone is
+    4.6 GB in fp16), the rest of which is NaN."""
+    NB, top = 140000, 139000
+    x = gen.make_case(2, 32, 8, [3000, 1000], seed=402)
+    nb_used = x.k_cache.shape[0]
+    ids = torch.arange(top, top + nb_used, device="cuda")
+    bt = np.where(x.block_tables >= 0, x.block_tables + top, -1).astype(np.int32)
+    if fp8:
+        x8 = gen.to_fp8(x)
+        kp = torch.full((NB, 8, 8, 16, 16), gen.FP8_NAN_BYTE, dtype=torch.uint8, device="cuda")
+        vp = torch.full((NB, 8, 16, 128), gen.FP8_NAN_BYTE, dtype=torch.uint8, device="cuda")
+        kp.index_copy_(0, ids, torch.from_numpy(gen.pack_k_fp8(x8.k8)).cuda())
+        vp.index_copy_(0, ids, torch.from_numpy(x8.v8).cuda())
+    else:
+        kp = torch.full((NB, 8, 16, 16, 8), float("nan"), dtype=torch.float16, device="cuda")
+        vp = torch.full((NB, 8, 16, 128), float("nan"), dtype=torch.float16, device="cuda")
+        kp.index_copy_(0, ids, torch.from_numpy(gen.pack_k(x.k_cache)).cuda())
+        vp.index_copy_(0, ids, torch.from_numpy(x.v_cache).cuda())
+    top_offset = top * kp[0].numel() * kp.element_size()  # bytes before block `top`
+    assert top_offset > (1 << 31) and (fp8 or top_offset > (1 << 32))
+    q = torch.from_numpy(x.q).cuda()
+    btd = torch.from_numpy(bt).cuda()
+    ctx = torch.from_numpy(x.context_lens).cuda()
+    if fp8:
+        out = ops.paged_attn_decode_fp8(q, kp, vp, btd, ctx, x.scale, x8.k_scale, x8.v_scale)
+        ref = orc.paged_attention_fp8_f64(x8.q, x8.k8, x8.v8, x8.block_tables, x8.context_lens,
+                                          x8.scale, x8.k_scale, x8.v_scale)
+    else:
+        out = ops.paged_attn_decode(q, kp, vp, btd, ctx, x.scale)
+        ref = oracle(x)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    del kp, vp
+    torch.cuda.empty_cache()
+    assert_close(got, ref, f"offsets > 4 GiB fp8={fp8}")
