@@ -81,7 +81,7 @@ def parse():
                     help="KV cache element type (fp8 = OCP E4M3 with per-tensor scales)")
     ap.add_argument("--prefetch-distance", type=int, default=0,
                     help="L2-touch distance k in wave iterations (modes 1, 3); 0 = 1")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
@@ -94,6 +94,25 @@ def parse():
     ap.add_argument("--sweep-max-gb", type=float, default=16.0,
                     help="skip points whose K+V pool exceeds this many GB")
     return ap.parse_args()
+
+
+# sweep counter pass: modes off, register look-ahead, L2 touch; launches each
+SWEEP_PROFILE_MODES = [0, 2, 1]
+SWEEP_PROFILE_LAUNCHES = 2
+
+
+def calibrate_counters(torch, ops):
+    """Kernels of known size for scaling the HBM byte counters: a 1 GiB
+    streaming read (reads 2^30 B) and a 1 GiB fp16 elementwise copy (reads
+    and writes 2^30 B each), three times each."""
+    src = torch.empty(1 << 29, dtype=torch.float16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        ops.stream_read(src)
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": {"stream_read_bytes": 1 << 30, "copy_read_bytes": 1 << 30,
+                                      "copy_write_bytes": 1 << 30}}), flush=True)
 
 
 def run_sweep(args):
@@ -112,6 +131,7 @@ def run_sweep(args):
     batches = [int(v) for v in args.sweep_batches.split(",")]
     contexts = [int(v) for v in args.sweep_contexts.split(",")]
     stream = torch.cuda.current_stream()
+    steps = min(args.steps, 100)
     for bi, B in enumerate(batches):
         for ci, ctx in enumerate(contexts):
             kv_bytes = acc.step_kv_bytes(w.num_kv_heads, 128, [ctx] * B)
@@ -122,6 +142,22 @@ def run_sweep(args):
             out = torch.empty_like(d["q"])
             ws = ops.new_workspace(d["q"], d["k_cache"], d["block_tables"])
             plan = ops.plan(d["q"], d["k_cache"], d["block_tables"])
+            if args.profile:
+                # for a counter pass: a fixed number of launches per mode, in
+                # this order, so the dispatches can be mapped back to points
+                for pf in SWEEP_PROFILE_MODES:
+                    for _ in range(SWEEP_PROFILE_LAUNCHES):
+                        ops.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"],
+                                              d["block_tables"], d["context_lens"], d["scale"],
+                                              out, prefetch=pf, workspace=ws)
+                torch.cuda.synchronize()
+                print(json.dumps({"sweep_profile": args.workload, "batch": B, "context": ctx,
+                                  "kv_bytes": kv_bytes, "partitions": plan["num_partitions"],
+                                  "modes": SWEEP_PROFILE_MODES,
+                                  "launches_per_mode": SWEEP_PROFILE_LAUNCHES}), flush=True)
+                del d, out, ws
+                torch.cuda.empty_cache()
+                continue
             times = {}
             for pf in (0, plan["prefetch"]):
                 f = lambda: ops.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"],
@@ -132,11 +168,11 @@ def run_sweep(args):
                 torch.cuda.synchronize()
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
-                for _ in range(args.steps):
+                for _ in range(steps):
                     f()
                 b.record(stream)
                 torch.cuda.synchronize()
-                times[pf] = a.elapsed_time(b) * 1e3 / args.steps
+                times[pf] = a.elapsed_time(b) * 1e3 / steps
             seqs = [0, B - 1]
             x = gen.host_subset(d, seqs)
             rows = np.array([[i, h] for i in range(len(seqs)) for h in range(w.num_q_heads)])
@@ -156,6 +192,8 @@ def run_sweep(args):
                 "parity_rel": float((diff / np.maximum(np.abs(ref), 1e-3)).max())}), flush=True)
             del d, out, ws
             torch.cuda.empty_cache()
+    if args.profile:
+        calibrate_counters(torch, ops)
 
 
 def main():
@@ -262,20 +300,9 @@ def main():
         for pf, dist, structure in MODE_RUNS:
             if not (fp8 and structure):
                 timed(pf, args.steps, args.warmup, dist, structure=structure)
-        # Calibration kernels of known size for the HBM byte counters: a 1 GiB
-        # streaming read (reads 2^30 B) and a 1 GiB fp16 elementwise copy
-        # (reads and writes 2^30 B each).
-        src = torch.empty(1 << 29, dtype=torch.float16, device=dev).normal_()
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            ops.stream_read(src)
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
+        calibrate_counters(torch, ops)
         print(json.dumps({"profile_run": args.workload, "kv_dtype": args.kv_dtype,
-                          "steps": args.steps,
-                          "calibration": {"stream_read_bytes": 1 << 30,
-                                          "copy_read_bytes": 1 << 30,
-                                          "copy_write_bytes": 1 << 30}}), flush=True)
+                          "steps": args.steps}), flush=True)
         return
 
     us = timed(mode, args.steps, args.warmup, min_warm_s=0.25)
@@ -380,7 +407,7 @@ def main():
                 ref = orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
                                               x.context_lens, x.scale)
             runs.append(time.perf_counter() - t1)
-            if time.time() > deadline or len(runs) >= 5:
+            if time.time() > deadline or len(runs) >= 200:
                 break
         t_cpu = sorted(runs)[len(runs) // 2]
         diff = np.abs(got - ref)
@@ -389,7 +416,7 @@ def main():
             "us_per_step": round(t_cpu * 1e6, 1), "cores": orc.max_threads(), "kind": "oracle",
             "sample": f"the whole {args.workload} step ({args.kv_dtype} KV, all "
                       f"{w.num_seqs * w.num_q_heads} (sequence, head) rows), fp64, median of "
-                      f"{len(runs)} run(s)"}
+                      f"{len(runs)} run(s) over {sum(runs):.1f} s of CPU time"}
         result["parity"] = {"abs": float(diff.max()),
                             "rel": float((diff / np.maximum(np.abs(ref), 1e-3)).max()),
                             "rows_checked": int(w.num_seqs * w.num_q_heads)}

@@ -24,6 +24,7 @@ import argparse
 import collections
 import csv
 import glob
+import json
 import os
 import re
 import sys
@@ -93,6 +94,50 @@ def kernel_stats(d):
              float(r["MaxNs"]) / 1e3, float(r["Percentage"])) for r in rows]
 
 
+def sweep_fetch(profile_jsonl, fetch_dir, workload, out_dir, command):
+    """FETCH_SIZE per point of a `bench.py --sweep --profile` run: the decode
+    dispatches, in launch order, are matched to the points the run printed
+    (modes x launches each), scaled by the 1 GiB streaming-read calibration
+    and divided by the point's algorithmic KV bytes."""
+    points = [json.loads(l) for l in open(profile_jsonl) if l.startswith('{"sweep_profile"')]
+    rows = sorted(_rows(fetch_dir, "_counter_collection.csv"), key=lambda r: int(r["Dispatch_Id"]))
+    per_dispatch = collections.OrderedDict()
+    for r in rows:
+        if r["Counter_Name"] == "FETCH_SIZE":
+            key = int(r["Dispatch_Id"])
+            if key not in per_dispatch:
+                per_dispatch[key] = [r["Kernel_Name"], 0.0]
+            per_dispatch[key][1] += float(r["Counter_Value"])
+    fk = calibration({(n, "FETCH_SIZE"): [v] for n, v in per_dispatch.values()}, "FETCH_SIZE",
+                     "stream")
+    decode = [(decode_mode(n), v) for n, v in per_dispatch.values() if decode_mode(n) is not None]
+    lines = [f"# FETCH_SIZE per point of the batch x context sweep: {workload}", "", "```",
+             "command:", *["    " + c for c in command.split(" ;; ") if c],
+             f"FETCH_SIZE scale: {fk} (1 GiB streaming read in the same process)", "```", "",
+             "HBM read bytes / algorithmic KV bytes, per look-ahead mode (mean over the "
+             "launches of each mode):", "",
+             "| batch | context | KV bytes | partitions | off | reg | l2 |",
+             "|---|---|---|---|---|---|---|"]
+    i = 0
+    for pt in points:
+        ratios = {}
+        for m in pt["modes"]:
+            vals = []
+            for _ in range(pt["launches_per_mode"]):
+                mode, v = decode[i]
+                i += 1
+                assert mode == m, (pt, mode, m)
+                vals.append(v)
+            ratios[m] = sum(vals) / len(vals) * 1024 * fk / pt["kv_bytes"]
+        lines.append(f"| {pt['batch']} | {pt['context']} | {pt['kv_bytes']} | "
+                     f"{pt['partitions']} | {ratios[0]:.4f} | {ratios[2]:.4f} | {ratios[1]:.4f} |")
+    assert i == len(decode), (i, len(decode))
+    path = os.path.join(out_dir, f"pa_decode_sweep_{workload}_fetch.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
@@ -105,6 +150,8 @@ def main(argv=None):
     ap.add_argument("--command", default="", help="the command lines that produced the inputs")
     ap.add_argument("--source-hash", default="")
     ap.add_argument("--out-dir", default="profiles")
+    ap.add_argument("--sweep-profile", help="JSON lines of `bench.py --sweep --profile`; with "
+                                            "--fetch, writes the per-point FETCH_SIZE table")
     a = ap.parse_args(argv)
 
     sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
@@ -113,6 +160,9 @@ def main(argv=None):
 
     global KV8
     KV8 = a.kv_dtype == "fp8"
+    if a.sweep_profile:
+        print(sweep_fetch(a.sweep_profile, a.fetch, a.workload, a.out_dir, a.command))
+        return 0
     tag = a.workload + ("_fp8" if KV8 else "")
     w = gen.WORKLOADS[a.workload]
     ctx = gen.workload_context_lens(w)
