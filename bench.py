@@ -48,6 +48,16 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def profile_tag(workload: str, kv_dtype: str) -> str:
     return workload if kv_dtype == "fp16" else f"{workload}_{kv_dtype}"
 
@@ -289,7 +299,8 @@ def main():
             b.record(stream)
         torch.cuda.synchronize()
         ts = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
-        return sum(ts) / len(ts), ts[len(ts) // 2]
+        pick = lambda f: ts[min(len(ts) - 1, int(f * len(ts)))]
+        return sum(ts) / len(ts), ts[len(ts) // 2], pick(0.1), pick(0.9)
 
     mode = plan["prefetch"]
     mode_names = nat.PREFETCH_NAMES
@@ -306,7 +317,7 @@ def main():
         return
 
     us = timed(mode, args.steps, args.warmup, min_warm_s=0.25)
-    launch_avg, launch_med = per_launch(mode, args.steps)
+    launch_avg, launch_med, launch_p10, launch_p90 = per_launch(mode, args.steps)
     modes = {}
     for pf, dist, structure in MODE_RUNS:
         if fp8 and structure:
@@ -350,7 +361,9 @@ def main():
                                                                     " + pa_reduce_kernel"),
                 "kernel_us_avg": round(us, 2),
                 "event_pair_us_avg": round(launch_avg, 2),
-                "event_pair_us_median": round(launch_med, 2)}
+                "event_pair_us_median": round(launch_med, 2),
+                "event_pair_us_p10": round(launch_p10, 2),
+                "event_pair_us_p90": round(launch_p90, 2)}
 
     result = {
         "metric": METRIC,
@@ -414,6 +427,8 @@ def main():
         result["cpu_baseline"] = {
             "value": round(kv_bytes / t_cpu / 1e9, 3), "unit": "GB/s",
             "us_per_step": round(t_cpu * 1e6, 1), "cores": orc.max_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
             "sample": f"the whole {args.workload} step ({args.kv_dtype} KV, all "
                       f"{w.num_seqs * w.num_q_heads} (sequence, head) rows), fp64, median of "
                       f"{len(runs)} run(s) over {sum(runs):.1f} s of CPU time"}

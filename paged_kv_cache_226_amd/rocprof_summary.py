@@ -147,6 +147,8 @@ def main(argv=None):
     ap.add_argument("--write")
     ap.add_argument("--tcc")
     ap.add_argument("--sq")
+    ap.add_argument("--valu", help="pass with SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_BUSY_CYCLES "
+                                   "SQ_INSTS SQ_WAVE_CYCLES GRBM_GUI_ACTIVE")
     ap.add_argument("--command", default="", help="the command lines that produced the inputs")
     ap.add_argument("--source-hash", default="")
     ap.add_argument("--out-dir", default="profiles")
@@ -199,13 +201,22 @@ def main(argv=None):
         wait, wcyc = per_mode(sq, "SQ_WAIT_INST_ANY"), per_mode(sq, "SQ_WAVE_CYCLES")
         valu, waves = per_mode(sq, "SQ_INSTS_VALU"), per_mode(sq, "SQ_WAVES")
         vmem = per_mode(sq, "SQ_INSTS_VMEM_RD")
+        va = counters(a.valu) if a.valu else {}
+        v_act, v_mfma = per_mode(va, "SQ_ACTIVE_INST_VALU"), per_mode(va, "SQ_VALU_MFMA_BUSY_CYCLES")
+        v_insts, v_wcyc = per_mode(va, "SQ_INSTS"), per_mode(va, "SQ_WAVE_CYCLES")
+        v_gui = per_mode(va, "GRBM_GUI_ACTIVE")
         lines = ["# pa_decode counters per look-ahead mode: " + tag, "", "```", *head,
                  f"FETCH_SIZE scale: {fk_stream} (1 GiB streaming read), {fk_copy} (1 GiB copy)",
                  f"WRITE_SIZE scale: {wk_copy} (1 GiB copy)", "```", "",
+                 "GRBM_GUI_ACTIVE is summed over the 8 XCDs in the CSV: divided by 8.",
+                 "VALU busy = 100 * SQ_ACTIVE_INST_VALU / 256 CUs / GRBM_GUI_ACTIVE "
+                 "(rocprofv3's VALUBusy); MFMA util = 100 * SQ_VALU_MFMA_BUSY_CYCLES / "
+                 "(GRBM_GUI_ACTIVE * 1024 SIMDs) (its MfmaUtil); cycles / instruction = "
+                 "4 * SQ_WAVE_CYCLES / SQ_INSTS (per wave).", "",
                  "| mode | HBM read bytes | read / algorithmic | HBM write bytes | L2 hit rate |"
                  " stall share (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES) | VALU insts / wave |"
-                 " VMEM reads / wave |",
-                 "|---|---|---|---|---|---|---|---|"]
+                 " VMEM reads / wave | VALU busy | MFMA util | cycles / instruction |",
+                 "|---|---|---|---|---|---|---|---|---|---|---|"]
         traffic = {}
         for m in sorted(fetch):
             rb = fetch[m] * 1024 * fk if fk else float("nan")
@@ -215,8 +226,13 @@ def main(argv=None):
             st = wait[m] / wcyc[m] if m in wait and wcyc.get(m) else float("nan")
             vw = valu[m] / waves[m] if m in valu and waves.get(m) else float("nan")
             mw = vmem[m] / waves[m] if m in vmem and waves.get(m) else float("nan")
+            gui = v_gui.get(m, float("nan")) / 8
+            vb = 100 * v_act.get(m, float("nan")) / 256 / gui if gui else float("nan")
+            mu = 100 * v_mfma.get(m, float("nan")) / (gui * 1024) if gui else float("nan")
+            cpi = 4 * v_wcyc[m] / v_insts[m] if v_insts.get(m) and m in v_wcyc else float("nan")
             lines.append(f"| {MODE_NAMES[m]} | {rb:.4g} | {rb / kv:.4f} | {wb:.4g} | "
-                         f"{100 * hr:.2f} % | {100 * st:.1f} % | {vw:.0f} | {mw:.0f} |")
+                         f"{100 * hr:.2f} % | {100 * st:.1f} % | {vw:.0f} | {mw:.0f} | "
+                         f"{vb:.1f} % | {mu:.1f} % | {cpi:.1f} |")
         with open(os.path.join(a.out_dir, f"pa_decode_{tag}_counters.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
         with open(os.path.join(a.out_dir, f"pa_decode_{tag}_traffic.txt"), "w") as f:
