@@ -13,7 +13,9 @@ measured in the same run, and the fp64 CPU oracle timed on the host cores
 (plus the parity of the GPU output against it).
 
 Inputs are synthetic (seeded N(0,1) Q/K/V, shuffled block tables) with the
-shapes of the workload; see paged_kv_cache_226_amd/inputs.py.  With
+shapes of the workload; see paged_kv_cache_226_amd/inputs.py.  The caches
+live in one pool with each (block, KV head)'s K and V slices side by side
+(--kv-layout separate: two pools, vLLM's layout).  With
 --kv-dtype fp8 the same draw is quantized to OCP E4M3 with per-tensor scales
 and the KV bytes count one byte per value.
 """
@@ -87,6 +89,9 @@ def parse():
                     help="untimed steps before the timed region (and at least 250 ms of them)")
     ap.add_argument("--workload", default="llama2_7b")
     ap.add_argument("--prefetch", type=int, default=-1, help="-1 = library default")
+    ap.add_argument("--kv-layout", choices=("separate", "adjacent"), default="adjacent",
+                    help="separate K and V pools (vLLM's layout), or one pool with each "
+                         "(block, head)'s K and V slices side by side")
     ap.add_argument("--kv-dtype", choices=("fp16", "fp8"), default="fp16",
                     help="KV cache element type (fp8 = OCP E4M3 with per-tensor scales)")
     ap.add_argument("--prefetch-distance", type=int, default=0,
@@ -245,6 +250,16 @@ def main():
     else:
         d["k_cache"] = torch.from_numpy(gen.pack_k(x.k_cache)).to(dev)
         d["v_cache"] = torch.from_numpy(x.v_cache).to(dev)
+    if args.kv_layout == "adjacent":
+        # one pool [block][head][K slice | V slice]; K and V are strided views
+        kc, vc = d["k_cache"], d["v_cache"]
+        NBp, Hp = kc.shape[:2]
+        pool = torch.empty((NBp, Hp, 2, kc[0, 0].numel()), dtype=kc.dtype, device=dev)
+        pool[:, :, 0] = kc.reshape(NBp, Hp, -1)
+        pool[:, :, 1] = vc.reshape(NBp, Hp, -1)
+        d["k_cache"] = pool[:, :, 0].view(kc.shape)
+        d["v_cache"] = pool[:, :, 1].view(vc.shape)
+        del kc, vc
     out = torch.empty_like(d["q"])
     Hkv = x.k_cache.shape[1]
     kv_bytes = acc.step_kv_bytes(Hkv, 128, x.context_lens, elem_bytes=1 if fp8 else 2)
@@ -382,6 +397,7 @@ def main():
         "accumulate": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "kv_dtype": "e4m3" if fp8 else "f16",
+                   "kv_layout": args.kv_layout,
                    "batch": w.num_seqs, "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "head_dim": 128, "block_size": 16,
                    "context_sum": int(np.maximum(x.context_lens, 0).sum()),

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 #define PA_HEAD_DIM 128
 #define PA_BLOCK_SIZE 16
 #define PA_G_MAX 16      /* query heads per KV head */
@@ -132,6 +132,21 @@ typedef struct pa_shape {
     int32_t block_size;         /* must be 16 */
     int32_t max_blocks_per_seq; /* row stride of block_tables, >= 1 */
     int64_t num_blocks;         /* pool size, >= 1 */
+    /* Byte strides of the caches, 0 = the dense layout below.  Each (block,
+       KV head) slice (4 KiB fp16, 2 KiB E4M3) must itself be laid out as
+       documented; these only say where the slices are:
+           K slice (p, h) at k_cache + p * k_block_stride + h * k_head_stride
+           V slice (p, h) at v_cache + p * v_block_stride + h * v_head_stride
+       Dense: head stride = slice bytes, block stride = num_kv_heads * that.
+       Strides must be multiples of 16, head strides >= the slice bytes and
+       block strides >= num_kv_heads * head stride (slices never overlap).
+       One pool with K and V side by side per (block, head), for example,
+       is k_head_stride = v_head_stride = 2 * slice, block strides
+       num_kv_heads * 2 * slice and v_cache = k_cache + slice. */
+    int64_t k_block_stride;
+    int64_t k_head_stride;
+    int64_t v_block_stride;
+    int64_t v_head_stride;
 } pa_shape;
 
 typedef struct pa_options {

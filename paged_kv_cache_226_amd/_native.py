@@ -27,7 +27,9 @@ class PaShape(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
-                ("num_blocks", ctypes.c_int64)]
+                ("num_blocks", ctypes.c_int64),
+                ("k_block_stride", ctypes.c_int64), ("k_head_stride", ctypes.c_int64),
+                ("v_block_stride", ctypes.c_int64), ("v_head_stride", ctypes.c_int64)]
 
 
 class PaOptions(ctypes.Structure):
@@ -100,9 +102,13 @@ def default_options() -> PaOptions:
 
 
 def make_shape(num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, num_blocks,
-               head_dim=128, block_size=16) -> PaShape:
+               head_dim=128, block_size=16, k_block_stride=0, k_head_stride=0,
+               v_block_stride=0, v_head_stride=0) -> PaShape:
+    """pa_shape; the strides are in bytes, 0 = the dense layout."""
     return PaShape(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim),
-                   int(block_size), int(max_blocks_per_seq), int(num_blocks))
+                   int(block_size), int(max_blocks_per_seq), int(num_blocks),
+                   int(k_block_stride), int(k_head_stride), int(v_block_stride),
+                   int(v_head_stride))
 
 
 def plan(shape: PaShape, opts: PaOptions = None) -> dict:

@@ -57,6 +57,12 @@ int check_shape(const pa_shape* sh) {
   if (sh->num_kv_heads > 65535 || sh->num_seqs > 65535) return PA_ERR_UNSUPPORTED;
   // Byte offsets of the pool and token counts must fit their types.
   if (sh->num_blocks > (INT64_MAX / 8192) / sh->num_kv_heads) return PA_ERR_UNSUPPORTED;
+  const int64_t strides[4] = {sh->k_block_stride, sh->k_head_stride, sh->v_block_stride,
+                              sh->v_head_stride};
+  for (int64_t st : strides) {
+    if (st < 0 || (st & 15)) return PA_ERR_INVALID_ARG;
+    if (st > 0 && st > INT64_MAX / 4 / sh->num_blocks) return PA_ERR_UNSUPPORTED;
+  }
   if (sh->max_blocks_per_seq > INT32_MAX / PA_BLOCK_SIZE) return PA_ERR_UNSUPPORTED;
   return PA_OK;
 }
@@ -196,6 +202,15 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   Plan pl;
   int rc = make_plan(sh, o, &pl);
   if (rc) return rc;
+  // cache strides: 0 = dense; slices may be spread out but never overlap
+  const int64_t slice = (int64_t)PA_BLOCK_SIZE * PA_HEAD_DIM * (kv8 ? 1 : 2);
+  const int64_t k_head = sh->k_head_stride ? sh->k_head_stride : slice;
+  const int64_t v_head = sh->v_head_stride ? sh->v_head_stride : slice;
+  const int64_t k_blk = sh->k_block_stride ? sh->k_block_stride : k_head * sh->num_kv_heads;
+  const int64_t v_blk = sh->v_block_stride ? sh->v_block_stride : v_head * sh->num_kv_heads;
+  if (k_head < slice || v_head < slice || k_blk < k_head * sh->num_kv_heads ||
+      v_blk < v_head * sh->num_kv_heads)
+    return PA_ERR_INVALID_ARG;
   pa_options d;
   paged_attn_default_options(&d);
   if (!o) o = &d;
@@ -233,7 +248,10 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.P = pl.P;
   a.PB = pl.PB;
   a.NB = sh->num_blocks;
-  a.blk_bytes = (int64_t)sh->num_kv_heads * PA_BLOCK_SIZE * PA_HEAD_DIM * (kv8 ? 1 : 2);
+  a.k_head = k_head;
+  a.v_head = v_head;
+  a.k_blk = k_blk;
+  a.v_blk = v_blk;
   a.lds_bt_bytes = pa::lds_bt_bytes_for(pl.PB);
   // Default distance 1, except the register look-ahead over an E4M3 cache:
   // its blocks are half the bytes, and two of them ahead (at 142 VGPRs, still

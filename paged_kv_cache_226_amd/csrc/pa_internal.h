@@ -29,7 +29,8 @@ struct DecodeArgs {
   int P;                 // partitions in the grid
   int PB;                // blocks per partition
   int64_t NB;            // pool blocks
-  int64_t blk_bytes;     // bytes from one physical block to the next (Hkv * 4096)
+  int64_t k_blk, v_blk;    // bytes from one physical block to the next, K and V
+  int64_t k_head, v_head;  // bytes from one KV head's slice to the next
   int lds_bt_bytes;      // LDS bytes reserved for the block-table slice
   int pf_dist;           // L2-touch distance in iterations of a wave, 1..63
   int sink_enable;

@@ -158,10 +158,8 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
   for (int t = 0; t < 8; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int kHeadBytes = KV8 ? kBlockHeadBytes / 2 : kBlockHeadBytes;
-  const unsigned char* kbase =
-      reinterpret_cast<const unsigned char*>(a.k) + (int64_t)kvh * kHeadBytes;
-  const unsigned char* vbase =
-      reinterpret_cast<const unsigned char*>(a.v) + (int64_t)kvh * kHeadBytes;
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k) + kvh * a.k_head;
+  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v) + kvh * a.v_head;
   const int k_off = (lg * kT + pic) * 16;      // the 16-byte piece of K row pic
   const int v_off = lane * (KV8 ? 8 : 16);     // token lg, dims 8c..8c+7
   typedef BlockBuf<KV8> Buf;
@@ -173,8 +171,8 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
   // Every load instruction reads 1 KiB (fp16) or 512 B / 1 KiB (FP8 V / K)
   // of contiguous memory.
   auto load_block = [&](Buf& buf, int64_t ph) {
-    const unsigned char* kb = kbase + ph * a.blk_bytes + k_off;
-    const unsigned char* vb = vbase + ph * a.blk_bytes + v_off;
+    const unsigned char* kb = kbase + ph * a.k_blk + k_off;
+    const unsigned char* vb = vbase + ph * a.v_blk + v_off;
     if constexpr (KV8) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -196,7 +194,7 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
   // (32 fp16 / 16 FP8), lanes 32-63 those of the V block.
   auto touch_block = [&](int64_t ph) -> uint32_t {
     constexpr int kLines = kHeadBytes / 128;
-    const unsigned char* base = (lane < 32 ? kbase : vbase) + ph * a.blk_bytes;
+    const unsigned char* base = lane < 32 ? kbase + ph * a.k_blk : vbase + ph * a.v_blk;
     return *reinterpret_cast<const uint32_t*>(base + (lane & (kLines - 1)) * 128);
   };
 
@@ -477,25 +475,23 @@ __device__ __forceinline__ void walk_two_loop(const DecodeArgs& a, const int b, 
   }
   __syncthreads();
 
-  const unsigned char* kbase =
-      reinterpret_cast<const unsigned char*>(a.k) + (int64_t)kvh * kBlockHeadBytes;
-  const unsigned char* vbase =
-      reinterpret_cast<const unsigned char*>(a.v) + (int64_t)kvh * kBlockHeadBytes;
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k) + kvh * a.k_head;
+  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v) + kvh * a.v_head;
   const int k_off = (lg * kT + pic) * 16;
   const int v_off = lane * 16;
   const int j0 = s + wave;
   const int n_it = j0 < e ? (e - j0 + W - 1) / W : 0;
   // table entry of iteration it (the range's slice is in LDS)
   auto phys_it = [&](int it) -> int64_t { return (int64_t)bt_s[wave + it * W]; };
-  auto load4 = [&](u32x4* r, const unsigned char* base, int64_t ph, int off) {
-    const unsigned char* p = base + ph * a.blk_bytes + off;
+  auto load4 = [&](u32x4* r, const unsigned char* base, int64_t blk, int64_t ph, int off) {
+    const unsigned char* p = base + ph * blk + off;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       r[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 1024 * i));
   };
   // one dword of each 128 B line of a 4 KiB K or V block
-  auto touch = [&](const unsigned char* base, int64_t ph) -> uint32_t {
-    return *reinterpret_cast<const uint32_t*>(base + ph * a.blk_bytes + (lane & 31) * 128);
+  auto touch = [&](const unsigned char* base, int64_t blk, int64_t ph) -> uint32_t {
+    return *reinterpret_cast<const uint32_t*>(base + ph * blk + (lane & 31) * 128);
   };
   uint32_t sink = 0;
 
@@ -521,23 +517,23 @@ __device__ __forceinline__ void walk_two_loop(const DecodeArgs& a, const int b, 
   };
   if constexpr (PF >= 2) {
     u32x4 ka[4], kb[4];
-    if (n_it > 0) load4(ka, kbase, phys_it(0), k_off);
+    if (n_it > 0) load4(ka, kbase, a.k_blk, phys_it(0), k_off);
     int it = 0;
     for (; it + 2 < n_it; it += 2) {
       __builtin_amdgcn_sched_barrier(0);
-      load4(kb, kbase, phys_it(it + 1), k_off);
-      if (PF == 3 && it + 2 < n_it) sink ^= touch(kbase, phys_it(it + 2));
+      load4(kb, kbase, a.k_blk, phys_it(it + 1), k_off);
+      if (PF == 3 && it + 2 < n_it) sink ^= touch(kbase, a.k_blk, phys_it(it + 2));
       __builtin_amdgcn_sched_barrier(0);
       scores(ka, j0 + it * W);
       __builtin_amdgcn_sched_barrier(0);
-      load4(ka, kbase, phys_it(it + 2), k_off);
-      if (PF == 3 && it + 3 < n_it) sink ^= touch(kbase, phys_it(it + 3));
+      load4(ka, kbase, a.k_blk, phys_it(it + 2), k_off);
+      if (PF == 3 && it + 3 < n_it) sink ^= touch(kbase, a.k_blk, phys_it(it + 3));
       __builtin_amdgcn_sched_barrier(0);
       scores(kb, j0 + (it + 1) * W);
       __builtin_amdgcn_sched_barrier(0);
     }
     for (; it < n_it; ++it) {
-      if (it + 1 < n_it) load4(kb, kbase, phys_it(it + 1), k_off);
+      if (it + 1 < n_it) load4(kb, kbase, a.k_blk, phys_it(it + 1), k_off);
       scores(ka, j0 + it * W);
 #pragma unroll
       for (int i = 0; i < 4; ++i) ka[i] = kb[i];
@@ -546,8 +542,8 @@ __device__ __forceinline__ void walk_two_loop(const DecodeArgs& a, const int b, 
     for (int it = 0; it < n_it; ++it) {
       u32x4 kh[4];
       __builtin_amdgcn_sched_barrier(0);
-      load4(kh, kbase, phys_it(it), k_off);
-      if (PF == 1 && it + 1 < n_it) sink ^= touch(kbase, phys_it(it + 1));
+      load4(kh, kbase, a.k_blk, phys_it(it), k_off);
+      if (PF == 1 && it + 1 < n_it) sink ^= touch(kbase, a.k_blk, phys_it(it + 1));
       __builtin_amdgcn_sched_barrier(0);
       scores(kh, j0 + it * W);
     }
@@ -594,23 +590,23 @@ __device__ __forceinline__ void walk_two_loop(const DecodeArgs& a, const int b, 
   };
   if constexpr (PF >= 2) {
     u32x4 va[4], vb[4];
-    if (n_it > 0) load4(va, vbase, phys_it(0), v_off);
+    if (n_it > 0) load4(va, vbase, a.v_blk, phys_it(0), v_off);
     int it = 0;
     for (; it + 2 < n_it; it += 2) {
       __builtin_amdgcn_sched_barrier(0);
-      load4(vb, vbase, phys_it(it + 1), v_off);
-      if (PF == 3 && it + 2 < n_it) sink ^= touch(vbase, phys_it(it + 2));
+      load4(vb, vbase, a.v_blk, phys_it(it + 1), v_off);
+      if (PF == 3 && it + 2 < n_it) sink ^= touch(vbase, a.v_blk, phys_it(it + 2));
       __builtin_amdgcn_sched_barrier(0);
       weigh(va, j0 + it * W);
       __builtin_amdgcn_sched_barrier(0);
-      load4(va, vbase, phys_it(it + 2), v_off);
-      if (PF == 3 && it + 3 < n_it) sink ^= touch(vbase, phys_it(it + 3));
+      load4(va, vbase, a.v_blk, phys_it(it + 2), v_off);
+      if (PF == 3 && it + 3 < n_it) sink ^= touch(vbase, a.v_blk, phys_it(it + 3));
       __builtin_amdgcn_sched_barrier(0);
       weigh(vb, j0 + (it + 1) * W);
       __builtin_amdgcn_sched_barrier(0);
     }
     for (; it < n_it; ++it) {
-      if (it + 1 < n_it) load4(vb, vbase, phys_it(it + 1), v_off);
+      if (it + 1 < n_it) load4(vb, vbase, a.v_blk, phys_it(it + 1), v_off);
       weigh(va, j0 + it * W);
 #pragma unroll
       for (int i = 0; i < 4; ++i) va[i] = vb[i];
@@ -619,8 +615,8 @@ __device__ __forceinline__ void walk_two_loop(const DecodeArgs& a, const int b, 
     for (int it = 0; it < n_it; ++it) {
       u32x4 vh[4];
       __builtin_amdgcn_sched_barrier(0);
-      load4(vh, vbase, phys_it(it), v_off);
-      if (PF == 1 && it + 1 < n_it) sink ^= touch(vbase, phys_it(it + 1));
+      load4(vh, vbase, a.v_blk, phys_it(it), v_off);
+      if (PF == 1 && it + 1 < n_it) sink ^= touch(vbase, a.v_blk, phys_it(it + 1));
       __builtin_amdgcn_sched_barrier(0);
       weigh(vh, j0 + it * W);
     }

@@ -31,10 +31,29 @@ def _check(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int):
         raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
 
 
-def shape_of(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor) -> nat.PaShape:
+def _slice_contiguous(t: torch.Tensor) -> bool:
+    """Dims 2.. (one (block, head) slice) contiguous; dims 0-1 may be strided."""
+    expect = 1
+    for d in range(t.dim() - 1, 1, -1):
+        if t.shape[d] != 1 and t.stride(d) != expect:
+            return False
+        expect *= t.shape[d]
+    return True
+
+
+def shape_of(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,
+             v_cache: Optional[torch.Tensor] = None) -> nat.PaShape:
+    """pa_shape of these tensors; K and V may be views into a larger pool
+    (their strides over blocks and heads are passed on in bytes)."""
     B, Hq, D = q.shape
     NB, Hkv, G8, T, X = k_cache.shape
-    return nat.make_shape(B, Hq, Hkv, block_tables.shape[1], NB, head_dim=G8 * X, block_size=T)
+    ek = k_cache.element_size()
+    kw = dict(k_block_stride=k_cache.stride(0) * ek, k_head_stride=k_cache.stride(1) * ek)
+    if v_cache is not None:
+        ev = v_cache.element_size()
+        kw.update(v_block_stride=v_cache.stride(0) * ev, v_head_stride=v_cache.stride(1) * ev)
+    return nat.make_shape(B, Hq, Hkv, block_tables.shape[1], NB, head_dim=G8 * X, block_size=T,
+                          **kw)
 
 
 def options(prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0,
@@ -80,9 +99,20 @@ def workspace_bytes(q, k_cache, block_tables, **kw) -> int:
 
 
 def _check_kv(t: torch.Tensor, name: str, fp8: bool, ndim: int):
+    """A cache: the right dtype and rank, each (block, head) slice contiguous
+    (the pool itself may be a strided view)."""
     if fp8 and isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
         t = t.view(torch.uint8)
-    _check(t, name, torch.uint8 if fp8 else torch.float16, ndim)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    want = torch.uint8 if fp8 else torch.float16
+    if t.dtype != want:
+        raise TypeError(f"{name} must be {want}, got {t.dtype}")
+    if t.dim() != ndim or not _slice_contiguous(t):
+        raise ValueError(f"{name} must be a {ndim}-d tensor whose (block, head) slices are "
+                         "contiguous")
 
 
 def _decode(fp8: bool, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
@@ -110,7 +140,7 @@ def _decode(fp8: bool, q, k_cache, v_cache, block_tables, context_lens, scale, k
         _check(out, "out", torch.float16, 3)
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
-    sh = shape_of(q, k_cache, block_tables)
+    sh = shape_of(q, k_cache, block_tables, v_cache)
     o = options(prefetch, partition_blocks, waves_per_wg, prefetch_distance, seq_order,
                 structure, debug_gather_k, debug_trace, debug_error_word)
     need = int(nat.lib().paged_attn_workspace_size(ctypes.byref(sh), ctypes.byref(o)))

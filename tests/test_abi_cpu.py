@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function(native_lib):
 
 
 def test_version_and_error_strings(native_lib):
-    assert native_lib.paged_attn_abi_version() == 2
+    assert native_lib.paged_attn_abi_version() == 3
     assert nat.error_string(0) == "ok"
     for code in range(1, 5):
         assert nat.error_string(code) not in ("ok", "unknown status")
@@ -96,6 +96,11 @@ def good_shape(**kw):
     (dict(shape=dict(num_seqs=0)), nat.PA_ERR_INVALID_ARG),
     (dict(shape=dict(num_q_heads=6, num_kv_heads=4)), nat.PA_ERR_INVALID_ARG),
     (dict(shape=dict(num_blocks=0)), nat.PA_ERR_INVALID_ARG),
+    (dict(shape=dict(k_head_stride=4104)), nat.PA_ERR_INVALID_ARG),
+    (dict(shape=dict(v_block_stride=-16)), nat.PA_ERR_INVALID_ARG),
+    (dict(shape=dict(k_head_stride=2048)), nat.PA_ERR_INVALID_ARG),
+    (dict(shape=dict(v_head_stride=8192, v_block_stride=8192)), nat.PA_ERR_INVALID_ARG),
+    (dict(shape=dict(k_block_stride=1 << 60)), nat.PA_ERR_UNSUPPORTED),
     (dict(shape=dict(head_dim=64)), nat.PA_ERR_UNSUPPORTED),
     (dict(shape=dict(block_size=32)), nat.PA_ERR_UNSUPPORTED),
     (dict(shape=dict(num_q_heads=34, num_kv_heads=2)), nat.PA_ERR_UNSUPPORTED),

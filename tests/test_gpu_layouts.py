@@ -1,0 +1,99 @@
+"""Cache layouts given by strides (MI355X): K and V side by side in one pool,
+a [block][K|V][head] pool, and padded slices, all bitwise equal to the dense
+layout and to the oracle within tolerance."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from paged_kv_cache_226_amd import inputs as gen
+from paged_kv_cache_226_amd import ops
+
+from parity import assert_close, bits, oracle, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu(native_lib):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def place(kp: np.ndarray, v: np.ndarray, layout: str, fp8: bool):
+    """Device views (k, v) of packed K and token-major V in the given layout;
+    every byte outside the slices is NaN (0x7F for E4M3)."""
+    NB, H = kp.shape[:2]
+    n = kp[0, 0].size  # values per slice
+    dt = torch.uint8 if fp8 else torch.float16
+    fill = gen.FP8_NAN_BYTE if fp8 else float("nan")
+    kt = torch.from_numpy(np.ascontiguousarray(kp).reshape(NB, H, n)).cuda()
+    vt = torch.from_numpy(np.ascontiguousarray(v).reshape(NB, H, n)).cuda()
+    if layout == "adjacent":
+        pool = torch.full((NB, H, 2, n), fill, dtype=dt, device="cuda")
+        pool[:, :, 0] = kt
+        pool[:, :, 1] = vt
+        k, vv = pool[:, :, 0], pool[:, :, 1]
+    elif layout == "kv_major":
+        pool = torch.full((NB, 2, H, n), fill, dtype=dt, device="cuda")
+        pool[:, 0] = kt
+        pool[:, 1] = vt
+        k, vv = pool[:, 0], pool[:, 1]
+    elif layout == "padded":
+        pk = torch.full((NB, H, n + 128), fill, dtype=dt, device="cuda")
+        pv = torch.full((NB + 1, H + 1, n + 64), fill, dtype=dt, device="cuda")
+        pk[:, :, :n] = kt
+        pv[1:, 1:, :n] = vt
+        k, vv = pk[:, :, :n], pv[1:, 1:, :n]
+    else:
+        raise ValueError(layout)
+    return k.view(*kp.shape), vv.view(*v.shape)
+
+
+@pytest.mark.parametrize("layout", ["adjacent", "kv_major", "padded"])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_strided_layouts_give_the_dense_bits(layout, fp8):
+    x = gen.make_case(4, 16, 4, [700, 33, 2100, 1], seed=600, extra_pool_blocks=5)
+    dense = to_device(x)
+    if fp8:
+        x8 = gen.to_fp8(x)
+        kp, v = gen.pack_k_fp8(x8.k8), x8.v8
+        dense["k_cache"] = torch.from_numpy(kp).cuda()
+        dense["v_cache"] = torch.from_numpy(v).cuda()
+        ref = orc.paged_attention_fp8_f64(x8.q, x8.k8, x8.v8, x8.block_tables, x8.context_lens,
+                                          x8.scale, x8.k_scale, x8.v_scale)
+    else:
+        kp, v = gen.pack_k(x.k_cache), x.v_cache
+        ref = oracle(x)
+    k, vv = place(kp, v, layout, fp8)
+    assert not k.is_contiguous() or not vv.is_contiguous()
+
+    def call(kc, vc, **kw):
+        if fp8:
+            o = ops.paged_attn_decode_fp8(dense["q"], kc, vc, dense["block_tables"],
+                                          dense["context_lens"], x.scale, x8.k_scale,
+                                          x8.v_scale, **kw)
+        else:
+            o = ops.paged_attn_decode(dense["q"], kc, vc, dense["block_tables"],
+                                      dense["context_lens"], x.scale, **kw)
+        torch.cuda.synchronize()
+        return o.cpu().numpy()
+
+    for kw in (dict(), dict(prefetch=0), dict(prefetch=1), dict(prefetch=3),
+               dict(prefetch=2, prefetch_distance=2), dict(partition_blocks=8, waves_per_wg=2)):
+        want = call(dense["k_cache"], dense["v_cache"], **kw)
+        got = call(k, vv, **kw)
+        assert np.array_equal(bits(got), bits(want)), (layout, kw)
+        assert_close(got, ref, f"{layout} fp8={fp8} {kw}")
+    if not fp8:
+        got = call(k, vv, structure=1)
+        assert np.array_equal(bits(got), bits(call(dense["k_cache"], dense["v_cache"],
+                                                   structure=1)))
+
+
+def test_a_slice_that_is_not_contiguous_is_rejected():
+    x = gen.make_case(2, 4, 2, [40, 17], seed=601)
+    d = to_device(x)
+    k_t = d["k_cache"].transpose(2, 3)  # token and dim-group axes swapped
+    with pytest.raises(ValueError, match="slices"):
+        ops.paged_attn_decode(d["q"], k_t, d["v_cache"], d["block_tables"], d["context_lens"])
