@@ -81,7 +81,10 @@ extern "C" {
 enum pa_status {
     PA_OK = 0,
     PA_ERR_INVALID_ARG = 1, /* null pointer, bad count, misaligned pointer */
-    PA_ERR_UNSUPPORTED = 2, /* head_dim != 128, block_size != 16, g > PA_G_MAX */
+    PA_ERR_UNSUPPORTED = 2, /* head_dim != 128, block_size != 16, g > PA_G_MAX,
+                               an option outside its range, or a plan whose
+                               work-group needs more than the 160 KiB of LDS
+                               a gfx950 work-group can hold */
     PA_ERR_WORKSPACE = 3,   /* plan needs a workspace that is missing or too small */
     PA_ERR_HIP = 4          /* a kernel launch failed (hipGetLastError) */
 };
@@ -93,8 +96,12 @@ enum pa_prefetch {
                              brought into L2 / Infinity Cache; data discarded */
     PA_PREFETCH_REG = 2,  /* load block j + k*w into registers (k = 1 or 2
                              buffers ahead) */
-    PA_PREFETCH_BOTH = 3  /* REG for block j + w, plus an L2 touch of
+    PA_PREFETCH_BOTH = 3, /* REG for block j + w, plus an L2 touch of
                              block j + (1 + k)*w */
+    PA_PREFETCH_LDS = 4   /* block j + w copied straight from HBM into an
+                             LDS slot of the wavefront (no registers), read
+                             out when its turn comes; distance 1 only, fused
+                             structure only */
 };
 
 /* Which sequence each row of the launch grid takes.  Work-groups start in

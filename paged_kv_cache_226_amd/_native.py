@@ -15,8 +15,8 @@ PA_ERR_UNSUPPORTED = 2
 PA_ERR_WORKSPACE = 3
 PA_ERR_HIP = 4
 
-PREFETCH_OFF, PREFETCH_L2, PREFETCH_REG, PREFETCH_BOTH = 0, 1, 2, 3
-PREFETCH_NAMES = {0: "off", 1: "l2", 2: "reg", 3: "both"}
+PREFETCH_OFF, PREFETCH_L2, PREFETCH_REG, PREFETCH_BOTH, PREFETCH_LDS = 0, 1, 2, 3, 4
+PREFETCH_NAMES = {0: "off", 1: "l2", 2: "reg", 3: "both", 4: "lds"}
 ORDER_AUTO, ORDER_NATURAL, ORDER_LONGEST_FIRST = 0, 1, 2
 ORDER_NAMES = {1: "natural", 2: "longest_first"}
 RANK_MAX_SEQS = 256

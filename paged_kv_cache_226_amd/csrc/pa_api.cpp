@@ -13,7 +13,7 @@ namespace {
 
 constexpr int kDefaultPrefetch = PA_PREFETCH_REG;
 constexpr int kMaxPartitionBlocks = 1024;  // LDS slice of the block table: 4 KiB
-constexpr size_t kMaxLdsBytes = 65536;     // dynamic LDS per work-group
+constexpr size_t kMaxLdsBytes = 163840;    // LDS one gfx950 work-group can hold
 // Auto plan, from measurements over the model shapes, their tensor-parallel
 // shards and a batch x context grid (U = sequences x KV heads):
 //  * U >= kOnePartitionUnits (one work-group per CU on 256 CUs): no split, so
@@ -88,9 +88,12 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   const int g = sh->num_q_heads / sh->num_kv_heads;
 
   int pf = o->prefetch < 0 ? kDefaultPrefetch : o->prefetch;
-  if (pf > PA_PREFETCH_BOTH) return PA_ERR_INVALID_ARG;
-  // registers hold at most two blocks ahead
+  if (pf > PA_PREFETCH_LDS) return PA_ERR_INVALID_ARG;
+  // registers hold at most two blocks ahead, an LDS slot one
   if (pf == PA_PREFETCH_REG && o->prefetch_distance > 2) return PA_ERR_UNSUPPORTED;
+  if (pf == PA_PREFETCH_LDS && (o->prefetch_distance > 1 || two)) return PA_ERR_UNSUPPORTED;
+  // the LDS-staged look-ahead's per-wave slot (sized for fp16, the larger)
+  const size_t slot = pf == PA_PREFETCH_LDS ? 2 * PA_BLOCK_SIZE * PA_HEAD_DIM * 2 : 0;
 
   const int B = sh->num_seqs, Hkv = sh->num_kv_heads;
   const int MB = sh->max_blocks_per_seq;
@@ -109,7 +112,7 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
                                                 : o->partition_blocks >= MB;
     waves = 4;
     if (whole && units < kFourWaveUnits && MB >= kLongTableBlocks && MB <= kMaxPartitionBlocks &&
-        pa::decode_lds_bytes(MB, g, 8, B, rank) <= kMaxLdsBytes)
+        pa::decode_lds_bytes(MB, g, 8, B, rank, 8 * slot) <= kMaxLdsBytes)
       waves = 8;
   }
 
@@ -134,7 +137,7 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   const int P = (MB + PB - 1) / PB;
   if (P > 65535) return PA_ERR_UNSUPPORTED;  // grid.z
   const size_t lds = two ? pa::two_loop_lds_bytes(PB, g, waves, B, rank)
-                         : pa::decode_lds_bytes(PB, g, waves, B, rank);
+                         : pa::decode_lds_bytes(PB, g, waves, B, rank, waves * slot);
   if (lds > kMaxLdsBytes) return PA_ERR_UNSUPPORTED;
   memset(pl, 0, sizeof(*pl));
   pl->order = order;
@@ -271,8 +274,11 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   if (pl.two) {
     if (pa::launch_decode_two_loop(a, pl.pf, pl.waves, st) != hipSuccess) return PA_ERR_HIP;
   } else {
-    // the register look-ahead at distance 2 is its own kernel instance
-    const int variant = pl.pf == PA_PREFETCH_REG && a.pf_dist == 2 ? 4 : pl.pf;
+    // the register look-ahead at distance 2 and the LDS-staged look-ahead
+    // are kernel instances 4 and 5
+    const int variant = pl.pf == PA_PREFETCH_LDS                     ? 5
+                        : pl.pf == PA_PREFETCH_REG && a.pf_dist == 2 ? 4
+                                                                      : pl.pf;
     if (pa::launch_decode(a, variant, dbg, kv8, pl.waves, st) != hipSuccess) return PA_ERR_HIP;
   }
   if (pl.P > 1 && pa::launch_reduce(a, st) != hipSuccess) return PA_ERR_HIP;

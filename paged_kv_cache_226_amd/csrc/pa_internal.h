@@ -44,8 +44,11 @@ inline int lds_bt_bytes_for(int PB) { return ((PB * 4) + 15) / 16 * 16; }
 // merge area, which are written only after the ranking is done.
 inline size_t rank_lds_bytes(int B) { return (size_t)((B + 3) / 4 * 4) * 4 + 16; }
 
-inline size_t decode_lds_bytes(int PB, int g, int waves, int B, bool rank) {
-  const size_t main = (size_t)lds_bt_bytes_for(PB) + (size_t)waves * g * (128 + 2) * 4;
+// `slots`: the LDS-staged look-ahead's per-wave slots, which overlay the
+// merge records (they are free by the time the records are written).
+inline size_t decode_lds_bytes(int PB, int g, int waves, int B, bool rank, size_t slots = 0) {
+  const size_t rec = (size_t)waves * g * (128 + 2) * 4;
+  const size_t main = (size_t)lds_bt_bytes_for(PB) + (rec > slots ? rec : slots);
   const size_t r = rank ? rank_lds_bytes(B) : 0;
   return main > r ? main : r;
 }

@@ -97,6 +97,12 @@ __device__ __forceinline__ u32x4 widen_fp8x8(uint32_t w0, uint32_t w1) {
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true))};
 }
 
+// Pointers of the direct global-to-LDS copy; its cache policy is
+// non-temporal, like the direct loads.
+typedef __attribute__((address_space(1))) const void gbyte;
+typedef __attribute__((address_space(3))) void lbyte;
+constexpr int kCachePolicyNT = 2;
+
 // Compile-time flags for the block compute: may the block be a sequence's
 // partial last block?
 template <bool V>
@@ -358,6 +364,76 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
       compute(buf, j, kMayTail);
     }
     sink ^= pend;
+  } else if constexpr (PF == 5) {
+    // LDS staging: block j+W is copied by the direct global-to-LDS path
+    // (global_load_lds_dwordx4, no registers involved) into this wave's LDS
+    // slot while block j, already read out into registers, is computed.  The
+    // copy keeps the slice's byte order (1 KiB contiguous per instruction);
+    // the read-back takes the same per-lane pieces as the direct loads.
+    // Holding the look-ahead block in LDS instead of registers frees about
+    // 32 VGPRs per lane.
+    constexpr int kSlot = 2 * kHeadBytes;
+    unsigned char* slot = reinterpret_cast<unsigned char*>(merge_s) + wave * kSlot;
+    auto dma_block = [&](int64_t ph) {
+      const unsigned char* ks = kbase + ph * a.k_blk + lane * 16;
+      const unsigned char* vs = vbase + ph * a.v_blk + lane * 16;
+#pragma unroll
+      for (int q = 0; q < kHeadBytes / 1024; ++q) {
+        __builtin_amdgcn_global_load_lds((gbyte*)(ks + 1024 * q),
+                                         (lbyte*)(slot + 1024 * q), 16, 0,
+                                         kCachePolicyNT);
+        __builtin_amdgcn_global_load_lds((gbyte*)(vs + 1024 * q),
+                                         (lbyte*)(slot + kHeadBytes + 1024 * q),
+                                         16, 0, kCachePolicyNT);
+      }
+    };
+    auto read_block = [&](Buf& buf) {
+      const unsigned char* kb = slot + k_off;
+      const unsigned char* vb = slot + kHeadBytes + v_off;
+      if constexpr (KV8) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) buf.k[i] = *reinterpret_cast<const u32x4*>(kb + 1024 * i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) buf.v[i] = *reinterpret_cast<const u32x2*>(vb + 512 * i);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) buf.k[i] = *reinterpret_cast<const u32x4*>(kb + 1024 * i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) buf.v[i] = *reinterpret_cast<const u32x4*>(vb + 1024 * i);
+      }
+    };
+    // Wait for the copy of block `it`, read it out, wait for the reads (the
+    // slot is then free), start the copy of block it+1.  The waits are
+    // explicit: the copy is a memory write the compiler does not track.
+    auto stage = [&](Buf& buf, int it) {
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      read_block(buf);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (n_it > 0) dma_block(phys_it(0));
+    int it = 0;
+    for (; it + 1 < n_it; ++it) {
+      const int j = j0 + it * W;
+      Buf buf;
+      stage(buf, it);
+      dma_block(phys_it(it + 1));
+      trace_put(j + W, 1, wave);
+      __builtin_amdgcn_sched_barrier(0);
+      trace_put(j, 0, (wave << 16) | it);
+      compute(buf, j, kNoTail);
+      advance(it);
+    }
+    if (it < n_it) {  // this wave's last block: nothing left to copy ahead
+      const int j = j0 + it * W;
+      Buf buf;
+      stage(buf, it);
+      trace_put(j, 0, (wave << 16) | it);
+      compute(buf, j, kMayTail);
+    }
+    // the merge records below overlay the slots of other waves
+    __syncthreads();
   } else {
     // Register look-ahead of depth D: block j + D*W is fetched into a ring of
     // D+1 buffers while block j is computed.  The steady loop is unrolled
@@ -836,23 +912,27 @@ static hipError_t launch_decode_t(const DecodeArgs& a, dim3 grid, dim3 block, si
 hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int waves,
                          hipStream_t st) {
   typedef hipError_t (*fn_t)(const DecodeArgs&, dim3, dim3, size_t, hipStream_t);
-  // pf 0..3 are the look-ahead modes; 4 is the register look-ahead of depth 2
-  static const fn_t table[20] = {
+  // pf 0..3 are the look-ahead modes; 4 is the register look-ahead of depth
+  // 2, 5 the LDS-staged look-ahead
+  static const fn_t table[24] = {
       launch_decode_t<0, false, false>, launch_decode_t<0, true, false>,
       launch_decode_t<1, false, false>, launch_decode_t<1, true, false>,
       launch_decode_t<2, false, false>, launch_decode_t<2, true, false>,
       launch_decode_t<3, false, false>, launch_decode_t<3, true, false>,
       launch_decode_t<4, false, false>, launch_decode_t<4, true, false>,
+      launch_decode_t<5, false, false>, launch_decode_t<5, true, false>,
       launch_decode_t<0, false, true>,  launch_decode_t<0, true, true>,
       launch_decode_t<1, false, true>,  launch_decode_t<1, true, true>,
       launch_decode_t<2, false, true>,  launch_decode_t<2, true, true>,
       launch_decode_t<3, false, true>,  launch_decode_t<3, true, true>,
-      launch_decode_t<4, false, true>,  launch_decode_t<4, true, true>};
-  if (pf < 0 || pf > 4) return hipErrorInvalidValue;
+      launch_decode_t<4, false, true>,  launch_decode_t<4, true, true>,
+      launch_decode_t<5, false, true>,  launch_decode_t<5, true, true>};
+  if (pf < 0 || pf > 5) return hipErrorInvalidValue;
   const dim3 grid(a.Hkv, a.B, a.P);
   const dim3 block(kWave * waves);
-  return table[(kv8 ? 10 : 0) + pf * 2 + (dbg ? 1 : 0)](
-      a, grid, block, decode_lds_bytes(a.PB, a.G, waves, a.B, a.rank_seqs != 0), st);
+  const size_t slots = pf == 5 ? (size_t)waves * (kv8 ? 4096 : 8192) : 0;
+  return table[(kv8 ? 12 : 0) + pf * 2 + (dbg ? 1 : 0)](
+      a, grid, block, decode_lds_bytes(a.PB, a.G, waves, a.B, a.rank_seqs != 0, slots), st);
 }
 
 hipError_t launch_decode_two_loop(const DecodeArgs& a, int pf, int waves, hipStream_t st) {

@@ -104,7 +104,9 @@ def good_shape(**kw):
     (dict(shape=dict(head_dim=64)), nat.PA_ERR_UNSUPPORTED),
     (dict(shape=dict(block_size=32)), nat.PA_ERR_UNSUPPORTED),
     (dict(shape=dict(num_q_heads=34, num_kv_heads=2)), nat.PA_ERR_UNSUPPORTED),
-    (dict(opts=dict(prefetch=4)), nat.PA_ERR_INVALID_ARG),
+    (dict(opts=dict(prefetch=5)), nat.PA_ERR_INVALID_ARG),
+    (dict(opts=dict(prefetch=4, prefetch_distance=2)), nat.PA_ERR_UNSUPPORTED),
+    (dict(opts=dict(prefetch=4, structure=1)), nat.PA_ERR_UNSUPPORTED),
     (dict(opts=dict(waves_per_wg=3)), nat.PA_ERR_INVALID_ARG),
     (dict(opts=dict(prefetch_distance=64)), nat.PA_ERR_INVALID_ARG),
     (dict(opts=dict(prefetch_distance=-1)), nat.PA_ERR_INVALID_ARG),
@@ -116,9 +118,9 @@ def good_shape(**kw):
     (dict(opts=dict(structure=2)), nat.PA_ERR_INVALID_ARG),
     (dict(opts=dict(structure=1, prefetch_distance=2)), nat.PA_ERR_UNSUPPORTED),
     (dict(shape=dict(num_seqs=257), opts=dict(seq_order=2)), nat.PA_ERR_UNSUPPORTED),
-    # too much LDS: 8 waves x 16 heads of merge records
-    (dict(shape=dict(num_q_heads=32, num_kv_heads=2), opts=dict(waves_per_wg=8)),
-     nat.PA_ERR_UNSUPPORTED),
+    # too much LDS: the two-loop scores of 1024 blocks x 16 heads (1 MiB)
+    (dict(shape=dict(num_q_heads=32, num_kv_heads=2),
+          opts=dict(structure=1, partition_blocks=1024)), nat.PA_ERR_UNSUPPORTED),
     # 4096 blocks per sequence need several partitions: no workspace given
     (dict(), nat.PA_ERR_WORKSPACE),
     (dict(opts=dict(workspace=FAKE, workspace_bytes=16)), nat.PA_ERR_WORKSPACE),
@@ -193,7 +195,7 @@ def test_auto_plan_rule(native_lib, B, Hkv, MB, waves, P, PB):
     assert (p["waves_per_wg"], p["num_partitions"], p["partition_blocks"]) == (waves, P, PB)
 
 
-@pytest.mark.parametrize("g,PB", [(1, 32), (4, 32), (8, 32), (16, 16)])
+@pytest.mark.parametrize("g,PB", [(1, 32), (4, 32), (8, 32), (16, 32)])
 def test_two_loop_plan_keeps_the_scores_in_lds(native_lib, g, PB):
     o = nat.default_options()
     o.structure = nat.STRUCTURE_TWO_LOOP

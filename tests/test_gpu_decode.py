@@ -14,7 +14,7 @@ from parity import assert_close, bits, oracle, run, to_device
 
 pytestmark = pytest.mark.gpu
 
-MODES = [0, 1, 2, 3]
+MODES = [0, 1, 2, 3, 4]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -73,7 +73,7 @@ def test_waves_and_partitions(waves, pb):
     ref = oracle(x)
     dev = to_device(x)
     pb_eff = max(pb, 0)
-    for pf in (0, 3):
+    for pf in (0, 3, 4):
         o = run(x, dev, prefetch=pf, waves_per_wg=waves, partition_blocks=pb_eff)
         assert_close(o, ref, f"w={waves} pb={pb} pf={pf}")
 
@@ -105,7 +105,8 @@ def test_trace_follows_the_lookahead_schedule(pf, waves, pb, dist):
     Hkv = x.k_cache.shape[1]
     trace = torch.full((B, Hkv, MB, 2), -1, dtype=torch.int32, device="cuda")
     kw = dict(prefetch=pf, waves_per_wg=waves, partition_blocks=pb, prefetch_distance=dist)
-    if pf == 2 and dist > 2:  # registers hold at most two blocks ahead
+    # registers hold at most two blocks ahead, an LDS slot one
+    if (pf == 2 and dist > 2) or (pf == 4 and dist > 1):
         with pytest.raises(RuntimeError, match="unsupported"):
             run(x, dev, debug_trace=trace, **kw)
         return
@@ -120,8 +121,8 @@ def test_trace_follows_the_lookahead_schedule(pf, waves, pb, dist):
     seen = np.zeros((B, Hkv, MB), dtype=bool)
     for b, h, s, e in ranges:
         # slot 1 holds the L2 touch in mode 1 and the register fetch in mode
-        # 2 (distance dist), the register fetch of block j + W in mode 3
-        exp = sch.expected_trace(s, e, W, 1 if pf == 3 else dist)
+        # 2 (distance dist), the fetch of block j + W in modes 3 and 4
+        exp = sch.expected_trace(s, e, W, 1 if pf in (3, 4) else dist)
         for j in range(s, e):
             wave, it, fetcher = exp[j]
             assert tr[b, h, j, 0] == (wave << 16 | it), (b, h, j)

@@ -17,7 +17,7 @@ from parity import assert_close, bits
 
 pytestmark = pytest.mark.gpu
 
-MODES = [0, 1, 2, 3]
+MODES = [0, 1, 2, 3, 4]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -94,7 +94,7 @@ def test_fp8_waves_and_partitions(waves, pb):
     x8 = case8(3, 8, 2, [700, 33, 1], seed=220)
     ref = oracle8(x8)
     dev = to_device8(x8)
-    for pf in (0, 3):
+    for pf in (0, 3, 4):
         assert_close(run8(x8, dev, prefetch=pf, waves_per_wg=waves, partition_blocks=pb), ref,
                      f"fp8 w={waves} pb={pb} pf={pf}")
 
@@ -216,21 +216,31 @@ def test_fp8_workload_sampled_rows(name):
                                     dev["block_tables"], dev["context_lens"], x8.scale,
                                     x8.k_scale, x8.v_scale)
     torch.cuda.synchronize()
+    dec = lambda **kw: ops.paged_attn_decode_fp8(dev["q"], dev["k_cache"], dev["v_cache"],
+                                                 dev["block_tables"], dev["context_lens"],
+                                                 x8.scale, x8.k_scale, x8.v_scale, **kw)
     for pf, dist in ((0, 0), (1, 0), (3, 0), (2, 2)):
-        o2 = ops.paged_attn_decode_fp8(dev["q"], dev["k_cache"], dev["v_cache"],
-                                       dev["block_tables"], dev["context_lens"], x8.scale,
-                                       x8.k_scale, x8.v_scale, prefetch=pf,
-                                       prefetch_distance=dist)
+        o2 = dec(prefetch=pf, prefetch_distance=dist)
         torch.cuda.synchronize()
         assert torch.equal(o2.view(torch.int16), out.view(torch.int16)), f"mode {pf}"
-    got = out.cpu().numpy()
-    del dev, out
+    # the LDS-staged look-ahead may plan fewer waves; on the same plan it
+    # matches the register look-ahead bit for bit
+    lds_plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], prefetch=4)
+    same = dict(waves_per_wg=lds_plan["waves_per_wg"],
+                partition_blocks=lds_plan["partition_blocks"])
+    lds = dec(prefetch=4, **same)
+    reg = dec(prefetch=2, prefetch_distance=2, **same)
+    torch.cuda.synchronize()
+    assert torch.equal(lds.view(torch.int16), reg.view(torch.int16)), f"lds vs reg {same}"
+    got, got_lds = out.cpu().numpy(), lds.cpu().numpy()
+    del dev, out, lds, reg
     rows = sample_rows(x8, 48, seed=len(name) + 1)
     print(f"[fp8 workload] {name}: oracle on {len(rows)} rows", flush=True)
     ref = orc.paged_attention_fp8_rows_f64(x8.q, x8.k8, x8.v8, x8.block_tables,
                                            x8.context_lens, x8.scale, x8.k_scale, x8.v_scale,
                                            rows)
     e = assert_close(got[rows[:, 0], rows[:, 1]], ref, name)
+    assert_close(got_lds[rows[:, 0], rows[:, 1]], ref, name + " lds")
     print(f"[fp8 workload] {name}: {e}", flush=True)
 
 

@@ -80,7 +80,8 @@ def test_strided_layouts_give_the_dense_bits(layout, fp8):
         return o.cpu().numpy()
 
     for kw in (dict(), dict(prefetch=0), dict(prefetch=1), dict(prefetch=3),
-               dict(prefetch=2, prefetch_distance=2), dict(partition_blocks=8, waves_per_wg=2)):
+               dict(prefetch=2, prefetch_distance=2), dict(prefetch=4),
+               dict(partition_blocks=8, waves_per_wg=2)):
         want = call(dense["k_cache"], dense["v_cache"], **kw)
         got = call(k, vv, **kw)
         assert np.array_equal(bits(got), bits(want)), (layout, kw)

@@ -47,19 +47,30 @@ def test_workload_sampled_rows(name):
                                 dev["context_lens"], x.scale)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
+    dec = lambda **kw: ops.paged_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"],
+                                             dev["block_tables"], dev["context_lens"],
+                                             x.scale, **kw)
     for pf, dist in ((0, 0), (1, 0), (2, 0), (3, 0), (2, 2)):
-        o2 = ops.paged_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"],
-                                   dev["block_tables"], dev["context_lens"], x.scale,
-                                   prefetch=pf, prefetch_distance=dist)
+        o2 = dec(prefetch=pf, prefetch_distance=dist)
         torch.cuda.synchronize()
         assert torch.equal(o2.view(torch.int16), out.view(torch.int16)), f"mode {pf}"
-    got = out.cpu().numpy()
-    del dev, out
+    # the LDS-staged look-ahead may plan fewer waves (its slots share the
+    # work-group's LDS); with the same plan it matches the register look-ahead
+    lds_plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], prefetch=4)
+    same = dict(waves_per_wg=lds_plan["waves_per_wg"],
+                partition_blocks=lds_plan["partition_blocks"])
+    lds = dec(prefetch=4, **same)
+    reg = dec(prefetch=2, **same)
+    torch.cuda.synchronize()
+    assert torch.equal(lds.view(torch.int16), reg.view(torch.int16)), f"lds vs reg {same}"
+    got, got_lds = out.cpu().numpy(), lds.cpu().numpy()
+    del dev, out, lds, reg
     rows = sample_rows(x, 48, seed=len(name))
     print(f"[workload] {name}: oracle on {len(rows)} rows", flush=True)
     ref = orc.paged_attention_rows_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
                                        x.context_lens, x.scale, rows)
     e = assert_close(got[rows[:, 0], rows[:, 1]], ref, name)
+    assert_close(got_lds[rows[:, 0], rows[:, 1]], ref, name + " lds")
     print(f"[workload] {name}: {e}", flush=True)
 
 
