@@ -38,7 +38,7 @@ KERNEL_SOURCES = ["paged_kv_cache_226_amd/csrc/pa_kernels.hip",
 # (mode, distance, structure) of the per-mode timings: the four modes at
 # distance 1, the register look-ahead two blocks ahead, the LDS-staged
 # look-ahead, and (fp16 only) the four modes of the two-loop structure
-MODE_RUNS = [(0, 1, 0), (1, 1, 0), (2, 1, 0), (3, 1, 0), (2, 2, 0), (4, 1, 0),
+MODE_RUNS = [(0, 1, 0), (1, 1, 0), (2, 1, 0), (3, 1, 0), (2, 2, 0), (4, 1, 0), (4, 2, 0),
              (0, 1, 1), (1, 1, 1), (2, 1, 1), (3, 1, 1)]
 
 

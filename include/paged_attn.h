@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 #define PA_HEAD_DIM 128
 #define PA_BLOCK_SIZE 16
 #define PA_G_MAX 16      /* query heads per KV head */
@@ -98,10 +98,17 @@ enum pa_prefetch {
                              buffers ahead) */
     PA_PREFETCH_BOTH = 3, /* REG for block j + w, plus an L2 touch of
                              block j + (1 + k)*w */
-    PA_PREFETCH_LDS = 4   /* block j + w copied straight from HBM into an
-                             LDS slot of the wavefront (no registers), read
-                             out when its turn comes; distance 1 only, fused
-                             structure only */
+    PA_PREFETCH_LDS = 4   /* block j + k*w copied straight from HBM into
+                             one of k+1 LDS slots of the wavefront (no
+                             registers; k = 1 or 2), read out when its turn
+                             comes; fused structure only */
+};
+
+/* What the caches hold. */
+enum pa_kv_dtype {
+    PA_KV_F16 = 0,  /* IEEE binary16 (paged_attn_decode) */
+    PA_KV_E4M3 = 1  /* OCP FP8 E4M3 with per-tensor scales
+                       (paged_attn_decode_fp8) */
 };
 
 /* Which sequence each row of the launch grid takes.  Work-groups start in
@@ -154,6 +161,11 @@ typedef struct pa_shape {
     int64_t k_head_stride;
     int64_t v_block_stride;
     int64_t v_head_stride;
+    int32_t kv_dtype;           /* enum pa_kv_dtype; the plan (waves, LDS,
+                                   default look-ahead distance) depends on it.
+                                   paged_attn_decode needs PA_KV_F16 and
+                                   paged_attn_decode_fp8 PA_KV_E4M3, else
+                                   PA_ERR_INVALID_ARG */
 } pa_shape;
 
 typedef struct pa_options {
@@ -167,12 +179,14 @@ typedef struct pa_options {
                                   batches of 256..767 pairs whose block table
                                   is 512..1024 blocks wide, else 4 */
     int32_t prefetch_distance; /* k, the look-ahead distance in iterations of
-                                  a wave (0 = 1, or 2 for mode 2 over an E4M3
-                                  cache): mode 1 touches block j+k*w
+                                  a wave (0 = 1, or 2 for modes 2 and 4 over
+                                  an E4M3 cache): mode 1 touches block j+k*w
                                   (k <= 63); mode 2 fetches block j+k*w into
-                                  registers (k <= 2, else PA_ERR_UNSUPPORTED);
-                                  mode 3 fetches j+w into registers and
-                                  touches j+(1+k)*w (k <= 63) */
+                                  registers and mode 4 into LDS (k <= 2, else
+                                  PA_ERR_UNSUPPORTED); mode 3 fetches j+w
+                                  into registers and touches j+(1+k)*w
+                                  (k <= 63).  The two-loop structure takes
+                                  k = 1 only */
     int32_t seq_order;         /* enum pa_seq_order; LONGEST_FIRST needs
                                   num_seqs <= PA_RANK_MAX_SEQS */
     int32_t structure;         /* enum pa_structure */
@@ -204,6 +218,7 @@ typedef struct pa_plan_info {
     size_t workspace_bytes;    /* 0 when num_partitions == 1 */
     int32_t seq_order;         /* PA_ORDER_NATURAL or PA_ORDER_LONGEST_FIRST */
     int32_t structure;         /* enum pa_structure */
+    int32_t prefetch_distance; /* the look-ahead distance k in effect */
 } pa_plan_info;
 
 /* Fill *opts with the defaults (prefetch = library default, auto sizes). */

@@ -21,6 +21,7 @@ ORDER_AUTO, ORDER_NATURAL, ORDER_LONGEST_FIRST = 0, 1, 2
 ORDER_NAMES = {1: "natural", 2: "longest_first"}
 RANK_MAX_SEQS = 256
 STRUCTURE_FUSED, STRUCTURE_TWO_LOOP = 0, 1
+KV_F16, KV_E4M3 = 0, 1
 
 
 class PaShape(ctypes.Structure):
@@ -29,7 +30,8 @@ class PaShape(ctypes.Structure):
                 ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("num_blocks", ctypes.c_int64),
                 ("k_block_stride", ctypes.c_int64), ("k_head_stride", ctypes.c_int64),
-                ("v_block_stride", ctypes.c_int64), ("v_head_stride", ctypes.c_int64)]
+                ("v_block_stride", ctypes.c_int64), ("v_head_stride", ctypes.c_int64),
+                ("kv_dtype", ctypes.c_int32)]
 
 
 class PaOptions(ctypes.Structure):
@@ -45,7 +47,8 @@ class PaPlanInfo(ctypes.Structure):
     _fields_ = [("prefetch", ctypes.c_int32), ("waves_per_wg", ctypes.c_int32),
                 ("partition_blocks", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
                 ("workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
-                ("seq_order", ctypes.c_int32), ("structure", ctypes.c_int32)]
+                ("seq_order", ctypes.c_int32), ("structure", ctypes.c_int32),
+                ("prefetch_distance", ctypes.c_int32)]
 
 
 _lib = None
@@ -103,12 +106,13 @@ def default_options() -> PaOptions:
 
 def make_shape(num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, num_blocks,
                head_dim=128, block_size=16, k_block_stride=0, k_head_stride=0,
-               v_block_stride=0, v_head_stride=0) -> PaShape:
-    """pa_shape; the strides are in bytes, 0 = the dense layout."""
+               v_block_stride=0, v_head_stride=0, kv_dtype=0) -> PaShape:
+    """pa_shape; the strides are in bytes, 0 = the dense layout; kv_dtype
+    KV_F16 or KV_E4M3."""
     return PaShape(int(num_seqs), int(num_q_heads), int(num_kv_heads), int(head_dim),
                    int(block_size), int(max_blocks_per_seq), int(num_blocks),
                    int(k_block_stride), int(k_head_stride), int(v_block_stride),
-                   int(v_head_stride))
+                   int(v_head_stride), int(kv_dtype))
 
 
 def plan(shape: PaShape, opts: PaOptions = None) -> dict:

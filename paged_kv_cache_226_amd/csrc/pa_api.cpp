@@ -36,7 +36,7 @@ constexpr int kMaxAutoPartition = 256;
 constexpr int kTwoLoopPartitionBlocks = 32;
 
 struct Plan {
-  int pf, waves, PB, P, order, two;
+  int pf, dist, waves, PB, P, order, two;
   int64_t wgs;
   size_t ws_bytes;
 };
@@ -64,6 +64,7 @@ int check_shape(const pa_shape* sh) {
     if (st > 0 && st > INT64_MAX / 4 / sh->num_blocks) return PA_ERR_UNSUPPORTED;
   }
   if (sh->max_blocks_per_seq > INT32_MAX / PA_BLOCK_SIZE) return PA_ERR_UNSUPPORTED;
+  if (sh->kv_dtype != PA_KV_F16 && sh->kv_dtype != PA_KV_E4M3) return PA_ERR_INVALID_ARG;
   return PA_OK;
 }
 
@@ -77,7 +78,8 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   if (o->structure != PA_STRUCTURE_FUSED && o->structure != PA_STRUCTURE_TWO_LOOP)
     return PA_ERR_INVALID_ARG;
   const bool two = o->structure == PA_STRUCTURE_TWO_LOOP;
-  if (two && o->prefetch_distance > 1) return PA_ERR_UNSUPPORTED;
+  const bool kv8 = sh->kv_dtype == PA_KV_E4M3;
+  if (two && (o->prefetch_distance > 1 || kv8)) return PA_ERR_UNSUPPORTED;
   int order = o->seq_order;
   if (order < PA_ORDER_AUTO || order > PA_ORDER_LONGEST_FIRST) return PA_ERR_INVALID_ARG;
   if (order == PA_ORDER_AUTO)
@@ -89,11 +91,19 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
 
   int pf = o->prefetch < 0 ? kDefaultPrefetch : o->prefetch;
   if (pf > PA_PREFETCH_LDS) return PA_ERR_INVALID_ARG;
-  // registers hold at most two blocks ahead, an LDS slot one
-  if (pf == PA_PREFETCH_REG && o->prefetch_distance > 2) return PA_ERR_UNSUPPORTED;
-  if (pf == PA_PREFETCH_LDS && (o->prefetch_distance > 1 || two)) return PA_ERR_UNSUPPORTED;
-  // the LDS-staged look-ahead's per-wave slot (sized for fp16, the larger)
-  const size_t slot = pf == PA_PREFETCH_LDS ? 2 * PA_BLOCK_SIZE * PA_HEAD_DIM * 2 : 0;
+  // Default distance 1, except the register and LDS look-aheads over an E4M3
+  // cache: its blocks are half the bytes, and two of them ahead (at 142
+  // VGPRs, still 3 waves per SIMD, for the registers) measured up to 10 %
+  // faster on a ragged batch.
+  const bool ring = pf == PA_PREFETCH_REG || pf == PA_PREFETCH_LDS;
+  const int dist = o->prefetch_distance > 0 ? o->prefetch_distance : (kv8 && ring ? 2 : 1);
+  // the register and LDS rings hold at most two blocks ahead
+  if (ring && dist > 2) return PA_ERR_UNSUPPORTED;
+  if (pf == PA_PREFETCH_LDS && two) return PA_ERR_UNSUPPORTED;
+  // the LDS ring: dist + 1 slots of one block's K and V per wave
+  const size_t slot = pf == PA_PREFETCH_LDS
+                          ? (size_t)(dist + 1) * 2 * PA_BLOCK_SIZE * PA_HEAD_DIM * (kv8 ? 1 : 2)
+                          : 0;
 
   const int B = sh->num_seqs, Hkv = sh->num_kv_heads;
   const int MB = sh->max_blocks_per_seq;
@@ -143,6 +153,7 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   pl->order = order;
   pl->two = two ? 1 : 0;
   pl->pf = pf;
+  pl->dist = dist;
   pl->waves = waves;
   pl->PB = PB;
   pl->P = P;
@@ -175,6 +186,7 @@ int paged_attn_plan(const pa_shape* sh, const pa_options* o, pa_plan_info* info)
   info->workspace_bytes = pl.ws_bytes;
   info->seq_order = pl.order;
   info->structure = pl.two;
+  info->prefetch_distance = pl.dist;
   return PA_OK;
 }
 
@@ -202,6 +214,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
   if (!isfinite(k_scale) || !isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f))
     return PA_ERR_INVALID_ARG;
+  if (sh && sh->kv_dtype != (kv8 ? PA_KV_E4M3 : PA_KV_F16)) return PA_ERR_INVALID_ARG;
   Plan pl;
   int rc = make_plan(sh, o, &pl);
   if (rc) return rc;
@@ -256,13 +269,9 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.k_blk = k_blk;
   a.v_blk = v_blk;
   a.lds_bt_bytes = pa::lds_bt_bytes_for(pl.PB);
-  // Default distance 1, except the register look-ahead over an E4M3 cache:
-  // its blocks are half the bytes, and two of them ahead (at 142 VGPRs, still
-  // 3 waves per SIMD) measured up to 10 % faster on a ragged batch.
-  a.pf_dist = o->prefetch_distance > 0 ? o->prefetch_distance
-                                       : (kv8 && pl.pf == PA_PREFETCH_REG ? 2 : 1);
+  a.pf_dist = pl.dist;
   const bool dbg = o->debug_gather_k || o->debug_trace || o->debug_error_word;
-  if (pl.two && (kv8 || dbg)) return PA_ERR_UNSUPPORTED;
+  if (pl.two && dbg) return PA_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   if (pl.P > 1) {
@@ -274,11 +283,11 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   if (pl.two) {
     if (pa::launch_decode_two_loop(a, pl.pf, pl.waves, st) != hipSuccess) return PA_ERR_HIP;
   } else {
-    // the register look-ahead at distance 2 and the LDS-staged look-ahead
-    // are kernel instances 4 and 5
-    const int variant = pl.pf == PA_PREFETCH_LDS                     ? 5
-                        : pl.pf == PA_PREFETCH_REG && a.pf_dist == 2 ? 4
-                                                                      : pl.pf;
+    // the register look-ahead at distance 2 is kernel instance 4, the LDS
+    // ring at distance 1 and 2 instances 5 and 6
+    const int variant = pl.pf == PA_PREFETCH_LDS ? 4 + pl.dist
+                        : pl.pf == PA_PREFETCH_REG && pl.dist == 2 ? 4
+                                                                   : pl.pf;
     if (pa::launch_decode(a, variant, dbg, kv8, pl.waves, st) != hipSuccess) return PA_ERR_HIP;
   }
   if (pl.P > 1 && pa::launch_reduce(a, st) != hipSuccess) return PA_ERR_HIP;

@@ -32,13 +32,18 @@
 // only when some head's running maximum changed (rescaling by 1 is exact, so
 // skipping it changes no bits).
 //
-// Look-ahead modes (PF): 0 none; 1 an L2 / Infinity-Cache touch of every
+// Look-ahead instances (PF): 0 none; 1 an L2 / Infinity-Cache touch of every
 // 128 B line of block j+kW (one dword per lane, value discarded); 2 block j+W
 // loaded into a second register buffer before block j is computed; 3 both,
-// with the touch moved to block j+(1+k)W.  k (a.pf_dist, 1..63) is the
-// touch distance in iterations; the pages' Algorithm 1 is k = 1.  The
-// arithmetic is the same code in every mode, so results are bitwise
-// identical.
+// with the touch moved to block j+(1+k)W; 4 the register ring two blocks
+// ahead (j+2W); 5 and 6 an LDS ring one and two blocks ahead, filled by
+// direct global-to-LDS copies.  k (a.pf_dist, 1..63) is the touch distance
+// in iterations; the pages' Algorithm 1 is k = 1.  The arithmetic is the
+// same code in every instance, so results are bitwise identical.
+//
+// Where the slices are: the (block p, KV head h) slice of K starts at byte
+// p * k_blk + h * k_head of the K pool (V likewise), so K and V may share a
+// pool or be padded; each slice itself has the layout below.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -364,17 +369,19 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
       compute(buf, j, kMayTail);
     }
     sink ^= pend;
-  } else if constexpr (PF == 5) {
-    // LDS staging: block j+W is copied by the direct global-to-LDS path
-    // (global_load_lds_dwordx4, no registers involved) into this wave's LDS
-    // slot while block j, already read out into registers, is computed.  The
-    // copy keeps the slice's byte order (1 KiB contiguous per instruction);
-    // the read-back takes the same per-lane pieces as the direct loads.
-    // Holding the look-ahead block in LDS instead of registers frees about
-    // 32 VGPRs per lane.
-    constexpr int kSlot = 2 * kHeadBytes;
-    unsigned char* slot = reinterpret_cast<unsigned char*>(merge_s) + wave * kSlot;
-    auto dma_block = [&](int64_t ph) {
+  } else if constexpr (PF == 5 || PF == 6) {
+    // LDS ring of depth D: block j+D*W is copied by the direct global-to-LDS
+    // path (global_load_lds_dwordx4, no registers involved) into one of this
+    // wave's D+1 LDS slots while block j is read out of another and
+    // computed.  The copy keeps the slice's byte order (1 KiB contiguous per
+    // instruction); the read-back takes the same per-lane pieces as the
+    // direct loads.  Holding the look-ahead blocks in LDS instead of
+    // registers frees about 32 VGPRs per lane and block.
+    constexpr int D = PF - 4;
+    constexpr int kSlot = 2 * kHeadBytes;             // one block's K and V
+    constexpr int kCopies = 2 * (kHeadBytes / 1024);  // copy instructions per block
+    unsigned char* const ring = reinterpret_cast<unsigned char*>(merge_s) + wave * (D + 1) * kSlot;
+    auto dma_block = [&](int64_t ph, unsigned char* slot) {
       const unsigned char* ks = kbase + ph * a.k_blk + lane * 16;
       const unsigned char* vs = vbase + ph * a.v_blk + lane * 16;
 #pragma unroll
@@ -387,7 +394,7 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
                                          16, 0, kCachePolicyNT);
       }
     };
-    auto read_block = [&](Buf& buf) {
+    auto read_block = [&](Buf& buf, const unsigned char* slot) {
       const unsigned char* kb = slot + k_off;
       const unsigned char* vb = slot + kHeadBytes + v_off;
       if constexpr (KV8) {
@@ -402,37 +409,63 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
         for (int i = 0; i < 4; ++i) buf.v[i] = *reinterpret_cast<const u32x4*>(vb + 1024 * i);
       }
     };
-    // Wait for the copy of block `it`, read it out, wait for the reads (the
-    // slot is then free), start the copy of block it+1.  The waits are
-    // explicit: the copy is a memory write the compiler does not track.
-    auto stage = [&](Buf& buf, int it) {
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      read_block(buf);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    if (n_it > 0) dma_block(phys_it(0));
+    // The waits are explicit: the copies are memory writes whose completion
+    // only the vector-memory counter reports, in issue order.  Before a slot
+    // is refilled its reads must have returned (lgkmcnt 0); before a slot is
+    // read its copy must have landed, which with the D later blocks' copies
+    // issued after it is vmcnt <= D * kCopies (other vector memory operations
+    // issued in between only make the wait stricter).
+    // block it of this wave lives in slot it mod (D+1)
+    int slot_cur = 0;  // slot of iteration it
+    int slot_new = D;  // slot of the next copy, block it+D
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (d < n_it) dma_block(phys_it(d), ring + d * kSlot);
     int it = 0;
-    for (; it + 1 < n_it; ++it) {
+    for (; it + D < n_it; ++it) {
       const int j = j0 + it * W;
       Buf buf;
-      stage(buf, it);
-      dma_block(phys_it(it + 1));
-      trace_put(j + W, 1, wave);
       __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      dma_block(phys_it(it + D), ring + slot_new * kSlot);
+      if constexpr (D * kCopies == 16)
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      else if constexpr (D * kCopies == 8)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      read_block(buf, ring + slot_cur * kSlot);
+      __builtin_amdgcn_sched_barrier(0);
+      trace_put(j + D * W, 1, wave);
       trace_put(j, 0, (wave << 16) | it);
       compute(buf, j, kNoTail);
       advance(it);
+      slot_cur = slot_cur == D ? 0 : slot_cur + 1;
+      slot_new = slot_new == D ? 0 : slot_new + 1;
     }
-    if (it < n_it) {  // this wave's last block: nothing left to copy ahead
+    // this wave's last D blocks: nothing left to copy ahead; the copies of
+    // the blocks after `it` may still be in flight
+    for (; it < n_it; ++it) {
       const int j = j0 + it * W;
       Buf buf;
-      stage(buf, it);
+      __builtin_amdgcn_sched_barrier(0);
+      if (D == 2 && it + 1 < n_it) {
+        if constexpr (kCopies == 8)
+          asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      read_block(buf, ring + slot_cur * kSlot);
+      __builtin_amdgcn_sched_barrier(0);
       trace_put(j, 0, (wave << 16) | it);
       compute(buf, j, kMayTail);
+      advance(it);
+      slot_cur = slot_cur == D ? 0 : slot_cur + 1;
     }
     // the merge records below overlay the slots of other waves
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __syncthreads();
   } else {
     // Register look-ahead of depth D: block j + D*W is fetched into a ring of
@@ -913,25 +946,28 @@ hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int wa
                          hipStream_t st) {
   typedef hipError_t (*fn_t)(const DecodeArgs&, dim3, dim3, size_t, hipStream_t);
   // pf 0..3 are the look-ahead modes; 4 is the register look-ahead of depth
-  // 2, 5 the LDS-staged look-ahead
-  static const fn_t table[24] = {
+  // 2, 5 and 6 the LDS ring of depth 1 and 2
+  static const fn_t table[28] = {
       launch_decode_t<0, false, false>, launch_decode_t<0, true, false>,
       launch_decode_t<1, false, false>, launch_decode_t<1, true, false>,
       launch_decode_t<2, false, false>, launch_decode_t<2, true, false>,
       launch_decode_t<3, false, false>, launch_decode_t<3, true, false>,
       launch_decode_t<4, false, false>, launch_decode_t<4, true, false>,
       launch_decode_t<5, false, false>, launch_decode_t<5, true, false>,
+      launch_decode_t<6, false, false>, launch_decode_t<6, true, false>,
       launch_decode_t<0, false, true>,  launch_decode_t<0, true, true>,
       launch_decode_t<1, false, true>,  launch_decode_t<1, true, true>,
       launch_decode_t<2, false, true>,  launch_decode_t<2, true, true>,
       launch_decode_t<3, false, true>,  launch_decode_t<3, true, true>,
       launch_decode_t<4, false, true>,  launch_decode_t<4, true, true>,
-      launch_decode_t<5, false, true>,  launch_decode_t<5, true, true>};
-  if (pf < 0 || pf > 5) return hipErrorInvalidValue;
+      launch_decode_t<5, false, true>,  launch_decode_t<5, true, true>,
+      launch_decode_t<6, false, true>,  launch_decode_t<6, true, true>};
+  if (pf < 0 || pf > 6) return hipErrorInvalidValue;
   const dim3 grid(a.Hkv, a.B, a.P);
   const dim3 block(kWave * waves);
-  const size_t slots = pf == 5 ? (size_t)waves * (kv8 ? 4096 : 8192) : 0;
-  return table[(kv8 ? 12 : 0) + pf * 2 + (dbg ? 1 : 0)](
+  // the LDS ring: depth + 1 slots of one block's K and V per wave
+  const size_t slots = pf >= 5 ? (size_t)waves * (pf - 3) * (kv8 ? 4096 : 8192) : 0;
+  return table[(kv8 ? 14 : 0) + pf * 2 + (dbg ? 1 : 0)](
       a, grid, block, decode_lds_bytes(a.PB, a.G, waves, a.B, a.rank_seqs != 0, slots), st);
 }
 

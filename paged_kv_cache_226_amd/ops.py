@@ -44,16 +44,18 @@ def _slice_contiguous(t: torch.Tensor) -> bool:
 def shape_of(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,
              v_cache: Optional[torch.Tensor] = None) -> nat.PaShape:
     """pa_shape of these tensors; K and V may be views into a larger pool
-    (their strides over blocks and heads are passed on in bytes)."""
+    (their strides over blocks and heads are passed on in bytes).  A one-byte
+    K cache is E4M3."""
     B, Hq, D = q.shape
     NB, Hkv, G8, T, X = k_cache.shape
     ek = k_cache.element_size()
+    kw0 = dict(kv_dtype=nat.KV_E4M3 if ek == 1 else nat.KV_F16)
     kw = dict(k_block_stride=k_cache.stride(0) * ek, k_head_stride=k_cache.stride(1) * ek)
     if v_cache is not None:
         ev = v_cache.element_size()
         kw.update(v_block_stride=v_cache.stride(0) * ev, v_head_stride=v_cache.stride(1) * ev)
     return nat.make_shape(B, Hq, Hkv, block_tables.shape[1], NB, head_dim=G8 * X, block_size=T,
-                          **kw)
+                          **kw0, **kw)
 
 
 def options(prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0,

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function(native_lib):
 
 
 def test_version_and_error_strings(native_lib):
-    assert native_lib.paged_attn_abi_version() == 3
+    assert native_lib.paged_attn_abi_version() == 4
     assert nat.error_string(0) == "ok"
     for code in range(1, 5):
         assert nat.error_string(code) not in ("ok", "unknown status")
@@ -105,7 +105,13 @@ def good_shape(**kw):
     (dict(shape=dict(block_size=32)), nat.PA_ERR_UNSUPPORTED),
     (dict(shape=dict(num_q_heads=34, num_kv_heads=2)), nat.PA_ERR_UNSUPPORTED),
     (dict(opts=dict(prefetch=5)), nat.PA_ERR_INVALID_ARG),
-    (dict(opts=dict(prefetch=4, prefetch_distance=2)), nat.PA_ERR_UNSUPPORTED),
+    (dict(opts=dict(prefetch=4, prefetch_distance=3)), nat.PA_ERR_UNSUPPORTED),
+    (dict(shape=dict(kv_dtype=2)), nat.PA_ERR_INVALID_ARG),
+    (dict(shape=dict(kv_dtype=-1)), nat.PA_ERR_INVALID_ARG),
+    # an E4M3 shape given to the fp16 entry point
+    (dict(shape=dict(kv_dtype=nat.KV_E4M3)), nat.PA_ERR_INVALID_ARG),
+    # three fp16 LDS slots per wave for 8 waves: 192 KiB
+    (dict(opts=dict(prefetch=4, prefetch_distance=2, waves_per_wg=8)), nat.PA_ERR_UNSUPPORTED),
     (dict(opts=dict(prefetch=4, structure=1)), nat.PA_ERR_UNSUPPORTED),
     (dict(opts=dict(waves_per_wg=3)), nat.PA_ERR_INVALID_ARG),
     (dict(opts=dict(prefetch_distance=64)), nat.PA_ERR_INVALID_ARG),
@@ -204,13 +210,53 @@ def test_two_loop_plan_keeps_the_scores_in_lds(native_lib, g, PB):
     assert p["num_partitions"] == -(-512 // PB)
 
 
+def call8(shape, opts=None):
+    return nat.lib().paged_attn_decode_fp8(
+        *[ctypes.c_void_p(FAKE)] * 5, ctypes.c_float(0.1), ctypes.c_float(1.0),
+        ctypes.c_float(1.0), ctypes.c_void_p(FAKE), ctypes.byref(shape),
+        ctypes.byref(opts) if opts is not None else None, None)
+
+
 def test_two_loop_rejects_e4m3_and_debug_outputs(native_lib):
     o = nat.default_options()
     o.structure = nat.STRUCTURE_TWO_LOOP
+    sh8 = good_shape(max_blocks_per_seq=16, kv_dtype=nat.KV_E4M3)
+    assert call8(sh8, o) == nat.PA_ERR_UNSUPPORTED
+    with pytest.raises(ValueError, match="unsupported"):
+        nat.plan(sh8, o)
     sh = good_shape(max_blocks_per_seq=16)
-    f = nat.lib().paged_attn_decode_fp8
-    rc = f(*[ctypes.c_void_p(FAKE)] * 5, ctypes.c_float(0.1), ctypes.c_float(1.0),
-           ctypes.c_float(1.0), ctypes.c_void_p(FAKE), ctypes.byref(sh), ctypes.byref(o), None)
-    assert rc == nat.PA_ERR_UNSUPPORTED
     o.debug_error_word = FAKE
     assert call(sh, o) == nat.PA_ERR_UNSUPPORTED
+
+
+def test_e4m3_entry_point_needs_an_e4m3_shape(native_lib):
+    # 4096 blocks per sequence need partitions, so a shape that passes every
+    # other check stops at the missing workspace, before any launch
+    assert call8(good_shape()) == nat.PA_ERR_INVALID_ARG
+    assert call8(good_shape(kv_dtype=nat.KV_E4M3)) == nat.PA_ERR_WORKSPACE
+    assert call(good_shape(kv_dtype=nat.KV_E4M3)) == nat.PA_ERR_INVALID_ARG
+    assert call(good_shape()) == nat.PA_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kv,pf,dist", [
+    (0, 0, 1), (0, 1, 1), (0, 2, 1), (0, 3, 1), (0, 4, 1),
+    (1, 0, 1), (1, 1, 1), (1, 2, 2), (1, 3, 1), (1, 4, 2)])
+def test_default_lookahead_distance_depends_on_the_cache_type(native_lib, kv, pf, dist):
+    o = nat.default_options()
+    o.prefetch = pf
+    p = nat.plan(good_shape(max_blocks_per_seq=16, kv_dtype=kv), o)
+    assert (p["prefetch"], p["prefetch_distance"]) == (pf, dist)
+    o.prefetch_distance = 1
+    assert nat.plan(good_shape(max_blocks_per_seq=16, kv_dtype=kv), o)["prefetch_distance"] == 1
+
+
+@pytest.mark.parametrize("kv,dist,waves", [(0, 1, 8), (0, 2, 4), (1, 1, 8), (1, 2, 8)])
+def test_lds_ring_slots_count_in_the_wave_choice(native_lib, kv, dist, waves):
+    """8 waves need (dist + 1) slots of one block's K and V each: 128 KiB for
+    two fp16 slots fit in 160 KiB, 192 KiB for three do not (4 waves then);
+    E4M3 slots are half the size."""
+    o = nat.default_options()
+    o.prefetch = nat.PREFETCH_LDS
+    o.prefetch_distance = dist
+    p = nat.plan(nat.make_shape(64, 32, 8, 512, 1000, kv_dtype=kv), o)
+    assert (p["waves_per_wg"], p["num_partitions"]) == (waves, 1)

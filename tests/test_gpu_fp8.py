@@ -166,8 +166,8 @@ def test_fp8_trace_follows_the_lookahead_schedule(pf):
         nb = -(-int(L) // 16)
         for h in range(Hkv):
             for s in range(0, nb, PB):
-                # the register look-ahead over E4M3 runs two blocks ahead by default
-                exp = sch.expected_trace(s, min(nb, s + PB), W, 2 if pf == 2 else 1)
+                # the register and LDS rings over E4M3 run two blocks ahead by default
+                exp = sch.expected_trace(s, min(nb, s + PB), W, 2 if pf in (2, 4) else 1)
                 for j, (wave, it, fetcher) in exp.items():
                     assert tr[b, h, j, 0] == (wave << 16 | it), (b, h, j)
                     assert tr[b, h, j, 1] == (-1 if pf == 0 else fetcher), (b, h, j, pf)
@@ -225,13 +225,15 @@ def test_fp8_workload_sampled_rows(name):
         assert torch.equal(o2.view(torch.int16), out.view(torch.int16)), f"mode {pf}"
     # the LDS-staged look-ahead may plan fewer waves; on the same plan it
     # matches the register look-ahead bit for bit
-    lds_plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], prefetch=4)
-    same = dict(waves_per_wg=lds_plan["waves_per_wg"],
-                partition_blocks=lds_plan["partition_blocks"])
-    lds = dec(prefetch=4, **same)
-    reg = dec(prefetch=2, prefetch_distance=2, **same)
-    torch.cuda.synchronize()
-    assert torch.equal(lds.view(torch.int16), reg.view(torch.int16)), f"lds vs reg {same}"
+    for dist in (1, 2):
+        lds_plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], prefetch=4,
+                            prefetch_distance=dist)
+        same = dict(waves_per_wg=lds_plan["waves_per_wg"],
+                    partition_blocks=lds_plan["partition_blocks"], prefetch_distance=dist)
+        lds = dec(prefetch=4, **same)
+        reg = dec(prefetch=2, **same)
+        torch.cuda.synchronize()
+        assert torch.equal(lds.view(torch.int16), reg.view(torch.int16)), f"lds vs reg {same}"
     got, got_lds = out.cpu().numpy(), lds.cpu().numpy()
     del dev, out, lds, reg
     rows = sample_rows(x8, 48, seed=len(name) + 1)

@@ -56,13 +56,15 @@ def test_workload_sampled_rows(name):
         assert torch.equal(o2.view(torch.int16), out.view(torch.int16)), f"mode {pf}"
     # the LDS-staged look-ahead may plan fewer waves (its slots share the
     # work-group's LDS); with the same plan it matches the register look-ahead
-    lds_plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], prefetch=4)
-    same = dict(waves_per_wg=lds_plan["waves_per_wg"],
-                partition_blocks=lds_plan["partition_blocks"])
-    lds = dec(prefetch=4, **same)
-    reg = dec(prefetch=2, **same)
-    torch.cuda.synchronize()
-    assert torch.equal(lds.view(torch.int16), reg.view(torch.int16)), f"lds vs reg {same}"
+    for dist in (1, 2):
+        lds_plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], prefetch=4,
+                            prefetch_distance=dist)
+        same = dict(waves_per_wg=lds_plan["waves_per_wg"],
+                    partition_blocks=lds_plan["partition_blocks"], prefetch_distance=dist)
+        lds = dec(prefetch=4, **same)
+        reg = dec(prefetch=2, **same)
+        torch.cuda.synchronize()
+        assert torch.equal(lds.view(torch.int16), reg.view(torch.int16)), f"lds vs reg {same}"
     got, got_lds = out.cpu().numpy(), lds.cpu().numpy()
     del dev, out, lds, reg
     rows = sample_rows(x, 48, seed=len(name))
