@@ -265,7 +265,8 @@ def main():
     kv_bytes = acc.step_kv_bytes(Hkv, 128, x.context_lens, elem_bytes=1 if fp8 else 2)
     other_bytes = acc.step_other_bytes(w.num_seqs, w.num_q_heads, 128, x.context_lens)
     flops = acc.step_flops(w.num_q_heads, 128, x.context_lens)
-    plan = ops.plan(d["q"], d["k_cache"], d["block_tables"], prefetch=args.prefetch)
+    plan = ops.plan(d["q"], d["k_cache"], d["block_tables"], prefetch=args.prefetch,
+                    prefetch_distance=args.prefetch_distance)
     ws = ops.new_workspace(d["q"], d["k_cache"], d["block_tables"], prefetch=args.prefetch)
     stream = torch.cuda.current_stream()
 
@@ -319,9 +320,9 @@ def main():
 
     mode = plan["prefetch"]
     mode_names = nat.PREFETCH_NAMES
-    # the library's default distance: 2 for the register look-ahead over E4M3
-    dist = args.prefetch_distance or (2 if fp8 and mode == nat.PREFETCH_REG else 1)
-    mode_label = mode_names[mode] + ("2" if mode == nat.PREFETCH_REG and dist == 2 else "")
+    dist = plan["prefetch_distance"]  # the library's default unless given
+    ring = mode in (nat.PREFETCH_REG, nat.PREFETCH_LDS)
+    mode_label = mode_names[mode] + ("2" if ring and dist == 2 else "")
     if args.profile:
         for pf, dist, structure in MODE_RUNS:
             if not (fp8 and structure):
