@@ -116,7 +116,9 @@ enum pa_kv_dtype {
    ragged batch.  The result does not depend on the order. */
 enum pa_seq_order {
     PA_ORDER_AUTO = 0,          /* LONGEST_FIRST when 2 <= num_seqs <=
-                                   PA_RANK_MAX_SEQS, else NATURAL */
+                                   PA_RANK_MAX_SEQS and the grid has more
+                                   work-groups than the CUs hold at once,
+                                   else NATURAL */
     PA_ORDER_NATURAL = 1,       /* row r takes sequence r */
     PA_ORDER_LONGEST_FIRST = 2  /* row r takes the sequence with the r-th most
                                    blocks, ties by index; each work-group

@@ -34,6 +34,16 @@ constexpr int kLongTableBlocks = 512;
 constexpr int kMinAutoPartition = 64;
 constexpr int kMaxAutoPartition = 256;
 constexpr int kTwoLoopPartitionBlocks = 32;
+//  * Auto order ranks the sequences (longest first) only when the grid is
+//    larger than what the CUs hold at once.  When every work-group is
+//    resident from the start the dispatch order changes nothing, and the
+//    ranking (a dependent read of every context length before the block
+//    table) only adds latency: 2-4 us on grids of 256 work-groups.
+//    Residency: kCUs x min(kResidentWavesPerCU / W, LDS per CU / LDS per
+//    work-group); 3 waves per SIMD is what the register ring's VGPRs allow.
+constexpr int64_t kCUs = 256;
+constexpr int kResidentWavesPerCU = 12;
+constexpr size_t kLdsPerCU = 163840;
 
 struct Plan {
   int pf, dist, waves, PB, P, order, two;
@@ -108,7 +118,7 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   const int B = sh->num_seqs, Hkv = sh->num_kv_heads;
   const int MB = sh->max_blocks_per_seq;
   const int64_t units = (int64_t)B * Hkv;
-  const bool rank = order == PA_ORDER_LONGEST_FIRST;
+  bool rank = order == PA_ORDER_LONGEST_FIRST;
   if (o->waves_per_wg != 0 && o->waves_per_wg != 1 && o->waves_per_wg != 2 &&
       o->waves_per_wg != 4 && o->waves_per_wg != 8)
     return PA_ERR_INVALID_ARG;
@@ -146,8 +156,21 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   }
   const int P = (MB + PB - 1) / PB;
   if (P > 65535) return PA_ERR_UNSUPPORTED;  // grid.z
-  const size_t lds = two ? pa::two_loop_lds_bytes(PB, g, waves, B, rank)
-                         : pa::decode_lds_bytes(PB, g, waves, B, rank, waves * slot);
+  auto lds_for = [&](bool r) {
+    return two ? pa::two_loop_lds_bytes(PB, g, waves, B, r)
+               : pa::decode_lds_bytes(PB, g, waves, B, r, waves * slot);
+  };
+  const int64_t wgs = (int64_t)P * Hkv * B;
+  if (o->seq_order == PA_ORDER_AUTO && rank) {
+    const size_t l = lds_for(true);
+    const int64_t by_waves = kResidentWavesPerCU / waves;
+    const int64_t by_lds = (int64_t)(kLdsPerCU / (l > 0 ? l : 1));
+    if (wgs <= kCUs * (by_waves < by_lds ? by_waves : by_lds)) {
+      order = PA_ORDER_NATURAL;
+      rank = false;
+    }
+  }
+  const size_t lds = lds_for(rank);
   if (lds > kMaxLdsBytes) return PA_ERR_UNSUPPORTED;
   memset(pl, 0, sizeof(*pl));
   pl->order = order;
@@ -157,7 +180,7 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   pl->waves = waves;
   pl->PB = PB;
   pl->P = P;
-  pl->wgs = (int64_t)P * Hkv * B;
+  pl->wgs = wgs;
   pl->ws_bytes = P > 1 ? (size_t)B * sh->num_q_heads * P * (2 + PA_HEAD_DIM) * sizeof(float) : 0;
   return PA_OK;
 }

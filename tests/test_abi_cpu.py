@@ -178,12 +178,20 @@ def test_stream_read_validation(native_lib):
     assert f(ctypes.c_void_p(FAKE + 4), 1024, ctypes.c_void_p(FAKE), None) == nat.PA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("B,order,want", [(1, 0, 1), (2, 0, 2), (256, 0, 2), (257, 0, 1),
-                                          (64, 1, 1), (1, 2, 2), (256, 2, 2)])
-def test_sequence_order_of_the_plan(native_lib, B, order, want):
+@pytest.mark.parametrize("B,Hkv,MB,order,want", [
+    (1, 2, 16, 0, 1),      # one sequence: nothing to order
+    (2, 2, 16, 0, 1),      # 4 work-groups, all resident at once
+    (96, 8, 64, 0, 1),     # 768 4-wave work-groups: 3 per CU on 256 CUs
+    (97, 8, 64, 0, 2),     # 776: some wait for a CU, so the longest go first
+    (64, 8, 512, 0, 2),    # 512 8-wave work-groups, one per CU at a time
+    (256, 8, 512, 0, 2),
+    (257, 8, 512, 0, 1),   # more sequences than the in-kernel ranking takes
+    (64, 2, 16, 1, 1), (1, 2, 16, 2, 2), (256, 2, 16, 2, 2)])
+def test_sequence_order_of_the_plan(native_lib, B, Hkv, MB, order, want):
     o = nat.default_options()
     o.seq_order = order
-    assert nat.plan(good_shape(num_seqs=B, max_blocks_per_seq=16), o)["seq_order"] == want
+    sh = good_shape(num_seqs=B, num_q_heads=4 * Hkv, num_kv_heads=Hkv, max_blocks_per_seq=MB)
+    assert nat.plan(sh, o)["seq_order"] == want
 
 
 @pytest.mark.parametrize("B,Hkv,MB,waves,P,PB", [

@@ -252,8 +252,9 @@ def test_longest_first_order_changes_no_bits(pb, waves):
     assert np.array_equal(bits(lpt), bits(nat_))
     assert not lpt[3].any()
     assert_close(lpt, oracle(x), f"pb={pb} w={waves}")
+    # a grid this small is resident at once: auto takes the natural order
     p = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], seq_order=0)
-    assert p["seq_order"] == 2
+    assert p["seq_order"] == 1
 
 
 @pytest.mark.parametrize("waves,pb", [(1, 0), (2, 3), (4, 0), (4, 5), (8, 0), (4, 1024)])
