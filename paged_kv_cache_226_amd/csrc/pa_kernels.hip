@@ -870,10 +870,29 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Cross-partition combine: one work-group of 128 threads per (sequence, head).
+// Its time is latency: with at most kReduceRegs partitions every partial is
+// loaded together with the context length (partitions past the sequence's
+// last block are masked afterwards, their words never used), so one memory
+// round trip precedes the arithmetic instead of two.  Both branches combine
+// in the same order, so the results are the same bits.
+constexpr int kReduceRegs = 8;
 __global__ void __launch_bounds__(128) pa_reduce_kernel(const DecodeArgs a) {
   const int row = blockIdx.x;  // b * Hq + h
   const int b = row / a.Hq;
   const int d = threadIdx.x;
+  const float* ml = a.ws_ml + (int64_t)row * a.P * 2;
+  const float* o = a.ws_o + (int64_t)row * a.P * kD;
+  float mq[kReduceRegs], lq[kReduceRegs], oq[kReduceRegs];
+  if (a.P <= kReduceRegs) {
+#pragma unroll
+    for (int q = 0; q < kReduceRegs; ++q) {
+      if (q < a.P) {
+        mq[q] = ml[2 * q];
+        lq[q] = ml[2 * q + 1];
+        oq[q] = o[(int64_t)q * kD + d];
+      }
+    }
+  }
   int ctx = a.ctx[b];
   ctx = min(ctx, a.MB * kT);
   const int nb = ctx > 0 ? (ctx + kT - 1) / kT : 0;
@@ -882,8 +901,23 @@ __global__ void __launch_bounds__(128) pa_reduce_kernel(const DecodeArgs a) {
     a.out[(int64_t)row * kD + d] = 0;
     return;
   }
-  const float* ml = a.ws_ml + (int64_t)row * a.P * 2;
-  const float* o = a.ws_o + (int64_t)row * a.P * kD;
+  if (a.P <= kReduceRegs) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kReduceRegs; ++q)
+      if (q < np) M = fmaxf(M, mq[q]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int q = 0; q < kReduceRegs; ++q) {
+      if (q < np) {
+        const float al = fast_exp2(mq[q] - M);
+        L += al * lq[q];
+        O += al * oq[q];
+      }
+    }
+    a.out[(int64_t)row * kD + d] = f32_to_f16_bits(O * a.v_scale / L);
+    return;
+  }
   float M = -INFINITY;
   for (int q = 0; q < np; ++q) M = fmaxf(M, ml[2 * q]);
   float L = 0.f, O = 0.f;
