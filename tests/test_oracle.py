@@ -256,6 +256,15 @@ MUTATIONS = {
                            "for (t = 0; t < L - 1; ++t) {\n        s[t] = exp"),
     "scale_dropped": ("s[t] = scale * dot;", "s[t] = dot;"),
     "q_head_row": ("((int64_t)b * Hq + h) * D", "((int64_t)b * Hq + kvh) * D"),
+    # the E4M3 path
+    "e4m3_bias": ("ldexp((double)(8 + frac), expo - 10)", "ldexp((double)(8 + frac), expo - 11)"),
+    "e4m3_subnormal": ("mag = ldexp((double)frac, -9);", "mag = ldexp((double)frac, -10);"),
+    "e4m3_nan_code": ("if (expo == 0xf && frac == 0x7) {", "if (expo == 0xf && frac == 0x6) {"),
+    "e4m3_sign": ("ldexp((double)(8 + frac), expo - 10);\n    }\n    return sign ? -mag : mag;",
+                  "ldexp((double)(8 + frac), expo - 10);\n    }\n    return mag;"),
+    "fp8_scales_swapped": ("pao_pool k = {k_cache, 1, (double)k_scale}, v = {v_cache, 1, (double)v_scale};",
+                           "pao_pool k = {k_cache, 1, (double)v_scale}, v = {v_cache, 1, (double)k_scale};"),
+    "fp8_scale_dropped": ("[idx]) * p.scale;", "[idx]);"),
 }
 
 
@@ -273,6 +282,8 @@ def _pins_pass(lib_path):
             test_uniform_weights_give_mean_of_v("zero_q")
             test_gqa_equals_mha_with_repeated_kv_heads_bitwise()
             test_small_head_dim_and_block_size()
+            test_e4m3_decoder_all_bit_patterns()
+            test_fp8_oracle_matches_sdpa()
         finally:
             ob.LIB = real
     except (AssertionError, RuntimeError):
@@ -282,23 +293,36 @@ def _pins_pass(lib_path):
     return True
 
 
-@pytest.mark.parametrize("name", sorted(MUTATIONS))
-def test_planted_mistake_is_caught(name):
-    src_path = os.path.join(os.path.dirname(orc.__file__), "pa_oracle.c")
-    src = open(src_path).read()
-    old, new = MUTATIONS[name]
-    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
-    mutated = src.replace(old, new)
+def _build_and_check(source):
     tmp = tempfile.mkdtemp(prefix="oracle_mut_")
     try:
         c = os.path.join(tmp, "m.c")
         so = os.path.join(tmp, "libm.so")
-        open(c, "w").write(mutated)
+        open(c, "w").write(source)
         subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
                         "-ffp-contract=off", c, "-o", so, "-lm"], check=True)
-        assert not _pins_pass(so), f"no pin caught the planted mistake {name}"
+        return _pins_pass(so)
     finally:
         shutil.rmtree(tmp)
+
+
+def _oracle_source():
+    return open(os.path.join(os.path.dirname(orc.__file__), "pa_oracle.c")).read()
+
+
+def test_unmutated_oracle_passes_the_pins():
+    """The control for the planted mistakes: the same build of the real
+    source passes every pin they are checked against."""
+    assert _build_and_check(_oracle_source())
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name):
+    src = _oracle_source()
+    old, new = MUTATIONS[name]
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    assert not _build_and_check(src.replace(old, new)), \
+        f"no pin caught the planted mistake {name}"
 
 
 # ---------------------------------------------------------------------------
