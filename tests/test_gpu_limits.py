@@ -44,8 +44,13 @@ def test_context_of_64k_tokens(pb, waves):
     print(f"[limits] 64K tokens: {p}", flush=True)
     if pb == 1:
         assert p["num_partitions"] == 4096
-    assert_close(run(x, dev, partition_blocks=pb, waves_per_wg=waves), oracle(x),
-                 f"64K pb={pb} w={waves}")
+    base = run(x, dev, partition_blocks=pb, waves_per_wg=waves)
+    assert_close(base, oracle(x), f"64K pb={pb} w={waves}")
+    # the LDS ring on the same plan (three fp16 slots do not fit 8 waves)
+    W = p["waves_per_wg"]
+    for dist in ((1, 2) if W < 8 else (1,)):
+        lds = run(x, dev, partition_blocks=pb, waves_per_wg=W, prefetch=4, prefetch_distance=dist)
+        assert np.array_equal(bits(lds), bits(base)), f"LDS ring, distance {dist}"
 
 
 @pytest.mark.parametrize("fp8", [False, True])
@@ -73,15 +78,21 @@ def test_pool_offsets_beyond_4_gib(fp8):
     q = torch.from_numpy(x.q).cuda()
     btd = torch.from_numpy(bt).cuda()
     ctx = torch.from_numpy(x.context_lens).cuda()
+    dec = ((lambda **kw: ops.paged_attn_decode_fp8(q, kp, vp, btd, ctx, x.scale, x8.k_scale,
+                                                   x8.v_scale, **kw)) if fp8 else
+           (lambda **kw: ops.paged_attn_decode(q, kp, vp, btd, ctx, x.scale, **kw)))
+    out = dec()
     if fp8:
-        out = ops.paged_attn_decode_fp8(q, kp, vp, btd, ctx, x.scale, x8.k_scale, x8.v_scale)
         ref = orc.paged_attention_fp8_f64(x8.q, x8.k8, x8.v8, x8.block_tables, x8.context_lens,
                                           x8.scale, x8.k_scale, x8.v_scale)
     else:
-        out = ops.paged_attn_decode(q, kp, vp, btd, ctx, x.scale)
         ref = oracle(x)
+    # the LDS ring's copies address the same far blocks (same plan: 4 waves)
+    others = [dec(prefetch=4, prefetch_distance=dist) for dist in (1, 2)]
     torch.cuda.synchronize()
     got = out.cpu().numpy()
-    del kp, vp
+    for dist, o in zip((1, 2), others):
+        assert np.array_equal(bits(o.cpu().numpy()), bits(got)), f"LDS ring, distance {dist}"
+    del kp, vp, others
     torch.cuda.empty_cache()
     assert_close(got, ref, f"offsets > 4 GiB fp8={fp8}")
