@@ -19,17 +19,18 @@ def _need_gpu(native_lib):
         pytest.skip("no GPU")
 
 
-def _call(dev, scale, out, ws, fp8=None):
+def _call(dev, scale, out, ws, fp8=None, pf=-1):
     if fp8 is not None:
         return ops.paged_attn_decode_fp8(dev["q"], dev["k_cache"], dev["v_cache"],
                                          dev["block_tables"], dev["context_lens"], scale,
-                                         fp8[0], fp8[1], out, workspace=ws)
+                                         fp8[0], fp8[1], out, workspace=ws, prefetch=pf)
     return ops.paged_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
-                                 dev["context_lens"], scale, out, workspace=ws)
+                                 dev["context_lens"], scale, out, workspace=ws, prefetch=pf)
 
 
+@pytest.mark.parametrize("pf", [-1, 4])  # the default mode and the LDS ring
 @pytest.mark.parametrize("case", ["split", "whole", "fp8"])
-def test_graph_replays_match_eager(case):
+def test_graph_replays_match_eager(case, pf):
     if case == "whole":  # 256 (sequence, KV head) pairs: one partition, no reduce
         x = gen.make_case(64, 16, 4, list(np.random.default_rng(1).integers(1, 300, 64)),
                           seed=501)
@@ -46,22 +47,22 @@ def test_graph_replays_match_eager(case):
         fp8 = (x8.k_scale, x8.v_scale)
     else:
         dev = to_device(x)
-    p = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"])
+    p = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], prefetch=pf)
     assert (p["num_partitions"] > 1) == (case != "whole")
     out = torch.empty_like(dev["q"])
-    ws = ops.new_workspace(dev["q"], dev["k_cache"], dev["block_tables"])
-    eager = _call(dev, x.scale, out, ws, fp8).clone()
+    ws = ops.new_workspace(dev["q"], dev["k_cache"], dev["block_tables"], prefetch=pf)
+    eager = _call(dev, x.scale, out, ws, fp8, pf).clone()
     torch.cuda.synchronize()
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        _call(dev, x.scale, out, ws, fp8)
+        _call(dev, x.scale, out, ws, fp8, pf)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        _call(dev, x.scale, out, ws, fp8)
+        _call(dev, x.scale, out, ws, fp8, pf)
     for _ in range(5):
         out.fill_(1.0)   # eager work between the replays
         ws.fill_(0xFF)   # the workspace may hold anything
@@ -76,7 +77,7 @@ def test_graph_replays_match_eager(case):
     g.replay()
     torch.cuda.synchronize()
     replayed = out.clone()
-    fresh = _call(dev, x.scale, torch.empty_like(out), ws, fp8)
+    fresh = _call(dev, x.scale, torch.empty_like(out), ws, fp8, pf)
     torch.cuda.synchronize()
     assert np.array_equal(bits(replayed.cpu().numpy()), bits(fresh.cpu().numpy()))
     assert not np.array_equal(bits(replayed.cpu().numpy()), bits(eager.cpu().numpy()))
