@@ -53,6 +53,9 @@ class PaPlanInfo(ctypes.Structure):
 
 _lib = None
 
+# the PA_ABI_VERSION whose struct layouts the classes above mirror
+ABI_VERSION = 4
+
 
 class NativeLibraryMissing(RuntimeError):
     pass
@@ -90,6 +93,11 @@ def lib():
     L.paged_attn_error_string.restype = ctypes.c_char_p
     L.paged_attn_abi_version.argtypes = []
     L.paged_attn_abi_version.restype = ctypes.c_int
+    got = L.paged_attn_abi_version()
+    if got != ABI_VERSION:
+        raise NativeLibraryMissing(
+            f"{LIB_PATH} has ABI version {got}, this binding needs {ABI_VERSION}; rebuild it "
+            "with `python -m paged_kv_cache_226_amd.build`")
     _lib = L
     return L
 

@@ -15,9 +15,17 @@ import torch
 from . import _native as nat
 
 
-def _stream_handle(stream: Optional[torch.cuda.Stream]) -> ctypes.c_void_p:
-    s = stream if stream is not None else torch.cuda.current_stream()
+def _stream_handle(stream: Optional[torch.cuda.Stream], device: torch.device) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    if s.device != device:
+        raise ValueError(f"the stream is on {s.device}, the tensors on {device}")
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _same_device(device: torch.device, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, q on {device}")
 
 
 def _check(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int):
@@ -134,6 +142,10 @@ def _decode(fp8: bool, q, k_cache, v_cache, block_tables, context_lens, scale, k
                          % ((16, 16) if fp8 else (8, 8)))
     if block_tables.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("inconsistent shapes")
+    _same_device(q.device, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+                 context_lens=context_lens, out=out, workspace=workspace,
+                 debug_gather_k=debug_gather_k, debug_trace=debug_trace,
+                 debug_error_word=debug_error_word)
     if scale is None:
         scale = D ** -0.5
     if out is None:
@@ -155,15 +167,16 @@ def _decode(fp8: bool, q, k_cache, v_cache, block_tables, context_lens, scale, k
         o.workspace_bytes = workspace.numel() * workspace.element_size()
     ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (q, k_cache, v_cache, block_tables,
                                                       context_lens)]
-    if fp8:
-        rc = nat.lib().paged_attn_decode_fp8(
-            *ptrs, ctypes.c_float(scale), ctypes.c_float(k_scale), ctypes.c_float(v_scale),
-            ctypes.c_void_p(out.data_ptr()), ctypes.byref(sh), ctypes.byref(o),
-            _stream_handle(stream))
-    else:
-        rc = nat.lib().paged_attn_decode(
-            *ptrs, ctypes.c_float(scale), ctypes.c_void_p(out.data_ptr()), ctypes.byref(sh),
-            ctypes.byref(o), _stream_handle(stream))
+    st = _stream_handle(stream, q.device)
+    with torch.cuda.device(q.device):  # the library launches on the current device
+        if fp8:
+            rc = nat.lib().paged_attn_decode_fp8(
+                *ptrs, ctypes.c_float(scale), ctypes.c_float(k_scale), ctypes.c_float(v_scale),
+                ctypes.c_void_p(out.data_ptr()), ctypes.byref(sh), ctypes.byref(o), st)
+        else:
+            rc = nat.lib().paged_attn_decode(
+                *ptrs, ctypes.c_float(scale), ctypes.c_void_p(out.data_ptr()),
+                ctypes.byref(sh), ctypes.byref(o), st)
     if rc != nat.PA_OK:
         raise RuntimeError(f"{name}: {nat.error_string(rc)} ({rc})")
     return out
@@ -229,10 +242,15 @@ def stream_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None,
     sink_bytes = int(nat.lib().paged_attn_stream_read_sink_bytes(nbytes))
     if sink is None:
         sink = torch.zeros(sink_bytes // 4, dtype=torch.int32, device=buf.device)
-    rc = nat.lib().paged_attn_stream_read(ctypes.c_void_p(buf.data_ptr()),
-                                          ctypes.c_size_t(nbytes),
-                                          ctypes.c_void_p(sink.data_ptr()),
-                                          _stream_handle(stream))
+    elif (not sink.is_contiguous() or sink.device != buf.device or
+          sink.numel() * sink.element_size() < sink_bytes):
+        raise ValueError(f"sink must be a contiguous tensor of at least {sink_bytes} bytes "
+                         f"on {buf.device}")
+    st = _stream_handle(stream, buf.device)
+    with torch.cuda.device(buf.device):
+        rc = nat.lib().paged_attn_stream_read(ctypes.c_void_p(buf.data_ptr()),
+                                              ctypes.c_size_t(nbytes),
+                                              ctypes.c_void_p(sink.data_ptr()), st)
     if rc != nat.PA_OK:
         raise RuntimeError(f"paged_attn_stream_read: {nat.error_string(rc)} ({rc})")
     return sink

@@ -32,11 +32,20 @@ def test_library_exports_every_declared_function(native_lib):
 
 
 def test_version_and_error_strings(native_lib):
-    assert native_lib.paged_attn_abi_version() == 4
+    assert native_lib.paged_attn_abi_version() == nat.ABI_VERSION == 4
     assert nat.error_string(0) == "ok"
     for code in range(1, 5):
         assert nat.error_string(code) not in ("ok", "unknown status")
     assert nat.error_string(99) == "unknown status"
+
+
+def test_a_library_of_another_abi_version_is_refused(native_lib, monkeypatch):
+    """A stale build would read the structs with another layout: the binding
+    refuses it instead of calling it."""
+    monkeypatch.setattr(nat, "_lib", None)
+    monkeypatch.setattr(nat, "ABI_VERSION", nat.ABI_VERSION + 1)
+    with pytest.raises(nat.NativeLibraryMissing, match="ABI version"):
+        nat.lib()
 
 
 def test_struct_layouts_match_header(native_lib, tmp_path):

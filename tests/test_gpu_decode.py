@@ -225,6 +225,9 @@ def test_stream_read_touches_every_word():
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32).reshape(-1, 4), axis=0)
     want = np.bitwise_xor.reduce(host.reshape(-1, 4), axis=0)
     assert np.array_equal(got, want)
+    # a sink smaller than one 16-byte word per work-group is refused before any launch
+    with pytest.raises(ValueError, match="sink"):
+        ops.stream_read(buf, sink[: sink.numel() // 2])
 
 
 def test_debug_variant_computes_the_same_bits():
