@@ -3,8 +3,8 @@
     python -m paged_kv_cache_226_amd.build
 
 Packed-FP32 instructions are disabled for all device code
-(-target-feature -packed-fp32-ops): the kernels are written with scalar
-float arithmetic only.
+(-target-feature -packed-fp32-ops): no kernel writes one by hand, and the
+flag keeps the compiler from forming them out of ordinary float code.
 """
 import os
 import subprocess
