@@ -195,14 +195,19 @@ def test_empty_contexts_give_zeros():
         assert_close(o[1:2], oracle(x)[1:2])
 
 
-def test_debug_error_word_flags_bad_inputs_without_faulting():
+@pytest.mark.parametrize("pf", MODES)
+def test_debug_error_word_flags_bad_inputs_without_faulting(pf):
+    """The checked variant clamps a block id outside the pool (above it or
+    negative) to block 0 before any load or copy of it, and a context
+    longer than the table to the table; both set the error word."""
     x = gen.make_case(2, 4, 2, [40, 20], seed=156, extra_pool_blocks=2)
     dev = to_device(x)
     bt = dev["block_tables"].clone()
     bt[0, 1] = x.k_cache.shape[0] + 1000  # outside the pool
+    bt[0, 2] = -7
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = ops.paged_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"], bt,
-                                dev["context_lens"], x.scale, debug_error_word=err)
+                                dev["context_lens"], x.scale, debug_error_word=err, prefetch=pf)
     torch.cuda.synchronize()
     assert int(err.item()) & 1
     assert torch.isfinite(out.float()).all()
@@ -210,7 +215,7 @@ def test_debug_error_word_flags_bad_inputs_without_faulting():
     ctx = dev["context_lens"].clone()
     ctx[1] = x.block_tables.shape[1] * 16 + 50  # beyond the table
     ops.paged_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"], ctx,
-                          x.scale, debug_error_word=err)
+                          x.scale, debug_error_word=err, prefetch=pf)
     torch.cuda.synchronize()
     assert int(err.item()) & 2
 

@@ -174,14 +174,16 @@ def test_fp8_trace_follows_the_lookahead_schedule(pf):
         assert (tr[b, :, nb:, :] == -1).all()
 
 
-def test_fp8_debug_error_word_flags_a_bad_block_id():
+@pytest.mark.parametrize("pf", MODES)
+def test_fp8_debug_error_word_flags_a_bad_block_id(pf):
     x8 = case8(2, 4, 2, [40, 20], seed=270, extra=2)
     dev = to_device8(x8)
     dev["block_tables"][0, 1] = x8.k8.shape[0] + 1000
+    dev["block_tables"][0, 2] = -7
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = ops.paged_attn_decode_fp8(dev["q"], dev["k_cache"], dev["v_cache"],
                                     dev["block_tables"], dev["context_lens"], x8.scale,
-                                    x8.k_scale, x8.v_scale, debug_error_word=err)
+                                    x8.k_scale, x8.v_scale, debug_error_word=err, prefetch=pf)
     torch.cuda.synchronize()
     assert int(err.item()) & 1
     assert torch.isfinite(out.float()).all()
