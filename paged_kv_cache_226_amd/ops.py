@@ -22,10 +22,10 @@ def _stream_handle(stream: Optional[torch.cuda.Stream], device: torch.device) ->
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _same_device(device: torch.device, **tensors):
+def _same_device(index: int, **tensors):
     for name, t in tensors.items():
-        if t is not None and t.device != device:
-            raise ValueError(f"{name} is on {t.device}, q on {device}")
+        if t is not None and t.get_device() != index:
+            raise ValueError(f"{name} is on {t.device}, q on cuda:{index}")
 
 
 def _check(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int):
@@ -125,61 +125,126 @@ def _check_kv(t: torch.Tensor, name: str, fp8: bool, ndim: int):
                          "contiguous")
 
 
-def _decode(fp8: bool, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
-            v_scale, out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
-            seq_order, structure, workspace, debug_gather_k, debug_trace, debug_error_word,
-            stream):
-    name = "paged_attn_decode_fp8" if fp8 else "paged_attn_decode"
-    _check(q, "q", torch.float16, 3)
-    _check_kv(k_cache, "k_cache", fp8, 5)
-    _check_kv(v_cache, "v_cache", fp8, 4)
-    _check(block_tables, "block_tables", torch.int32, 2)
-    _check(context_lens, "context_lens", torch.int32, 1)
-    NB, Hkv, NG, T, X = k_cache.shape
-    B, Hq, D = q.shape
-    if tuple(v_cache.shape) != (NB, Hkv, T, NG * X) or NG * X != D or X != (16 if fp8 else 8):
-        raise ValueError("k_cache must be [NB, Hkv, D/%d, T, %d] and v_cache [NB, Hkv, T, D]"
-                         % ((16, 16) if fp8 else (8, 8)))
-    if block_tables.shape[0] != B or context_lens.shape[0] != B:
-        raise ValueError("inconsistent shapes")
-    _same_device(q.device, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
-                 context_lens=context_lens, out=out, workspace=workspace,
-                 debug_gather_k=debug_gather_k, debug_trace=debug_trace,
-                 debug_error_word=debug_error_word)
-    if scale is None:
-        scale = D ** -0.5
-    if out is None:
-        out = torch.empty_like(q)
-    else:
-        _check(out, "out", torch.float16, 3)
-        if out.shape != q.shape:
-            raise ValueError("out must have q's shape")
-    sh = shape_of(q, k_cache, block_tables, v_cache)
-    o = options(prefetch, partition_blocks, waves_per_wg, prefetch_distance, seq_order,
-                structure, debug_gather_k, debug_trace, debug_error_word)
-    need = int(nat.lib().paged_attn_workspace_size(ctypes.byref(sh), ctypes.byref(o)))
-    if need:
-        if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-        elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:
-            raise ValueError(f"workspace needs {need} bytes")
-        o.workspace = workspace.data_ptr()
-        o.workspace_bytes = workspace.numel() * workspace.element_size()
-    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (q, k_cache, v_cache, block_tables,
-                                                      context_lens)]
-    st = _stream_handle(stream, q.device)
-    with torch.cuda.device(q.device):  # the library launches on the current device
-        if fp8:
-            rc = nat.lib().paged_attn_decode_fp8(
-                *ptrs, ctypes.c_float(scale), ctypes.c_float(k_scale), ctypes.c_float(v_scale),
-                ctypes.c_void_p(out.data_ptr()), ctypes.byref(sh), ctypes.byref(o), st)
+class DecodeCall:
+    """One decode call, validated and marshalled once.
+
+    Calling it runs the step again on the same tensors, whose contents may
+    change between calls (their storage and shapes may not); it allocates
+    nothing and costs one C call, about what a C caller of the library pays.
+    The stream is the one given, or the device's current stream when the
+    call was prepared.  Calls on one DecodeCall must not overlap (they share
+    its workspace)."""
+
+    def __init__(self, fp8: bool, q, k_cache, v_cache, block_tables, context_lens, scale,
+                 k_scale, v_scale, out, prefetch, partition_blocks, waves_per_wg,
+                 prefetch_distance, seq_order, structure, workspace, debug_gather_k,
+                 debug_trace, debug_error_word, stream):
+        self.name = "paged_attn_decode_fp8" if fp8 else "paged_attn_decode"
+        _check(q, "q", torch.float16, 3)
+        _check_kv(k_cache, "k_cache", fp8, 5)
+        _check_kv(v_cache, "v_cache", fp8, 4)
+        _check(block_tables, "block_tables", torch.int32, 2)
+        _check(context_lens, "context_lens", torch.int32, 1)
+        NB, Hkv, NG, T, X = k_cache.shape
+        B, Hq, D = q.shape
+        if tuple(v_cache.shape) != (NB, Hkv, T, NG * X) or NG * X != D or X != (16 if fp8 else 8):
+            raise ValueError("k_cache must be [NB, Hkv, D/%d, T, %d] and v_cache [NB, Hkv, T, D]"
+                             % ((16, 16) if fp8 else (8, 8)))
+        if block_tables.shape[0] != B or context_lens.shape[0] != B:
+            raise ValueError("inconsistent shapes")
+        self.device = q.device
+        self._index = q.get_device()
+        _same_device(self._index, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
+                     context_lens=context_lens, out=out, workspace=workspace,
+                     debug_gather_k=debug_gather_k, debug_trace=debug_trace,
+                     debug_error_word=debug_error_word)
+        if scale is None:
+            scale = D ** -0.5
+        if out is None:
+            out = torch.empty_like(q)
         else:
-            rc = nat.lib().paged_attn_decode(
-                *ptrs, ctypes.c_float(scale), ctypes.c_void_p(out.data_ptr()),
-                ctypes.byref(sh), ctypes.byref(o), st)
-    if rc != nat.PA_OK:
-        raise RuntimeError(f"{name}: {nat.error_string(rc)} ({rc})")
-    return out
+            _check(out, "out", torch.float16, 3)
+            if out.shape != q.shape:
+                raise ValueError("out must have q's shape")
+        self._shape = shape_of(q, k_cache, block_tables, v_cache)
+        self._opts = options(prefetch, partition_blocks, waves_per_wg, prefetch_distance,
+                             seq_order, structure, debug_gather_k, debug_trace,
+                             debug_error_word)
+        L = nat.lib()
+        need = int(L.paged_attn_workspace_size(ctypes.byref(self._shape),
+                                               ctypes.byref(self._opts)))
+        if need:
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:
+                raise ValueError(f"workspace needs {need} bytes")
+            self._opts.workspace = workspace.data_ptr()
+            self._opts.workspace_bytes = workspace.numel() * workspace.element_size()
+        self.out, self.workspace = out, workspace
+        # the tensors whose storage the call reads or writes stay alive with it
+        self._keep = (q, k_cache, v_cache, block_tables, context_lens, debug_gather_k,
+                      debug_trace, debug_error_word)
+        ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (q, k_cache, v_cache, block_tables,
+                                                          context_lens)]
+        st = _stream_handle(stream, q.device)
+        if fp8:
+            self._fn = L.paged_attn_decode_fp8
+            self._args = (*ptrs, ctypes.c_float(scale), ctypes.c_float(k_scale),
+                          ctypes.c_float(v_scale), ctypes.c_void_p(out.data_ptr()),
+                          ctypes.byref(self._shape), ctypes.byref(self._opts), st)
+        else:
+            self._fn = L.paged_attn_decode
+            self._args = (*ptrs, ctypes.c_float(scale), ctypes.c_void_p(out.data_ptr()),
+                          ctypes.byref(self._shape), ctypes.byref(self._opts), st)
+
+    def __call__(self) -> torch.Tensor:
+        if torch.cuda.current_device() == self._index:
+            rc = self._fn(*self._args)
+        else:
+            with torch.cuda.device(self._index):  # the library launches on the current device
+                rc = self._fn(*self._args)
+        if rc != nat.PA_OK:
+            raise RuntimeError(f"{self.name}: {nat.error_string(rc)} ({rc})")
+        return self.out
+
+
+def prepare_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   block_tables: torch.Tensor, context_lens: torch.Tensor,
+                   scale: Optional[float] = None, out: Optional[torch.Tensor] = None, *,
+                   prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0,
+                   prefetch_distance: int = 0, seq_order: int = 0, structure: int = 0,
+                   workspace: Optional[torch.Tensor] = None,
+                   debug_gather_k: Optional[torch.Tensor] = None,
+                   debug_trace: Optional[torch.Tensor] = None,
+                   debug_error_word: Optional[torch.Tensor] = None,
+                   stream: Optional[torch.cuda.Stream] = None) -> DecodeCall:
+    """paged_attn_decode prepared for repeated calls on the same tensors."""
+    return DecodeCall(False, q, k_cache, v_cache, block_tables, context_lens, scale, 1.0, 1.0,
+                      out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
+                      seq_order, structure, workspace, debug_gather_k, debug_trace,
+                      debug_error_word, stream)
+
+
+def prepare_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       block_tables: torch.Tensor, context_lens: torch.Tensor,
+                       scale: Optional[float] = None, k_scale: float = 1.0,
+                       v_scale: float = 1.0, out: Optional[torch.Tensor] = None, *,
+                       prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0,
+                       prefetch_distance: int = 0, seq_order: int = 0, structure: int = 0,
+                       workspace: Optional[torch.Tensor] = None,
+                       debug_gather_k: Optional[torch.Tensor] = None,
+                       debug_trace: Optional[torch.Tensor] = None,
+                       debug_error_word: Optional[torch.Tensor] = None,
+                       stream: Optional[torch.cuda.Stream] = None) -> DecodeCall:
+    """paged_attn_decode_fp8 prepared for repeated calls on the same tensors."""
+    if k_cache.dtype == torch.float8_e4m3fn:
+        k_cache = k_cache.view(torch.uint8)
+    if v_cache.dtype == torch.float8_e4m3fn:
+        v_cache = v_cache.view(torch.uint8)
+    return DecodeCall(True, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+                      v_scale, out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
+                      seq_order, structure, workspace, debug_gather_k, debug_trace,
+                      debug_error_word, stream)
 
 
 def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -198,9 +263,12 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     dims); v_cache [NB, Hkv, 16, 128] fp16 (token, dim); block_tables [B, MB]
     int32; context_lens [B] int32; scale defaults to 1/sqrt(128).
     """
-    return _decode(False, q, k_cache, v_cache, block_tables, context_lens, scale, 1.0, 1.0,
-                   out, prefetch, partition_blocks, waves_per_wg, prefetch_distance, seq_order,
-                   structure, workspace, debug_gather_k, debug_trace, debug_error_word, stream)
+    return prepare_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                          prefetch=prefetch, partition_blocks=partition_blocks,
+                          waves_per_wg=waves_per_wg, prefetch_distance=prefetch_distance,
+                          seq_order=seq_order, structure=structure, workspace=workspace,
+                          debug_gather_k=debug_gather_k, debug_trace=debug_trace,
+                          debug_error_word=debug_error_word, stream=stream)()
 
 
 def paged_attn_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -222,14 +290,13 @@ def paged_attn_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
     [NB, Hkv, 16, 128] (token, dim); the rest as paged_attn_decode.
     debug_gather_k receives the widened K values before k_scale (fp16).
     """
-    if k_cache.dtype == torch.float8_e4m3fn:
-        k_cache = k_cache.view(torch.uint8)
-    if v_cache.dtype == torch.float8_e4m3fn:
-        v_cache = v_cache.view(torch.uint8)
-    return _decode(True, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
-                   v_scale, out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
-                   seq_order, structure, workspace, debug_gather_k, debug_trace,
-                   debug_error_word, stream)
+    return prepare_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+                              v_scale, out, prefetch=prefetch,
+                              partition_blocks=partition_blocks, waves_per_wg=waves_per_wg,
+                              prefetch_distance=prefetch_distance, seq_order=seq_order,
+                              structure=structure, workspace=workspace,
+                              debug_gather_k=debug_gather_k, debug_trace=debug_trace,
+                              debug_error_word=debug_error_word, stream=stream)()
 
 
 def stream_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None,
