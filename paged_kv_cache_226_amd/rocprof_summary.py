@@ -2,17 +2,22 @@
 
     python -m paged_kv_cache_226_amd.rocprof_summary --workload llama2_7b \
         [--kv-dtype fp16|fp8] \
-        --kernel-trace DIR [--fetch DIR --write DIR --tcc DIR --sq DIR] \
+        --kernel-trace DIR [--fetch DIR --write DIR --tcc DIR --sq DIR --valu DIR] \
         --command "..." --out-dir profiles
+    python -m paged_kv_cache_226_amd.rocprof_summary --workload llama2_7b \
+        --sweep-profile SWEEP.jsonl --fetch DIR --out-dir profiles
 
 Inputs are the directories rocprofv3 wrote with `--output-format csv`
 (`*_kernel_stats.csv`, `*_counter_collection.csv`).  Writes (the tag is the
 workload name, with `_fp8` appended for E4M3 caches):
   pa_decode_<tag>_kernel_trace.md   per-kernel durations
   pa_decode_<tag>_counters.md       per prefetch mode: HBM bytes, L2 hit
-                                         rate, stall share, instructions
+                                         rate, stall share, instructions,
+                                         VALU busy, MFMA utilisation
   pa_decode_<tag>_traffic.txt       HBM bytes per launch, read by bench.py
                                          while the kernel sources are unchanged
+  pa_decode_sweep_<workload>_fetch.md  HBM read bytes per point of the
+                                         batch x context sweep
 
 FETCH_SIZE and WRITE_SIZE are scaled by what the same counters read for
 kernels of known size in the same process (bench.py --profile runs a 1 GiB
