@@ -87,12 +87,19 @@ def test_pool_offsets_beyond_4_gib(fp8):
                                           x8.scale, x8.k_scale, x8.v_scale)
     else:
         ref = oracle(x)
-    # the LDS ring's copies address the same far blocks (same plan: 4 waves)
-    others = [dec(prefetch=4, prefetch_distance=dist) for dist in (1, 2)]
+    # the LDS ring's copies address the same far blocks; against the register
+    # ring on the LDS ring's own plan (its slots may rule out 8 waves)
+    pairs = []
+    for dist in (1, 2):
+        p = ops.plan(q, kp, btd, prefetch=4, prefetch_distance=dist)
+        same = dict(waves_per_wg=p["waves_per_wg"], partition_blocks=p["partition_blocks"],
+                    prefetch_distance=dist)
+        pairs.append((dist, dec(prefetch=4, **same), dec(prefetch=2, **same)))
     torch.cuda.synchronize()
     got = out.cpu().numpy()
-    for dist, o in zip((1, 2), others):
-        assert np.array_equal(bits(o.cpu().numpy()), bits(got)), f"LDS ring, distance {dist}"
-    del kp, vp, others
+    for dist, lds, reg in pairs:
+        assert np.array_equal(bits(lds.cpu().numpy()), bits(reg.cpu().numpy())), \
+            f"LDS ring, distance {dist}"
+    del kp, vp, pairs
     torch.cuda.empty_cache()
     assert_close(got, ref, f"offsets > 4 GiB fp8={fp8}")
