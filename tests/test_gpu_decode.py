@@ -265,6 +265,18 @@ def test_longest_first_order_changes_no_bits(pb, waves):
     assert p["seq_order"] == 1
 
 
+@pytest.mark.parametrize("lens", [[300] * 9, [300] * 4 + [301] + [300] * 4, [16] * 3 + [1]])
+def test_ranking_of_uniform_and_nearly_uniform_batches(lens):
+    """Equal block counts take the identity shortcut; one different count
+    takes the full ranking.  Either way the order changes no bit."""
+    x = gen.make_case(len(lens), 8, 2, lens, seed=158, extra_pool_blocks=2)
+    dev = to_device(x)
+    nat_ = run(x, dev, seq_order=1)
+    lpt = run(x, dev, seq_order=2)
+    assert np.array_equal(bits(lpt), bits(nat_))
+    assert_close(lpt, oracle(x), f"lens={lens}")
+
+
 @pytest.mark.parametrize("waves,pb", [(1, 0), (2, 3), (4, 0), (4, 5), (8, 0), (4, 1024)])
 def test_rings_change_no_bits(waves, pb):
     """The register ring two blocks ahead and the LDS ring one and two blocks
