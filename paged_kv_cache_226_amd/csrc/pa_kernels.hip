@@ -102,6 +102,13 @@ __device__ __forceinline__ u32x4 widen_fp8x8(uint32_t w0, uint32_t w1) {
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true))};
 }
 
+// Bytes 0-1 (HIGH false) or 2-3 (HIGH true) of an E4M3 dword widened to an
+// fp16 pair, lowest byte in the low half (exact, like widen_fp8x8).
+template <bool HIGH>
+__device__ __forceinline__ uint32_t widen_fp8x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HIGH));
+}
+
 // Pointers of the direct global-to-LDS copy; its cache policy is
 // non-temporal, like the direct loads.
 typedef __attribute__((address_space(1))) const void gbyte;
@@ -221,14 +228,16 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
   // copy a look-ahead buffer, a copy that would wait for its loads early.
   auto compute = [&](Buf& buf, int j, auto may_tail) {
     constexpr bool MayTail = decltype(may_tail)::value;
-    // fp16 operands: K chunks and V rows
+    // fp16 operands: K chunks and V rows (an E4M3 V stays in bytes until the
+    // P.V operands are built)
     u32x4 kh[4], vh[4];
+    u32x2 vb[4];
     if constexpr (KV8) {
 #pragma unroll
       for (int ch = 0; ch < 4; ++ch)
         kh[ch] = widen_fp8x8(buf.k[ch >> 1][2 * (ch & 1)], buf.k[ch >> 1][2 * (ch & 1) + 1]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vh[i] = widen_fp8x8(buf.v[i].x, buf.v[i].y);
+      for (int i = 0; i < 4; ++i) vb[i] = buf.v[i];
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -245,10 +254,16 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
     }
     const int rem = ctx - j * kT;  // valid tokens in this block, >= 1
     const bool tail = MayTail && rem < kT;
-    if (tail) {
+    if (tail) {  // tokens past the context: V zero (E4M3 0 widens to +0)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * i + lg >= rem) vh[i] = u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < 4; ++i) {
+        if (4 * i + lg >= rem) {
+          if constexpr (KV8)
+            vb[i] = u32x2{0u, 0u};
+          else
+            vh[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
     }
     // scores of tokens 4q+lg for head c
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
@@ -284,15 +299,35 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
       phi[q] = (_Float16)pr[q];
       plo[q] = (_Float16)(pr[q] - (float)phi[q]);
     }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int u = t >> 1, h = t & 1;
-      u32x2 vt;
-      vt.x = pick_halves(vh[0][u], vh[1][u], h);
-      vt.y = pick_halves(vh[2][u], vh[3][u], h);
-      const half4_t av = __builtin_bit_cast(half4_t, vt);
+    // Tile t takes dim t (of this lane's 8) of tokens 0..3 of the lane group:
+    // (token 0, token 1) in the low dword, (token 2, token 3) in the high.
+    auto pv_tile = [&](int t, uint32_t lo, uint32_t hi) {
+      const half4_t av = __builtin_bit_cast(half4_t, u32x2{lo, hi});
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, phi, acc[t], 0, 0, 0);
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, plo, acc[t], 0, 0, 0);
+    };
+    if constexpr (KV8) {
+      // One byte permute puts dims t and t+1 of two tokens in token order
+      // (t0.d, t1.d, t0.d+1, t1.d+1), so each conversion yields a tile's
+      // pair directly: 8 permutes and 16 conversions per block instead of
+      // widening every row (16) and then permuting the halves (16).
+#pragma unroll
+      for (int t = 0; t < 8; t += 2) {
+        const int b0 = t & 3;
+        const uint32_t sel = b0 | (4 + b0) << 8 | (b0 + 1) << 16 | (5 + b0) << 24;
+        const uint32_t w01 = __builtin_amdgcn_perm(t < 4 ? vb[1].x : vb[1].y,
+                                                   t < 4 ? vb[0].x : vb[0].y, sel);
+        const uint32_t w23 = __builtin_amdgcn_perm(t < 4 ? vb[3].x : vb[3].y,
+                                                   t < 4 ? vb[2].x : vb[2].y, sel);
+        pv_tile(t, widen_fp8x2<false>(w01), widen_fp8x2<false>(w23));
+        pv_tile(t + 1, widen_fp8x2<true>(w01), widen_fp8x2<true>(w23));
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int u = t >> 1, h = t & 1;
+        pv_tile(t, pick_halves(vh[0][u], vh[1][u], h), pick_halves(vh[2][u], vh[3][u], h));
+      }
     }
   };
 
