@@ -258,14 +258,7 @@ def main():
         d["v_cache"] = torch.from_numpy(x.v_cache).to(dev)
     if args.kv_layout == "adjacent":
         # one pool [block][head][K slice | V slice]; K and V are strided views
-        kc, vc = d["k_cache"], d["v_cache"]
-        NBp, Hp = kc.shape[:2]
-        pool = torch.empty((NBp, Hp, 2, kc[0, 0].numel()), dtype=kc.dtype, device=dev)
-        pool[:, :, 0] = kc.reshape(NBp, Hp, -1)
-        pool[:, :, 1] = vc.reshape(NBp, Hp, -1)
-        d["k_cache"] = pool[:, :, 0].view(kc.shape)
-        d["v_cache"] = pool[:, :, 1].view(vc.shape)
-        del kc, vc
+        d["k_cache"], d["v_cache"] = gen.side_by_side(d["k_cache"], d["v_cache"])
     out = torch.empty_like(d["q"])
     Hkv = x.k_cache.shape[1]
     kv_bytes = acc.step_kv_bytes(Hkv, 128, x.context_lens, elem_bytes=1 if fp8 else 2)

@@ -336,6 +336,24 @@ def make_case_device(num_seqs: int, num_q_heads: int, num_kv_heads: int, context
     return dict(q=q, k_cache=k, v_cache=v, block_tables=bt, context_lens=ctx, scale=scale)
 
 
+def side_by_side(k_cache, v_cache):
+    """Device views (k, v) into one new pool [NB][Hkv][2][slice] in which
+    each (block, KV head)'s K slice is followed by its V slice; the values
+    are copied from the given dense caches (K in the kernel's packed layout,
+    V token-major, fp16 or E4M3 bytes).  The views keep the dense shapes and
+    carry the pool's block and head strides."""
+    import torch
+
+    NB, H = k_cache.shape[:2]
+    n = k_cache[0, 0].numel()
+    if v_cache.shape[:2] != k_cache.shape[:2] or v_cache[0, 0].numel() != n:
+        raise ValueError("K and V caches must have the same pool shape and slice size")
+    pool = torch.empty((NB, H, 2, n), dtype=k_cache.dtype, device=k_cache.device)
+    pool[:, :, 0] = k_cache.reshape(NB, H, n)
+    pool[:, :, 1] = v_cache.reshape(NB, H, n)
+    return pool[:, :, 0].view(k_cache.shape), pool[:, :, 1].view(v_cache.shape)
+
+
 def host_subset(dev_case: Dict[str, object], seqs: Sequence[int]) -> PagedInputs:
     """Copy the given sequences of a device case back to the host as a small
     PagedInputs (their blocks only, renumbered, K unpacked to token-major),

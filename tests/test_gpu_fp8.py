@@ -236,6 +236,16 @@ def test_fp8_workload_sampled_rows(name):
         reg = dec(prefetch=2, **same)
         torch.cuda.synchronize()
         assert torch.equal(lds.view(torch.int16), reg.view(torch.int16)), f"lds vs reg {same}"
+    # the bench's launch: K and V side by side in one pool, prepared call
+    ks, vs = gen.side_by_side(dev["k_cache"], dev["v_cache"])
+    bench_out = torch.empty_like(out)
+    call = ops.prepare_decode_fp8(dev["q"], ks, vs, dev["block_tables"], dev["context_lens"],
+                                  x8.scale, x8.k_scale, x8.v_scale, bench_out)
+    call()
+    call()
+    torch.cuda.synchronize()
+    assert torch.equal(bench_out.view(torch.int16), out.view(torch.int16)), "side-by-side pool"
+    del ks, vs, call, bench_out
     got, got_lds = out.cpu().numpy(), lds.cpu().numpy()
     del dev, out, lds, reg
     rows = sample_rows(x8, 48, seed=len(name) + 1)

@@ -107,3 +107,17 @@ def test_fp8_pack_and_quantize():
     ref = x.k_cache.astype(np.float64)
     big = np.abs(ref) > 2.0 ** -6 * x8.k_scale * 8
     assert (np.abs(deq - ref)[big] <= np.abs(ref)[big] * 2.0 ** -4 + 1e-12).all()
+
+
+def test_side_by_side_pool_views():
+    import torch
+
+    for dt in (torch.float16, torch.uint8):
+        k = (torch.arange(3 * 2 * 16 * 16 * 8) % 251).to(dt).reshape(3, 2, 16, 16, 8)
+        v = (torch.arange(3 * 2 * 16 * 128) % 241).to(dt).reshape(3, 2, 16, 128)
+        ks, vs = gen.side_by_side(k, v)
+        assert ks.shape == k.shape and vs.shape == v.shape
+        assert torch.equal(ks, k) and torch.equal(vs, v)
+        n = 16 * 128
+        assert ks.stride()[:2] == (2 * 2 * n, 2 * n) and vs.stride()[:2] == (2 * 2 * n, 2 * n)
+        assert vs.data_ptr() - ks.data_ptr() == n * k.element_size()
