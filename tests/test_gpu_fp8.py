@@ -206,7 +206,7 @@ def test_fp8_repeated_runs_are_bitwise_identical():
         assert np.array_equal(bits(run8(x8, dev)), bits(first))
 
 
-@pytest.mark.parametrize("name", ["llama2_7b", "llama3_8b", "qwen25_14b"])
+@pytest.mark.parametrize("name", ["llama2_7b", "llama3_8b", "qwen25_7b", "qwen25_14b"])
 def test_fp8_workload_sampled_rows(name):
     from test_gpu_workloads import sample_rows
 
