@@ -204,6 +204,7 @@ def main(argv=None):
         hit, miss = per_mode(tcc, "TCC_HIT"), per_mode(tcc, "TCC_MISS")
         sq = counters(a.sq) if a.sq else {}
         wait, wcyc = per_mode(sq, "SQ_WAIT_INST_ANY"), per_mode(sq, "SQ_WAVE_CYCLES")
+        wait_any = per_mode(sq, "SQ_WAIT_ANY")
         valu, waves = per_mode(sq, "SQ_INSTS_VALU"), per_mode(sq, "SQ_WAVES")
         vmem = per_mode(sq, "SQ_INSTS_VMEM_RD")
         va = counters(a.valu) if a.valu else {}
@@ -217,11 +218,17 @@ def main(argv=None):
                  "VALU busy = 100 * SQ_ACTIVE_INST_VALU / 256 CUs / GRBM_GUI_ACTIVE "
                  "(rocprofv3's VALUBusy); MFMA util = 100 * SQ_VALU_MFMA_BUSY_CYCLES / "
                  "(GRBM_GUI_ACTIVE * 1024 SIMDs) (its MfmaUtil); cycles / instruction = "
-                 "4 * SQ_WAVE_CYCLES / SQ_INSTS (per wave).", "",
+                 "4 * SQ_WAVE_CYCLES / SQ_INSTS (per wave); stall cycles / instruction = "
+                 "4 * SQ_WAIT_INST_ANY / SQ_INSTS (cycles a wave waits per instruction it "
+                 "issues; the two counters come from different passes over the same launches); "
+                 "wait share = SQ_WAIT_ANY / SQ_WAVE_CYCLES (waiting for anything, "
+                 "s_waitcnt included).",
+                 "",
                  "| mode | HBM read bytes | read / algorithmic | HBM write bytes | L2 hit rate |"
                  " stall share (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES) | VALU insts / wave |"
-                 " VMEM reads / wave | VALU busy | MFMA util | cycles / instruction |",
-                 "|---|---|---|---|---|---|---|---|---|---|---|"]
+                 " VMEM reads / wave | VALU busy | MFMA util | cycles / instruction |"
+                 " stall cycles / instruction | wait share (SQ_WAIT_ANY / SQ_WAVE_CYCLES) |",
+                 "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
         traffic = {}
         for m in sorted(fetch):
             rb = fetch[m] * 1024 * fk if fk else float("nan")
@@ -235,9 +242,11 @@ def main(argv=None):
             vb = 100 * v_act.get(m, float("nan")) / 256 / gui if gui else float("nan")
             mu = 100 * v_mfma.get(m, float("nan")) / (gui * 1024) if gui else float("nan")
             cpi = 4 * v_wcyc[m] / v_insts[m] if v_insts.get(m) and m in v_wcyc else float("nan")
+            spi = 4 * wait[m] / v_insts[m] if v_insts.get(m) and m in wait else float("nan")
+            wa = wait_any[m] / wcyc[m] if m in wait_any and wcyc.get(m) else float("nan")
             lines.append(f"| {MODE_NAMES[m]} | {rb:.4g} | {rb / kv:.4f} | {wb:.4g} | "
                          f"{100 * hr:.2f} % | {100 * st:.1f} % | {vw:.0f} | {mw:.0f} | "
-                         f"{vb:.1f} % | {mu:.1f} % | {cpi:.1f} |")
+                         f"{vb:.1f} % | {mu:.1f} % | {cpi:.1f} | {spi:.1f} | {100 * wa:.1f} % |")
         with open(os.path.join(a.out_dir, f"pa_decode_{tag}_counters.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
         with open(os.path.join(a.out_dir, f"pa_decode_{tag}_traffic.txt"), "w") as f:
