@@ -178,6 +178,23 @@ def test_block_placement_invariance_bitwise():
     assert np.array_equal(bits(run(x)), bits(a))
 
 
+def test_sequences_sharing_prefix_blocks():
+    """Several block-table rows name the same physical blocks (a shared
+    prompt prefix, the PagedAttention answer's shared pages).  The kernel only
+    reads the pool, so sharing needs nothing special: every row must match
+    the oracle, and two sequences with the same query over the same shared
+    blocks must give the same bits."""
+    x = gen.make_case(4, 8, 2, [80, 80, 200, 300], seed=156, extra_pool_blocks=4)
+    for b in (1, 2, 3):
+        x.block_tables[b, :5] = x.block_tables[0, :5]  # an 80-token shared prefix
+    x.q[1] = x.q[0]
+    ref = oracle(x)
+    for pf in MODES:
+        o = run(x, prefetch=pf)
+        assert_close(o, ref, f"shared prefix pf={pf}")
+        assert np.array_equal(bits(o[1]), bits(o[0]))
+
+
 def test_repeated_runs_are_bitwise_identical():
     x = gen.make_case(4, 32, 8, [900, 33, 4000, 129], seed=154)
     dev = to_device(x)

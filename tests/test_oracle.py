@@ -88,6 +88,29 @@ def test_matches_sdpa_on_scattered_pool(seed, B, Hq, Hkv, lens):
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
 
 
+def test_shared_prefix_blocks_match_sdpa_on_the_concatenated_history():
+    """Table rows that name the same physical blocks (a shared prefix): each
+    sequence attends to the prefix's K/V followed by its own, as dense SDPA
+    over the concatenated history gives."""
+    q, kp, vp, bt, ctx, kc, vc = scatter_case(30, 3, 4, 2, [32, 20, 45])
+    # sequences 1 and 2 take sequence 0's two blocks as their first two
+    # blocks; their own blocks move up by two table slots
+    NB = kp.shape[0]
+    bt2 = np.full((3, bt.shape[1] + 2), -1, np.int32)
+    bt2[0, :2] = bt[0, :2]
+    kc2, vc2, lens2 = [kc[0]], [vc[0]], [32]
+    for b in (1, 2):
+        nb = -(-int(ctx[b]) // T)
+        bt2[b, :2] = bt[0, :2]
+        bt2[b, 2:2 + nb] = bt[b, :nb]
+        kc2.append(np.concatenate([kc[0], kc[b]], axis=1))
+        vc2.append(np.concatenate([vc[0], vc[b]], axis=1))
+        lens2.append(32 + int(ctx[b]))
+    assert bt2.max() < NB
+    got = orc.paged_attention_f64(q, kp, vp, bt2, np.asarray(lens2, np.int32), SCALE)
+    np.testing.assert_allclose(got, sdpa_ref(q, kc2, vc2, SCALE), rtol=0, atol=1e-12)
+
+
 def test_small_head_dim_and_block_size():
     """The definition does not depend on D = 128, T = 16."""
     q, kp, vp, bt, ctx, kc, vc = scatter_case(20, 2, 6, 3, [9, 23], d=8, t=4)
