@@ -65,6 +65,36 @@ constexpr int kRec = kD + 2;                  // merge record: m, l, o[128]
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Cross-lane steps of the reductions over a column's four lane groups
+// (rows of 16 lanes).  v_permlane16_swap exchanges rows 1 and 3 of its first
+// operand with rows 0 and 2 of its second, v_permlane32_swap the upper half
+// of the first with the lower half of the second.  With x in both operands,
+// the pair then holds x of lane l and of lane l ^ 16 (l ^ 32), and f of the
+// pair is f(x, x ^ 16) on every lane.  Both are VALU instructions (no LDS
+// crossbar); f is commutative here, so the order within the pair does not
+// matter and the result is bitwise that of f(x, __shfl_xor(x, 16)).
+template <typename F>
+__device__ __forceinline__ float xor16_combine(float x, F f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return f(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+template <typename F>
+__device__ __forceinline__ float xor32_combine(float x, F f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return f(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float fmax2(float a, float b) { return fmaxf(a, b); }
+__device__ __forceinline__ float fadd2(float a, float b) { return a + b; }
+// max / sum over the 4 lanes l, l ^ 16, l ^ 32, l ^ 48
+__device__ __forceinline__ float column_max(float x) {
+  return xor32_combine(xor16_combine(x, fmax2), fmax2);
+}
+__device__ __forceinline__ float column_sum(float x) {
+  return xor32_combine(xor16_combine(x, fadd2), fadd2);
+}
+
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
@@ -280,8 +310,7 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
         if (4 * q + lg >= rem) sc[q] = -INFINITY;
     }
     float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    bm = column_max(bm);
     const float m_new = fmaxf(m, bm);  // finite: every block has a valid token
     const float alpha = fast_exp2(m - m_new);
     float pr[4];
@@ -564,8 +593,7 @@ __device__ __forceinline__ void walk_range(const DecodeArgs& a, const int b, con
   if (a.sink_enable && sink == 0x9E3779B9u && lane == 0) a.sink[0] = (int32_t)sink;
 
   // ---- merge: the 4 lanes of a column, then the W waves through LDS -------
-  float lt = l + __shfl_xor(l, 16);
-  lt += __shfl_xor(lt, 32);
+  const float lt = column_sum(l);
   if (c < G) {
     float* rec = merge_s + (wave * G + c) * kRec;
     if (lg == 0) {
@@ -655,8 +683,7 @@ __device__ __forceinline__ void walk_two_loop(const DecodeArgs& a, const int b, 
       bm = fmaxf(bm, sc);
       if (c < G) logit_s[((j - s) * kT + 4 * q + lg) * G + c] = sc;
     }
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    bm = column_max(bm);
     m = fmaxf(m, bm);
   };
   if constexpr (PF >= 2) {
@@ -768,8 +795,7 @@ __device__ __forceinline__ void walk_two_loop(const DecodeArgs& a, const int b, 
   if (a.sink_enable && sink == 0x9E3779B9u && lane == 0) a.sink[0] = (int32_t)sink;
 
   // ---- records: the same layout as walk_range ------------------------------
-  float lt = l + __shfl_xor(l, 16);
-  lt += __shfl_xor(lt, 32);
+  const float lt = column_sum(l);
   if (c < G) {
     float* rec = merge_s + (wave * G + c) * kRec;
     if (lg == 0) {
