@@ -64,9 +64,9 @@ def profile_tag(workload: str, kv_dtype: str) -> str:
     return workload if kv_dtype == "fp16" else f"{workload}_{kv_dtype}"
 
 
-def read_traffic(workload: str, mode_name: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+def _profile_figures(workload: str):
+    """key: value pairs of the committed rocprofv3 summary of this workload,
+    if it was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", f"pa_decode_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -77,8 +77,32 @@ def read_traffic(workload: str, mode_name: str):
             kv[k.strip()] = v.strip()
     if kv.get("kernel_source_hash") != kernel_source_hash():
         return None
+    return kv
+
+
+def read_traffic(workload: str, mode_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    kv = _profile_figures(workload)
     key = f"hbm_bytes_per_launch_{mode_name}"
-    return float(kv[key]) if key in kv else None
+    return float(kv[key]) if kv and key in kv else None
+
+
+def read_lookahead_counters(workload: str, mode_name: str):
+    """The look-ahead evidence of the committed counter summary (same
+    current-sources rule as the traffic): L2 hit rate and wait share
+    (SQ_WAIT_ANY / SQ_WAVE_CYCLES) with the look-ahead off, as an L2 touch,
+    and in the timed mode; None if absent."""
+    kv = _profile_figures(workload)
+    if not kv:
+        return None
+    out = {"source": f"profiles/pa_decode_{workload}_counters.md"}
+    for fig in ("l2_hit_rate", "wait_share"):
+        vals = {m: float(kv[f"{fig}_{m}"]) for m in ("off", "l2", mode_name)
+                if f"{fig}_{m}" in kv}
+        if vals:
+            out[fig] = {m: round(v, 4) for m, v in vals.items()}
+    return out if len(out) > 1 else None
 
 
 def parse():
@@ -379,6 +403,8 @@ def main():
     decode_only = plan["num_partitions"] == 1
     achieved = kv_bytes / us / 1e3
     traffic = read_traffic(profile_tag(args.workload, args.kv_dtype), mode_label)
+    lookahead_counters = read_lookahead_counters(profile_tag(args.workload, args.kv_dtype),
+                                                 mode_label)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": acc.HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / acc.HBM_PEAK_GBPS, 4),
                 "traffic": traffic, "kernel": "pa_decode_kernel" + ("" if decode_only else
@@ -425,6 +451,7 @@ def main():
         "stream_read_same_size_GBps": round(stream_same_gbps, 1),
         "pct_of_same_size_stream": round(100 * kv_bytes / us / 1e3 / stream_same_gbps, 1),
         "roofline": roofline,
+        "lookahead_counters": lookahead_counters,
         "kernel_source_hash": kernel_source_hash(),
         "inputs_sha256": {k: v[:16] for k, v in gen.digests(x).items()},
     }

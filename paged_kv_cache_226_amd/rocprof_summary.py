@@ -229,7 +229,7 @@ def main(argv=None):
                  " VMEM reads / wave | VALU busy | MFMA util | cycles / instruction |"
                  " stall cycles / instruction | wait share (SQ_WAIT_ANY / SQ_WAVE_CYCLES) |",
                  "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
-        traffic = {}
+        traffic, evidence = {}, {}
         for m in sorted(fetch):
             rb = fetch[m] * 1024 * fk if fk else float("nan")
             wb = write.get(m, float("nan")) * 1024 * (wk_copy or 1.0)
@@ -244,6 +244,7 @@ def main(argv=None):
             cpi = 4 * v_wcyc[m] / v_insts[m] if v_insts.get(m) and m in v_wcyc else float("nan")
             spi = 4 * wait[m] / v_insts[m] if v_insts.get(m) and m in wait else float("nan")
             wa = wait_any[m] / wcyc[m] if m in wait_any and wcyc.get(m) else float("nan")
+            evidence[m] = (hr, wa, st)
             lines.append(f"| {MODE_NAMES[m]} | {rb:.4g} | {rb / kv:.4f} | {wb:.4g} | "
                          f"{100 * hr:.2f} % | {100 * st:.1f} % | {vw:.0f} | {mw:.0f} | "
                          f"{vb:.1f} % | {mu:.1f} % | {cpi:.1f} | {spi:.1f} | {100 * wa:.1f} % |")
@@ -257,6 +258,13 @@ def main(argv=None):
             f.write(f"algorithmic_kv_bytes: {kv}\n")
             for m, v in sorted(traffic.items()):
                 f.write(f"hbm_bytes_per_launch_{MODE_NAMES[m]}: {v:.0f}\n")
+            # the look-ahead evidence per mode: L2 hit rate, wait share
+            # (SQ_WAIT_ANY / SQ_WAVE_CYCLES), issue-stall share
+            # (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES); fractions, nan if not taken
+            for m, (hr, wa, st) in sorted(evidence.items()):
+                f.write(f"l2_hit_rate_{MODE_NAMES[m]}: {hr:.4f}\n")
+                f.write(f"wait_share_{MODE_NAMES[m]}: {wa:.4f}\n")
+                f.write(f"issue_stall_share_{MODE_NAMES[m]}: {st:.4f}\n")
     return 0
 
 
