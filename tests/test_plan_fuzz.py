@@ -1,0 +1,80 @@
+"""Property test of the host-side planner over random shapes and options (CPU).
+
+Every (shape, options) either plans or is refused with a documented status,
+never anything else; an accepted plan always satisfies the invariants the
+kernels' launch relies on.  No device memory is touched.
+"""
+import ctypes
+
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from paged_kv_cache_226_amd import _native as nat
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib(native_lib):
+    return native_lib
+
+
+def raw_plan(shape, opts):
+    info = nat.PaPlanInfo()
+    rc = nat.lib().paged_attn_plan(ctypes.byref(shape), ctypes.byref(opts), ctypes.byref(info))
+    return rc, {f: getattr(info, f) for f, _ in nat.PaPlanInfo._fields_}
+
+
+shapes = st.tuples(
+    st.integers(1, 600),                    # num_seqs
+    st.sampled_from([1, 2, 4, 8, 16, 32]),  # num_kv_heads
+    st.integers(1, 20),                     # group size g (>16 must be refused)
+    st.integers(1, 5000),                   # max_blocks_per_seq
+    st.sampled_from([nat.KV_F16, nat.KV_E4M3]))
+options = st.tuples(
+    st.integers(-1, 5),                     # prefetch (5 is out of range)
+    st.sampled_from([0, 0, 0, 1, 7, 16, 64, 1024, 1025]),  # partition_blocks
+    st.sampled_from([0, 0, 1, 2, 3, 4, 8, 16]),            # waves_per_wg (3, 16 invalid)
+    st.sampled_from([0, 0, 1, 2, 3, 63, 64]),              # prefetch_distance
+    st.sampled_from([0, 0, 1, 2]),                         # seq_order
+    st.sampled_from([0, 0, 0, 1]))                         # structure
+
+
+@settings(max_examples=600, deadline=None)
+@given(shapes, options)
+def test_every_accepted_plan_is_launchable(shape_t, opt_t):
+    B, Hkv, g, MB, kv = shape_t
+    pf, pb, waves, dist, order, structure = opt_t
+    sh = nat.make_shape(B, g * Hkv, Hkv, MB, 10 * MB * B, kv_dtype=kv)
+    o = nat.default_options()
+    o.prefetch, o.partition_blocks, o.waves_per_wg = pf, pb, waves
+    o.prefetch_distance, o.seq_order, o.structure = dist, order, structure
+    rc, p = raw_plan(sh, o)
+    assert rc in (nat.PA_OK, nat.PA_ERR_INVALID_ARG, nat.PA_ERR_UNSUPPORTED)
+    must_refuse = (g > 16 or pf > 4 or waves in (3, 16) or pb > 1024 or dist > 63
+                   or (order == nat.ORDER_LONGEST_FIRST and B > nat.RANK_MAX_SEQS))
+    if must_refuse:
+        assert rc != nat.PA_OK
+    if rc != nat.PA_OK:
+        return
+    PB, P = p["partition_blocks"], p["num_partitions"]
+    assert 1 <= PB <= min(MB, 1024)
+    assert P == -(-MB // PB) and P <= 65535
+    assert p["workgroups"] == P * Hkv * B
+    assert p["waves_per_wg"] in (1, 2, 4, 8)
+    if waves:
+        assert p["waves_per_wg"] == waves
+    if pb:
+        assert PB == min(pb, MB)
+    want_ws = B * g * Hkv * P * 130 * 4 if P > 1 else 0
+    assert p["workspace_bytes"] == want_ws
+    assert nat.lib().paged_attn_workspace_size(ctypes.byref(sh), ctypes.byref(o)) == want_ws
+    assert p["prefetch"] == (nat.PREFETCH_REG if pf < 0 else pf)
+    assert p["seq_order"] in (nat.ORDER_NATURAL, nat.ORDER_LONGEST_FIRST)
+    if order:
+        assert p["seq_order"] == order
+    if p["seq_order"] == nat.ORDER_LONGEST_FIRST:
+        assert B <= nat.RANK_MAX_SEQS
+    ring = p["prefetch"] in (nat.PREFETCH_REG, nat.PREFETCH_LDS)
+    assert 1 <= p["prefetch_distance"] <= (2 if ring else 63)
+    assert p["structure"] == structure
+    if structure == nat.STRUCTURE_TWO_LOOP:
+        assert kv == nat.KV_F16 and p["prefetch_distance"] == 1
