@@ -251,6 +251,32 @@ int paged_attn_decode_fp8(const void *q, const void *k_cache, const void *v_cach
                           float scale, float k_scale, float v_scale, void *out,
                           const pa_shape *shape, const pa_options *opts, void *stream);
 
+/* Bytes of the device scratch array that paged_attn_decode_noalloc uses in
+   place of a caller's workspace (one array per GPU, held until the process
+   ends). */
+#define PA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* paged_attn_decode for callers that cannot allocate device memory: code
+   under HIP graph capture, serving loops and harnesses that forbid
+   hipMalloc.  The same computation, kernels and plan as paged_attn_decode
+   (bitwise the same output), except that the partition partials live in a
+   library-owned device array of PA_NOALLOC_SCRATCH_BYTES on the current
+   device instead of in opts->workspace, which is ignored.  The call allocates
+   nothing: no hipMalloc / hipFree and no allocating library routine.
+   Returns PA_ERR_WORKSPACE, before any launch, when the plan needs more
+   partials than the array holds (paged_attn_workspace_size(shape, opts) >
+   PA_NOALLOC_SCRATCH_BYTES), PA_ERR_HIP if the array's device address
+   cannot be looked up (done once per device, on the first call there).
+   Every call on one GPU shares that GPU's array, and the array keeps the
+   last call's contents (nothing in it needs to start at zero: each call
+   writes every partial it reads).  Calls that overlap in time on one GPU --
+   on different streams, or from different host threads -- race on the array
+   and give undefined results; serialise them on one stream. */
+int paged_attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *block_tables, const int32_t *context_lens,
+                              float scale, void *out, const pa_shape *shape,
+                              const pa_options *opts, void *stream);
+
 /* Plan for (shape, opts) without launching.  Host-only. */
 int paged_attn_plan(const pa_shape *shape, const pa_options *opts,
                     pa_plan_info *info);

@@ -22,6 +22,8 @@ ORDER_NAMES = {1: "natural", 2: "longest_first"}
 RANK_MAX_SEQS = 256
 STRUCTURE_FUSED, STRUCTURE_TWO_LOOP = 0, 1
 KV_F16, KV_E4M3 = 0, 1
+# bytes of the device scratch array behind paged_attn_decode_noalloc
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class PaShape(ctypes.Structure):
@@ -76,6 +78,8 @@ def lib():
     L.paged_attn_decode.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp,
                                     ctypes.POINTER(PaShape), ctypes.POINTER(PaOptions), vp]
     L.paged_attn_decode.restype = ctypes.c_int
+    L.paged_attn_decode_noalloc.argtypes = L.paged_attn_decode.argtypes
+    L.paged_attn_decode_noalloc.restype = ctypes.c_int
     f32 = ctypes.c_float
     L.paged_attn_decode_fp8.argtypes = [vp, vp, vp, vp, vp, f32, f32, f32, vp,
                                         ctypes.POINTER(PaShape), ctypes.POINTER(PaOptions), vp]

@@ -239,11 +239,10 @@ size_t paged_attn_workspace_size(const pa_shape* sh, const pa_options* o) {
 
 namespace {
 
-// Shared by the fp16 and the E4M3 entry points.
-int decode_impl(const void* q, const void* k_cache, const void* v_cache,
-                const int32_t* block_tables, const int32_t* context_lens, float scale,
-                bool kv8, float k_scale, float v_scale, void* out, const pa_shape* sh,
-                const pa_options* o, void* stream) {
+// Checks of the tensor pointers and scalars of a decode call.
+int check_args(const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* context_lens, float scale, bool kv8,
+               float k_scale, float v_scale, const void* out, const pa_shape* sh) {
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
     return PA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
@@ -254,8 +253,19 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   if (!isfinite(k_scale) || !isfinite(v_scale) || !(k_scale > 0.f) || !(v_scale > 0.f))
     return PA_ERR_INVALID_ARG;
   if (sh && sh->kv_dtype != (kv8 ? PA_KV_E4M3 : PA_KV_F16)) return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+// Shared by the fp16 and the E4M3 entry points.
+int decode_impl(const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens, float scale,
+                bool kv8, float k_scale, float v_scale, void* out, const pa_shape* sh,
+                const pa_options* o, void* stream) {
+  int rc = check_args(q, k_cache, v_cache, block_tables, context_lens, scale, kv8, k_scale,
+                      v_scale, out, sh);
+  if (rc) return rc;
   Plan pl;
-  int rc = make_plan(sh, o, &pl);
+  rc = make_plan(sh, o, &pl);
   if (rc) return rc;
   // cache strides: 0 = dense; slices may be spread out but never overlap
   const int64_t slice = (int64_t)PA_BLOCK_SIZE * PA_HEAD_DIM * (kv8 ? 1 : 2);
@@ -351,6 +361,33 @@ int paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_cach
                           const pa_shape* sh, const pa_options* o, void* stream) {
   return decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, true, k_scale,
                      v_scale, out, sh, o, stream);
+}
+
+int paged_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              float scale, void* out, const pa_shape* sh, const pa_options* o,
+                              void* stream) {
+  int rc = check_args(q, k_cache, v_cache, block_tables, context_lens, scale, false, 1.f, 1.f,
+                      out, sh);
+  if (rc) return rc;
+  pa_options oo;
+  if (o) {
+    oo = *o;
+  } else {
+    paged_attn_default_options(&oo);
+  }
+  Plan pl;
+  rc = make_plan(sh, &oo, &pl);
+  if (rc) return rc;
+  if (pl.ws_bytes > pa::kNoAllocScratchBytes) return PA_ERR_WORKSPACE;
+  // the current device's copy of the library's scratch array (its address
+  // is looked up on the first call on each device); nothing is allocated
+  void* scratch = nullptr;
+  if (pa::noalloc_scratch(&scratch) != hipSuccess) return PA_ERR_HIP;
+  oo.workspace = scratch;
+  oo.workspace_bytes = pa::kNoAllocScratchBytes;
+  return decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, false, 1.f, 1.f,
+                     out, sh, &oo, stream);
 }
 
 // Streaming-read grid: 2048 work-groups of 256 threads (8 per CU on 256

@@ -62,6 +62,13 @@ inline size_t two_loop_lds_bytes(int PB, int g, int waves, int B, bool rank) {
   return main > r ? main : r;
 }
 
+// Bytes of the per-device scratch array of paged_attn_decode_noalloc
+// (PA_NOALLOC_SCRATCH_BYTES in paged_attn.h).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+// The current device's address of that array (looked up on the first call
+// on each device, then cached).
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_decode_two_loop(const DecodeArgs& a, int pf, int waves, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int waves,
                          hipStream_t st);

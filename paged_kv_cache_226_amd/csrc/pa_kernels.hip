@@ -47,6 +47,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -1088,6 +1090,34 @@ hipError_t launch_decode_two_loop(const DecodeArgs& a, int pf, int waves, hipStr
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(pa_reduce_kernel, dim3((unsigned)(a.B * a.Hq)), dim3(kD), 0, st, a);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the no-allocation entry point: the partition partials of calls
+// that cannot allocate.  Every GPU the library runs on holds its own copy
+// for the life of the process.  On the host, `noalloc_scratch_array` names a
+// host-side stand-in, never a device address: its device address is looked
+// up once per device (with that device current) and cached.
+static __device__ __align__(256) unsigned char noalloc_scratch_array[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch_array));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_stream_read(const void* buf, size_t bytes, void* sink, int groups,

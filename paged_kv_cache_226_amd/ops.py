@@ -133,13 +133,18 @@ class DecodeCall:
     nothing and costs one C call, about what a C caller of the library pays.
     The stream is the one given, or the device's current stream when the
     call was prepared.  Calls on one DecodeCall must not overlap (they share
-    its workspace)."""
+    its workspace).  With noalloc, the call goes to paged_attn_decode_noalloc,
+    whose partials live in the library's per-device scratch array: no
+    workspace is allocated or taken, and calls that overlap on one GPU race."""
 
     def __init__(self, fp8: bool, q, k_cache, v_cache, block_tables, context_lens, scale,
                  k_scale, v_scale, out, prefetch, partition_blocks, waves_per_wg,
                  prefetch_distance, seq_order, structure, workspace, debug_gather_k,
-                 debug_trace, debug_error_word, stream):
-        self.name = "paged_attn_decode_fp8" if fp8 else "paged_attn_decode"
+                 debug_trace, debug_error_word, stream, noalloc: bool = False):
+        if noalloc and (fp8 or workspace is not None):
+            raise ValueError("the no-allocation call takes an fp16 cache and no workspace")
+        self.name = ("paged_attn_decode_noalloc" if noalloc else
+                     "paged_attn_decode_fp8" if fp8 else "paged_attn_decode")
         _check(q, "q", torch.float16, 3)
         _check_kv(k_cache, "k_cache", fp8, 5)
         _check_kv(v_cache, "v_cache", fp8, 4)
@@ -173,7 +178,11 @@ class DecodeCall:
         L = nat.lib()
         need = int(L.paged_attn_workspace_size(ctypes.byref(self._shape),
                                                ctypes.byref(self._opts)))
-        if need:
+        if noalloc:
+            if need > nat.NOALLOC_SCRATCH_BYTES:
+                raise ValueError(f"{self.name}: the plan needs {need} bytes of partials, the "
+                                 f"scratch array holds {nat.NOALLOC_SCRATCH_BYTES}")
+        elif need:
             if workspace is None:
                 workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
             elif not workspace.is_cuda or workspace.numel() * workspace.element_size() < need:
@@ -193,7 +202,7 @@ class DecodeCall:
                           ctypes.c_float(v_scale), ctypes.c_void_p(out.data_ptr()),
                           ctypes.byref(self._shape), ctypes.byref(self._opts), st)
         else:
-            self._fn = L.paged_attn_decode
+            self._fn = L.paged_attn_decode_noalloc if noalloc else L.paged_attn_decode
             self._args = (*ptrs, ctypes.c_float(scale), ctypes.c_void_p(out.data_ptr()),
                           ctypes.byref(self._shape), ctypes.byref(self._opts), st)
 
@@ -223,6 +232,34 @@ def prepare_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                       out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
                       seq_order, structure, workspace, debug_gather_k, debug_trace,
                       debug_error_word, stream)
+
+
+def prepare_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           scale: Optional[float] = None, out: Optional[torch.Tensor] = None, *,
+                           prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0,
+                           prefetch_distance: int = 0, seq_order: int = 0, structure: int = 0,
+                           debug_gather_k: Optional[torch.Tensor] = None,
+                           debug_trace: Optional[torch.Tensor] = None,
+                           debug_error_word: Optional[torch.Tensor] = None,
+                           stream: Optional[torch.cuda.Stream] = None) -> DecodeCall:
+    """paged_attn_decode_noalloc prepared for repeated calls; pass `out` to
+    keep the calls free of allocation."""
+    return DecodeCall(False, q, k_cache, v_cache, block_tables, context_lens, scale, 1.0, 1.0,
+                      out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
+                      seq_order, structure, None, debug_gather_k, debug_trace,
+                      debug_error_word, stream, noalloc=True)
+
+
+def paged_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              block_tables: torch.Tensor, context_lens: torch.Tensor,
+                              scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                              **kw) -> torch.Tensor:
+    """paged_attn_decode without a workspace: the partition partials go to the
+    library's per-device scratch array (PA_NOALLOC_SCRATCH_BYTES), so with
+    `out` given nothing is allocated.  Calls that overlap on one GPU race."""
+    return prepare_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                                  **kw)()
 
 
 def prepare_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -150,6 +150,33 @@ def test_validation_codes(native_lib, case, code):
     assert call(shape, o, **case) == code
 
 
+def test_noalloc_validation_codes(native_lib):
+    """paged_attn_decode_noalloc checks its arguments as paged_attn_decode does
+    and refuses, before any device call, a plan whose partials exceed its
+    scratch array; a caller's workspace is ignored."""
+    def noalloc(shape, opts=None, q=FAKE, out=FAKE):
+        return native_lib.paged_attn_decode_noalloc(
+            ctypes.c_void_p(q), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+            ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), ctypes.c_float(0.088),
+            ctypes.c_void_p(out), ctypes.byref(shape) if shape is not None else None,
+            ctypes.byref(opts) if opts is not None else None, None)
+    m = re.search(r"#define PA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == nat.NOALLOC_SCRATCH_BYTES
+    assert noalloc(good_shape(), q=0) == nat.PA_ERR_INVALID_ARG
+    assert noalloc(good_shape(), out=FAKE + 8) == nat.PA_ERR_INVALID_ARG
+    assert noalloc(None) == nat.PA_ERR_INVALID_ARG
+    assert noalloc(good_shape(head_dim=64)) == nat.PA_ERR_UNSUPPORTED
+    assert noalloc(good_shape(kv_dtype=nat.KV_E4M3)) == nat.PA_ERR_INVALID_ARG
+    # 255 sequences x 16 heads in partitions of 16 blocks of a 1024-block table
+    big = good_shape(num_seqs=255, num_q_heads=16, num_kv_heads=1, max_blocks_per_seq=1024)
+    o = nat.default_options()
+    o.partition_blocks = 16
+    need = native_lib.paged_attn_workspace_size(ctypes.byref(big), ctypes.byref(o))
+    assert need > nat.NOALLOC_SCRATCH_BYTES
+    o.workspace, o.workspace_bytes = FAKE, need  # ignored by this entry point
+    assert noalloc(big, o) == nat.PA_ERR_WORKSPACE
+
+
 def test_plans_of_the_workloads(native_lib):
     from paged_kv_cache_226_amd import inputs as gen
     # (partitions, waves) of the auto plan
