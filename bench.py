@@ -1,16 +1,19 @@
 """Benchmark: paged decode attention on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--prefetch MODE]
-                    [--kv-dtype fp16|fp8]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--also NAMES]
+                    [--prefetch MODE] [--kv-dtype fp16|fp8]
 
 A step is one paged_attn_decode call over the whole batch (the decode kernel,
 plus the cross-partition reduce when the plan splits contexts), i.e. one
 layer's decode attention, with every input already resident in HBM.  The
-printed JSON line reports effective KV GB/s (algorithmic KV bytes / time)
-as `value`, µs/step, the fraction of the 8 TB/s HBM peak, the roofline of
-the decode kernel, per-prefetch-mode timings, the streaming-read ceiling
-measured in the same run, and the fp64 CPU oracle timed on the host cores
-(plus the parity of the GPU output against it).
+printed JSON line reports, for the headline workload (--workload, default the
+Llama2-7B-shaped MHA layer), effective KV GB/s (algorithmic KV bytes / time)
+as `value`, µs/step, the fraction of the 8 TB/s HBM peak, the roofline of the
+decode kernel, per-prefetch-mode timings, the streaming-read ceiling measured
+in the same run, the fp64 CPU oracle timed on the host cores, and the parity
+of the timed call's own output against the oracle.  Every workload of --also
+(default: the Llama3-8B-shaped GQA 4:1 layer) gets the same block, without
+the CPU timing, under `targets`.
 
 Inputs are synthetic (seeded N(0,1) Q/K/V, shuffled block tables) with the
 shapes of the workload; see paged_kv_cache_226_amd/inputs.py.  The caches
@@ -88,21 +91,42 @@ def read_traffic(workload: str, mode_name: str):
     return float(kv[key]) if kv and key in kv else None
 
 
+# look-ahead evidence per mode in the committed counter summaries (fractions
+# or per-instruction cycle counts; rocprof_summary writes them):
+#   l2_hit_rate        TCC_HIT / (TCC_HIT + TCC_MISS)
+#   issue_stall_share  SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (the stall share of
+#                      the measurement plan: waves waiting to issue)
+#   stall_cycles_per_inst  4 * SQ_WAIT_INST_ANY / SQ_INSTS
+#   cycles_per_inst    4 * SQ_WAVE_CYCLES / SQ_INSTS (CPI of a wave)
+#   wait_share         SQ_WAIT_ANY / SQ_WAVE_CYCLES (waiting for anything,
+#                      s_waitcnt on loads included)
+#   kernel_us          rocprofv3 kernel-trace average duration
+LOOKAHEAD_FIGURES = ("l2_hit_rate", "issue_stall_share", "stall_cycles_per_inst",
+                     "cycles_per_inst", "wait_share", "kernel_us")
+
+
 def read_lookahead_counters(workload: str, mode_name: str):
     """The look-ahead evidence of the committed counter summary (same
-    current-sources rule as the traffic): L2 hit rate and wait share
-    (SQ_WAIT_ANY / SQ_WAVE_CYCLES) with the look-ahead off, as an L2 touch,
-    and in the timed mode; None if absent."""
+    current-sources rule as the traffic) with the look-ahead off, as an L2
+    touch, as both, and in the timed mode; None if absent."""
     kv = _profile_figures(workload)
     if not kv:
         return None
     out = {"source": f"profiles/pa_decode_{workload}_counters.md"}
-    for fig in ("l2_hit_rate", "wait_share"):
-        vals = {m: float(kv[f"{fig}_{m}"]) for m in ("off", "l2", mode_name)
+    for fig in LOOKAHEAD_FIGURES:
+        vals = {m: float(kv[f"{fig}_{m}"]) for m in ("off", "l2", "both", mode_name)
                 if f"{fig}_{m}" in kv}
         if vals:
             out[fig] = {m: round(v, 4) for m, v in vals.items()}
     return out if len(out) > 1 else None
+
+
+def read_kernel_us(workload: str, mode_name: str):
+    """rocprofv3's average duration of the decode kernel of this mode, from
+    the committed summary of the current kernel sources; None if absent."""
+    kv = _profile_figures(workload)
+    key = f"kernel_us_{mode_name}"
+    return float(kv[key]) if kv and key in kv else None
 
 
 def parse():
@@ -111,7 +135,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=100,
                     help="untimed steps before the timed region (and at least 250 ms of them)")
-    ap.add_argument("--workload", default="llama2_7b")
+    ap.add_argument("--workload", default="llama2_7b",
+                    help="the headline workload (its figures are the line's value)")
+    ap.add_argument("--also", default="llama3_8b",
+                    help="comma-separated further workloads measured the same way and "
+                         "reported under `targets` ('' for none)")
     ap.add_argument("--prefetch", type=int, default=-1, help="-1 = library default")
     ap.add_argument("--kv-layout", choices=("separate", "adjacent"), default="adjacent",
                     help="separate K and V pools (vLLM's layout), or one pool with each "
@@ -121,7 +149,7 @@ def parse():
     ap.add_argument("--prefetch-distance", type=int, default=0,
                     help="L2-touch distance k in wave iterations (modes 1, 3); 0 = 1")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="CPU time budget of the oracle baseline")
+                    help="wall-time budget of the oracle baseline (repeated full steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3: every prefetch mode, no CPU leg")
@@ -179,7 +207,6 @@ def run_sweep(args):
             d = gen.make_case_device(B, w.num_q_heads, w.num_kv_heads, ctx,
                                      seed=10_000 + 100 * bi + ci)
             out = torch.empty_like(d["q"])
-            ws = ops.new_workspace(d["q"], d["k_cache"], d["block_tables"])
             plan = ops.plan(d["q"], d["k_cache"], d["block_tables"])
             if args.profile:
                 # for a counter pass: a fixed number of launches per mode, in
@@ -188,20 +215,19 @@ def run_sweep(args):
                     for _ in range(SWEEP_PROFILE_LAUNCHES):
                         ops.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"],
                                               d["block_tables"], d["context_lens"], d["scale"],
-                                              out, prefetch=pf, workspace=ws)
+                                              out, prefetch=pf)
                 torch.cuda.synchronize()
                 print(json.dumps({"sweep_profile": args.workload, "batch": B, "context": ctx,
                                   "kv_bytes": kv_bytes, "partitions": plan["num_partitions"],
                                   "modes": SWEEP_PROFILE_MODES,
                                   "launches_per_mode": SWEEP_PROFILE_LAUNCHES}), flush=True)
-                del d, out, ws
+                del d, out
                 torch.cuda.empty_cache()
                 continue
             times = {}
             for pf in (0, plan["prefetch"]):
                 f = ops.prepare_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
-                                       d["context_lens"], d["scale"], out, prefetch=pf,
-                                       workspace=ws)
+                                       d["context_lens"], d["scale"], out, prefetch=pf)
                 # warm up for at least 50 ms: the GPU runs slower for a while
                 # after the input generation or an idle gap
                 t_end = time.perf_counter() + 0.05
@@ -235,10 +261,241 @@ def run_sweep(args):
                 "speedup_on_vs_off": round(times[0] / on, 4),
                 "parity_abs": float(diff.max()),
                 "parity_rel": float((diff / np.maximum(np.abs(ref), 1e-3)).max())}), flush=True)
-            del d, out, ws
+            del d, out
             torch.cuda.empty_cache()
     if args.profile:
         calibrate_counters(torch, ops)
+
+
+def mode_name_of(nat, pf: int, dist: int, structure: int = 0) -> str:
+    """Name of a (mode, distance, structure) run, as in the profiles."""
+    ring = pf in (nat.PREFETCH_REG, nat.PREFETCH_LDS)
+    return (("two_loop_" if structure else "") + nat.PREFETCH_NAMES[pf] +
+            ("2" if ring and dist == 2 else ""))
+
+
+def parity_of(got_f16, ref_f64):
+    """abs = max |g - r|, rel = max |g - r| / max(|r|, 1e-3) over every element."""
+    import numpy as np
+    diff = np.abs(got_f16.astype(np.float64) - ref_f64)
+    return {"abs": float(diff.max()),
+            "rel": float((diff / np.maximum(np.abs(ref_f64), 1e-3)).max())}
+
+
+def measure_workload(args, name, env, cpu_leg):
+    """Time one workload's decode step and check the timed call's output
+    against the fp64 oracle.  Returns (block for the JSON line, extras)."""
+    import numpy as np
+    torch, ops, nat, acc, gen = env["torch"], env["ops"], env["nat"], env["acc"], env["gen"]
+    dev, stream = env["dev"], env["stream"]
+    w = gen.WORKLOADS[name]
+    t0 = time.time()
+    x = gen.make_inputs(w)
+    print(f"[bench] generated {name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    fp8 = args.kv_dtype == "fp8"
+    d = {k: torch.from_numpy(getattr(x, k)).to(dev) for k in ("q", "block_tables", "context_lens")}
+    x8 = None
+    if fp8:
+        x8 = gen.to_fp8(x)
+        d["k_cache"] = torch.from_numpy(gen.pack_k_fp8(x8.k8)).to(dev)
+        d["v_cache"] = torch.from_numpy(x8.v8).to(dev)
+    else:
+        d["k_cache"] = torch.from_numpy(gen.pack_k(x.k_cache)).to(dev)
+        d["v_cache"] = torch.from_numpy(x.v_cache).to(dev)
+    if args.kv_layout == "adjacent":
+        # one pool [block][head][K slice | V slice]; K and V are strided views
+        d["k_cache"], d["v_cache"] = gen.side_by_side(d["k_cache"], d["v_cache"])
+    Hkv = x.k_cache.shape[1]
+    kv_bytes = acc.step_kv_bytes(Hkv, 128, x.context_lens, elem_bytes=1 if fp8 else 2)
+    plan = ops.plan(d["q"], d["k_cache"], d["block_tables"], prefetch=args.prefetch,
+                    prefetch_distance=args.prefetch_distance)
+
+    # One prepared call per configuration, each with its own output tensor
+    # and its own workspace (sized for its own plan): a step is then one C
+    # call into the library, as for a C caller, and every configuration's
+    # output stays readable after the timings.
+    calls, outs = {}, {}
+
+    def step(key):
+        if key not in calls:
+            pf, dist, structure = key
+            outs[key] = torch.empty_like(d["q"])
+            if fp8:
+                calls[key] = ops.prepare_decode_fp8(
+                    d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                    x.scale, x8.k_scale, x8.v_scale, outs[key], prefetch=pf,
+                    prefetch_distance=dist)
+            else:
+                calls[key] = ops.prepare_decode(
+                    d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                    x.scale, outs[key], prefetch=pf, prefetch_distance=dist,
+                    structure=structure)
+        calls[key]()
+
+    def timed(key, steps, warmup, min_warm_s=0.0):
+        # Warm-up: `warmup` steps, and at least `min_warm_s` seconds of them.
+        # Coming out of idle (e.g. after the host built the inputs) the first
+        # tens of milliseconds of GPU work run measurably slower.
+        t_end = time.perf_counter() + min_warm_s
+        done = 0
+        while done < warmup or time.perf_counter() < t_end:
+            for _ in range(max(1, min(warmup - done, 50)) if done < warmup else 50):
+                step(key)
+                done += 1
+            torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            step(key)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / steps  # µs per step
+
+    def per_launch(key, steps):
+        """Average single-launch duration: an event pair around each call."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            a.record(stream)
+            step(key)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        pick = lambda f: ts[min(len(ts) - 1, int(f * len(ts)))]
+        return sum(ts) / len(ts), ts[len(ts) // 2], pick(0.1), pick(0.9)
+
+    mode = plan["prefetch"]
+    dist = plan["prefetch_distance"]  # the library's default unless given
+    mode_label = mode_name_of(nat, mode, dist)
+    timed_key = (mode, args.prefetch_distance, 0)
+
+    if args.profile:
+        for pf, dist_r, structure in MODE_RUNS:
+            if not (fp8 and structure):
+                timed((pf, dist_r, structure), args.steps, args.warmup)
+        return None, None
+
+    us = timed(timed_key, args.steps, args.warmup, min_warm_s=0.25)
+    launch_avg, launch_med, launch_p10, launch_p90 = per_launch(timed_key, args.steps)
+    modes = {}
+    for pf, dist_r, structure in MODE_RUNS:
+        if fp8 and structure:
+            continue
+        u = timed((pf, dist_r, structure), max(20, args.steps // 4), 5)
+        modes[mode_name_of(nat, pf, dist_r, structure)] = {
+            "us_per_step": round(u, 2), "GBps": round(kv_bytes / u / 1e3, 1)}
+
+    # the streaming read over exactly this step's KV bytes: the ramp-up and
+    # drain of a launch weigh more on a shorter read than on the 4 GiB one
+    buf = env["stream_buf"]
+    n_same = min(kv_bytes, buf.numel()) // 16 * 16
+    sink = ops.stream_read(buf[:n_same])
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(10):
+        ops.stream_read(buf[:n_same], sink)
+    b.record(stream)
+    torch.cuda.synchronize()
+    stream_same_gbps = n_same / (a.elapsed_time(b) * 1e3 / 10) / 1e3
+
+    # The decode kernel is the dominant kernel.  With one partition it is the
+    # only kernel of a step, and its average duration is the timed region over
+    # the steps; otherwise the step also holds the reduce kernel and the
+    # figure covers both.
+    tag = profile_tag(name, args.kv_dtype)
+    decode_only = plan["num_partitions"] == 1
+    achieved = kv_bytes / us / 1e3
+    kernel_us_rocprof = read_kernel_us(tag, mode_label)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": acc.HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / acc.HBM_PEAK_GBPS, 4),
+                "traffic": read_traffic(tag, mode_label),
+                "kernel": "pa_decode_kernel" + ("" if decode_only else " + pa_reduce_kernel"),
+                "step_us_avg": round(us, 2),
+                "kernel_us_rocprof": kernel_us_rocprof,
+                "kernel_us_rocprof_source": (f"profiles/pa_decode_{tag}_kernel_trace.md"
+                                             if kernel_us_rocprof is not None else None),
+                "event_pair_us_avg": round(launch_avg, 2),
+                "event_pair_us_median": round(launch_med, 2),
+                "event_pair_us_p10": round(launch_p10, 2),
+                "event_pair_us_p90": round(launch_p90, 2)}
+
+    off_us = modes["off"]["us_per_step"]
+    block = {
+        "workload": name,
+        "config": {"workload": name, "kv_dtype": "e4m3" if fp8 else "f16",
+                   "kv_layout": args.kv_layout,
+                   "batch": w.num_seqs, "q_heads": w.num_q_heads,
+                   "kv_heads": w.num_kv_heads, "head_dim": 128, "block_size": 16,
+                   "context_sum": int(np.maximum(x.context_lens, 0).sum()),
+                   "context_min": int(x.context_lens.min()),
+                   "context_max": int(x.context_lens.max()),
+                   "prefetch": mode_label, "prefetch_distance": dist,
+                   "waves_per_wg": plan["waves_per_wg"],
+                   "partition_blocks": plan["partition_blocks"],
+                   "num_partitions": plan["num_partitions"],
+                   "seq_order": nat.ORDER_NAMES.get(plan["seq_order"], plan["seq_order"]),
+                   "parallelism": "single GPU"},
+        "us_per_step": round(us, 2),
+        "GBps": round(achieved, 1),
+        "pct_hbm_peak": round(100 * achieved / acc.HBM_PEAK_GBPS, 2),
+        "kv_bytes_per_step": kv_bytes,
+        "other_bytes_per_step": acc.step_other_bytes(w.num_seqs, w.num_q_heads, 128,
+                                                     x.context_lens),
+        "flops_per_step": acc.step_flops(w.num_q_heads, 128, x.context_lens),
+        "roofline": roofline,
+        "lookahead": {"off_us_per_step": off_us, "timed_mode": mode_label,
+                      "timed_us_per_step": round(us, 2),
+                      "speedup_timed_vs_off": round(off_us / us, 4)},
+        "prefetch_modes": modes,
+        "stream_read_same_size_GBps": round(stream_same_gbps, 1),
+        "pct_of_same_size_stream": round(100 * achieved / stream_same_gbps, 1),
+        "lookahead_counters": read_lookahead_counters(tag, mode_label),
+        "inputs_sha256": {k: v[:16] for k, v in gen.digests(x).items()},
+    }
+
+    # Parity of the timed call's own output (and of every other
+    # configuration's) against the fp64 oracle on the same host inputs.
+    from oracle import oracle as orc
+
+    def oracle_step():
+        if fp8:
+            return orc.paged_attention_fp8_f64(x8.q, x8.k8, x8.v8, x8.block_tables,
+                                               x8.context_lens, x8.scale, x8.k_scale,
+                                               x8.v_scale)
+        return orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                       x.context_lens, x.scale)
+
+    runs = []
+    deadline = time.time() + (args.cpu_seconds if cpu_leg else 0.0)
+    while True:
+        t1 = time.perf_counter()
+        ref = oracle_step()
+        runs.append(time.perf_counter() - t1)
+        if time.time() > deadline or len(runs) >= 200:
+            break
+    torch.cuda.synchronize()
+    got = outs[timed_key].cpu().numpy()
+    par = parity_of(got, ref)
+    par.update({"rows_checked": int(w.num_seqs * w.num_q_heads), "elements_checked": int(got.size),
+                "output_of": f"the timed call ({mode_label})", "abs_tol": 2e-3, "rel_tol": 1e-2,
+                "pass": par["abs"] <= 2e-3 and par["rel"] <= 1e-2})
+    bitwise = {}
+    for key, o in outs.items():
+        if key == timed_key:
+            continue
+        nm = mode_name_of(nat, *key)
+        gk = o.cpu().numpy()
+        bitwise[nm] = bool(np.array_equal(gk.view(np.uint16), got.view(np.uint16)))
+        if nm in modes:
+            pk = parity_of(gk, ref)
+            modes[nm]["parity_abs"] = pk["abs"]
+            modes[nm]["parity_rel"] = pk["rel"]
+    par["bitwise_equal_to_timed"] = bitwise
+    block["parity"] = par
+    t_cpu = sorted(runs)[len(runs) // 2]
+    block["oracle_wall_s"] = round(t_cpu, 3)
+    return block, {"t_cpu": t_cpu, "runs": runs, "kv_bytes": kv_bytes, "us": us}
 
 
 def main():
@@ -249,7 +506,6 @@ def main():
                                    "is a single-GPU path (no collectives). Use --gpus 1."}))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from paged_kv_cache_226_amd import accounting as acc
@@ -266,113 +522,15 @@ def main():
     if args.sweep:
         run_sweep(args)
         return
-
-    w = gen.WORKLOADS[args.workload]
-    t0 = time.time()
-    x = gen.make_inputs(w)
-    print(f"[bench] generated {args.workload} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    fp8 = args.kv_dtype == "fp8"
-    d = {k: torch.from_numpy(getattr(x, k)).to(dev) for k in ("q", "block_tables", "context_lens")}
-    if fp8:
-        x8 = gen.to_fp8(x)
-        d["k_cache"] = torch.from_numpy(gen.pack_k_fp8(x8.k8)).to(dev)
-        d["v_cache"] = torch.from_numpy(x8.v8).to(dev)
-    else:
-        d["k_cache"] = torch.from_numpy(gen.pack_k(x.k_cache)).to(dev)
-        d["v_cache"] = torch.from_numpy(x.v_cache).to(dev)
-    if args.kv_layout == "adjacent":
-        # one pool [block][head][K slice | V slice]; K and V are strided views
-        d["k_cache"], d["v_cache"] = gen.side_by_side(d["k_cache"], d["v_cache"])
-    out = torch.empty_like(d["q"])
-    Hkv = x.k_cache.shape[1]
-    kv_bytes = acc.step_kv_bytes(Hkv, 128, x.context_lens, elem_bytes=1 if fp8 else 2)
-    other_bytes = acc.step_other_bytes(w.num_seqs, w.num_q_heads, 128, x.context_lens)
-    flops = acc.step_flops(w.num_q_heads, 128, x.context_lens)
-    plan = ops.plan(d["q"], d["k_cache"], d["block_tables"], prefetch=args.prefetch,
-                    prefetch_distance=args.prefetch_distance)
-    ws = ops.new_workspace(d["q"], d["k_cache"], d["block_tables"], prefetch=args.prefetch)
     stream = torch.cuda.current_stream()
+    env = dict(torch=torch, ops=ops, nat=nat, acc=acc, gen=gen, dev=dev, stream=stream)
 
-    ws_two = None if fp8 else ops.new_workspace(d["q"], d["k_cache"], d["block_tables"],
-                                                structure=1)
-
-    # One prepared call per configuration: each step is then one C call into
-    # the library, as for a C caller (the one-shot Python entry points
-    # re-validate their arguments every time, 10-20 us of host work).
-    calls = {}
-
-    def step(pf, dist=None, structure=0):
-        dist = args.prefetch_distance if dist is None else dist
-        key = (pf, dist, structure)
-        if key not in calls:
-            if fp8:
-                calls[key] = ops.prepare_decode_fp8(
-                    d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
-                    x.scale, x8.k_scale, x8.v_scale, out, prefetch=pf, workspace=ws,
-                    prefetch_distance=dist)
-            else:
-                calls[key] = ops.prepare_decode(
-                    d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
-                    x.scale, out, prefetch=pf, workspace=ws_two if structure else ws,
-                    prefetch_distance=dist, structure=structure)
-        calls[key]()
-
-    def timed(pf, steps, warmup, dist=None, min_warm_s=0.0, structure=0):
-        # Warm-up: `warmup` steps, and at least `min_warm_s` seconds of them.
-        # Coming out of idle (e.g. after the host built the inputs) the first
-        # tens of milliseconds of GPU work run measurably slower.
-        t_end = time.perf_counter() + min_warm_s
-        done = 0
-        while done < warmup or time.perf_counter() < t_end:
-            for _ in range(max(1, min(warmup - done, 50)) if done < warmup else 50):
-                step(pf, dist, structure)
-                done += 1
-            torch.cuda.synchronize()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(steps):
-            step(pf, dist, structure)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / steps  # µs per step
-
-    def per_launch(pf, steps):
-        """Average single-launch duration: an event pair around each call."""
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        for a, b in evs:
-            a.record(stream)
-            step(pf)
-            b.record(stream)
-        torch.cuda.synchronize()
-        ts = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
-        pick = lambda f: ts[min(len(ts) - 1, int(f * len(ts)))]
-        return sum(ts) / len(ts), ts[len(ts) // 2], pick(0.1), pick(0.9)
-
-    mode = plan["prefetch"]
-    mode_names = nat.PREFETCH_NAMES
-    dist = plan["prefetch_distance"]  # the library's default unless given
-    ring = mode in (nat.PREFETCH_REG, nat.PREFETCH_LDS)
-    mode_label = mode_names[mode] + ("2" if ring and dist == 2 else "")
     if args.profile:
-        for pf, dist, structure in MODE_RUNS:
-            if not (fp8 and structure):
-                timed(pf, args.steps, args.warmup, dist, structure=structure)
+        measure_workload(args, args.workload, env, cpu_leg=False)
         calibrate_counters(torch, ops)
         print(json.dumps({"profile_run": args.workload, "kv_dtype": args.kv_dtype,
                           "steps": args.steps}), flush=True)
         return
-
-    us = timed(mode, args.steps, args.warmup, min_warm_s=0.25)
-    launch_avg, launch_med, launch_p10, launch_p90 = per_launch(mode, args.steps)
-    modes = {}
-    for pf, dist, structure in MODE_RUNS:
-        if fp8 and structure:
-            continue
-        u = timed(pf, max(20, args.steps // 4), 5, dist, structure=structure)
-        name = ("two_loop_" if structure else "") + mode_names[pf] + ("2" if dist == 2 else "")
-        modes[name] = {"us_per_step": round(u, 2), "GBps": round(kv_bytes / u / 1e3, 1)}
 
     # streaming-read ceiling over a buffer larger than every cache
     buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
@@ -385,108 +543,64 @@ def main():
     b.record(stream)
     torch.cuda.synchronize()
     stream_gbps = (4 << 30) / (a.elapsed_time(b) * 1e3 / 10) / 1e3
-    # the same read over exactly this step's KV bytes: the ramp-up and drain
-    # of a launch weigh more on a shorter read
-    n_same = min(kv_bytes, 4 << 30) // 16 * 16
-    a.record(stream)
-    for _ in range(10):
-        ops.stream_read(buf[:n_same], sink)
-    b.record(stream)
-    torch.cuda.synchronize()
-    stream_same_gbps = n_same / (a.elapsed_time(b) * 1e3 / 10) / 1e3
-    del buf
+    env["stream_buf"] = buf
 
-    # The decode kernel is the dominant kernel.  With one partition it is the
-    # only kernel of a step, and its average duration is the timed region over
-    # the steps; otherwise the step also holds the reduce kernel and the
-    # figure covers both.
-    decode_only = plan["num_partitions"] == 1
-    achieved = kv_bytes / us / 1e3
-    traffic = read_traffic(profile_tag(args.workload, args.kv_dtype), mode_label)
-    lookahead_counters = read_lookahead_counters(profile_tag(args.workload, args.kv_dtype),
-                                                 mode_label)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": acc.HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / acc.HBM_PEAK_GBPS, 4),
-                "traffic": traffic, "kernel": "pa_decode_kernel" + ("" if decode_only else
-                                                                    " + pa_reduce_kernel"),
-                "kernel_us_avg": round(us, 2),
-                "event_pair_us_avg": round(launch_avg, 2),
-                "event_pair_us_median": round(launch_med, 2),
-                "event_pair_us_p10": round(launch_p10, 2),
-                "event_pair_us_p90": round(launch_p90, 2)}
+    cpu_leg = not args.no_cpu_baseline
+    head, hx = measure_workload(args, args.workload, env, cpu_leg=cpu_leg)
+    targets = {args.workload: head}
+    for name in [n for n in args.also.split(",") if n and n != args.workload]:
+        torch.cuda.empty_cache()
+        blk, _ = measure_workload(args, name, env, cpu_leg=False)
+        targets[name] = blk
+    del buf, env["stream_buf"]
 
+    us = hx["us"]
     result = {
         "metric": METRIC,
-        "value": round(kv_bytes / us / 1e3, 1),
+        "value": head["GBps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(us / 1e3, 5),
-        "us_per_step": round(us, 2),
-        "pct_hbm_peak": round(100 * kv_bytes / us / 1e3 / acc.HBM_PEAK_GBPS, 2),
+        "us_per_step": head["us_per_step"],
+        "pct_hbm_peak": head["pct_hbm_peak"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "accumulate": "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "kv_dtype": "e4m3" if fp8 else "f16",
-                   "kv_layout": args.kv_layout,
-                   "batch": w.num_seqs, "q_heads": w.num_q_heads,
-                   "kv_heads": w.num_kv_heads, "head_dim": 128, "block_size": 16,
-                   "context_sum": int(np.maximum(x.context_lens, 0).sum()),
-                   "context_min": int(x.context_lens.min()),
-                   "context_max": int(x.context_lens.max()),
-                   "prefetch": mode_label, "prefetch_distance": dist,
-                   "waves_per_wg": plan["waves_per_wg"],
-                   "partition_blocks": plan["partition_blocks"],
-                   "num_partitions": plan["num_partitions"], "parallelism": "single GPU"},
-        "kv_bytes_per_step": kv_bytes,
-        "other_bytes_per_step": other_bytes,
-        "flops_per_step": flops,
-        "prefetch_modes": modes,
+        "config": head["config"],
+        "kv_bytes_per_step": head["kv_bytes_per_step"],
+        "other_bytes_per_step": head["other_bytes_per_step"],
+        "flops_per_step": head["flops_per_step"],
+        "prefetch_modes": head["prefetch_modes"],
         "stream_read_ceiling_GBps": round(stream_gbps, 1),
-        "pct_of_stream_ceiling": round(100 * kv_bytes / us / 1e3 / stream_gbps, 1),
-        "stream_read_same_size_GBps": round(stream_same_gbps, 1),
-        "pct_of_same_size_stream": round(100 * kv_bytes / us / 1e3 / stream_same_gbps, 1),
-        "roofline": roofline,
-        "lookahead_counters": lookahead_counters,
+        "pct_of_stream_ceiling": round(100 * head["GBps"] / stream_gbps, 1),
+        "stream_read_same_size_GBps": head["stream_read_same_size_GBps"],
+        "pct_of_same_size_stream": head["pct_of_same_size_stream"],
+        "roofline": head["roofline"],
+        "lookahead": head["lookahead"],
+        "lookahead_counters": head["lookahead_counters"],
+        "parity": head["parity"],
         "kernel_source_hash": kernel_source_hash(),
-        "inputs_sha256": {k: v[:16] for k, v in gen.digests(x).items()},
+        "inputs_sha256": head["inputs_sha256"],
+        "targets": {n: {k: v for k, v in blk.items() if k not in ("inputs_sha256",)}
+                    for n, blk in targets.items()},
     }
-
-    if not args.no_cpu_baseline:
+    if cpu_leg:
         from oracle import oracle as orc
-        got = out.cpu().numpy().astype(np.float64)
-        ref = None
-        runs = []
-        deadline = time.time() + args.cpu_seconds
-        while True:
-            t1 = time.perf_counter()
-            if fp8:
-                ref = orc.paged_attention_fp8_f64(x8.q, x8.k8, x8.v8, x8.block_tables,
-                                                  x8.context_lens, x8.scale, x8.k_scale,
-                                                  x8.v_scale)
-            else:
-                ref = orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
-                                              x.context_lens, x.scale)
-            runs.append(time.perf_counter() - t1)
-            if time.time() > deadline or len(runs) >= 200:
-                break
-        t_cpu = sorted(runs)[len(runs) // 2]
-        diff = np.abs(got - ref)
+        runs, t_cpu = hx["runs"], hx["t_cpu"]
+        w = gen.WORKLOADS[args.workload]
         result["cpu_baseline"] = {
-            "value": round(kv_bytes / t_cpu / 1e9, 3), "unit": "GB/s",
+            "value": round(hx["kv_bytes"] / t_cpu / 1e9, 3), "unit": "GB/s",
             "us_per_step": round(t_cpu * 1e6, 1), "cores": orc.max_threads(), "kind": "oracle",
             "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
             "sample": f"the whole {args.workload} step ({args.kv_dtype} KV, all "
                       f"{w.num_seqs * w.num_q_heads} (sequence, head) rows), fp64, median of "
-                      f"{len(runs)} run(s) over {sum(runs):.1f} s of CPU time"}
-        result["parity"] = {"abs": float(diff.max()),
-                            "rel": float((diff / np.maximum(np.abs(ref), 1e-3)).max()),
-                            "rows_checked": int(w.num_seqs * w.num_q_heads)}
+                      f"{len(runs)} run(s) over {sum(runs):.1f} s of wall time"}
         result["gpu_speedup_vs_cpu_oracle"] = round(t_cpu * 1e6 / us, 1)
 
     print(json.dumps(result), flush=True)

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 4
+#define PA_ABI_VERSION 5
 #define PA_HEAD_DIM 128
 #define PA_BLOCK_SIZE 16
 #define PA_G_MAX 16      /* query heads per KV head */
@@ -223,6 +223,27 @@ typedef struct pa_plan_info {
     int32_t prefetch_distance; /* the look-ahead distance k in effect */
 } pa_plan_info;
 
+/* What the auto plan takes from the device.  paged_attn_plan,
+   paged_attn_workspace_size and the decode calls plan for the current device,
+   whose figures are queried once (hipDeviceGetAttribute: multiprocessor
+   count, LDS per multiprocessor and per block) and cached per device; where
+   no device can be queried the MI355X figures stand in.  A stream restricted
+   to fewer CUs (a CU mask) is not seen by the query: plan such a device with
+   paged_attn_plan_for_device instead of relying on the auto sizes. */
+typedef struct pa_device_info {
+    int32_t compute_units;           /* CUs a launch is spread over: 256 on MI355X */
+    int32_t lds_bytes_per_cu;        /* LDS a CU holds: 163840 on gfx950 */
+    int32_t lds_bytes_per_workgroup; /* LDS one work-group may take: 163840 on
+                                        gfx950; <= lds_bytes_per_cu */
+    int32_t queried;                 /* set by paged_attn_device_info: 1 if read
+                                        from the device, 0 for the MI355X
+                                        figures; ignored as an input */
+} pa_device_info;
+
+/* The current device's figures (or the MI355X ones, queried = 0, when there
+   is none).  Host-only; never synchronises. */
+int paged_attn_device_info(pa_device_info *info);
+
 /* Fill *opts with the defaults (prefetch = library default, auto sizes). */
 void paged_attn_default_options(pa_options *opts);
 
@@ -277,13 +298,32 @@ int paged_attn_decode_noalloc(const void *q, const void *k_cache, const void *v_
                               float scale, void *out, const pa_shape *shape,
                               const pa_options *opts, void *stream);
 
-/* Plan for (shape, opts) without launching.  Host-only. */
+/* Plan for (shape, opts) on the current device without launching.
+   Host-only. */
 int paged_attn_plan(const pa_shape *shape, const pa_options *opts,
                     pa_plan_info *info);
+
+/* The plan the library would make on a device with these figures
+   (compute_units 1..65536, 1024 <= lds_bytes_per_workgroup <=
+   lds_bytes_per_cu, else PA_ERR_INVALID_ARG).  Host-only. */
+int paged_attn_plan_for_device(const pa_shape *shape, const pa_options *opts,
+                               const pa_device_info *device, pa_plan_info *info);
 
 /* Workspace bytes paged_attn_decode needs for (shape, opts); 0 if none or if
    the arguments are invalid.  Host-only. */
 size_t paged_attn_workspace_size(const pa_shape *shape, const pa_options *opts);
+
+/* K from the plain token-major layout [num_blocks][num_kv_heads][16][128]
+   (token, dim; one value per element, fp16 or E4M3 bytes by kv_dtype) into
+   the grouped layout paged_attn_decode / paged_attn_decode_fp8 read (see
+   the layouts above): within each (block, KV head) slice, the 16-byte piece
+   of token t holding dims 8g..8g+7 (fp16) or 16g..16g+15 (E4M3) moves to
+   position (g, t).  A pure reindexing, bit for bit.  Both pointers are
+   device pointers to dense pools, 16-byte aligned; the two ranges must not
+   overlap (PA_ERR_INVALID_ARG).  Asynchronous on `stream` like the decode
+   calls.  V needs no packing: its layout is the token-major one. */
+int paged_attn_pack_k(const void *k_token_major, void *k_cache, int64_t num_blocks,
+                      int32_t num_kv_heads, int32_t kv_dtype, void *stream);
 
 /* Streaming-read ceiling: reads `bytes` (a multiple of 16, 16-byte aligned)
    from device buffer `buf` once, in 8 KiB chunks per wavefront of the same

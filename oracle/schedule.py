@@ -16,20 +16,16 @@ Event = Tuple[int, int, Optional[int]]  # (iteration, computed block, fetched-ah
 
 
 def wave_schedule(s: int, e: int, w: int, wave: int, distance: int = 1) -> List[Event]:
-    """Events of one wave, in program order.  `distance` generalises the
-    look-ahead to block_idx + distance * w (Algorithm 1 is distance 1)."""
+    """Events of one wave, in program order.  The wave's blocks are the
+    arithmetic progression s + wave, s + wave + w, ... below e; in its n-th
+    iteration it computes the n-th of them and fetches ahead the block
+    distance * w further on, if that one is still below e (the review's
+    Algorithm 1 is distance 1)."""
     if w <= 0 or not 0 <= wave < w or distance < 1:
         raise ValueError("need 0 <= wave < w and distance >= 1")
-    events: List[Event] = []
-    block_idx = s + wave
-    it = 0
-    while block_idx < e:
-        tgt = block_idx + distance * w
-        ahead = tgt if tgt < e else None
-        events.append((it, block_idx, ahead))
-        block_idx += w
-        it += 1
-    return events
+    blocks = range(s + wave, e, w)
+    return [(n, j, j + distance * w if j + distance * w < e else None)
+            for n, j in enumerate(blocks)]
 
 
 def group_schedule(s: int, e: int, w: int, distance: int = 1) -> Dict[int, List[Event]]:

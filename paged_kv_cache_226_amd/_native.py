@@ -53,10 +53,15 @@ class PaPlanInfo(ctypes.Structure):
                 ("prefetch_distance", ctypes.c_int32)]
 
 
+class PaDeviceInfo(ctypes.Structure):
+    _fields_ = [("compute_units", ctypes.c_int32), ("lds_bytes_per_cu", ctypes.c_int32),
+                ("lds_bytes_per_workgroup", ctypes.c_int32), ("queried", ctypes.c_int32)]
+
+
 _lib = None
 
 # the PA_ABI_VERSION whose struct layouts the classes above mirror
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class NativeLibraryMissing(RuntimeError):
@@ -87,8 +92,16 @@ def lib():
     L.paged_attn_plan.argtypes = [ctypes.POINTER(PaShape), ctypes.POINTER(PaOptions),
                                   ctypes.POINTER(PaPlanInfo)]
     L.paged_attn_plan.restype = ctypes.c_int
+    L.paged_attn_plan_for_device.argtypes = [ctypes.POINTER(PaShape), ctypes.POINTER(PaOptions),
+                                             ctypes.POINTER(PaDeviceInfo),
+                                             ctypes.POINTER(PaPlanInfo)]
+    L.paged_attn_plan_for_device.restype = ctypes.c_int
+    L.paged_attn_device_info.argtypes = [ctypes.POINTER(PaDeviceInfo)]
+    L.paged_attn_device_info.restype = ctypes.c_int
     L.paged_attn_workspace_size.argtypes = [ctypes.POINTER(PaShape), ctypes.POINTER(PaOptions)]
     L.paged_attn_workspace_size.restype = ctypes.c_size_t
+    L.paged_attn_pack_k.argtypes = [vp, vp, ctypes.c_int64, i32, i32, vp]
+    L.paged_attn_pack_k.restype = ctypes.c_int
     L.paged_attn_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
     L.paged_attn_stream_read.restype = ctypes.c_int
     L.paged_attn_stream_read_sink_bytes.argtypes = [ctypes.c_size_t]
@@ -127,10 +140,27 @@ def make_shape(num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq, num_bloc
                    int(v_head_stride), int(kv_dtype))
 
 
-def plan(shape: PaShape, opts: PaOptions = None) -> dict:
+def plan(shape: PaShape, opts: PaOptions = None, device: dict = None) -> dict:
+    """The plan on the current device, or on a device with the given figures
+    (compute_units, lds_bytes_per_cu, lds_bytes_per_workgroup)."""
     info = PaPlanInfo()
-    rc = lib().paged_attn_plan(ctypes.byref(shape), ctypes.byref(opts) if opts else None,
-                               ctypes.byref(info))
+    o = ctypes.byref(opts) if opts else None
+    if device is None:
+        rc = lib().paged_attn_plan(ctypes.byref(shape), o, ctypes.byref(info))
+    else:
+        dv = PaDeviceInfo(int(device["compute_units"]), int(device["lds_bytes_per_cu"]),
+                          int(device["lds_bytes_per_workgroup"]), 0)
+        rc = lib().paged_attn_plan_for_device(ctypes.byref(shape), o, ctypes.byref(dv),
+                                              ctypes.byref(info))
     if rc != PA_OK:
         raise ValueError(f"paged_attn_plan: {error_string(rc)} ({rc})")
     return {f: getattr(info, f) for f, _ in PaPlanInfo._fields_}
+
+
+def device_info() -> dict:
+    """The figures the library plans the current device with."""
+    d = PaDeviceInfo()
+    rc = lib().paged_attn_device_info(ctypes.byref(d))
+    if rc != PA_OK:
+        raise RuntimeError(f"paged_attn_device_info: {error_string(rc)} ({rc})")
+    return {f: getattr(d, f) for f, _ in PaDeviceInfo._fields_}

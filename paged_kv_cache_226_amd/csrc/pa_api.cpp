@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/paged_attn.h"
 #include "pa_internal.h"
 
@@ -13,30 +15,40 @@ namespace {
 
 constexpr int kDefaultPrefetch = PA_PREFETCH_REG;
 constexpr int kMaxPartitionBlocks = 1024;  // LDS slice of the block table: 4 KiB
-constexpr size_t kMaxLdsBytes = 163840;    // LDS one gfx950 work-group can hold
+
+// What the plan needs to know of the device: the CUs the grid is spread
+// over and the LDS a CU and a work-group can hold.  Queried once per device
+// (hipDeviceGetAttribute) and cached; where no device can be queried the
+// MI355X figures stand in (256 CUs, 160 KiB of LDS per CU and per
+// work-group).
+struct DeviceInfo {
+  int64_t cus;
+  size_t lds_per_cu;
+  size_t lds_per_wg;
+};
+constexpr DeviceInfo kMI355X = {256, 163840, 163840};
+
 // Auto plan, from measurements over the model shapes, their tensor-parallel
-// shards and a batch x context grid (U = sequences x KV heads):
-//  * U >= kOnePartitionUnits (one work-group per CU on 256 CUs): no split, so
-//    no partials and no reduce launch.  Splitting further only added
-//    per-partition overhead, even for ragged batches once the longest
-//    sequences are dispatched first.
-//  * Such work-groups get 8 waves while U < kFourWaveUnits and the table is
-//    at least kLongTableBlocks wide: with under three work-groups per CU the
-//    long sequences then finish on twice the waves (up to 9 % on a ragged
-//    batch, within 2 % either way on uniform ones).  Otherwise 4 waves: at 3
-//    resident waves per SIMD a CU holds three 4-wave work-groups but only one
-//    8-wave one.
-//  * U < kOnePartitionUnits: about kOnePartitionUnits / U partitions of
-//    kMinAutoPartition..kMaxAutoPartition blocks, 8 waves (equal or better
-//    than 4 on every split plan measured).  Partitions may shrink to
-//    kMinShortPartition blocks while that gives at most kReducePartitions
-//    of them (the reduce then loads every partial at once): batch 8 x 1K
-//    tokens of a GQA 32/8 layer, 34 MB, took 12.9 us as one partition and
-//    9.9 us as four 16-block ones.  Beyond that many partitions the reduce
-//    costs more than the extra CUs bring (two 64K-token sequences: 37 us in
-//    64-block partitions, 52 us in 32-block ones).
-constexpr int64_t kOnePartitionUnits = 256;
-constexpr int64_t kFourWaveUnits = 768;
+// shards and a batch x context grid (U = sequences x KV heads, C = CUs):
+//  * U >= C (one work-group per CU): no split, so no partials and no reduce
+//    launch.  Splitting further only added per-partition overhead, even for
+//    ragged batches once the longest sequences are dispatched first.
+//  * Such work-groups get 8 waves while U < kFourWaveUnitsPerCU * C and the
+//    table is at least kLongTableBlocks wide: with under three work-groups
+//    per CU the long sequences then finish on twice the waves (up to 9 % on
+//    a ragged batch, within 2 % either way on uniform ones).  Otherwise 4
+//    waves: at 3 resident waves per SIMD a CU holds three 4-wave
+//    work-groups but only one 8-wave one.
+//  * U < C: about C / U partitions of kMinAutoPartition..kMaxAutoPartition
+//    blocks, 8 waves (equal or better than 4 on every split plan measured).
+//    Partitions may shrink to kMinShortPartition blocks while that gives at
+//    most kReducePartitions of them (the reduce then loads every partial at
+//    once): batch 8 x 1K tokens of a GQA 32/8 layer, 34 MB, took 12.9 us as
+//    one partition and 9.9 us as four 16-block ones.  Beyond that many
+//    partitions the reduce costs more than the extra CUs bring (two
+//    64K-token sequences: 37 us in 64-block partitions, 52 us in 32-block
+//    ones).
+constexpr int64_t kFourWaveUnitsPerCU = 3;
 constexpr int kLongTableBlocks = 512;
 constexpr int kMinAutoPartition = 64;
 constexpr int kMinShortPartition = 16;
@@ -48,11 +60,61 @@ constexpr int kTwoLoopPartitionBlocks = 32;
 //    resident from the start the dispatch order changes nothing, and the
 //    ranking (a dependent read of every context length before the block
 //    table) only adds latency: 2-4 us on grids of 256 work-groups.
-//    Residency: kCUs x min(kResidentWavesPerCU / W, LDS per CU / LDS per
-//    work-group); 3 waves per SIMD is what the register ring's VGPRs allow.
-constexpr int64_t kCUs = 256;
+//    Residency: C x min(kResidentWavesPerCU / W, LDS per CU / LDS per
+//    work-group); 3 waves per SIMD (of the 4 of a CDNA CU) is what the
+//    register ring's VGPRs allow.
 constexpr int kResidentWavesPerCU = 12;
-constexpr size_t kLdsPerCU = 163840;
+
+bool valid_device(const pa_device_info* d) {
+  return d && d->compute_units >= 1 && d->compute_units <= 65536 &&
+         d->lds_bytes_per_workgroup >= 1024 &&
+         d->lds_bytes_per_cu >= d->lds_bytes_per_workgroup;
+}
+
+DeviceInfo from_public(const pa_device_info* d) {
+  return DeviceInfo{d->compute_units, (size_t)d->lds_bytes_per_cu,
+                    (size_t)d->lds_bytes_per_workgroup};
+}
+
+// The current device's figures, cached per device; the MI355X figures (and
+// queried = 0) when there is no device to query.
+void current_device(pa_device_info* out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static pa_device_info cache[kMaxDevices];
+  static bool have[kMaxDevices];
+  out->compute_units = (int32_t)kMI355X.cus;
+  out->lds_bytes_per_cu = (int32_t)kMI355X.lds_per_cu;
+  out->lds_bytes_per_workgroup = (int32_t)kMI355X.lds_per_wg;
+  out->queried = 0;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!have[dev]) {
+    int cus = 0, lds_cu = 0, lds_wg = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                              dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds_wg, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess)
+      return;
+    pa_device_info q;
+    q.compute_units = cus;
+    q.lds_bytes_per_workgroup = lds_wg;
+    q.lds_bytes_per_cu = lds_cu > lds_wg ? lds_cu : lds_wg;
+    q.queried = 1;
+    if (!valid_device(&q)) return;
+    cache[dev] = q;
+    have[dev] = true;
+  }
+  *out = cache[dev];
+}
+
+DeviceInfo current_device_info() {
+  pa_device_info d;
+  current_device(&d);
+  return from_public(&d);
+}
 
 struct Plan {
   int pf, dist, waves, PB, P, order, two;
@@ -87,7 +149,7 @@ int check_shape(const pa_shape* sh) {
   return PA_OK;
 }
 
-int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
+int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Plan* pl) {
   int rc = check_shape(sh);
   if (rc) return rc;
   pa_options d;
@@ -137,15 +199,15 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   int waves = o->waves_per_wg;
   if (waves == 0 && two) waves = 4;
   if (waves == 0) {
-    const bool whole = o->partition_blocks == 0 ? units >= kOnePartitionUnits
-                                                : o->partition_blocks >= MB;
+    const bool whole = o->partition_blocks == 0 ? units >= dv.cus : o->partition_blocks >= MB;
     waves = 4;
-    if (whole && units < kFourWaveUnits && MB >= kLongTableBlocks && MB <= kMaxPartitionBlocks &&
-        pa::decode_lds_bytes(MB, g, 8, B, rank, 8 * slot) <= kMaxLdsBytes)
+    if (whole && units < kFourWaveUnitsPerCU * dv.cus && MB >= kLongTableBlocks &&
+        MB <= kMaxPartitionBlocks &&
+        pa::decode_lds_bytes(MB, g, 8, B, rank, 8 * slot) <= dv.lds_per_wg)
       waves = 8;
     const int split_pb = MB < kMaxAutoPartition ? MB : kMaxAutoPartition;
     if (o->partition_blocks == 0 && !whole &&
-        pa::decode_lds_bytes(split_pb, g, 8, B, rank, 8 * slot) <= kMaxLdsBytes)
+        pa::decode_lds_bytes(split_pb, g, 8, B, rank, 8 * slot) <= dv.lds_per_wg)
       waves = 8;
   }
 
@@ -155,11 +217,11 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   } else if (two) {
     // 512-token partitions, halved until the scores fit in LDS
     PB = kTwoLoopPartitionBlocks < MB ? kTwoLoopPartitionBlocks : MB;
-    while (PB > 1 && pa::two_loop_lds_bytes(PB, g, waves, B, rank) > kMaxLdsBytes) PB /= 2;
-  } else if (units >= kOnePartitionUnits) {
+    while (PB > 1 && pa::two_loop_lds_bytes(PB, g, waves, B, rank) > dv.lds_per_wg) PB /= 2;
+  } else if (units >= dv.cus) {
     PB = MB < kMaxPartitionBlocks ? MB : kMaxPartitionBlocks;
   } else {
-    const int64_t want = (kOnePartitionUnits + units - 1) / units;
+    const int64_t want = (dv.cus + units - 1) / units;
     int64_t pb = (MB + want - 1) / want;
     pb = (pb + waves - 1) / waves * waves;  // whole rounds of the W waves
     if (pb < kMinAutoPartition) {
@@ -180,14 +242,14 @@ int make_plan(const pa_shape* sh, const pa_options* o, Plan* pl) {
   if (o->seq_order == PA_ORDER_AUTO && rank) {
     const size_t l = lds_for(true);
     const int64_t by_waves = kResidentWavesPerCU / waves;
-    const int64_t by_lds = (int64_t)(kLdsPerCU / (l > 0 ? l : 1));
-    if (wgs <= kCUs * (by_waves < by_lds ? by_waves : by_lds)) {
+    const int64_t by_lds = (int64_t)(dv.lds_per_cu / (l > 0 ? l : 1));
+    if (wgs <= dv.cus * (by_waves < by_lds ? by_waves : by_lds)) {
       order = PA_ORDER_NATURAL;
       rank = false;
     }
   }
   const size_t lds = lds_for(rank);
-  if (lds > kMaxLdsBytes) return PA_ERR_UNSUPPORTED;
+  if (lds > dv.lds_per_wg) return PA_ERR_UNSUPPORTED;
   memset(pl, 0, sizeof(*pl));
   pl->order = order;
   pl->two = two ? 1 : 0;
@@ -211,10 +273,17 @@ void paged_attn_default_options(pa_options* o) {
   o->prefetch = -1;
 }
 
-int paged_attn_plan(const pa_shape* sh, const pa_options* o, pa_plan_info* info) {
+int paged_attn_device_info(pa_device_info* info) {
+  if (!info) return PA_ERR_INVALID_ARG;
+  current_device(info);
+  return PA_OK;
+}
+
+static int plan_info(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv,
+                     pa_plan_info* info) {
   if (!info) return PA_ERR_INVALID_ARG;
   Plan pl;
-  int rc = make_plan(sh, o, &pl);
+  int rc = make_plan(sh, o, dv, &pl);
   if (rc) return rc;
   memset(info, 0, sizeof(*info));
   info->prefetch = pl.pf;
@@ -229,9 +298,19 @@ int paged_attn_plan(const pa_shape* sh, const pa_options* o, pa_plan_info* info)
   return PA_OK;
 }
 
+int paged_attn_plan(const pa_shape* sh, const pa_options* o, pa_plan_info* info) {
+  return plan_info(sh, o, current_device_info(), info);
+}
+
+int paged_attn_plan_for_device(const pa_shape* sh, const pa_options* o,
+                               const pa_device_info* dev, pa_plan_info* info) {
+  if (!valid_device(dev)) return PA_ERR_INVALID_ARG;
+  return plan_info(sh, o, from_public(dev), info);
+}
+
 size_t paged_attn_workspace_size(const pa_shape* sh, const pa_options* o) {
   Plan pl;
-  if (make_plan(sh, o, &pl)) return 0;
+  if (make_plan(sh, o, current_device_info(), &pl)) return 0;
   return pl.ws_bytes;
 }
 
@@ -265,7 +344,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
                       v_scale, out, sh);
   if (rc) return rc;
   Plan pl;
-  rc = make_plan(sh, o, &pl);
+  rc = make_plan(sh, o, current_device_info(), &pl);
   if (rc) return rc;
   // cache strides: 0 = dense; slices may be spread out but never overlap
   const int64_t slice = (int64_t)PA_BLOCK_SIZE * PA_HEAD_DIM * (kv8 ? 1 : 2);
@@ -377,7 +456,7 @@ int paged_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_
     paged_attn_default_options(&oo);
   }
   Plan pl;
-  rc = make_plan(sh, &oo, &pl);
+  rc = make_plan(sh, &oo, current_device_info(), &pl);
   if (rc) return rc;
   if (pl.ws_bytes > pa::kNoAllocScratchBytes) return PA_ERR_WORKSPACE;
   // the current device's copy of the library's scratch array (its address
@@ -388,6 +467,25 @@ int paged_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_
   oo.workspace_bytes = pa::kNoAllocScratchBytes;
   return decode_impl(q, k_cache, v_cache, block_tables, context_lens, scale, false, 1.f, 1.f,
                      out, sh, &oo, stream);
+}
+
+int paged_attn_pack_k(const void* k_token_major, void* k_cache, int64_t num_blocks,
+                      int32_t num_kv_heads, int32_t kv_dtype, void* stream) {
+  if (!k_token_major || !k_cache || !aligned16(k_token_major) || !aligned16(k_cache))
+    return PA_ERR_INVALID_ARG;
+  if (num_blocks < 1 || num_kv_heads < 1) return PA_ERR_INVALID_ARG;
+  if (kv_dtype != PA_KV_F16 && kv_dtype != PA_KV_E4M3) return PA_ERR_INVALID_ARG;
+  const int64_t slice = (int64_t)PA_BLOCK_SIZE * PA_HEAD_DIM * (kv_dtype == PA_KV_E4M3 ? 1 : 2);
+  if (num_blocks > INT64_MAX / 4 / slice / num_kv_heads) return PA_ERR_UNSUPPORTED;
+  const int64_t slices = num_blocks * num_kv_heads;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(k_token_major);
+  const uintptr_t b = reinterpret_cast<uintptr_t>(k_cache);
+  const uintptr_t n = (uintptr_t)(slices * slice);
+  if (a < b + n && b < a + n) return PA_ERR_INVALID_ARG;  // the two must not overlap
+  if (pa::launch_pack_k(k_token_major, k_cache, slices, kv_dtype == PA_KV_E4M3,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
+    return PA_ERR_HIP;
+  return PA_OK;
 }
 
 // Streaming-read grid: 2048 work-groups of 256 threads (8 per CU on 256

@@ -73,6 +73,7 @@ hipError_t launch_decode_two_loop(const DecodeArgs& a, int pf, int waves, hipStr
 hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int waves,
                          hipStream_t st);
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_pack_k(const void* in, void* out, int64_t slices, bool kv8, hipStream_t st);
 hipError_t launch_stream_read(const void* buf, size_t bytes, void* sink, int groups,
                               hipStream_t st);
 

@@ -1093,6 +1093,26 @@ hipError_t launch_reduce(const DecodeArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
+// K from the token-major layout to the grouped one.  A (block, head) slice is
+// 16 token rows of R 16-byte pieces (R = 16 for fp16, 8 for E4M3); piece
+// (t, g) of the input becomes piece (g, t) of the output.  Each thread moves
+// one piece per step of a grid-stride loop, so every load instruction reads
+// 1 KiB of contiguous input.
+__global__ void __launch_bounds__(256) pack_k_kernel(const u32x4* __restrict__ in,
+                                                     u32x4* __restrict__ out, int64_t slices,
+                                                     int R) {
+  const int64_t per = 16 * (int64_t)R;  // pieces per slice
+  const int64_t total = slices * per;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t sl = i / per;
+    const int p = (int)(i - sl * per);
+    const int t = p / R, g = p - t * R;
+    out[sl * per + g * 16 + t] = in[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Scratch of the no-allocation entry point: the partition partials of calls
 // that cannot allocate.  Every GPU the library runs on holds its own copy
 // for the life of the process.  On the host, `noalloc_scratch_array` names a
@@ -1118,6 +1138,16 @@ hipError_t noalloc_scratch(void** ptr) {
   }
   *ptr = addr[dev];
   return hipSuccess;
+}
+
+hipError_t launch_pack_k(const void* in, void* out, int64_t slices, bool kv8, hipStream_t st) {
+  const int R = kv8 ? 8 : 16;
+  const int64_t pieces = slices * 16 * R;
+  int64_t groups = (pieces + 255) / 256;
+  if (groups > 65536) groups = 65536;  // grid-stride beyond
+  hipLaunchKernelGGL(pack_k_kernel, dim3((unsigned)groups), dim3(256), 0, st,
+                     reinterpret_cast<const u32x4*>(in), reinterpret_cast<u32x4*>(out), slices, R);
+  return hipGetLastError();
 }
 
 hipError_t launch_stream_read(const void* buf, size_t bytes, void* sink, int groups,

@@ -49,6 +49,31 @@ def _slice_contiguous(t: torch.Tensor) -> bool:
     return True
 
 
+def _pool_strides_nonzero(t: torch.Tensor, name: str):
+    """A zero byte stride means 'dense' to the library, so a pool whose block
+    or head dimension is a broadcast (stride 0, e.g. from expand) would be read
+    as a dense pool of that many distinct slices: refuse it."""
+    for d in (0, 1):
+        if t.shape[d] > 1 and t.stride(d) == 0:
+            raise ValueError(f"{name} has stride 0 over dimension {d} (a broadcast view); "
+                             "the cache needs one slice per (block, head)")
+
+
+def check_debug_shapes(B: int, Hkv: int, MB: int, debug_gather_k=None, debug_trace=None,
+                       debug_error_word=None):
+    """The debug outputs must be exactly as large as the kernel writes them:
+    debug_gather_k [B, Hkv, MB*16, 128], debug_trace [B, Hkv, MB, 2], and at
+    least one error word."""
+    if debug_gather_k is not None and tuple(debug_gather_k.shape) != (B, Hkv, MB * 16, 128):
+        raise ValueError(f"debug_gather_k must be [{B}, {Hkv}, {MB * 16}, 128], got "
+                         f"{list(debug_gather_k.shape)}")
+    if debug_trace is not None and tuple(debug_trace.shape) != (B, Hkv, MB, 2):
+        raise ValueError(f"debug_trace must be [{B}, {Hkv}, {MB}, 2], got "
+                         f"{list(debug_trace.shape)}")
+    if debug_error_word is not None and debug_error_word.numel() < 1:
+        raise ValueError("debug_error_word must hold at least one int32")
+
+
 def shape_of(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,
              v_cache: Optional[torch.Tensor] = None) -> nat.PaShape:
     """pa_shape of these tensors; K and V may be views into a larger pool
@@ -56,6 +81,9 @@ def shape_of(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,
     K cache is E4M3."""
     B, Hq, D = q.shape
     NB, Hkv, G8, T, X = k_cache.shape
+    _pool_strides_nonzero(k_cache, "k_cache")
+    if v_cache is not None:
+        _pool_strides_nonzero(v_cache, "v_cache")
     ek = k_cache.element_size()
     kw0 = dict(kv_dtype=nat.KV_E4M3 if ek == 1 else nat.KV_F16)
     kw = dict(k_block_stride=k_cache.stride(0) * ek, k_head_stride=k_cache.stride(1) * ek)
@@ -157,6 +185,8 @@ class DecodeCall:
                              % ((16, 16) if fp8 else (8, 8)))
         if block_tables.shape[0] != B or context_lens.shape[0] != B:
             raise ValueError("inconsistent shapes")
+        check_debug_shapes(B, Hkv, block_tables.shape[1], debug_gather_k, debug_trace,
+                           debug_error_word)
         self.device = q.device
         self._index = q.get_device()
         _same_device(self._index, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
@@ -334,6 +364,40 @@ def paged_attn_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                               structure=structure, workspace=workspace,
                               debug_gather_k=debug_gather_k, debug_trace=debug_trace,
                               debug_error_word=debug_error_word, stream=stream)()
+
+
+def pack_k(k_token_major: torch.Tensor, out: Optional[torch.Tensor] = None,
+           stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """K from the token-major layout [NB, Hkv, 16, 128] (fp16, or E4M3 as
+    uint8 / float8_e4m3fn) into the layout the decode calls read: fp16
+    [NB, Hkv, 16, 16, 8], E4M3 [NB, Hkv, 8, 16, 16] (paged_attn_pack_k, on the
+    device, bit for bit)."""
+    k = k_token_major
+    if k.dtype == torch.float8_e4m3fn:
+        k = k.view(torch.uint8)
+    if not isinstance(k, torch.Tensor) or not k.is_cuda or not k.is_contiguous():
+        raise ValueError("k_token_major must be a contiguous device tensor")
+    if k.dim() != 4 or tuple(k.shape[2:]) != (16, 128):
+        raise ValueError("k_token_major must be [NB, Hkv, 16, 128]")
+    if k.dtype not in (torch.float16, torch.uint8):
+        raise TypeError(f"k_token_major must be fp16 or E4M3 bytes, got {k.dtype}")
+    fp8 = k.dtype == torch.uint8
+    NB, Hkv = k.shape[:2]
+    shape = (NB, Hkv, 8, 16, 16) if fp8 else (NB, Hkv, 16, 16, 8)
+    if out is None:
+        out = torch.empty(shape, dtype=k.dtype, device=k.device)
+    elif (tuple(out.shape) != shape or out.dtype != k.dtype or not out.is_contiguous() or
+          out.device != k.device):
+        raise ValueError(f"out must be a contiguous {k.dtype} tensor {list(shape)} on {k.device}")
+    st = _stream_handle(stream, k.device)
+    with torch.cuda.device(k.device):
+        rc = nat.lib().paged_attn_pack_k(ctypes.c_void_p(k.data_ptr()),
+                                         ctypes.c_void_p(out.data_ptr()), ctypes.c_int64(NB),
+                                         ctypes.c_int32(Hkv),
+                                         ctypes.c_int32(nat.KV_E4M3 if fp8 else nat.KV_F16), st)
+    if rc != nat.PA_OK:
+        raise RuntimeError(f"paged_attn_pack_k: {nat.error_string(rc)} ({rc})")
+    return out
 
 
 def stream_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None,

@@ -143,6 +143,65 @@ def sweep_fetch(profile_jsonl, fetch_dir, workload, out_dir, command):
     return path
 
 
+def sweep_timing(jsonl, workload, out_dir, command):
+    """µs and GB/s per point of a `bench.py --sweep` run, look-ahead off and
+    in the default mode, with the sampled parity of the default mode."""
+    points = [json.loads(l) for l in open(jsonl) if l.startswith('{"sweep"')]
+    lines = [f"# Batch x context sweep, timings: {workload}", "", "```", "command:",
+             *["    " + c for c in command.split(" ;; ") if c], "```", "",
+             "One decode step per point (prepared call, event-timed mean over the steps); "
+             "KV bytes = 2 * Hkv * 128 * 2 B * batch * context.  'on' is the library's "
+             "default look-ahead; parity is the default mode's output on the first and last "
+             "sequence (every head) against the fp64 oracle.", "",
+             "| batch | context | KV bytes | partitions | us off | us on | GB/s off | GB/s on |"
+             " % of 8 TB/s on | on vs off | parity abs | parity rel |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for p in points:
+        off_gbps = p["kv_bytes"] / p["us_off"] / 1e3
+        lines.append(f"| {p['batch']} | {p['context']} | {p['kv_bytes']} | {p['partitions']} | "
+                     f"{p['us_off']:.2f} | {p['us_on']:.2f} | {off_gbps:.0f} | "
+                     f"{p['GBps_on']:.0f} | {p['pct_hbm_peak_on']:.1f} | "
+                     f"{p['speedup_on_vs_off']:.3f} | {p['parity_abs']:.2e} | "
+                     f"{p['parity_rel']:.2e} |")
+    path = os.path.join(out_dir, f"pa_decode_sweep_{workload}_timing.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
+def request_path_table(dirs, tag, head, out_dir, kernel_us):
+    """Per look-ahead mode, the mean per launch of every counter in the given
+    passes (summed over the dimensions rocprofv3 reports, e.g. TCC channels
+    and XCDs), next to the kernel-trace duration."""
+    per = collections.defaultdict(dict)
+    names = []
+    for d in dirs:
+        agg = collections.defaultdict(float)
+        launches = collections.defaultdict(set)
+        for r in _rows(d, "_counter_collection.csv"):
+            m = decode_mode(r["Kernel_Name"])
+            if m is None:
+                continue
+            agg[(m, r["Counter_Name"])] += float(r["Counter_Value"])
+            launches[m].add(r["Dispatch_Id"])
+        for (m, c), v in agg.items():
+            per[m][c] = v / max(1, len(launches[m]))
+            if c not in names:
+                names.append(c)
+    lines = ["# pa_decode memory request path per look-ahead mode: " + tag, "", "```", *head,
+             "```", "", "Mean per decode launch of each counter (summed over instances).", "",
+             "| mode | kernel us | " + " | ".join(names) + " |",
+             "|---|---|" + "---|" * len(names)]
+    for m in sorted(per):
+        us = kernel_us.get(m)
+        lines.append(f"| {MODE_NAMES[m]} | {us:.2f} | " if us else f"| {MODE_NAMES[m]} | | ")
+        lines[-1] += " | ".join(f"{per[m].get(c, float('nan')):.4g}" for c in names) + " |"
+    path = os.path.join(out_dir, f"pa_decode_{tag}_request_path.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
@@ -154,6 +213,12 @@ def main(argv=None):
     ap.add_argument("--sq")
     ap.add_argument("--valu", help="pass with SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_BUSY_CYCLES "
                                    "SQ_INSTS SQ_WAVE_CYCLES GRBM_GUI_ACTIVE")
+    ap.add_argument("--request-path", nargs="*", default=[],
+                    help="counter directories of passes over the memory request path "
+                         "(TA / TD / TCP / TCC / EA counters): one table of their per-mode "
+                         "means, pa_decode_<tag>_request_path.md")
+    ap.add_argument("--sweep-timing", help="JSON lines of `bench.py --sweep`: writes the "
+                                           "per-point timing table")
     ap.add_argument("--command", default="", help="the command lines that produced the inputs")
     ap.add_argument("--source-hash", default="")
     ap.add_argument("--out-dir", default="profiles")
@@ -169,6 +234,9 @@ def main(argv=None):
     KV8 = a.kv_dtype == "fp8"
     if a.sweep_profile:
         print(sweep_fetch(a.sweep_profile, a.fetch, a.workload, a.out_dir, a.command))
+        return 0
+    if a.sweep_timing:
+        print(sweep_timing(a.sweep_timing, a.workload, a.out_dir, a.command))
         return 0
     tag = a.workload + ("_fp8" if KV8 else "")
     w = gen.WORKLOADS[a.workload]
@@ -191,6 +259,16 @@ def main(argv=None):
                          f"{pct:.1f} | {gbps} |")
         with open(os.path.join(a.out_dir, f"pa_decode_{tag}_kernel_trace.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
+
+    # average duration of each mode's decode kernel (kernel trace)
+    kernel_us = {}
+    if a.kernel_trace:
+        for name, calls, avg, mn, mx, pct in kernel_stats(a.kernel_trace):
+            if decode_mode(name) is not None:
+                kernel_us[decode_mode(name)] = avg
+
+    if a.request_path:
+        request_path_table(a.request_path, tag, head, a.out_dir, kernel_us)
 
     if a.fetch and a.write:
         fa, wa = counters(a.fetch), counters(a.write)
@@ -244,7 +322,7 @@ def main(argv=None):
             cpi = 4 * v_wcyc[m] / v_insts[m] if v_insts.get(m) and m in v_wcyc else float("nan")
             spi = 4 * wait[m] / v_insts[m] if v_insts.get(m) and m in wait else float("nan")
             wa = wait_any[m] / wcyc[m] if m in wait_any and wcyc.get(m) else float("nan")
-            evidence[m] = (hr, wa, st)
+            evidence[m] = (hr, wa, st, spi, cpi)
             lines.append(f"| {MODE_NAMES[m]} | {rb:.4g} | {rb / kv:.4f} | {wb:.4g} | "
                          f"{100 * hr:.2f} % | {100 * st:.1f} % | {vw:.0f} | {mw:.0f} | "
                          f"{vb:.1f} % | {mu:.1f} % | {cpi:.1f} | {spi:.1f} | {100 * wa:.1f} % |")
@@ -260,11 +338,17 @@ def main(argv=None):
                 f.write(f"hbm_bytes_per_launch_{MODE_NAMES[m]}: {v:.0f}\n")
             # the look-ahead evidence per mode: L2 hit rate, wait share
             # (SQ_WAIT_ANY / SQ_WAVE_CYCLES), issue-stall share
-            # (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES); fractions, nan if not taken
-            for m, (hr, wa, st) in sorted(evidence.items()):
+            # (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES) as fractions; stall cycles
+            # per instruction and cycles per instruction of a wave; the
+            # kernel-trace average duration; nan if not taken
+            for m, (hr, wa, st, spi, cpi) in sorted(evidence.items()):
                 f.write(f"l2_hit_rate_{MODE_NAMES[m]}: {hr:.4f}\n")
                 f.write(f"wait_share_{MODE_NAMES[m]}: {wa:.4f}\n")
                 f.write(f"issue_stall_share_{MODE_NAMES[m]}: {st:.4f}\n")
+                f.write(f"stall_cycles_per_inst_{MODE_NAMES[m]}: {spi:.2f}\n")
+                f.write(f"cycles_per_inst_{MODE_NAMES[m]}: {cpi:.2f}\n")
+            for m, us in sorted(kernel_us.items()):
+                f.write(f"kernel_us_{MODE_NAMES[m]}: {us:.2f}\n")
     return 0
 
 

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function(native_lib):
 
 
 def test_version_and_error_strings(native_lib):
-    assert native_lib.paged_attn_abi_version() == nat.ABI_VERSION == 4
+    assert native_lib.paged_attn_abi_version() == nat.ABI_VERSION == 5
     assert nat.error_string(0) == "ok"
     for code in range(1, 5):
         assert nat.error_string(code) not in ("ok", "unknown status")
@@ -52,7 +52,7 @@ def test_struct_layouts_match_header(native_lib, tmp_path):
     """Every field offset and struct size of the ctypes mirror equals what a C
     compiler makes of include/paged_attn.h."""
     structs = {"pa_shape": nat.PaShape, "pa_options": nat.PaOptions,
-               "pa_plan_info": nat.PaPlanInfo}
+               "pa_plan_info": nat.PaPlanInfo, "pa_device_info": nat.PaDeviceInfo}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "paged_attn.h"',
              'int main(void) {']
     for cname, py in structs.items():
@@ -306,3 +306,133 @@ def test_lds_ring_slots_count_in_the_wave_choice(native_lib, kv, dist, waves):
     o.prefetch_distance = dist
     p = nat.plan(nat.make_shape(64, 32, 8, 512, 1000, kv_dtype=kv), o)
     assert (p["waves_per_wg"], p["num_partitions"]) == (waves, 1)
+
+
+def test_binding_refuses_debug_outputs_of_the_wrong_size(native_lib):
+    """The kernel writes the debug outputs at their full documented size, so a
+    smaller (or otherwise shaped) tensor is refused by the binding."""
+    import torch
+    from paged_kv_cache_226_amd import ops
+    B, Hkv, MB = 3, 2, 5
+    ops.check_debug_shapes(B, Hkv, MB, torch.empty(B, Hkv, MB * 16, 128),
+                           torch.empty(B, Hkv, MB, 2), torch.empty(1))
+    for bad in (dict(debug_gather_k=torch.empty(B, Hkv, MB * 16 - 1, 128)),
+                dict(debug_gather_k=torch.empty(B, Hkv, MB, 16, 128)),
+                dict(debug_trace=torch.empty(B, Hkv, MB - 1, 2)),
+                dict(debug_trace=torch.empty(B, Hkv + 1, MB, 2)),
+                dict(debug_error_word=torch.empty(0))):
+        with pytest.raises(ValueError):
+            ops.check_debug_shapes(B, Hkv, MB, **bad)
+
+
+def test_binding_refuses_broadcast_pools(native_lib):
+    """A zero byte stride reaches the library as 'dense': an expanded (stride
+    0) block or head dimension of a cache is refused instead."""
+    import torch
+    from paged_kv_cache_226_amd import ops
+    q = torch.empty(2, 4, 128, dtype=torch.float16)
+    bt = torch.zeros(2, 4, dtype=torch.int32)
+    one = torch.empty(1, 2, 16, 16, 8, dtype=torch.float16)
+    sh = ops.shape_of(q, one, bt)  # one block: stride 0 is not needed
+    assert sh.num_blocks == 1
+    with pytest.raises(ValueError, match="stride 0"):
+        ops.shape_of(q, one.expand(64, 2, 16, 16, 8), bt)
+    head = torch.empty(8, 1, 16, 16, 8, dtype=torch.float16)
+    with pytest.raises(ValueError, match="stride 0"):
+        ops.shape_of(q, head.expand(8, 2, 16, 16, 8), bt)
+    v1 = torch.empty(1, 2, 16, 128, dtype=torch.float16)
+    with pytest.raises(ValueError, match="v_cache"):
+        ops.shape_of(q, torch.empty(64, 2, 16, 16, 8, dtype=torch.float16), bt,
+                     v1.expand(64, 2, 16, 128))
+    ok = ops.shape_of(q, torch.empty(64, 2, 16, 16, 8, dtype=torch.float16), bt,
+                      torch.empty(64, 2, 16, 128, dtype=torch.float16))
+    assert ok.num_blocks == 64 and ok.v_block_stride == 2 * 16 * 128 * 2
+
+
+MI355X = dict(compute_units=256, lds_bytes_per_cu=163840, lds_bytes_per_workgroup=163840)
+
+
+def test_device_figures_without_a_device_are_the_mi355x_ones(native_lib):
+    """Here no device can be queried: the library plans with the MI355X
+    figures, and planning for those figures explicitly gives the same plans."""
+    import torch
+    info = nat.device_info()
+    if torch.cuda.is_available():
+        pytest.skip("a device is visible: its own figures are used")
+    assert info == dict(MI355X, queried=0)
+    from paged_kv_cache_226_amd import inputs as gen
+    for name, w in gen.WORKLOADS.items():
+        MB = w.max_blocks_per_seq or max(-(-c // 16) for c in w.context_lens)
+        sh = nat.make_shape(w.num_seqs, w.num_q_heads, w.num_kv_heads, MB, w.pool_blocks or 1)
+        for pf in (-1, 0, 4):
+            o = nat.default_options()
+            o.prefetch = pf
+            assert nat.plan(sh, o) == nat.plan(sh, o, device=MI355X), (name, pf)
+
+
+@pytest.mark.parametrize("bad", [dict(compute_units=0), dict(compute_units=70000),
+                                 dict(lds_bytes_per_workgroup=512),
+                                 dict(lds_bytes_per_cu=65536)])
+def test_plan_for_device_refuses_bad_figures(native_lib, bad):
+    dev = dict(MI355X, **bad)
+    with pytest.raises(ValueError, match="invalid argument"):
+        nat.plan(good_shape(), device=dev)
+
+
+@pytest.mark.parametrize("cus", [32, 64, 128, 256, 304, 512])
+def test_plan_rules_follow_the_cu_count(native_lib, cus):
+    """The partition, wave and order rules scale with the device's CU count:
+    one partition per sequence iff there are at least as many (sequence, KV
+    head) units as CUs; 8 waves for such unsplit long tables while there are
+    fewer than three units per CU; longest-first order iff the grid holds
+    more work-groups than the CUs keep resident (three 4-wave ones each)."""
+    dev = dict(MI355X, compute_units=cus)
+    for B in (1, 2, 4, 8, 16, 32, 64, 96, 128, 200, 256):
+        units = B * 8
+        p = nat.plan(nat.make_shape(B, 32, 8, 512, 1), device=dev)
+        assert (p["num_partitions"] == 1) == (units >= cus), (B, p)
+        if units >= cus:
+            assert p["waves_per_wg"] == (8 if units < 3 * cus else 4), (B, p)
+        else:
+            assert p["num_partitions"] >= min(-(-cus // units), 2) and p["waves_per_wg"] == 8
+        # short tables: 4 waves, one partition when units >= cus
+        q = nat.plan(nat.make_shape(B, 32, 8, 64, 1), device=dev)
+        if units >= cus:
+            want = nat.ORDER_LONGEST_FIRST if B >= 2 and units > 3 * cus else nat.ORDER_NATURAL
+            assert (q["waves_per_wg"], q["num_partitions"], q["seq_order"]) == (4, 1, want), (B, q)
+
+
+def test_plan_lds_rules_follow_the_device(native_lib):
+    """The LDS limits come from the device: a plan whose work-group needs more
+    LDS than the device allows is refused, and the residency count that
+    decides the order uses the LDS per CU."""
+    sh = good_shape(max_blocks_per_seq=64)
+    o = nat.default_options()
+    o.prefetch, o.prefetch_distance, o.waves_per_wg = 4, 2, 4  # 96 KiB of LDS slots
+    assert nat.plan(sh, o, device=MI355X)["prefetch"] == 4
+    small = dict(MI355X, lds_bytes_per_cu=65536, lds_bytes_per_workgroup=65536)
+    with pytest.raises(ValueError, match="unsupported"):
+        nat.plan(sh, o, device=small)
+    # 20 sequences x 8 KV heads, 4-wave work-groups with 64 KiB of LDS ring
+    # each (2 per CU by LDS): 256 CUs hold the whole grid at once, 64 CUs
+    # only 128 of its 160 work-groups
+    sh2 = nat.make_shape(20, 64, 8, 64, 1)
+    o2 = nat.default_options()
+    o2.prefetch, o2.prefetch_distance, o2.waves_per_wg = 4, 1, 4
+    assert nat.plan(sh2, o2, device=MI355X)["seq_order"] == nat.ORDER_NATURAL
+    few = dict(MI355X, compute_units=64)
+    assert nat.plan(sh2, o2, device=few)["seq_order"] == nat.ORDER_LONGEST_FIRST
+
+
+def test_pack_k_validation(native_lib):
+    f = native_lib.paged_attn_pack_k
+    A, B = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + (1 << 24))
+    assert f(None, B, 4, 2, nat.KV_F16, None) == nat.PA_ERR_INVALID_ARG
+    assert f(A, ctypes.c_void_p(FAKE + (1 << 24) + 8), 4, 2, nat.KV_F16, None) == \
+        nat.PA_ERR_INVALID_ARG
+    assert f(A, B, 0, 2, nat.KV_F16, None) == nat.PA_ERR_INVALID_ARG
+    assert f(A, B, 4, 0, nat.KV_F16, None) == nat.PA_ERR_INVALID_ARG
+    assert f(A, B, 4, 2, 7, None) == nat.PA_ERR_INVALID_ARG
+    # the output overlaps the input: 4 blocks x 2 heads x 4 KiB = 32 KiB
+    assert f(A, ctypes.c_void_p(FAKE + 16384), 4, 2, nat.KV_F16, None) == nat.PA_ERR_INVALID_ARG
+    assert f(A, B, 1 << 62, 2, nat.KV_F16, None) == nat.PA_ERR_UNSUPPORTED

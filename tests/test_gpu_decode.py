@@ -94,6 +94,28 @@ def test_debug_gather_is_bitwise_the_block_table_gather():
                 f"b={b} pf={pf}"
 
 
+def test_debug_outputs_of_the_wrong_size_are_refused_before_any_launch():
+    """The kernel writes the dumps at their full size; an undersized one is
+    refused by the binding and nothing runs (out keeps its fill)."""
+    x = gen.make_case(3, 8, 2, [200, 31, 64], seed=131, extra_pool_blocks=7)
+    dev = to_device(x)
+    B, MB = x.block_tables.shape
+    Hkv = x.k_cache.shape[1]
+    out = torch.full_like(dev["q"], 3.0)
+    bad = [dict(debug_gather_k=torch.zeros((B, Hkv, MB * 16 - 16, 128), dtype=torch.float16,
+                                           device="cuda")),
+           dict(debug_trace=torch.zeros((B, Hkv, MB - 1, 2), dtype=torch.int32, device="cuda")),
+           dict(debug_error_word=torch.zeros(0, dtype=torch.int32, device="cuda"))]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            ops.paged_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
+                                  dev["context_lens"], x.scale, out, **kw)
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all())
+    for kw in bad:
+        assert all(int(t.abs().sum()) == 0 for t in kw.values())
+
+
 @pytest.mark.parametrize("pf", MODES)
 @pytest.mark.parametrize("waves,pb,dist", [(4, 0, 1), (2, 0, 1), (4, 8, 1), (2, 5, 1), (8, 16, 1),
                                            (1, 3, 1), (4, 0, 2), (2, 0, 5), (4, 32, 3),
