@@ -174,9 +174,12 @@ typedef struct pa_options {
     int32_t prefetch;          /* enum pa_prefetch; negative = library default */
     int32_t partition_blocks;  /* blocks per split-context partition, at most
                                   1024; 0 = auto: one partition per sequence
-                                  when the batch has at least 256 (sequence,
-                                  KV head) pairs, else about 256 / pairs
-                                  partitions of 64..256 blocks */
+                                  when the batch has at least as many
+                                  (sequence, KV head) pairs as the device has
+                                  CUs, else the balanced split (see
+                                  pa_plan_info.balanced) or, when that does
+                                  not apply, about CUs / pairs partitions of
+                                  64..256 blocks */
     int32_t waves_per_wg;      /* w in {1, 2, 4, 8}; 0 = auto: 8 for unsplit
                                   batches of 256..767 pairs whose block table
                                   is 512..1024 blocks wide, else 4 */
@@ -221,6 +224,18 @@ typedef struct pa_plan_info {
     int32_t seq_order;         /* PA_ORDER_NATURAL or PA_ORDER_LONGEST_FIRST */
     int32_t structure;         /* enum pa_structure */
     int32_t prefetch_distance; /* the look-ahead distance k in effect */
+    int32_t balanced;          /* 1: balanced split.  The partition size is
+                                  then chosen on the device from the context
+                                  lengths, per call: the smallest multiple of
+                                  waves_per_wg, at least partition_blocks,
+                                  with which all sequences need at most
+                                  workgroups / num_kv_heads partitions (about
+                                  one work-group per CU); num_partitions is
+                                  the most one sequence can get.  Chosen for
+                                  auto partitions when the batch has 2..256
+                                  sequences and fewer (sequence, KV head)
+                                  pairs than CUs, with seq_order AUTO and the
+                                  fused structure */
 } pa_plan_info;
 
 /* What the auto plan takes from the device.  paged_attn_plan,

@@ -10,7 +10,7 @@ fetching it into the cache before computing Q*K^T on the current one.  The
 third page (section 2.2) assigns warp i the blocks i, i + 4, i + 8, ... of a
 4-warp block, so wave i starts at s + i.
 """
-from typing import Dict, List, Optional, Tuple
+from typing import Dict, List, Optional, Sequence, Tuple
 
 Event = Tuple[int, int, Optional[int]]  # (iteration, computed block, fetched-ahead block)
 
@@ -45,3 +45,32 @@ def expected_trace(s: int, e: int, w: int, distance: int = 1):
             if ahead is not None:
                 out[ahead][2] = wave
     return out
+
+
+def balanced_split(block_counts: Sequence[int], pb_min: int, pb_max: int, step: int,
+                   slots: int, max_parts: int, few: int = 8,
+                   big: int = 64) -> Tuple[int, List[Tuple[int, int, int, int]]]:
+    """The launch's balanced split of ragged sequences (not a step of the
+    method: which work-group walks which block range).  The partition size is
+    the smallest multiple of `step` in [pb_min, pb_max] with which all
+    sequences together need at most `slots` partitions, none needs more than
+    `max_parts`, and none more than `few` unless the size is at least `big`;
+    the partitions are listed sequence by sequence.  Returns (size,
+    [(sequence, index, s, e)]) with each range [s, e) of block indices;
+    sequences without blocks get none.  Written from that definition by plain
+    enumeration."""
+    size = None
+    for pb in range(pb_min, pb_max + 1, step):
+        most = max([-(-n // pb) for n in block_counts] + [0])
+        if (sum(-(-n // pb) for n in block_counts) <= slots and most <= max_parts and
+                (most <= few or pb >= big)):
+            size = pb
+            break
+    if size is None:
+        raise ValueError("no partition size fits the slots")
+    parts = []
+    for b, n in enumerate(block_counts):
+        for i, s in enumerate(range(0, n, size)):
+            parts.append((b, i, s, min(n, s + size)))
+    assert len(parts) <= slots
+    return size, parts

@@ -50,7 +50,7 @@ class PaPlanInfo(ctypes.Structure):
                 ("partition_blocks", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
                 ("workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
                 ("seq_order", ctypes.c_int32), ("structure", ctypes.c_int32),
-                ("prefetch_distance", ctypes.c_int32)]
+                ("prefetch_distance", ctypes.c_int32), ("balanced", ctypes.c_int32)]
 
 
 class PaDeviceInfo(ctypes.Structure):

@@ -50,9 +50,9 @@ constexpr DeviceInfo kMI355X = {256, 163840, 163840};
 //    ones).
 constexpr int64_t kFourWaveUnitsPerCU = 3;
 constexpr int kLongTableBlocks = 512;
-constexpr int kMinAutoPartition = 64;
+constexpr int kMinAutoPartition = pa::kReduceBigPartition;
 constexpr int kMinShortPartition = 16;
-constexpr int kReducePartitions = 8;
+constexpr int kReducePartitions = pa::kReduceRegs;
 constexpr int kMaxAutoPartition = 256;
 constexpr int kTwoLoopPartitionBlocks = 32;
 //  * Auto order ranks the sequences (longest first) only when the grid is
@@ -120,7 +120,17 @@ struct Plan {
   int pf, dist, waves, PB, P, order, two;
   int64_t wgs;
   size_t ws_bytes;
+  int bal, nslot, pb_max;  // balanced split: grid rows per KV head, largest size
 };
+
+// Balanced split (auto partitions of a ragged batch with fewer (sequence,
+// KV head) pairs than CUs, 2..PA_RANK_MAX_SEQS sequences): the device picks
+// the partition size from the context lengths so that each KV head's
+// partitions fill about one work-group per CU; sizes are multiples of the
+// wave count from kMinShortPartition blocks up.  On uniform batches it
+// makes the same partitions as the fixed rule; on llama3_8b-shaped TP
+// shards the longest sequences no longer run alone on their CUs.
+constexpr int kBalancedMaxTable = 65536;  // blocks; keeps the device's float division exact
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -232,13 +242,43 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
     if (pb > MB) pb = MB;
     PB = (int)pb;
   }
-  const int P = (MB + PB - 1) / PB;
+  int P = (MB + PB - 1) / PB;
   if (P > 65535) return PA_ERR_UNSUPPORTED;  // grid.z
+  // the balanced split replaces the fixed partitions of an auto split plan
+  int bal = 0, nslot = 0, pb_max = 0;
+  if (!two && o->partition_blocks == 0 && units < dv.cus && o->seq_order == PA_ORDER_AUTO &&
+      B >= 2 && B <= PA_RANK_MAX_SEQS && MB <= kBalancedMaxTable) {
+    const int pb_min = (kMinShortPartition + waves - 1) / waves * waves;
+    const int cap = MB < kMaxPartitionBlocks ? MB : kMaxPartitionBlocks;
+    pb_max = (cap + waves - 1) / waves * waves;
+    if (pb_max < pb_min) pb_max = pb_min;
+    // rows per KV head: one work-group per CU, and at least what the
+    // largest size needs in the worst case
+    const int64_t need = (int64_t)B * ((MB + pb_max - 1) / pb_max);
+    const int64_t rows = dv.cus / Hkv > need ? dv.cus / Hkv : need;
+    // partitions one sequence can get: its table in partitions of the
+    // smallest size, at most kReducePartitions of them unless they hold at
+    // least kMinAutoPartition blocks (the device keeps both rules), and at
+    // most rows - B + 1
+    int64_t per_seq = (MB + pb_min - 1) / pb_min;
+    const int64_t big = (MB + kMinAutoPartition - 1) / kMinAutoPartition;
+    const int64_t red = big > kReducePartitions ? big : kReducePartitions;
+    per_seq = per_seq < red ? per_seq : red;
+    const int64_t most = rows - B + 1;
+    if (rows <= 65535 && per_seq > 1) {  // one partition per sequence needs no split
+      bal = 1;
+      nslot = (int)rows;
+      PB = pb_min;
+      P = (int)(per_seq < most ? per_seq : most);
+      order = PA_ORDER_NATURAL;
+      rank = false;
+    }
+  }
   auto lds_for = [&](bool r) {
     return two ? pa::two_loop_lds_bytes(PB, g, waves, B, r)
-               : pa::decode_lds_bytes(PB, g, waves, B, r, waves * slot);
+               : pa::decode_lds_bytes(bal ? pb_max : PB, g, waves, B, r, waves * slot);
   };
-  const int64_t wgs = (int64_t)P * Hkv * B;
+  const int64_t wgs = bal ? (int64_t)nslot * Hkv : (int64_t)P * Hkv * B;
   if (o->seq_order == PA_ORDER_AUTO && rank) {
     const size_t l = lds_for(true);
     const int64_t by_waves = kResidentWavesPerCU / waves;
@@ -259,7 +299,15 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   pl->PB = PB;
   pl->P = P;
   pl->wgs = wgs;
-  pl->ws_bytes = P > 1 ? (size_t)B * sh->num_q_heads * P * (2 + PA_HEAD_DIM) * sizeof(float) : 0;
+  pl->bal = bal;
+  pl->nslot = nslot;
+  pl->pb_max = pb_max;
+  // partials [B][Hq][P][128] and [B][Hq][P][2] in fp32; the balanced split
+  // adds the sequences' partition counts (B int32, padded to 16 bytes)
+  pl->ws_bytes = P > 1 ? ((size_t)(bal ? (B + 3) / 4 * 4 : 0) +
+                          (size_t)B * sh->num_q_heads * P * (2 + PA_HEAD_DIM)) *
+                             sizeof(float)
+                       : 0;
   return PA_OK;
 }
 
@@ -295,6 +343,7 @@ static int plan_info(const pa_shape* sh, const pa_options* o, const DeviceInfo& 
   info->seq_order = pl.order;
   info->structure = pl.two;
   info->prefetch_distance = pl.dist;
+  info->balanced = pl.bal;
   return PA_OK;
 }
 
@@ -396,17 +445,25 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.v_head = v_head;
   a.k_blk = k_blk;
   a.v_blk = v_blk;
-  a.lds_bt_bytes = pa::lds_bt_bytes_for(pl.PB);
+  a.lds_bt_bytes = pa::lds_bt_bytes_for(pl.bal ? pl.pb_max : pl.PB);
+  a.balanced = pl.bal;
+  a.nslot = pl.nslot;
+  a.pb_max = pl.pb_max;
+  if (pl.bal) a.k_uniform = pl.nslot / sh->num_seqs < pl.P ? pl.nslot / sh->num_seqs : pl.P;
   a.pf_dist = pl.dist;
   const bool dbg = o->debug_gather_k || o->debug_trace || o->debug_error_word;
   if (pl.two && dbg) return PA_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   if (pl.P > 1) {
+    // [rows][128] unnormalised outputs first, so every 512-byte row starts
+    // on a cache line, then [rows][2] (m, l), then the balanced split's
+    // per-sequence partition counts
     float* ws = static_cast<float*>(o->workspace);
     const size_t rows = (size_t)sh->num_seqs * sh->num_q_heads * pl.P;
-    a.ws_ml = ws;
-    a.ws_o = ws + rows * 2;
+    a.ws_o = ws;
+    a.ws_ml = ws + rows * PA_HEAD_DIM;
+    if (pl.bal) a.ws_np = reinterpret_cast<int32_t*>(a.ws_ml + rows * 2);
   }
   if (pl.two) {
     if (pa::launch_decode_two_loop(a, pl.pf, pl.waves, st) != hipSuccess) return PA_ERR_HIP;

@@ -17,7 +17,7 @@ struct DecodeArgs {
   const int32_t* ctx;    // [B]
   uint16_t* out;         // [B][Hq][128] fp16
   float* ws_ml;          // [B][Hq][P][2]   (max in log2 units, sum)
-  float* ws_o;           // [B][Hq][P][128] unnormalised output
+  float* ws_o;           // [B][Hq][P][128] unnormalised output (the workspace's start)
   uint16_t* dbg_k;       // see pa_options.debug_gather_k
   int32_t* dbg_trace;    // see pa_options.debug_trace
   int32_t* dbg_err;      // see pa_options.debug_error_word
@@ -35,7 +35,24 @@ struct DecodeArgs {
   int pf_dist;           // L2-touch distance in iterations of a wave, 1..63
   int sink_enable;
   int rank_seqs;         // 1: grid row r takes the sequence of rank r (most blocks first)
+  // Balanced split (balanced = 1): grid (Hkv, nslot); the partition size is
+  // chosen on the device from the context lengths, a multiple of the wave
+  // count between PB and pb_max, so that all sequences need at most nslot
+  // partitions.  P is then the workspace's partition stride (the most
+  // partitions one sequence can get) and ws_np[b] receives sequence b's
+  // partition count for the reduce.
+  int balanced;
+  int nslot;
+  int pb_max;
+  int k_uniform;         // min(nslot / B, P): partitions per sequence of a uniform batch
+  int32_t* ws_np;
 };
+
+// Partials the reduce kernel merges with one memory round trip, and the
+// partition size from which the auto plans let a sequence have more of them
+// (more, smaller partitions cost the reduce more than the extra CUs bring).
+constexpr int kReduceRegs = 8;
+constexpr int kReduceBigPartition = 64;
 
 inline int lds_bt_bytes_for(int PB) { return ((PB * 4) + 15) / 16 * 16; }
 

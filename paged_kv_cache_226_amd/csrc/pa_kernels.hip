@@ -873,6 +873,182 @@ __device__ __forceinline__ int ranked_sequence(const DecodeArgs& a, int r, int t
   return b;
 }
 
+// ---------------------------------------------------------------------------
+// Balanced split.  With ragged contexts and fewer (sequence, KV head) pairs
+// than CUs, fixed-size partitions leave the longest sequences' partitions
+// running alone on their CUs long after the rest have finished (a CU reads
+// at most about 130 x 128 B in flight).  Here every work-group of KV head
+// kvh reads all B context lengths and takes the same decision: the
+// partition size PB is the smallest multiple of the wave count W in
+// [a.PB, a.pb_max] for which all sequences together need at most a.nslot
+// partitions and no sequence needs more than a.P (the workspace's partition
+// stride) and, unless partitions hold at least kReduceBigPartition blocks,
+// none needs more than the reduce merges in one round trip (kReduceRegs);
+// grid row y then takes partition y of the list (sequence 0's
+// partitions first, then sequence 1's, ...) or nothing.  Each wave computes it
+// (B <= 256: lane l of each wave holds sequences 4l..4l+3).
+struct Slot {
+  int b, p, np, pb;  // sequence, its partition index and count, blocks per partition
+  int ctx;           // the sequence's context length as stored
+};
+
+// Sum over the 64 lanes, in every lane, without the LDS crossbar: DPP
+// rotations and quad permutes within each row of 16 lanes, then the row
+// swaps v_permlane16_swap / v_permlane32_swap across rows.
+__device__ __forceinline__ int wave_sum_i32(int x) {
+  x += __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror:8
+  x += __builtin_amdgcn_mov_dpp(x, 0x124, 0xF, 0xF, false);  // row_ror:4
+  x += __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  x += __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  const auto r16 = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  x = (int)r16[0] + (int)r16[1];
+  const auto r32 = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return (int)r32[0] + (int)r32[1];
+}
+
+// Maximum over the 64 lanes, in every lane (same steps as wave_sum_i32).
+__device__ __forceinline__ int wave_max_i32(int x) {
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));  // row_ror:8
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x124, 0xF, 0xF, false));  // row_ror:4
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  const auto r16 = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  x = max((int)r16[0], (int)r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return max((int)r32[0], (int)r32[1]);
+}
+
+// Inclusive prefix sum over the 64 lanes: row-local shifts (lanes shifted in
+// from outside the row add 0), then the last lane of each row broadcast into
+// the rows after it.
+__device__ __forceinline__ int wave_prefix_i32(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+// ceil(n / d) for 0 <= n < 2^24, 1 <= d < 2^24: a float estimate corrected
+// to the exact quotient (cheaper than the integer division sequence).
+__device__ __forceinline__ int ceil_div_small(int n, int d, float rd) {
+  const int x = n + d - 1;
+  int q = (int)((float)x * rd);
+  if ((q + 1) * d <= x) ++q;
+  if (q * d > x) --q;
+  return q;
+}
+
+// Every wave computes the same slot (the inputs are the same and the
+// arithmetic is deterministic), so no LDS or barrier is needed to share it.
+__device__ Slot balanced_slot(const DecodeArgs& a, int slot, int tab_tokens) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int W = blockDim.x / kWave;
+  int nb[4], raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = 4 * lane + i;
+    raw[i] = idx < a.B ? a.ctx[idx] : 0;
+    const int c = raw[i] < 0 ? 0 : (raw[i] > tab_tokens ? tab_tokens : raw[i]);
+    nb[i] = (c + kT - 1) / kT;
+  }
+  int pb;
+  const int nb0 = __builtin_amdgcn_readfirstlane(nb[0]);
+  bool same = true;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) same &= 4 * lane + i >= a.B || nb[i] == nb0;
+  if (__builtin_amdgcn_ballot_w64(!same) == 0) {
+    // every sequence has nb0 blocks and may take a.k_uniform = min(nslot / B,
+    // P) partitions: the size is the smallest step multiple >= nb0 / that,
+    // and >= the reduce bound below
+    pb = ceil_div_small(nb0, a.k_uniform, 1.0f / (float)a.k_uniform);
+    const int red = (nb0 + kReduceRegs - 1) / kReduceRegs;
+    const int red_lo = red < kReduceBigPartition ? red : kReduceBigPartition;
+    pb = pb < red_lo ? red_lo : pb;
+    pb = (pb + W - 1) / W * W;
+    pb = pb < a.PB ? a.PB : (pb > a.pb_max ? a.pb_max : pb);
+  } else {
+    auto parts = [&](int size) {  // partitions of `size` blocks over all sequences
+      const float rd = 1.0f / (float)size;
+      int n = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) n += ceil_div_small(nb[i], size, rd);
+      return wave_sum_i32(n);
+    };
+    // The count falls as the size grows, and the host sized nslot so that
+    // pb_max always fits.  With T blocks over B' non-empty sequences, a
+    // size below T / nslot cannot fit and one of T / (nslot - B') always
+    // does (each sequence adds at most one partly filled partition), so
+    // the search starts from that bracket.
+    int t = 0, ne = 0, mx = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      t += nb[i];
+      ne += nb[i] > 0;
+      mx = nb[i] > mx ? nb[i] : mx;
+    }
+    t = wave_sum_i32(t);
+    ne = wave_sum_i32(ne);
+    mx = wave_max_i32(mx);
+    // a size below ceil(mx / P) would give the longest sequence more
+    // partitions than the workspace holds; one below min(64, ceil(mx / 8))
+    // more than the reduce merges in one round trip, in small partitions
+    const int lo_p = (mx + a.P - 1) / a.P;
+    const int red = (mx + kReduceRegs - 1) / kReduceRegs;
+    const int red_lo = red < kReduceBigPartition ? red : kReduceBigPartition;
+    int lo = (t + a.nslot - 1) / a.nslot;
+    lo = lo < lo_p ? lo_p : lo;
+    lo = lo < red_lo ? red_lo : lo;
+    int hi = a.nslot > ne ? (t + (a.nslot - ne) - 1) / (a.nslot - ne) : a.pb_max;
+    hi = hi < lo ? lo : hi;
+    lo = (lo + W - 1) / W;  // in units of W
+    hi = (hi + W - 1) / W;
+    lo = lo < a.PB / W ? a.PB / W : lo;
+    hi = hi > a.pb_max / W ? a.pb_max / W : hi;
+    hi = hi < lo ? lo : hi;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (parts(mid * W) <= a.nslot)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    pb = lo * W;
+  }
+  const float rd = 1.0f / (float)pb;
+  int np[4], mine = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    np[i] = ceil_div_small(nb[i], pb, rd);
+    mine += np[i];
+  }
+  int start = wave_prefix_i32(mine) - mine;  // partitions of the lanes before
+  int found = -1, fp = 0, fnp = 0, fctx = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (slot >= start && slot < start + np[i]) {
+      found = 4 * lane + i;
+      fp = slot - start;
+      fnp = np[i];
+      fctx = raw[i];
+    }
+    start += np[i];
+  }
+  // at most one lane holds the slot; move its values to every lane
+  const uint64_t owner = __builtin_amdgcn_ballot_w64(found >= 0);
+  Slot r = {-1, 0, 0, pb, 0};
+  if (owner) {
+    const int ol = __builtin_ctzll(owner);
+    r.b = __builtin_amdgcn_readlane(found, ol);
+    r.p = __builtin_amdgcn_readlane(fp, ol);
+    r.np = __builtin_amdgcn_readlane(fnp, ol);
+    r.ctx = __builtin_amdgcn_readlane(fctx, ol);
+  }
+  return r;
+}
+
 // TWO selects the two-loop walk (fp16, no debug outputs).
 template <int PF, bool DBG, bool KV8, bool TWO = false>
 __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
@@ -889,16 +1065,28 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
   const int tid = threadIdx.x;
   const int W = blockDim.x / kWave;
   const int tab_tokens = a.MB * kT;
-  const int b = a.rank_seqs ? ranked_sequence(a, blockIdx.y, tab_tokens, smem_raw) : blockIdx.y;
-
-  int ctx = a.ctx[b];
+  int b, part = p, np_seq = a.P, pb = a.PB, ctx;
+  if (a.balanced) {
+    const Slot sl = balanced_slot(a, blockIdx.y, tab_tokens);
+    if (sl.b < 0) return;  // a grid row past the last partition
+    b = sl.b;
+    part = sl.p;
+    np_seq = sl.np;
+    pb = sl.pb;
+    ctx = sl.ctx;
+    // the reduce takes each sequence's partition count from here
+    if (part == 0 && kvh == 0 && tid == 0) a.ws_np[b] = np_seq;
+  } else {
+    b = a.rank_seqs ? ranked_sequence(a, blockIdx.y, tab_tokens, smem_raw) : blockIdx.y;
+    ctx = a.ctx[b];
+  }
   if (ctx > tab_tokens) {
     if (DBG && tid == 0 && a.dbg_err) atomicOr(a.dbg_err, 2);
     ctx = tab_tokens;
   }
   const int nb = ctx > 0 ? (ctx + kT - 1) / kT : 0;
-  const int s = p * a.PB;
-  const int e = min(nb, s + a.PB);
+  const int s = part * pb;
+  const int e = min(nb, s + pb);
 
   if (s >= e) {
     // Nothing to attend in this partition.  With one partition the output
@@ -925,10 +1113,10 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
     float M, L, O;
     combine_waves(merge_s, W, G, h, d, M, L, O);
     const int64_t row = (int64_t)b * a.Hq + kvh * G + h;
-    if (a.P == 1) {
+    if (a.P == 1 || np_seq == 1) {  // the sequence's only partition
       a.out[row * kD + d] = f32_to_f16_bits(O * a.v_scale / L);
     } else {
-      const int64_t pr = row * a.P + p;
+      const int64_t pr = row * a.P + part;
       if (d == 0) {
         a.ws_ml[pr * 2] = M;
         a.ws_ml[pr * 2 + 1] = L;
@@ -940,38 +1128,47 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Cross-partition combine: one work-group of 128 threads per (sequence, head).
-// Its time is latency: with at most kReduceRegs partitions every partial is
-// loaded together with the context length (partitions past the sequence's
-// last block are masked afterwards, their words never used), so one memory
-// round trip precedes the arithmetic instead of two.  Both branches combine
-// in the same order, so the results are the same bits.
-constexpr int kReduceRegs = 8;
+// Its time is latency.  The (m, l) pairs of the first kReduceRegs
+// partitions (one cache line) and the outputs of the first `spec` of them
+// are loaded together with the context length (and, under the balanced
+// split, the sequence's partition count) before either is known, so one
+// memory round trip precedes the arithmetic when the sequence has at most
+// `spec` partitions.  spec is the plan's partition count, or under the
+// balanced split the count every sequence of a uniform batch gets: loading
+// further speculative outputs would read workspace lines that no partition
+// wrote (straight from HBM).  Outputs between spec and the sequence's count
+// are loaded once it is known.  Every branch combines in the same order, so
+// the results are the same bits.
 __global__ void __launch_bounds__(128) pa_reduce_kernel(const DecodeArgs a) {
   const int row = blockIdx.x;  // b * Hq + h
   const int b = row / a.Hq;
   const int d = threadIdx.x;
   const float* ml = a.ws_ml + (int64_t)row * a.P * 2;
   const float* o = a.ws_o + (int64_t)row * a.P * kD;
+  const int spec = a.balanced ? a.k_uniform : a.P;
   float mq[kReduceRegs], lq[kReduceRegs], oq[kReduceRegs];
-  if (a.P <= kReduceRegs) {
 #pragma unroll
-    for (int q = 0; q < kReduceRegs; ++q) {
-      if (q < a.P) {
-        mq[q] = ml[2 * q];
-        lq[q] = ml[2 * q + 1];
-        oq[q] = o[(int64_t)q * kD + d];
-      }
+  for (int q = 0; q < kReduceRegs; ++q) {
+    if (q < a.P) {
+      mq[q] = ml[2 * q];
+      lq[q] = ml[2 * q + 1];
     }
+    if (q < spec) oq[q] = o[(int64_t)q * kD + d];
   }
   int ctx = a.ctx[b];
+  const int np_b = a.balanced ? a.ws_np[b] : 0;
   ctx = min(ctx, a.MB * kT);
   const int nb = ctx > 0 ? (ctx + kT - 1) / kT : 0;
-  const int np = (nb + a.PB - 1) / a.PB;
+  const int np = nb == 0 ? 0 : (a.balanced ? np_b : (nb + a.PB - 1) / a.PB);
   if (np == 0) {
     a.out[(int64_t)row * kD + d] = 0;
     return;
   }
-  if (a.P <= kReduceRegs) {
+  if (a.balanced && np == 1) return;  // the decode kernel wrote this row
+  if (np <= kReduceRegs) {
+#pragma unroll
+    for (int q = 0; q < kReduceRegs; ++q)
+      if (q >= spec && q < np) oq[q] = o[(int64_t)q * kD + d];
     float M = -INFINITY;
 #pragma unroll
     for (int q = 0; q < kReduceRegs; ++q)
@@ -988,13 +1185,28 @@ __global__ void __launch_bounds__(128) pa_reduce_kernel(const DecodeArgs a) {
     a.out[(int64_t)row * kD + d] = f32_to_f16_bits(O * a.v_scale / L);
     return;
   }
+  // more partials: the maximum first, then the sums in chunks of
+  // kReduceRegs whose loads are issued together (same order of operations)
   float M = -INFINITY;
   for (int q = 0; q < np; ++q) M = fmaxf(M, ml[2 * q]);
   float L = 0.f, O = 0.f;
-  for (int q = 0; q < np; ++q) {
-    const float al = fast_exp2(ml[2 * q] - M);
-    L += al * ml[2 * q + 1];
-    O += al * o[(int64_t)q * kD + d];
+  for (int q0 = 0; q0 < np; q0 += kReduceRegs) {
+#pragma unroll
+    for (int i = 0; i < kReduceRegs; ++i) {
+      if (q0 + i < np) {
+        mq[i] = ml[2 * (q0 + i)];
+        lq[i] = ml[2 * (q0 + i) + 1];
+        oq[i] = o[(int64_t)(q0 + i) * kD + d];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kReduceRegs; ++i) {
+      if (q0 + i < np) {
+        const float al = fast_exp2(mq[i] - M);
+        L += al * lq[i];
+        O += al * oq[i];
+      }
+    }
   }
   a.out[(int64_t)row * kD + d] = f32_to_f16_bits(O * a.v_scale / L);
 }
@@ -1067,12 +1279,14 @@ hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int wa
       launch_decode_t<5, false, true>,  launch_decode_t<5, true, true>,
       launch_decode_t<6, false, true>,  launch_decode_t<6, true, true>};
   if (pf < 0 || pf > 6) return hipErrorInvalidValue;
-  const dim3 grid(a.Hkv, a.B, a.P);
+  const dim3 grid(a.Hkv, a.balanced ? a.nslot : a.B, a.balanced ? 1 : a.P);
   const dim3 block(kWave * waves);
   // the LDS ring: depth + 1 slots of one block's K and V per wave
   const size_t slots = pf >= 5 ? (size_t)waves * (pf - 3) * (kv8 ? 4096 : 8192) : 0;
   return table[(kv8 ? 14 : 0) + pf * 2 + (dbg ? 1 : 0)](
-      a, grid, block, decode_lds_bytes(a.PB, a.G, waves, a.B, a.rank_seqs != 0, slots), st);
+      a, grid, block,
+      decode_lds_bytes(a.balanced ? a.pb_max : a.PB, a.G, waves, a.B, a.rank_seqs != 0, slots),
+      st);
 }
 
 hipError_t launch_decode_two_loop(const DecodeArgs& a, int pf, int waves, hipStream_t st) {

@@ -169,10 +169,39 @@ def sweep_timing(jsonl, workload, out_dir, command):
     return path
 
 
+# Derived figures of the request-path passes, per decode launch.  The SQ
+# clock count GRBM_GUI_ACTIVE is summed over the 8 XCDs; per-CU figures
+# divide by the 256 CUs (one TA and one TCP each).
+REQUEST_PATH_DERIVED = [
+    ("kernel us", None),
+    ("TCP->TCC read requests", lambda c, k: c["TCP_TCC_READ_REQ_sum"]),
+    ("TCP->TCC mean read latency (cycles)",
+     lambda c, k: c["TCP_TCC_READ_REQ_LATENCY_sum"] / c["TCP_TCC_READ_REQ_sum"]),
+    ("TCP->TCC reads in flight per CU",
+     lambda c, k: c["TCP_TCC_READ_REQ_LATENCY_sum"] / (c["GRBM_GUI_ACTIVE"] / 8) / 256),
+    ("TA address stage stalled by TCP (% of CU cycles)",
+     lambda c, k: 100 * c["TA_ADDR_STALLED_BY_TC_CYCLES_sum"] / (c["GRBM_GUI_ACTIVE"] / 8) / 256),
+    ("TA busy (% of CU cycles)",
+     lambda c, k: 100 * c["TA_TA_BUSY_sum"] / (c["GRBM_GUI_ACTIVE"] / 8) / 256),
+    ("TCP stalled on data pending from L2 (% of CU cycles)",
+     lambda c, k: 100 * c["TCP_PENDING_STALL_CYCLES_sum"] / (c["GRBM_GUI_ACTIVE"] / 8) / 256),
+    ("TCP read tag-conflict stall cycles", lambda c, k: c["TCP_READ_TAGCONFLICT_STALL_CYCLES_sum"]),
+    ("L2 (TCC) requests", lambda c, k: c["TCC_REQ_sum"]),
+    ("L2 tag stall cycles", lambda c, k: c["TCC_TAG_STALL_sum"]),
+    ("HBM (EA) read requests", lambda c, k: c["TCC_EA0_RDREQ_sum"]),
+    ("HBM (EA) reads in flight", lambda c, k: c["TCC_EA0_RDREQ_LEVEL_sum"] / (c["GRBM_GUI_ACTIVE"] / 8)),
+    ("HBM (EA) mean read latency (cycles)",
+     lambda c, k: c["TCC_EA0_RDREQ_LEVEL_sum"] / c["TCC_EA0_RDREQ_sum"]),
+    ("DRAM credit stall cycles", lambda c, k: c["TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum"]),
+    ("address-translation misses (UTCL1)", lambda c, k: c["TCP_UTCL1_TRANSLATION_MISS_sum"]),
+]
+
+
 def request_path_table(dirs, tag, head, out_dir, kernel_us):
     """Per look-ahead mode, the mean per launch of every counter in the given
-    passes (summed over the dimensions rocprofv3 reports, e.g. TCC channels
-    and XCDs), next to the kernel-trace duration."""
+    passes (summed over the instances rocprofv3 reports, e.g. TCC channels
+    and XCDs), next to the kernel-trace duration, and the derived figures of
+    REQUEST_PATH_DERIVED."""
     per = collections.defaultdict(dict)
     names = []
     for d in dirs:
@@ -183,19 +212,42 @@ def request_path_table(dirs, tag, head, out_dir, kernel_us):
             if m is None:
                 continue
             agg[(m, r["Counter_Name"])] += float(r["Counter_Value"])
-            launches[m].add(r["Dispatch_Id"])
+            launches[(m, r["Counter_Name"])].add(r["Dispatch_Id"])
         for (m, c), v in agg.items():
-            per[m][c] = v / max(1, len(launches[m]))
+            per[m][c] = v / max(1, len(launches[(m, c)]))
             if c not in names:
                 names.append(c)
+
+    def fmt(v):
+        return f"{v:.4g}" if isinstance(v, float) else str(v)
+
+    def derived(m, f):
+        try:
+            return fmt(float(f(per[m], kernel_us.get(m))))
+        except (KeyError, ZeroDivisionError, TypeError):
+            return ""
+
+    modes = sorted(per)
     lines = ["# pa_decode memory request path per look-ahead mode: " + tag, "", "```", *head,
-             "```", "", "Mean per decode launch of each counter (summed over instances).", "",
-             "| mode | kernel us | " + " | ".join(names) + " |",
-             "|---|---|" + "---|" * len(names)]
-    for m in sorted(per):
-        us = kernel_us.get(m)
-        lines.append(f"| {MODE_NAMES[m]} | {us:.2f} | " if us else f"| {MODE_NAMES[m]} | | ")
-        lines[-1] += " | ".join(f"{per[m].get(c, float('nan')):.4g}" for c in names) + " |"
+             "```", "",
+             "Per decode launch (mean over the profiled launches of each mode).  "
+             "GRBM_GUI_ACTIVE is summed over the 8 XCDs, so per-CU figures use "
+             "GRBM_GUI_ACTIVE / 8 cycles and 256 CUs; 'in flight' is a latency sum "
+             "divided by the cycles (Little's law).", "",
+             "| figure | " + " | ".join(MODE_NAMES[m] for m in modes) + " |",
+             "|---|" + "---|" * len(modes)]
+    for label, f in REQUEST_PATH_DERIVED:
+        if f is None:
+            cells = [f"{kernel_us[m]:.2f}" if m in kernel_us else "" for m in modes]
+        else:
+            cells = [derived(m, f) for m in modes]
+        lines.append(f"| {label} | " + " | ".join(cells) + " |")
+    lines += ["", "Raw counters (sums over instances, per launch):", "",
+              "| counter | " + " | ".join(MODE_NAMES[m] for m in modes) + " |",
+              "|---|" + "---|" * len(modes)]
+    for c in names:
+        lines.append(f"| {c} | " + " | ".join(fmt(per[m].get(c, float('nan'))) for m in modes)
+                     + " |")
     path = os.path.join(out_dir, f"pa_decode_{tag}_request_path.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -247,6 +299,9 @@ def main(argv=None):
     head = [f"workload: {a.workload} ({w.description}), KV cache {'E4M3' if KV8 else 'fp16'}",
             f"algorithmic KV bytes per launch: {kv}  (Q, output, block tables: {other})",
             "command:", *["    " + c for c in a.command.split(" ;; ") if c]]
+    if a.source_hash:
+        head.append(f"kernel_source_hash: {a.source_hash} (bench.py kernel_source_hash of the "
+                    "profiled sources)")
 
     if a.kernel_trace:
         lines = ["# pa_decode kernel trace: " + tag, "", "```", *head, "```", "",

@@ -61,3 +61,17 @@ def assert_close(got_f16, ref_f64, what=""):
 
 def bits(a):
     return np.ascontiguousarray(a).view(np.uint16)
+
+
+def same_plan(plan, **extra):
+    """Options that reproduce `plan` (waves, partitions, order) for another
+    look-ahead mode: a balanced split is reproduced by asking for it again
+    (auto partitions and order with the same waves), a fixed one by its
+    partition size and order."""
+    if plan["balanced"]:
+        kw = dict(partition_blocks=0, waves_per_wg=plan["waves_per_wg"], seq_order=0)
+    else:
+        kw = dict(partition_blocks=plan["partition_blocks"], waves_per_wg=plan["waves_per_wg"],
+                  seq_order=plan["seq_order"])
+    kw.update(extra)
+    return kw

@@ -180,19 +180,29 @@ def test_noalloc_validation_codes(native_lib):
 def test_plans_of_the_workloads(native_lib):
     from paged_kv_cache_226_amd import inputs as gen
     # (partitions, waves) of the auto plan
-    expect = {"tiny": (1, 8), "llama2_7b": (1, 4), "llama3_8b": (1, 8), "qwen25_7b": (1, 4),
-              "qwen25_14b": (1, 4), "llama3_8b_tp2": (1, 8), "llama3_8b_tp4": (2, 8),
-              "llama3_8b_tp8": (4, 8), "qwen25_14b_tp2": (1, 8), "qwen25_14b_tp4": (1, 8),
-              "qwen25_14b_tp8": (2, 8)}
+    # (partitions, waves, balanced) of the auto plan; under the balanced
+    # split the partitions are the most one sequence can get
+    expect = {"tiny": (1, 8, 0), "llama2_7b": (1, 4, 0), "llama3_8b": (1, 8, 0),
+              "qwen25_7b": (1, 4, 0), "qwen25_14b": (1, 4, 0), "llama3_8b_tp2": (1, 8, 0),
+              "llama3_8b_tp4": (8, 8, 1), "llama3_8b_tp8": (8, 8, 1),
+              "qwen25_14b_tp2": (1, 8, 0), "qwen25_14b_tp4": (1, 8, 0),
+              "qwen25_14b_tp8": (8, 8, 1)}
     for name, w in gen.WORKLOADS.items():
         MB = w.max_blocks_per_seq or max(-(-c // 16) for c in w.context_lens)
         nb = w.pool_blocks or 1
         p = nat.plan(nat.make_shape(w.num_seqs, w.num_q_heads, w.num_kv_heads, MB, nb))
-        assert (p["num_partitions"], p["waves_per_wg"]) == expect[name], name
-        assert p["num_partitions"] * p["partition_blocks"] >= MB
-        assert p["workgroups"] == p["num_partitions"] * w.num_kv_heads * w.num_seqs
+        assert (p["num_partitions"], p["waves_per_wg"], p["balanced"]) == expect[name], name
+        if p["balanced"]:
+            # one grid row per CU and KV head (256 CUs), the smallest size 16
+            assert p["workgroups"] == 256 // w.num_kv_heads * w.num_kv_heads
+            assert p["partition_blocks"] == 16
+            header = -(-w.num_seqs // 4) * 4
+        else:
+            assert p["num_partitions"] * p["partition_blocks"] >= MB
+            assert p["workgroups"] == p["num_partitions"] * w.num_kv_heads * w.num_seqs
+            header = 0
         want = 0 if p["num_partitions"] == 1 else \
-            w.num_seqs * w.num_q_heads * p["num_partitions"] * 130 * 4
+            (header + w.num_seqs * w.num_q_heads * p["num_partitions"] * 130) * 4
         assert p["workspace_bytes"] == want
 
 
@@ -243,8 +253,40 @@ def test_sequence_order_of_the_plan(native_lib, B, Hkv, MB, order, want):
     (96, 8, 512, 4, 1, 512),      # 768 pairs: 4 waves
 ])
 def test_auto_plan_rule(native_lib, B, Hkv, MB, waves, P, PB):
-    p = nat.plan(nat.make_shape(B, Hkv * 4, Hkv, MB, 1000))
+    """The fixed split rule (an explicit sequence order keeps a split plan on
+    it; with the auto order, batches of 2..256 sequences take the balanced
+    split instead)."""
+    o = nat.default_options()
+    o.seq_order = nat.ORDER_NATURAL
+    p = nat.plan(nat.make_shape(B, Hkv * 4, Hkv, MB, 1000), o)
     assert (p["waves_per_wg"], p["num_partitions"], p["partition_blocks"]) == (waves, P, PB)
+    assert p["balanced"] == 0
+    auto = nat.plan(nat.make_shape(B, Hkv * 4, Hkv, MB, 1000))
+    assert auto["balanced"] == (1 if P > 1 and 2 <= B <= 256 and B * Hkv < 256 else 0)
+    if not auto["balanced"]:
+        assert (auto["waves_per_wg"], auto["num_partitions"], auto["partition_blocks"]) == \
+            (waves, P, PB)
+
+
+@pytest.mark.parametrize("B,Hkv,MB,cus,rows,P", [
+    (8, 8, 64, 256, 32, 4),      # 32 rows per KV head; 4 partitions of 16 at most
+    (64, 1, 512, 256, 256, 8),   # the llama3_8b TP8 shard: 8 partitions below 64 blocks
+    (255, 1, 188, 256, 256, 2),  # one spare row: at most 2 partitions per sequence
+    (2, 1, 4096, 256, 256, 64),  # 2 sequences of 4096 blocks: 64 partitions of 64
+    (200, 1, 1024, 256, 256, 16),
+    (4, 2, 8192, 16, 32, 29),    # few CUs: rows for 8 partitions of 1024 per sequence
+])
+def test_balanced_split_plan(native_lib, B, Hkv, MB, cus, rows, P):
+    """Rows per KV head (at least one per CU, at least what the largest size
+    needs), the most partitions one sequence can get (its table in partitions
+    of the smallest size; at most 8 unless they hold 64 blocks or more; at
+    most rows - B + 1), and the workspace (partials, then partition counts)."""
+    dev = dict(MI355X, compute_units=cus)
+    p = nat.plan(nat.make_shape(B, 4 * Hkv, Hkv, MB, 1), device=dev)
+    assert p["balanced"] == 1
+    assert (p["workgroups"], p["num_partitions"], p["partition_blocks"]) == (rows * Hkv, P, 16)
+    assert p["seq_order"] == nat.ORDER_NATURAL and p["waves_per_wg"] == 8
+    assert p["workspace_bytes"] == (-(-B // 4) * 4 + B * 4 * Hkv * P * 130) * 4
 
 
 @pytest.mark.parametrize("g,PB", [(1, 32), (4, 32), (8, 32), (16, 32)])

@@ -138,9 +138,16 @@ def test_trace_follows_the_lookahead_schedule(pf, waves, pb, dist):
     plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], prefetch=pf,
                     waves_per_wg=waves, partition_blocks=pb)
     W, PB = plan["waves_per_wg"], plan["partition_blocks"]
-    ranges = [(b, h, s, min(-(-int(L) // 16), s + PB))
-              for b, L in enumerate(x.context_lens) for h in range(Hkv)
-              for s in range(0, -(-int(L) // 16), PB)]
+    if plan["balanced"]:
+        # partition sizes chosen on the device from the context lengths
+        nbs = [-(-int(L) // 16) for L in x.context_lens]
+        _, parts = sch.balanced_split(nbs, PB, 1 << 16, W, plan["workgroups"] // Hkv,
+                                      plan["num_partitions"])
+        ranges = [(b, h, s, e) for b, _, s, e in parts for h in range(Hkv)]
+    else:
+        ranges = [(b, h, s, min(-(-int(L) // 16), s + PB))
+                  for b, L in enumerate(x.context_lens) for h in range(Hkv)
+                  for s in range(0, -(-int(L) // 16), PB)]
     seen = np.zeros((B, Hkv, MB), dtype=bool)
     for b, h, s, e in ranges:
         # slot 1 holds the L2 touch in mode 1 and the ring fetch in modes 2

@@ -13,7 +13,7 @@ from oracle import schedule as sch
 from paged_kv_cache_226_amd import inputs as gen
 from paged_kv_cache_226_amd import ops
 
-from parity import assert_close, bits
+from parity import assert_close, bits, same_plan
 
 pytestmark = pytest.mark.gpu
 
@@ -228,8 +228,7 @@ def test_fp8_workload_full_output(name):
     for dist in (1, 2):
         lds_plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], prefetch=4,
                             prefetch_distance=dist)
-        same = dict(waves_per_wg=lds_plan["waves_per_wg"],
-                    partition_blocks=lds_plan["partition_blocks"], prefetch_distance=dist)
+        same = same_plan(lds_plan, prefetch_distance=dist)
         lds = dec(prefetch=4, **same)
         reg = dec(prefetch=2, **same)
         torch.cuda.synchronize()

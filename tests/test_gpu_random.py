@@ -14,7 +14,7 @@ from oracle import oracle as orc
 from paged_kv_cache_226_amd import inputs as gen
 from paged_kv_cache_226_amd import ops
 
-from parity import assert_close, bits
+from parity import assert_close, bits, same_plan
 
 pytestmark = pytest.mark.gpu
 
@@ -97,8 +97,7 @@ def test_random_configuration(seed):
             dec(k, v, prefetch=c["pf"], prefetch_distance=c["dist"], **kw)
         return
     got = dec(k, v, prefetch=c["pf"], prefetch_distance=c["dist"], **kw)
-    same = dict(partition_blocks=plan["partition_blocks"], waves_per_wg=plan["waves_per_wg"],
-                seq_order=plan["seq_order"])
+    same = same_plan(plan)
     plain = dec(k, v, prefetch=0, **same)
     torch.cuda.synchronize()
     got = got.cpu().numpy()

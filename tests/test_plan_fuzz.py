@@ -56,15 +56,30 @@ def test_every_accepted_plan_is_launchable(shape_t, opt_t):
     if rc != nat.PA_OK:
         return
     PB, P = p["partition_blocks"], p["num_partitions"]
-    assert 1 <= PB <= min(MB, 1024)
-    assert P == -(-MB // PB) and P <= 65535
-    assert p["workgroups"] == P * Hkv * B
-    assert p["waves_per_wg"] in (1, 2, 4, 8)
+    W = p["waves_per_wg"]
+    assert W in (1, 2, 4, 8)
+    if p["balanced"]:
+        # only for auto partitions and order of a split batch of 2..256
+        # sequences; rows per KV head cover every sequence's largest-size
+        # partitions, and P bounds each sequence's partitions in the workspace
+        assert pb == 0 and order == 0 and structure == 0 and 2 <= B <= 256
+        assert B * Hkv < 256 and P > 1 and PB % W == 0 and PB >= 16
+        rows = p["workgroups"] // Hkv
+        assert p["workgroups"] == rows * Hkv and B <= rows <= 65535
+        pb_max = -(-min(MB, 1024) // W) * W
+        assert rows >= B * -(-MB // pb_max) and P <= rows - B + 1
+        assert P >= -(-MB // pb_max) and P <= -(-MB // PB)
+        assert p["seq_order"] == nat.ORDER_NATURAL
+        want_ws = (-(-B // 4) * 4 + B * g * Hkv * P * 130) * 4
+    else:
+        assert 1 <= PB <= min(MB, 1024)
+        assert P == -(-MB // PB) and P <= 65535
+        assert p["workgroups"] == P * Hkv * B
+        if pb:
+            assert PB == min(pb, MB)
+        want_ws = B * g * Hkv * P * 130 * 4 if P > 1 else 0
     if waves:
-        assert p["waves_per_wg"] == waves
-    if pb:
-        assert PB == min(pb, MB)
-    want_ws = B * g * Hkv * P * 130 * 4 if P > 1 else 0
+        assert W == waves
     assert p["workspace_bytes"] == want_ws
     assert nat.lib().paged_attn_workspace_size(ctypes.byref(sh), ctypes.byref(o)) == want_ws
     assert p["prefetch"] == (nat.PREFETCH_REG if pf < 0 else pf)

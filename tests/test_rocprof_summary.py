@@ -59,3 +59,50 @@ def test_sweep_fetch_maps_dispatches_to_points(tmp_path):
     table = [l for l in open(path) if l.startswith("| 8 ") or l.startswith("| 16 ")]
     assert table[0].split("|")[5:8] == [" 1.0000 ", " 1.0000 ", " 1.0000 "]
     assert table[1].split("|")[5:8] == [" 1.0000 ", " 1.0000 ", " 1.2500 "]
+
+
+def test_request_path_table_derives_little_law_figures(tmp_path):
+    """Per-mode means of summed counters and the derived figures: mean latency
+    = latency sum / requests, in flight = latency sum / cycles (per XCD clock,
+    over 256 CUs for per-CU figures)."""
+    head = ('"Correlation_Id","Dispatch_Id","Agent_Id","Queue_Id","Process_Id","Thread_Id",'
+            '"Grid_Size","Kernel_Id","Kernel_Name","Workgroup_Size","LDS_Block_Size",'
+            '"Scratch_Size","VGPR_Count","Accum_VGPR_Count","SGPR_Count","Counter_Name",'
+            '"Counter_Value","Start_Timestamp","End_Timestamp"')
+    dec = "void pa::pa_decode_kernel<{}, false, false, false>(pa::DecodeArgs)"
+    rows, did = [], 0
+    for m, scale in ((0, 1.0), (1, 2.0)):
+        for _ in range(2):  # two launches per mode, same values
+            did += 1
+            for c, v in (("GRBM_GUI_ACTIVE", 8000.0), ("TCP_TCC_READ_REQ_sum", 100.0 * scale),
+                         ("TCP_TCC_READ_REQ_LATENCY_sum", 256000.0 * scale),
+                         ("TCC_EA0_RDREQ_sum", 50.0), ("TCC_EA0_RDREQ_LEVEL_sum", 5000.0)):
+                rows.append(f'{did},{did},"A",1,1,1,1,1,"{dec.format(m)}",256,0,0,8,0,8,'
+                            f'"{c}",{v},0,0')
+    d = tmp_path / "rq"
+    d.mkdir()
+    (d / "x_counter_collection.csv").write_text(head + "\n" + "\n".join(rows) + "\n")
+    rs.KV8 = False
+    path = rs.request_path_table([str(d)], "w", ["h"], str(tmp_path), {0: 10.0, 1: 12.5})
+    lines = {l.split("|")[1].strip(): [c.strip() for c in l.split("|")[2:-1]]
+             for l in open(path) if l.startswith("| ")}
+    assert lines["kernel us"] == ["10.00", "12.50"]
+    assert lines["TCP->TCC read requests"] == ["100", "200"]
+    assert lines["TCP->TCC mean read latency (cycles)"] == ["2560", "2560"]
+    # 256000 latency-cycles over 1000 cycles per XCD = 256 in flight, 1 per CU
+    assert lines["TCP->TCC reads in flight per CU"] == ["1", "2"]
+    assert lines["HBM (EA) reads in flight"] == ["5", "5"]
+    assert lines["HBM (EA) mean read latency (cycles)"] == ["100", "100"]
+
+
+def test_sweep_timing_table(tmp_path):
+    import json
+    pts = [{"sweep": "w", "batch": 8, "context": 1024, "kv_bytes": 8000000, "partitions": 4,
+            "us_off": 10.0, "us_on": 8.0, "GBps_on": 1000.0, "pct_hbm_peak_on": 12.5,
+            "speedup_on_vs_off": 1.25, "parity_abs": 1e-5, "parity_rel": 2e-4}]
+    (tmp_path / "s.jsonl").write_text("noise\n" + "".join(json.dumps(p) + "\n" for p in pts))
+    path = rs.sweep_timing(str(tmp_path / "s.jsonl"), "w", str(tmp_path), "cmd a ;; cmd b")
+    text = open(path).read()
+    assert "    cmd a\n    cmd b\n" in text
+    row = [l for l in text.splitlines() if l.startswith("| 8 ")][0].split("|")
+    assert [c.strip() for c in row[5:10]] == ["10.00", "8.00", "800", "1000", "12.5"]

@@ -42,3 +42,33 @@ def test_longer_lookahead_targets_the_same_wave_k_iterations_later(w, k):
     tr = sch.expected_trace(s, e, w, k)
     fetched = [j for j in range(s, e) if tr[j][2] >= 0]
     assert fetched == list(range(s + k * w, e))
+
+
+def test_balanced_split_model():
+    # uniform counts: the same partitions as a fixed split into slots/B parts
+    size, parts = sch.balanced_split([64] * 8, 16, 64, 8, 32, 4)
+    assert size == 16 and len(parts) == 32
+    assert [p[2:] for p in parts[:4]] == [(0, 16), (16, 32), (32, 48), (48, 64)]
+    # ragged: the smallest step multiple that fits; empty sequences get none
+    size, parts = sch.balanced_split([100, 0, 7, 33], 16, 104, 8, 6, 6)
+    assert size == 40  # 32 would need 4 + 1 + 2 = 7 > 6 partitions
+    assert [(b, i) for b, i, _, _ in parts] == [(0, 0), (0, 1), (0, 2), (2, 0), (3, 0)]
+    assert parts[2][2:] == (80, 100)
+    for b, i, s, e in parts:
+        assert s == i * size and s < e
+    covered = {b: sum(e - s for bb, _, s, e in parts if bb == b) for b in range(4)}
+    assert covered == {0: 100, 1: 0, 2: 7, 3: 33}
+
+    # the per-sequence cap: slots would allow 16-block partitions, but the
+    # workspace holds at most 4 per sequence
+    size, parts = sch.balanced_split([100, 0, 0, 0], 16, 104, 8, 64, 4)
+    assert size == 32 and len(parts) == 4
+
+
+def test_balanced_split_keeps_the_reduce_rule():
+    # 12 partitions of 16 would fit the slots, but more than 8 partitions
+    # need at least 64 blocks each: 3 of 64 instead (sizes step by 8)
+    size, parts = sch.balanced_split([190], 16, 192, 8, 100, 100)
+    assert size == 24  # 24 gives ceil(190 / 24) = 8 partitions
+    size, parts = sch.balanced_split([1000], 16, 1024, 8, 100, 100)
+    assert size == 64 and len(parts) == 16
