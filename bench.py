@@ -254,7 +254,7 @@ def run_sweep(args):
             on = times[plan["prefetch"]]
             print(json.dumps({
                 "sweep": args.workload, "batch": B, "context": ctx, "kv_bytes": kv_bytes,
-                "partitions": plan["num_partitions"],
+                "partitions": plan["num_partitions"], "balanced": plan["balanced"],
                 "us_off": round(times[0], 2), "us_on": round(on, 2),
                 "GBps_on": round(kv_bytes / on / 1e3, 1),
                 "pct_hbm_peak_on": round(100 * kv_bytes / on / 1e3 / acc.HBM_PEAK_GBPS, 2),

@@ -152,14 +152,17 @@ def sweep_timing(jsonl, workload, out_dir, command):
              "One decode step per point (prepared call, event-timed mean over the steps); "
              "KV bytes = 2 * Hkv * 128 * 2 B * batch * context.  'on' is the library's "
              "default look-ahead; parity is the default mode's output on the first and last "
-             "sequence (every head) against the fp64 oracle.", "",
-             "| batch | context | KV bytes | partitions | us off | us on | GB/s off | GB/s on |"
-             " % of 8 TB/s on | on vs off | parity abs | parity rel |",
-             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+             "sequence (every head) against the fp64 oracle.  'partitions' is the plan's: "
+             "per sequence for a fixed split, the most one sequence may get for a balanced "
+             "one (sized on the device).", "",
+             "| batch | context | KV bytes | split | partitions | us off | us on | GB/s off |"
+             " GB/s on | % of 8 TB/s on | on vs off | parity abs | parity rel |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for p in points:
         off_gbps = p["kv_bytes"] / p["us_off"] / 1e3
-        lines.append(f"| {p['batch']} | {p['context']} | {p['kv_bytes']} | {p['partitions']} | "
-                     f"{p['us_off']:.2f} | {p['us_on']:.2f} | {off_gbps:.0f} | "
+        split = "one" if p["partitions"] == 1 else ("balanced" if p.get("balanced") else "fixed")
+        lines.append(f"| {p['batch']} | {p['context']} | {p['kv_bytes']} | {split} | "
+                     f"{p['partitions']} | {p['us_off']:.2f} | {p['us_on']:.2f} | {off_gbps:.0f} | "
                      f"{p['GBps_on']:.0f} | {p['pct_hbm_peak_on']:.1f} | "
                      f"{p['speedup_on_vs_off']:.3f} | {p['parity_abs']:.2e} | "
                      f"{p['parity_rel']:.2e} |")

@@ -105,4 +105,4 @@ def test_sweep_timing_table(tmp_path):
     text = open(path).read()
     assert "    cmd a\n    cmd b\n" in text
     row = [l for l in text.splitlines() if l.startswith("| 8 ")][0].split("|")
-    assert [c.strip() for c in row[5:10]] == ["10.00", "8.00", "800", "1000", "12.5"]
+    assert [c.strip() for c in row[4:11]] == ["fixed", "4", "10.00", "8.00", "800", "1000", "12.5"]
