@@ -40,9 +40,14 @@ KERNEL_SOURCES = ["paged_kv_cache_226_amd/csrc/pa_kernels.hip",
 
 # (mode, distance, structure) of the per-mode timings: the four modes at
 # distance 1, the register look-ahead two blocks ahead, the LDS-staged
-# look-ahead, and (fp16 only) the four modes of the two-loop structure
+# look-ahead, and (fp16 only) the four modes of the two-loop structure.
+# Each runs on its own plan for the workload (with the same context hint as
+# the timed call), as a caller switching the mode would get it.
 MODE_RUNS = [(0, 1, 0), (1, 1, 0), (2, 1, 0), (3, 1, 0), (2, 2, 0), (4, 1, 0), (4, 2, 0),
              (0, 1, 1), (1, 1, 1), (2, 1, 1), (3, 1, 1)]
+# modes timed again on the timed call's own shape (waves, partitions, order,
+# residency): only the look-ahead differs from the timed call
+SAME_SHAPE_RUNS = [(0, 1, 0), (1, 1, 0), (3, 1, 0)]
 
 
 def kernel_source_hash() -> str:
@@ -151,6 +156,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall-time budget of the oracle baseline (repeated full steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context-hint", action="store_true",
+                    help="plan without the shortest context as min_context_hint")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3: every prefetch mode, no CPU leg")
     ap.add_argument("--sweep", action="store_true",
@@ -207,7 +214,9 @@ def run_sweep(args):
             d = gen.make_case_device(B, w.num_q_heads, w.num_kv_heads, ctx,
                                      seed=10_000 + 100 * bi + ci)
             out = torch.empty_like(d["q"])
-            plan = ops.plan(d["q"], d["k_cache"], d["block_tables"])
+            # every context of a sweep point is `ctx`: the caller's hint
+            hint = 0 if args.no_context_hint else ctx
+            plan = ops.plan(d["q"], d["k_cache"], d["block_tables"], min_context_hint=hint)
             if args.profile:
                 # for a counter pass: a fixed number of launches per mode, in
                 # this order, so the dispatches can be mapped back to points
@@ -215,7 +224,7 @@ def run_sweep(args):
                     for _ in range(SWEEP_PROFILE_LAUNCHES):
                         ops.paged_attn_decode(d["q"], d["k_cache"], d["v_cache"],
                                               d["block_tables"], d["context_lens"], d["scale"],
-                                              out, prefetch=pf)
+                                              out, prefetch=pf, min_context_hint=hint)
                 torch.cuda.synchronize()
                 print(json.dumps({"sweep_profile": args.workload, "batch": B, "context": ctx,
                                   "kv_bytes": kv_bytes, "partitions": plan["num_partitions"],
@@ -227,7 +236,8 @@ def run_sweep(args):
             times = {}
             for pf in (0, plan["prefetch"]):
                 f = ops.prepare_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
-                                       d["context_lens"], d["scale"], out, prefetch=pf)
+                                       d["context_lens"], d["scale"], out, prefetch=pf,
+                                       min_context_hint=hint)
                 # warm up for at least 50 ms: the GPU runs slower for a while
                 # after the input generation or an idle gap
                 t_end = time.perf_counter() + 0.05
@@ -255,6 +265,8 @@ def run_sweep(args):
             print(json.dumps({
                 "sweep": args.workload, "batch": B, "context": ctx, "kv_bytes": kv_bytes,
                 "partitions": plan["num_partitions"], "balanced": plan["balanced"],
+                "waves_per_wg": plan["waves_per_wg"], "resident_wgs": plan["resident_wgs"],
+                "min_context_hint": hint,
                 "us_off": round(times[0], 2), "us_on": round(on, 2),
                 "GBps_on": round(kv_bytes / on / 1e3, 1),
                 "pct_hbm_peak_on": round(100 * kv_bytes / on / 1e3 / acc.HBM_PEAK_GBPS, 2),
@@ -307,8 +319,15 @@ def measure_workload(args, name, env, cpu_leg):
         d["k_cache"], d["v_cache"] = gen.side_by_side(d["k_cache"], d["v_cache"])
     Hkv = x.k_cache.shape[1]
     kv_bytes = acc.step_kv_bytes(Hkv, 128, x.context_lens, elem_bytes=1 if fp8 else 2)
+    # the caller knows its context lengths: the shortest one is the hint that
+    # lets the plan take the streaming shape when every context fills the
+    # block table (it changes no result)
+    hint = 0 if args.no_context_hint else max(int(x.context_lens.min()), 0)
     plan = ops.plan(d["q"], d["k_cache"], d["block_tables"], prefetch=args.prefetch,
-                    prefetch_distance=args.prefetch_distance)
+                    prefetch_distance=args.prefetch_distance, min_context_hint=hint)
+    shape_kw = dict(waves_per_wg=plan["waves_per_wg"], seq_order=plan["seq_order"],
+                    max_resident_wgs=plan["resident_wgs"],
+                    partition_blocks=0 if plan["balanced"] else plan["partition_blocks"])
 
     # One prepared call per configuration, each with its own output tensor
     # and its own workspace (sized for its own plan): a step is then one C
@@ -316,20 +335,27 @@ def measure_workload(args, name, env, cpu_leg):
     # output stays readable after the timings.
     calls, outs = {}, {}
 
+    plans = {}
+
     def step(key):
+        # key: (mode, distance, structure, on the timed call's shape?)
         if key not in calls:
-            pf, dist, structure = key
+            pf, dist, structure, same = key
             outs[key] = torch.empty_like(d["q"])
+            kw = dict(prefetch=pf, prefetch_distance=dist, min_context_hint=hint)
+            if same:
+                kw.update(shape_kw)
+            if structure:
+                kw["structure"] = structure
+            plans[key] = ops.plan(d["q"], d["k_cache"], d["block_tables"], **kw)
             if fp8:
                 calls[key] = ops.prepare_decode_fp8(
                     d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
-                    x.scale, x8.k_scale, x8.v_scale, outs[key], prefetch=pf,
-                    prefetch_distance=dist)
+                    x.scale, x8.k_scale, x8.v_scale, outs[key], **kw)
             else:
                 calls[key] = ops.prepare_decode(
                     d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
-                    x.scale, outs[key], prefetch=pf, prefetch_distance=dist,
-                    structure=structure)
+                    x.scale, outs[key], **kw)
         calls[key]()
 
     def timed(key, steps, warmup, min_warm_s=0.0):
@@ -368,13 +394,17 @@ def measure_workload(args, name, env, cpu_leg):
     mode = plan["prefetch"]
     dist = plan["prefetch_distance"]  # the library's default unless given
     mode_label = mode_name_of(nat, mode, dist)
-    timed_key = (mode, args.prefetch_distance, 0)
+    timed_key = (mode, args.prefetch_distance, 0, False)
 
     if args.profile:
         for pf, dist_r, structure in MODE_RUNS:
             if not (fp8 and structure):
-                timed((pf, dist_r, structure), args.steps, args.warmup)
+                timed((pf, dist_r, structure, False), args.steps, args.warmup)
         return None, None
+
+    def shape_of_plan(p):
+        return {k: p[k] for k in ("waves_per_wg", "partition_blocks", "num_partitions",
+                                  "seq_order", "resident_wgs", "balanced", "workgroups")}
 
     us = timed(timed_key, args.steps, args.warmup, min_warm_s=0.25)
     launch_avg, launch_med, launch_p10, launch_p90 = per_launch(timed_key, args.steps)
@@ -382,8 +412,18 @@ def measure_workload(args, name, env, cpu_leg):
     for pf, dist_r, structure in MODE_RUNS:
         if fp8 and structure:
             continue
-        u = timed((pf, dist_r, structure), max(20, args.steps // 4), 5)
+        key = (pf, dist_r, structure, False)
+        u = timed(key, max(20, args.steps // 4), 5)
+        p = plans[key]
         modes[mode_name_of(nat, pf, dist_r, structure)] = {
+            "us_per_step": round(u, 2), "GBps": round(kv_bytes / u / 1e3, 1),
+            "waves_per_wg": p["waves_per_wg"], "resident_wgs": p["resident_wgs"],
+            "num_partitions": p["num_partitions"]}
+    same_shape = {}
+    for pf, dist_r, structure in SAME_SHAPE_RUNS:
+        key = (pf, dist_r, structure, True)
+        u = timed(key, max(20, args.steps // 4), 5)
+        same_shape[mode_name_of(nat, pf, dist_r, structure)] = {
             "us_per_step": round(u, 2), "GBps": round(kv_bytes / u / 1e3, 1)}
 
     # the streaming read over exactly this step's KV bytes: the ramp-up and
@@ -431,6 +471,7 @@ def measure_workload(args, name, env, cpu_leg):
                    "context_min": int(x.context_lens.min()),
                    "context_max": int(x.context_lens.max()),
                    "prefetch": mode_label, "prefetch_distance": dist,
+                   "min_context_hint": hint, "resident_wgs": plan["resident_wgs"],
                    "waves_per_wg": plan["waves_per_wg"],
                    "partition_blocks": plan["partition_blocks"],
                    "num_partitions": plan["num_partitions"],
@@ -446,8 +487,12 @@ def measure_workload(args, name, env, cpu_leg):
         "roofline": roofline,
         "lookahead": {"off_us_per_step": off_us, "timed_mode": mode_label,
                       "timed_us_per_step": round(us, 2),
-                      "speedup_timed_vs_off": round(off_us / us, 4)},
+                      "speedup_timed_vs_off": round(off_us / us, 4),
+                      "off_same_shape_us_per_step": same_shape["off"]["us_per_step"],
+                      "speedup_timed_vs_off_same_shape":
+                          round(same_shape["off"]["us_per_step"] / us, 4)},
         "prefetch_modes": modes,
+        "prefetch_modes_on_the_timed_shape": same_shape,
         "stream_read_same_size_GBps": round(stream_same_gbps, 1),
         "pct_of_same_size_stream": round(100 * achieved / stream_same_gbps, 1),
         "lookahead_counters": read_lookahead_counters(tag, mode_label),
@@ -480,17 +525,23 @@ def measure_workload(args, name, env, cpu_leg):
     par.update({"rows_checked": int(w.num_seqs * w.num_q_heads), "elements_checked": int(got.size),
                 "output_of": f"the timed call ({mode_label})", "abs_tol": 2e-3, "rel_tol": 1e-2,
                 "pass": par["abs"] <= 2e-3 and par["rel"] <= 1e-2})
+    # every run against the oracle; the runs on the timed call's own shape
+    # (same waves, partitions, order) must also give its bits
     bitwise = {}
+    timed_shape = shape_of_plan(plans[timed_key])
     for key, o in outs.items():
         if key == timed_key:
             continue
-        nm = mode_name_of(nat, *key)
+        nm = mode_name_of(nat, *key[:3])
         gk = o.cpu().numpy()
-        bitwise[nm] = bool(np.array_equal(gk.view(np.uint16), got.view(np.uint16)))
-        if nm in modes:
-            pk = parity_of(gk, ref)
-            modes[nm]["parity_abs"] = pk["abs"]
-            modes[nm]["parity_rel"] = pk["rel"]
+        pk = parity_of(gk, ref)
+        table = same_shape if key[3] else modes
+        if nm in table:
+            table[nm]["parity_abs"] = pk["abs"]
+            table[nm]["parity_rel"] = pk["rel"]
+        if key[2] == 0 and shape_of_plan(plans[key]) == timed_shape:
+            tag_ = nm + ("@timed_shape" if key[3] else "")
+            bitwise[tag_] = bool(np.array_equal(gk.view(np.uint16), got.view(np.uint16)))
     par["bitwise_equal_to_timed"] = bitwise
     block["parity"] = par
     t_cpu = sorted(runs)[len(runs) // 2]
@@ -576,6 +627,7 @@ def main():
         "other_bytes_per_step": head["other_bytes_per_step"],
         "flops_per_step": head["flops_per_step"],
         "prefetch_modes": head["prefetch_modes"],
+        "prefetch_modes_on_the_timed_shape": head["prefetch_modes_on_the_timed_shape"],
         "stream_read_ceiling_GBps": round(stream_gbps, 1),
         "pct_of_stream_ceiling": round(100 * head["GBps"] / stream_gbps, 1),
         "stream_read_same_size_GBps": head["stream_read_same_size_GBps"],

@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 5
+#define PA_ABI_VERSION 6
 #define PA_HEAD_DIM 128
 #define PA_BLOCK_SIZE 16
 #define PA_G_MAX 16      /* query heads per KV head */
@@ -195,6 +195,25 @@ typedef struct pa_options {
     int32_t seq_order;         /* enum pa_seq_order; LONGEST_FIRST needs
                                   num_seqs <= PA_RANK_MAX_SEQS */
     int32_t structure;         /* enum pa_structure */
+    int32_t min_context_hint;  /* a lower bound, in tokens, on every
+                                  sequence's context length, when the caller
+                                  knows one (0 = none).  It only steers the
+                                  plan: with a bound of at least 7/8 of the
+                                  block table's width, a table of at least
+                                  64 blocks and a whole number of (sequence,
+                                  KV head) pairs per CU (1, 2, 3, 4, 6 or 8
+                                  for fp16; 1 or 4 for E4M3), auto waves,
+                                  partitions and residency, and the
+                                  look-ahead off or in registers (fp16 one
+                                  block ahead, E4M3 two), the plan takes the
+                                  streaming shape: waves per work-group and a
+                                  residency cap sized so that each CU keeps
+                                  about 32 KiB of K/V loads in flight from
+                                  start to end.  A wrong bound changes no
+                                  result, only the speed */
+    int32_t max_resident_wgs;  /* at most this many decode work-groups per CU
+                                  at once (0 = the plan's choice, 1..64): the
+                                  launch requests the LDS that enforces it */
     void *workspace;           /* device scratch for partition partials; may be
                                   NULL when the plan has one partition */
     size_t workspace_bytes;
@@ -236,6 +255,11 @@ typedef struct pa_plan_info {
                                   sequences and fewer (sequence, KV head)
                                   pairs than CUs, with seq_order AUTO and the
                                   fused structure */
+    int32_t resident_wgs;      /* the residency cap the launch enforces
+                                  (work-groups per CU), 0 = none */
+    size_t lds_bytes;          /* dynamic LDS per decode work-group: what the
+                                  walk needs, or more where a residency cap
+                                  is enforced */
 } pa_plan_info;
 
 /* What the auto plan takes from the device.  paged_attn_plan,

@@ -40,6 +40,7 @@ class PaOptions(ctypes.Structure):
     _fields_ = [("prefetch", ctypes.c_int32), ("partition_blocks", ctypes.c_int32),
                 ("waves_per_wg", ctypes.c_int32), ("prefetch_distance", ctypes.c_int32),
                 ("seq_order", ctypes.c_int32), ("structure", ctypes.c_int32),
+                ("min_context_hint", ctypes.c_int32), ("max_resident_wgs", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("debug_gather_k", ctypes.c_void_p), ("debug_trace", ctypes.c_void_p),
                 ("debug_error_word", ctypes.c_void_p)]
@@ -50,7 +51,8 @@ class PaPlanInfo(ctypes.Structure):
                 ("partition_blocks", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
                 ("workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
                 ("seq_order", ctypes.c_int32), ("structure", ctypes.c_int32),
-                ("prefetch_distance", ctypes.c_int32), ("balanced", ctypes.c_int32)]
+                ("prefetch_distance", ctypes.c_int32), ("balanced", ctypes.c_int32),
+                ("resident_wgs", ctypes.c_int32), ("lds_bytes", ctypes.c_size_t)]
 
 
 class PaDeviceInfo(ctypes.Structure):
@@ -61,7 +63,7 @@ class PaDeviceInfo(ctypes.Structure):
 _lib = None
 
 # the PA_ABI_VERSION whose struct layouts the classes above mirror
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class NativeLibraryMissing(RuntimeError):

@@ -64,6 +64,27 @@ constexpr int kTwoLoopPartitionBlocks = 32;
 //    work-group); 3 waves per SIMD (of the 4 of a CDNA CU) is what the
 //    register ring's VGPRs allow.
 constexpr int kResidentWavesPerCU = 12;
+//  * The streaming shape, for batches whose contexts all fill the table
+//    (pa_options.min_context_hint >= 7/8 of its width) with a whole number u
+//    of units per CU.  A CU streams best with about 32 KiB of K/V loads in
+//    flight: 4 fp16 blocks of one KV head (K and V, 8 KiB each), 8 E4M3
+//    ones.  The shapes above keep 8-24 blocks in flight and over-subscribe
+//    it by 4-6 %.  The streaming shape picks the waves per work-group and a
+//    residency cap from u and from the blocks each wave keeps in flight (1
+//    with the look-ahead off, 2 with the register look-ahead one block
+//    ahead, 3 two blocks ahead), so that every CU holds about that many
+//    from the start to the end of the launch (stream_shape below).
+//    Measured, us (default shape -> streaming shape, look-ahead on):
+//    MHA 32/32, 32 x 2K (llama2_7b-shaped) 159.5 -> 152.6; 8 x 4K 80.2 ->
+//    76.1; 16 x 2K 80.7 -> 76.4; 24 x 2K 120.1 -> 117.2; 48 x 1K 121.8 ->
+//    118.8; 64 x 1K 161.0 -> 158.0; GQA 28/4, 128 x 4K 160.2 -> 158.4;
+//    E4M3 32 x 2K 81.7 -> 78.6.  With the look-ahead off, 32 x 2K: 161.1 ->
+//    149.9.  Other u gained under 2 % or lost: a partial last round leaves
+//    CUs with one work-group and too few loads in flight.  A ragged batch
+//    must not take this shape: its long units then run alone on their CUs
+//    with 1-2 blocks in flight (llama3_8b-shaped, 64 x 512..8K tokens: 181 ->
+//    256 us), hence the hint.
+constexpr int kStreamMinBlocks = 64;
 
 bool valid_device(const pa_device_info* d) {
   return d && d->compute_units >= 1 && d->compute_units <= 65536 &&
@@ -121,7 +142,44 @@ struct Plan {
   int64_t wgs;
   size_t ws_bytes;
   int bal, nslot, pb_max;  // balanced split: grid rows per KV head, largest size
+  int cap;                 // residency cap (work-groups per CU), 0 = none
+  size_t lds;              // dynamic LDS per decode work-group
 };
+
+// Waves per work-group and residency cap of the streaming shape for u units
+// per CU, by the blocks `f` each wave keeps in flight ({0, 0} where it does
+// not apply: other u, the L2 touch, the LDS ring).
+struct StreamShape {
+  int waves, cap;
+};
+StreamShape stream_shape(int64_t u, bool kv8, int f) {
+  if (kv8) {  // 8 blocks of 4 KiB
+    if (f == 1 && u == 1) return {8, 0};
+    if (f == 1 && u == 4) return {2, 4};
+    if (f == 3 && u == 4) return {1, 4};
+    return {0, 0};
+  }
+  if (f == 1) {  // 4 blocks of 8 KiB: 4 waves per CU
+    switch (u) {
+      case 1: return {4, 0};
+      case 2: return {2, 0};
+      case 3: return {4, 1};
+      case 4: case 8: return {1, 4};
+      case 6: return {2, 2};
+      default: return {0, 0};
+    }
+  }
+  if (f == 2) {  // 2 waves per CU
+    switch (u) {
+      case 1: return {2, 0};
+      case 2: return {1, 0};
+      case 3: return {2, 1};
+      case 4: case 6: case 8: return {1, 2};
+      default: return {0, 0};
+    }
+  }
+  return {0, 0};
+}
 
 // Balanced split (auto partitions of a ragged batch with fewer (sequence,
 // KV head) pairs than CUs, 2..PA_RANK_MAX_SEQS sequences): the device picks
@@ -171,6 +229,8 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   const bool two = o->structure == PA_STRUCTURE_TWO_LOOP;
   const bool kv8 = sh->kv_dtype == PA_KV_E4M3;
   if (two && (o->prefetch_distance > 1 || kv8)) return PA_ERR_UNSUPPORTED;
+  if (o->min_context_hint < 0 || o->max_resident_wgs < 0 || o->max_resident_wgs > 64)
+    return PA_ERR_INVALID_ARG;
   int order = o->seq_order;
   if (order < PA_ORDER_AUTO || order > PA_ORDER_LONGEST_FIRST) return PA_ERR_INVALID_ARG;
   if (order == PA_ORDER_AUTO)
@@ -207,17 +267,40 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   if (o->partition_blocks > kMaxPartitionBlocks) return PA_ERR_UNSUPPORTED;
 
   int waves = o->waves_per_wg;
+  int cap = o->max_resident_wgs;
+  // the streaming shape: every context at least 7/8 of the table, a whole
+  // number of units per CU, the look-ahead off or in registers (the
+  // measured distances), waves, partitions and residency left to the plan
+  const int in_flight = pf == PA_PREFETCH_OFF ? 1 : pf == PA_PREFETCH_REG ? 1 + dist : 0;
+  if (o->min_context_hint > 0 &&
+      (int64_t)o->min_context_hint * 8 >= (int64_t)MB * PA_BLOCK_SIZE * 7 &&
+      MB >= kStreamMinBlocks && !two && in_flight > 0 && o->waves_per_wg == 0 &&
+      o->partition_blocks == 0 && o->max_resident_wgs == 0 && units >= dv.cus &&
+      units % dv.cus == 0) {
+    const StreamShape ss = stream_shape(units / dv.cus, kv8, in_flight);
+    if (ss.waves > 0) {
+      waves = ss.waves;
+      cap = ss.cap;
+      // uniform contexts: the ranking would be the identity
+      if (o->seq_order == PA_ORDER_AUTO) {
+        order = PA_ORDER_NATURAL;
+        rank = false;
+      }
+    }
+  }
   if (waves == 0 && two) waves = 4;
   if (waves == 0) {
     const bool whole = o->partition_blocks == 0 ? units >= dv.cus : o->partition_blocks >= MB;
     waves = 4;
     if (whole && units < kFourWaveUnitsPerCU * dv.cus && MB >= kLongTableBlocks &&
         MB <= kMaxPartitionBlocks &&
-        pa::decode_lds_bytes(MB, g, 8, B, rank, 8 * slot) <= dv.lds_per_wg)
+        pa::decode_lds_bytes(MB, g, 8, B, rank, 8 * slot) + pa::kCompilerLdsBytes <=
+            dv.lds_per_wg)
       waves = 8;
     const int split_pb = MB < kMaxAutoPartition ? MB : kMaxAutoPartition;
     if (o->partition_blocks == 0 && !whole &&
-        pa::decode_lds_bytes(split_pb, g, 8, B, rank, 8 * slot) <= dv.lds_per_wg)
+        pa::decode_lds_bytes(split_pb, g, 8, B, rank, 8 * slot) + pa::kCompilerLdsBytes <=
+            dv.lds_per_wg)
       waves = 8;
   }
 
@@ -227,7 +310,9 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   } else if (two) {
     // 512-token partitions, halved until the scores fit in LDS
     PB = kTwoLoopPartitionBlocks < MB ? kTwoLoopPartitionBlocks : MB;
-    while (PB > 1 && pa::two_loop_lds_bytes(PB, g, waves, B, rank) > dv.lds_per_wg) PB /= 2;
+    while (PB > 1 && pa::two_loop_lds_bytes(PB, g, waves, B, rank) + pa::kCompilerLdsBytes >
+                          dv.lds_per_wg)
+      PB /= 2;
   } else if (units >= dv.cus) {
     PB = MB < kMaxPartitionBlocks ? MB : kMaxPartitionBlocks;
   } else {
@@ -279,17 +364,23 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
                : pa::decode_lds_bytes(bal ? pb_max : PB, g, waves, B, r, waves * slot);
   };
   const int64_t wgs = bal ? (int64_t)nslot * Hkv : (int64_t)P * Hkv * B;
+  // a residency cap takes LDS: cap work-groups of it fill a CU
+  const size_t cap_lds = cap > 0 ? pa::residency_lds_bytes(dv.lds_per_cu, cap) : 0;
+  auto lds_with_cap = [&](bool r) {
+    const size_t l = lds_for(r);
+    return l > cap_lds ? l : cap_lds;
+  };
   if (o->seq_order == PA_ORDER_AUTO && rank) {
-    const size_t l = lds_for(true);
+    const size_t l = lds_with_cap(true) + pa::kCompilerLdsBytes;
     const int64_t by_waves = kResidentWavesPerCU / waves;
-    const int64_t by_lds = (int64_t)(dv.lds_per_cu / (l > 0 ? l : 1));
+    const int64_t by_lds = (int64_t)(dv.lds_per_cu / l);
     if (wgs <= dv.cus * (by_waves < by_lds ? by_waves : by_lds)) {
       order = PA_ORDER_NATURAL;
       rank = false;
     }
   }
-  const size_t lds = lds_for(rank);
-  if (lds > dv.lds_per_wg) return PA_ERR_UNSUPPORTED;
+  const size_t lds = lds_with_cap(rank);
+  if (lds + pa::kCompilerLdsBytes > dv.lds_per_wg) return PA_ERR_UNSUPPORTED;
   memset(pl, 0, sizeof(*pl));
   pl->order = order;
   pl->two = two ? 1 : 0;
@@ -302,6 +393,8 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   pl->bal = bal;
   pl->nslot = nslot;
   pl->pb_max = pb_max;
+  pl->cap = cap;
+  pl->lds = lds;
   // partials [B][Hq][P][128] and [B][Hq][P][2] in fp32; the balanced split
   // adds the sequences' partition counts (B int32, padded to 16 bytes)
   pl->ws_bytes = P > 1 ? ((size_t)(bal ? (B + 3) / 4 * 4 : 0) +
@@ -344,6 +437,8 @@ static int plan_info(const pa_shape* sh, const pa_options* o, const DeviceInfo& 
   info->structure = pl.two;
   info->prefetch_distance = pl.dist;
   info->balanced = pl.bal;
+  info->resident_wgs = pl.cap;
+  info->lds_bytes = pl.lds;
   return PA_OK;
 }
 
@@ -466,14 +561,16 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
     if (pl.bal) a.ws_np = reinterpret_cast<int32_t*>(a.ws_ml + rows * 2);
   }
   if (pl.two) {
-    if (pa::launch_decode_two_loop(a, pl.pf, pl.waves, st) != hipSuccess) return PA_ERR_HIP;
+    if (pa::launch_decode_two_loop(a, pl.pf, pl.waves, pl.lds, st) != hipSuccess)
+      return PA_ERR_HIP;
   } else {
     // the register look-ahead at distance 2 is kernel instance 4, the LDS
     // ring at distance 1 and 2 instances 5 and 6
     const int variant = pl.pf == PA_PREFETCH_LDS ? 4 + pl.dist
                         : pl.pf == PA_PREFETCH_REG && pl.dist == 2 ? 4
                                                                    : pl.pf;
-    if (pa::launch_decode(a, variant, dbg, kv8, pl.waves, st) != hipSuccess) return PA_ERR_HIP;
+    if (pa::launch_decode(a, variant, dbg, kv8, pl.waves, pl.lds, st) != hipSuccess)
+      return PA_ERR_HIP;
   }
   if (pl.P > 1 && pa::launch_reduce(a, st) != hipSuccess) return PA_ERR_HIP;
   return PA_OK;

@@ -61,6 +61,20 @@ inline int lds_bt_bytes_for(int PB) { return ((PB * 4) + 15) / 16 * 16; }
 // merge area, which are written only after the ranking is done.
 inline size_t rank_lds_bytes(int B) { return (size_t)((B + 3) / 4 * 4) * 4 + 16; }
 
+// LDS the compiler adds beside a kernel's dynamic allocation, at most (the
+// decode kernel's is 256 B: the scratch word of __syncthreads_or).  Plans
+// keep dynamic + this within the device's LDS per work-group.
+constexpr size_t kCompilerLdsBytes = 1024;
+
+// Dynamic LDS that holds at most `cap` work-groups on a CU with `per_cu`
+// bytes: per_cu / cap rounded down to 1 KiB, less kCompilerLdsBytes (so
+// that cap of them fit with their compiler LDS whatever the allocation
+// granularity up to 1 KiB, and cap + 1 do not).
+inline size_t residency_lds_bytes(size_t per_cu, int cap) {
+  const size_t share = per_cu / (size_t)cap / 1024 * 1024;
+  return share > kCompilerLdsBytes ? share - kCompilerLdsBytes : 0;
+}
+
 // `slots`: the LDS-staged look-ahead's per-wave slots, which overlay the
 // merge records (they are free by the time the records are written).
 inline size_t decode_lds_bytes(int PB, int g, int waves, int B, bool rank, size_t slots = 0) {
@@ -86,9 +100,10 @@ constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
 // on each device, then cached).
 hipError_t noalloc_scratch(void** ptr);
 
-hipError_t launch_decode_two_loop(const DecodeArgs& a, int pf, int waves, hipStream_t st);
+hipError_t launch_decode_two_loop(const DecodeArgs& a, int pf, int waves, size_t lds,
+                                  hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int waves,
-                         hipStream_t st);
+                         size_t lds, hipStream_t st);
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_pack_k(const void* in, void* out, int64_t slices, bool kv8, hipStream_t st);
 hipError_t launch_stream_read(const void* buf, size_t bytes, void* sink, int groups,

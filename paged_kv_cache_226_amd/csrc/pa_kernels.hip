@@ -1259,7 +1259,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, dim3 grid, dim3 block, si
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int waves,
-                         hipStream_t st) {
+                         size_t lds, hipStream_t st) {
   typedef hipError_t (*fn_t)(const DecodeArgs&, dim3, dim3, size_t, hipStream_t);
   // pf 0..3 are the look-ahead modes; 4 is the register look-ahead of depth
   // 2, 5 and 6 the LDS ring of depth 1 and 2
@@ -1281,15 +1281,17 @@ hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int wa
   if (pf < 0 || pf > 6) return hipErrorInvalidValue;
   const dim3 grid(a.Hkv, a.balanced ? a.nslot : a.B, a.balanced ? 1 : a.P);
   const dim3 block(kWave * waves);
-  // the LDS ring: depth + 1 slots of one block's K and V per wave
+  // what the walk needs (the LDS ring: depth + 1 slots of one block's K and
+  // V per wave); the plan may ask for more, to cap the residency
   const size_t slots = pf >= 5 ? (size_t)waves * (pf - 3) * (kv8 ? 4096 : 8192) : 0;
-  return table[(kv8 ? 14 : 0) + pf * 2 + (dbg ? 1 : 0)](
-      a, grid, block,
-      decode_lds_bytes(a.balanced ? a.pb_max : a.PB, a.G, waves, a.B, a.rank_seqs != 0, slots),
-      st);
+  const size_t need =
+      decode_lds_bytes(a.balanced ? a.pb_max : a.PB, a.G, waves, a.B, a.rank_seqs != 0, slots);
+  return table[(kv8 ? 14 : 0) + pf * 2 + (dbg ? 1 : 0)](a, grid, block, lds > need ? lds : need,
+                                                       st);
 }
 
-hipError_t launch_decode_two_loop(const DecodeArgs& a, int pf, int waves, hipStream_t st) {
+hipError_t launch_decode_two_loop(const DecodeArgs& a, int pf, int waves, size_t lds,
+                                  hipStream_t st) {
   typedef hipError_t (*fn_t)(const DecodeArgs&, dim3, dim3, size_t, hipStream_t);
   static const fn_t table[4] = {
       launch_decode_t<0, false, false, true>, launch_decode_t<1, false, false, true>,
@@ -1297,8 +1299,8 @@ hipError_t launch_decode_two_loop(const DecodeArgs& a, int pf, int waves, hipStr
   if (pf < 0 || pf > 3) return hipErrorInvalidValue;
   const dim3 grid(a.Hkv, a.B, a.P);
   const dim3 block(kWave * waves);
-  return table[pf](a, grid, block, two_loop_lds_bytes(a.PB, a.G, waves, a.B, a.rank_seqs != 0),
-                   st);
+  const size_t need = two_loop_lds_bytes(a.PB, a.G, waves, a.B, a.rank_seqs != 0);
+  return table[pf](a, grid, block, lds > need ? lds : need, st);
 }
 
 hipError_t launch_reduce(const DecodeArgs& a, hipStream_t st) {

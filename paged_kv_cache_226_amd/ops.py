@@ -98,9 +98,11 @@ def options(prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0
             prefetch_distance: int = 0, seq_order: int = 0, structure: int = 0,
             debug_gather_k: Optional[torch.Tensor] = None,
             debug_trace: Optional[torch.Tensor] = None,
-            debug_error_word: Optional[torch.Tensor] = None) -> nat.PaOptions:
+            debug_error_word: Optional[torch.Tensor] = None, *,
+            min_context_hint: int = 0, max_resident_wgs: int = 0) -> nat.PaOptions:
     """pa_options for these settings (any debug tensor selects the checked
-    kernel variant)."""
+    kernel variant).  min_context_hint: a lower bound on every context length
+    (tokens) that the caller knows, 0 = none; it only steers the auto plan."""
     o = nat.default_options()
     o.prefetch = int(prefetch)
     o.partition_blocks = int(partition_blocks)
@@ -108,6 +110,8 @@ def options(prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0
     o.prefetch_distance = int(prefetch_distance)
     o.seq_order = int(seq_order)
     o.structure = int(structure)
+    o.min_context_hint = int(min_context_hint)
+    o.max_resident_wgs = int(max_resident_wgs)
     if debug_gather_k is not None:
         _check(debug_gather_k, "debug_gather_k", torch.float16, 4)
         o.debug_gather_k = debug_gather_k.data_ptr()
@@ -168,7 +172,8 @@ class DecodeCall:
     def __init__(self, fp8: bool, q, k_cache, v_cache, block_tables, context_lens, scale,
                  k_scale, v_scale, out, prefetch, partition_blocks, waves_per_wg,
                  prefetch_distance, seq_order, structure, workspace, debug_gather_k,
-                 debug_trace, debug_error_word, stream, noalloc: bool = False):
+                 debug_trace, debug_error_word, stream, noalloc: bool = False,
+                 min_context_hint: int = 0, max_resident_wgs: int = 0):
         if noalloc and (fp8 or workspace is not None):
             raise ValueError("the no-allocation call takes an fp16 cache and no workspace")
         self.name = ("paged_attn_decode_noalloc" if noalloc else
@@ -204,7 +209,8 @@ class DecodeCall:
         self._shape = shape_of(q, k_cache, block_tables, v_cache)
         self._opts = options(prefetch, partition_blocks, waves_per_wg, prefetch_distance,
                              seq_order, structure, debug_gather_k, debug_trace,
-                             debug_error_word)
+                             debug_error_word, min_context_hint=min_context_hint,
+                             max_resident_wgs=max_resident_wgs)
         L = nat.lib()
         need = int(L.paged_attn_workspace_size(ctypes.byref(self._shape),
                                                ctypes.byref(self._opts)))
@@ -256,12 +262,14 @@ def prepare_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                    debug_gather_k: Optional[torch.Tensor] = None,
                    debug_trace: Optional[torch.Tensor] = None,
                    debug_error_word: Optional[torch.Tensor] = None,
-                   stream: Optional[torch.cuda.Stream] = None) -> DecodeCall:
+                   stream: Optional[torch.cuda.Stream] = None, min_context_hint: int = 0,
+                   max_resident_wgs: int = 0) -> DecodeCall:
     """paged_attn_decode prepared for repeated calls on the same tensors."""
     return DecodeCall(False, q, k_cache, v_cache, block_tables, context_lens, scale, 1.0, 1.0,
                       out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
                       seq_order, structure, workspace, debug_gather_k, debug_trace,
-                      debug_error_word, stream)
+                      debug_error_word, stream, min_context_hint=min_context_hint,
+                      max_resident_wgs=max_resident_wgs)
 
 
 def prepare_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -272,13 +280,15 @@ def prepare_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                            debug_gather_k: Optional[torch.Tensor] = None,
                            debug_trace: Optional[torch.Tensor] = None,
                            debug_error_word: Optional[torch.Tensor] = None,
-                           stream: Optional[torch.cuda.Stream] = None) -> DecodeCall:
+                           stream: Optional[torch.cuda.Stream] = None,
+                           min_context_hint: int = 0, max_resident_wgs: int = 0) -> DecodeCall:
     """paged_attn_decode_noalloc prepared for repeated calls; pass `out` to
     keep the calls free of allocation."""
     return DecodeCall(False, q, k_cache, v_cache, block_tables, context_lens, scale, 1.0, 1.0,
                       out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
                       seq_order, structure, None, debug_gather_k, debug_trace,
-                      debug_error_word, stream, noalloc=True)
+                      debug_error_word, stream, noalloc=True, min_context_hint=min_context_hint,
+                      max_resident_wgs=max_resident_wgs)
 
 
 def paged_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -302,7 +312,8 @@ def prepare_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                        debug_gather_k: Optional[torch.Tensor] = None,
                        debug_trace: Optional[torch.Tensor] = None,
                        debug_error_word: Optional[torch.Tensor] = None,
-                       stream: Optional[torch.cuda.Stream] = None) -> DecodeCall:
+                       stream: Optional[torch.cuda.Stream] = None, min_context_hint: int = 0,
+                       max_resident_wgs: int = 0) -> DecodeCall:
     """paged_attn_decode_fp8 prepared for repeated calls on the same tensors."""
     if k_cache.dtype == torch.float8_e4m3fn:
         k_cache = k_cache.view(torch.uint8)
@@ -311,7 +322,8 @@ def prepare_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
     return DecodeCall(True, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
                       v_scale, out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
                       seq_order, structure, workspace, debug_gather_k, debug_trace,
-                      debug_error_word, stream)
+                      debug_error_word, stream, min_context_hint=min_context_hint,
+                      max_resident_wgs=max_resident_wgs)
 
 
 def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -323,7 +335,8 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       debug_gather_k: Optional[torch.Tensor] = None,
                       debug_trace: Optional[torch.Tensor] = None,
                       debug_error_word: Optional[torch.Tensor] = None,
-                      stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+                      stream: Optional[torch.cuda.Stream] = None, min_context_hint: int = 0,
+                      max_resident_wgs: int = 0) -> torch.Tensor:
     """One decode step of paged attention; returns out (fp16 [B, Hq, 128]).
 
     q [B, Hq, 128] fp16; k_cache [NB, Hkv, 16, 16, 8] fp16 (dim group, token, 8
@@ -335,7 +348,9 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                           waves_per_wg=waves_per_wg, prefetch_distance=prefetch_distance,
                           seq_order=seq_order, structure=structure, workspace=workspace,
                           debug_gather_k=debug_gather_k, debug_trace=debug_trace,
-                          debug_error_word=debug_error_word, stream=stream)()
+                          debug_error_word=debug_error_word, stream=stream,
+                          min_context_hint=min_context_hint,
+                          max_resident_wgs=max_resident_wgs)()
 
 
 def paged_attn_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -349,7 +364,8 @@ def paged_attn_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                           debug_gather_k: Optional[torch.Tensor] = None,
                           debug_trace: Optional[torch.Tensor] = None,
                           debug_error_word: Optional[torch.Tensor] = None,
-                          stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+                          stream: Optional[torch.cuda.Stream] = None,
+                          min_context_hint: int = 0, max_resident_wgs: int = 0) -> torch.Tensor:
     """Decode over an OCP E4M3 cache (uint8 or float8_e4m3fn); a cached value
     is decode(byte) * k_scale (K) or * v_scale (V).
 
@@ -363,7 +379,9 @@ def paged_attn_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                               prefetch_distance=prefetch_distance, seq_order=seq_order,
                               structure=structure, workspace=workspace,
                               debug_gather_k=debug_gather_k, debug_trace=debug_trace,
-                              debug_error_word=debug_error_word, stream=stream)()
+                              debug_error_word=debug_error_word, stream=stream,
+                              min_context_hint=min_context_hint,
+                              max_resident_wgs=max_resident_wgs)()
 
 
 def pack_k(k_token_major: torch.Tensor, out: Optional[torch.Tensor] = None,

@@ -67,11 +67,13 @@ def same_plan(plan, **extra):
     """Options that reproduce `plan` (waves, partitions, order) for another
     look-ahead mode: a balanced split is reproduced by asking for it again
     (auto partitions and order with the same waves), a fixed one by its
-    partition size and order."""
+    partition size and order.  A residency cap is kept (it changes no bits,
+    only how many work-groups share a CU)."""
     if plan["balanced"]:
         kw = dict(partition_blocks=0, waves_per_wg=plan["waves_per_wg"], seq_order=0)
     else:
         kw = dict(partition_blocks=plan["partition_blocks"], waves_per_wg=plan["waves_per_wg"],
                   seq_order=plan["seq_order"])
+    kw["max_resident_wgs"] = plan["resident_wgs"]
     kw.update(extra)
     return kw

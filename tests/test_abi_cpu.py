@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function(native_lib):
 
 
 def test_version_and_error_strings(native_lib):
-    assert native_lib.paged_attn_abi_version() == nat.ABI_VERSION == 5
+    assert native_lib.paged_attn_abi_version() == nat.ABI_VERSION == 6
     assert nat.error_string(0) == "ok"
     for code in range(1, 5):
         assert nat.error_string(code) not in ("ok", "unknown status")
@@ -478,3 +478,155 @@ def test_pack_k_validation(native_lib):
     # the output overlaps the input: 4 blocks x 2 heads x 4 KiB = 32 KiB
     assert f(A, ctypes.c_void_p(FAKE + 16384), 4, 2, nat.KV_F16, None) == nat.PA_ERR_INVALID_ARG
     assert f(A, B, 1 << 62, 2, nat.KV_F16, None) == nat.PA_ERR_UNSUPPORTED
+
+
+def hinted(min_ctx, **kw):
+    o = nat.default_options()
+    o.min_context_hint = min_ctx
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+# (B, Hq, Hkv, kv_dtype) -> (waves, cap) on 256 CUs with every context at
+# the table's width: a whole number u of (sequence, KV head) units per CU
+@pytest.mark.parametrize("B,Hq,Hkv,kv,want", [
+    (8, 32, 32, nat.KV_F16, (2, 0)),     # u = 1
+    (16, 32, 32, nat.KV_F16, (1, 0)),    # u = 2
+    (128, 28, 4, nat.KV_F16, (1, 0)),    # u = 2, GQA 7:1
+    (24, 32, 32, nat.KV_F16, (2, 1)),    # u = 3
+    (32, 32, 32, nat.KV_F16, (1, 2)),    # u = 4 (the llama2_7b shape)
+    (128, 40, 8, nat.KV_F16, (1, 2)),    # u = 4, GQA 5:1
+    (48, 32, 32, nat.KV_F16, (1, 2)),    # u = 6
+    (64, 32, 32, nat.KV_F16, (1, 2)),    # u = 8
+    (32, 32, 32, nat.KV_E4M3, (1, 4)),   # u = 4, E4M3
+])
+def test_streaming_shape_for_uniform_contexts(native_lib, B, Hq, Hkv, kv, want):
+    MB = 128
+    sh = nat.make_shape(B, Hq, Hkv, MB, 1, kv_dtype=kv)
+    p = nat.plan(sh, hinted(MB * 16), device=MI355X)
+    assert (p["waves_per_wg"], p["resident_wgs"]) == want
+    assert p["prefetch"] == nat.PREFETCH_REG and p["num_partitions"] == 1
+    assert p["seq_order"] == nat.ORDER_NATURAL
+    if want[1]:
+        # cap work-groups of the LDS fill a CU, cap + 1 do not
+        share = 163840 // want[1] // 1024 * 1024 - 1024
+        assert p["lds_bytes"] == share
+        assert want[1] * (share + 1024) <= 163840 < (want[1] + 1) * (share + 256)
+    # the hint is the only difference from the default plan
+    base = nat.plan(sh, device=MI355X)
+    assert base["resident_wgs"] == 0
+    assert (base["waves_per_wg"], base["resident_wgs"]) != want
+
+
+@pytest.mark.parametrize("case", [
+    "no hint", "ragged", "short table", "not a multiple", "u = 5", "u = 16", "e4m3 u = 2",
+    "explicit waves", "l2 touch", "lds ring", "fp16 two blocks ahead", "e4m3 one block ahead",
+    "explicit partitions",
+    "explicit cap", "two-loop"])
+def test_streaming_shape_needs_every_condition(native_lib, case):
+    B, Hq, Hkv, MB, kv, hint, kw = 32, 32, 32, 128, nat.KV_F16, 128 * 16, {}
+    if case == "no hint":
+        hint = 0
+    elif case == "ragged":
+        hint = 128 * 16 * 7 // 8 - 1  # one token under 7/8 of the table
+    elif case == "short table":
+        MB, hint = 63, 63 * 16
+    elif case == "not a multiple":
+        B = 33
+    elif case == "u = 5":
+        B = 40
+    elif case == "u = 16":
+        B = 128
+    elif case == "e4m3 u = 2":
+        B, kv = 16, nat.KV_E4M3
+    elif case == "explicit waves":
+        kw = dict(waves_per_wg=4)
+    elif case == "l2 touch":
+        kw = dict(prefetch=nat.PREFETCH_L2)
+    elif case == "lds ring":
+        kw = dict(prefetch=nat.PREFETCH_LDS)
+    elif case == "fp16 two blocks ahead":
+        kw = dict(prefetch_distance=2)
+    elif case == "e4m3 one block ahead":
+        kv, kw = nat.KV_E4M3, dict(prefetch_distance=1)
+    elif case == "explicit partitions":
+        kw = dict(partition_blocks=128)
+    elif case == "explicit cap":
+        kw = dict(max_resident_wgs=3)
+    elif case == "two-loop":
+        kw = dict(structure=nat.STRUCTURE_TWO_LOOP)
+    sh = nat.make_shape(B, Hq, Hkv, MB, 1, kv_dtype=kv)
+    p = nat.plan(sh, hinted(hint, **kw), device=MI355X)
+    q = nat.plan(sh, hinted(0, **kw), device=MI355X)
+    assert p == q, case
+
+
+# the same, look-ahead off: one block in flight per wave, so about 4 waves
+# per CU (8 for E4M3)
+@pytest.mark.parametrize("B,Hq,Hkv,kv,want", [
+    (8, 32, 32, nat.KV_F16, (4, 0)),     # u = 1
+    (16, 32, 32, nat.KV_F16, (2, 0)),    # u = 2
+    (24, 32, 32, nat.KV_F16, (4, 1)),    # u = 3
+    (32, 32, 32, nat.KV_F16, (1, 4)),    # u = 4
+    (48, 32, 32, nat.KV_F16, (2, 2)),    # u = 6
+    (64, 32, 32, nat.KV_F16, (1, 4)),    # u = 8
+    (8, 32, 32, nat.KV_E4M3, (8, 0)),    # u = 1
+    (32, 32, 32, nat.KV_E4M3, (2, 4)),   # u = 4
+])
+def test_streaming_shape_with_the_lookahead_off(native_lib, B, Hq, Hkv, kv, want):
+    sh = nat.make_shape(B, Hq, Hkv, 128, 1, kv_dtype=kv)
+    p = nat.plan(sh, hinted(128 * 16, prefetch=nat.PREFETCH_OFF), device=MI355X)
+    assert (p["prefetch"], p["waves_per_wg"], p["resident_wgs"]) == (0, *want)
+
+
+@pytest.mark.parametrize("kv,dist", [(nat.KV_F16, 1), (nat.KV_E4M3, 2)])
+def test_explicit_default_distance_keeps_the_streaming_shape(native_lib, kv, dist):
+    sh = nat.make_shape(32, 32, 32, 128, 1, kv_dtype=kv)
+    auto = nat.plan(sh, hinted(128 * 16), device=MI355X)
+    expl = nat.plan(sh, hinted(128 * 16, prefetch=nat.PREFETCH_REG, prefetch_distance=dist),
+                    device=MI355X)
+    assert auto == expl and auto["resident_wgs"] > 0
+
+
+def test_the_hint_at_exactly_seven_eighths_of_the_table(native_lib):
+    sh = nat.make_shape(32, 32, 32, 128, 1)
+    assert nat.plan(sh, hinted(128 * 16 * 7 // 8), device=MI355X)["resident_wgs"] == 2
+
+
+@pytest.mark.parametrize("cap", [1, 2, 3, 4, 5, 8, 16, 64])
+def test_residency_cap_sizes_the_lds(native_lib, cap):
+    sh = nat.make_shape(32, 32, 8, 64, 1)
+    p = nat.plan(sh, hinted(0, max_resident_wgs=cap), device=MI355X)
+    base = nat.plan(sh, device=MI355X)
+    share = max(163840 // cap // 1024 * 1024 - 1024, 0)
+    assert p["resident_wgs"] == cap
+    assert p["lds_bytes"] == max(share, base["lds_bytes"])
+    assert p["lds_bytes"] + 1024 <= 163840
+    # nothing else changes
+    for k in ("prefetch", "waves_per_wg", "partition_blocks", "num_partitions", "workgroups",
+              "workspace_bytes", "prefetch_distance", "balanced"):
+        assert p[k] == base[k], k
+
+
+@pytest.mark.parametrize("bad", [dict(max_resident_wgs=-1), dict(max_resident_wgs=65),
+                                 dict(min_context_hint=-5)])
+def test_hint_and_cap_are_validated(native_lib, bad):
+    with pytest.raises(ValueError, match="invalid argument"):
+        nat.plan(good_shape(max_blocks_per_seq=16), hinted(0, **bad))
+    assert call(good_shape(max_blocks_per_seq=16), hinted(0, **bad)) == nat.PA_ERR_INVALID_ARG
+
+
+def test_lds_limit_leaves_room_for_the_compilers_lds(native_lib):
+    """A work-group's dynamic LDS plus what the compiler adds (256 B here,
+    1 KiB allowed) must fit the device's LDS per work-group: a plan whose
+    dynamic LDS alone would just fit is refused."""
+    sh = good_shape(max_blocks_per_seq=64)
+    o = nat.default_options()
+    o.prefetch, o.prefetch_distance, o.waves_per_wg = 4, 2, 4  # 96 KiB of LDS slots + table
+    need = nat.plan(sh, o, device=MI355X)["lds_bytes"]
+    fits = dict(MI355X, lds_bytes_per_cu=163840, lds_bytes_per_workgroup=need + 1024)
+    assert nat.plan(sh, o, device=fits)["lds_bytes"] == need
+    tight = dict(MI355X, lds_bytes_per_cu=163840, lds_bytes_per_workgroup=need + 512)
+    with pytest.raises(ValueError, match="unsupported"):
+        nat.plan(sh, o, device=tight)

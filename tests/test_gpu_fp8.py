@@ -211,18 +211,19 @@ def test_fp8_workload_full_output(name):
     print(f"[fp8 workload] {name}: generating", flush=True)
     x8 = gen.to_fp8(gen.make_inputs(name))
     dev = to_device8(x8)
-    print(f"[fp8 workload] {name}: decode", flush=True)
-    out = ops.paged_attn_decode_fp8(dev["q"], dev["k_cache"], dev["v_cache"],
-                                    dev["block_tables"], dev["context_lens"], x8.scale,
-                                    x8.k_scale, x8.v_scale)
-    torch.cuda.synchronize()
+    hint = int(x8.context_lens.min())
+    print(f"[fp8 workload] {name}: decode (hint {hint})", flush=True)
     dec = lambda **kw: ops.paged_attn_decode_fp8(dev["q"], dev["k_cache"], dev["v_cache"],
                                                  dev["block_tables"], dev["context_lens"],
                                                  x8.scale, x8.k_scale, x8.v_scale, **kw)
-    for pf, dist in ((0, 0), (1, 0), (3, 0), (2, 2)):
-        o2 = dec(prefetch=pf, prefetch_distance=dist)
+    out = dec(min_context_hint=hint)
+    plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], min_context_hint=hint)
+    torch.cuda.synchronize()
+    for pf, dist in ((0, 0), (1, 0), (3, 0), (2, 1), (2, 2)):
+        o2 = dec(prefetch=pf, prefetch_distance=dist, **same_plan(plan))
         torch.cuda.synchronize()
         assert torch.equal(o2.view(torch.int16), out.view(torch.int16)), f"mode {pf}"
+    no_hint = dec().cpu().numpy()
     # the LDS-staged look-ahead may plan fewer waves; on the same plan it
     # matches the register look-ahead bit for bit
     for dist in (1, 2):
@@ -237,7 +238,8 @@ def test_fp8_workload_full_output(name):
     ks, vs = gen.side_by_side(dev["k_cache"], dev["v_cache"])
     bench_out = torch.empty_like(out)
     call = ops.prepare_decode_fp8(dev["q"], ks, vs, dev["block_tables"], dev["context_lens"],
-                                  x8.scale, x8.k_scale, x8.v_scale, bench_out)
+                                  x8.scale, x8.k_scale, x8.v_scale, bench_out,
+                                  min_context_hint=hint)
     call()
     call()
     torch.cuda.synchronize()
@@ -251,6 +253,7 @@ def test_fp8_workload_full_output(name):
                                       x8.scale, x8.k_scale, x8.v_scale)
     e = assert_close(got, ref, name)
     assert_close(got_lds, ref, name + " lds")
+    assert_close(no_hint, ref, name + " without the hint")
     print(f"[fp8 workload] {name}: {e}", flush=True)
 
 

@@ -1,10 +1,11 @@
 """Full-size workloads on the GPU: every output element against the oracle
 (MI355X).
 
-The decode call uses the default options, i.e. the launch configuration the
-bench times; every prefetch mode must give the same bits on the whole output,
-and the whole output (all B x Hq rows) must be within tolerance of the fp64
-oracle's.
+The decode call is the bench's: default options plus the shortest context as
+min_context_hint (the streaming shape where every context fills the table).
+Every prefetch mode on the same plan must give the same bits on the whole
+output, and the whole output (all B x Hq rows) must be within tolerance of
+the fp64 oracle's, as must the plan without the hint.
 """
 import numpy as np
 import pytest
@@ -32,18 +33,20 @@ def test_workload_full_output(name):
     print(f"[workload] {name}: generating", flush=True)
     x = gen.make_inputs(name)
     dev = to_device(x)
-    print(f"[workload] {name}: decode", flush=True)
-    out = ops.paged_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["block_tables"],
-                                dev["context_lens"], x.scale)
-    torch.cuda.synchronize()
-    assert torch.isfinite(out.float()).all()
+    hint = int(x.context_lens.min())
+    print(f"[workload] {name}: decode (hint {hint})", flush=True)
     dec = lambda **kw: ops.paged_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"],
                                              dev["block_tables"], dev["context_lens"],
                                              x.scale, **kw)
+    out = dec(min_context_hint=hint)
+    plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], min_context_hint=hint)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
     for pf, dist in ((0, 0), (1, 0), (2, 0), (3, 0), (2, 2)):
-        o2 = dec(prefetch=pf, prefetch_distance=dist)
+        o2 = dec(prefetch=pf, prefetch_distance=dist, **same_plan(plan))
         torch.cuda.synchronize()
         assert torch.equal(o2.view(torch.int16), out.view(torch.int16)), f"mode {pf}"
+    no_hint = dec().cpu().numpy()
     # the LDS-staged look-ahead may plan fewer waves (its slots share the
     # work-group's LDS); with the same plan it matches the register look-ahead
     for dist in (1, 2):
@@ -59,7 +62,7 @@ def test_workload_full_output(name):
     ks, vs = gen.side_by_side(dev["k_cache"], dev["v_cache"])
     bench_out = torch.empty_like(out)
     call = ops.prepare_decode(dev["q"], ks, vs, dev["block_tables"], dev["context_lens"],
-                              x.scale, bench_out)
+                              x.scale, bench_out, min_context_hint=hint)
     call()
     call()
     torch.cuda.synchronize()
@@ -72,6 +75,7 @@ def test_workload_full_output(name):
                                   x.scale)
     e = assert_close(got, ref, name)
     assert_close(got_lds, ref, name + " lds")
+    assert_close(no_hint, ref, name + " without the hint")
     print(f"[workload] {name}: {e}", flush=True)
 
 
