@@ -199,16 +199,19 @@ typedef struct pa_options {
                                   sequence's context length, when the caller
                                   knows one (0 = none).  It only steers the
                                   plan: with a bound of at least 7/8 of the
-                                  block table's width, a table of at least
-                                  64 blocks and a whole number of (sequence,
-                                  KV head) pairs per CU (1, 2, 3, 4, 6 or 8
-                                  for fp16; 1 or 4 for E4M3), auto waves,
+                                  block table's width, a table of 64..1024
+                                  blocks (256.. for GQA), auto waves,
                                   partitions and residency, and the
                                   look-ahead off or in registers (fp16 one
                                   block ahead, E4M3 two), the plan takes the
-                                  streaming shape: waves per work-group and a
-                                  residency cap sized so that each CU keeps
-                                  about 32 KiB of K/V loads in flight from
+                                  streaming shape where it has one: for a
+                                  whole number of (sequence, KV head) pairs
+                                  per CU (1, 2, 3, 4 or 6 for fp16; 1 or 4
+                                  for E4M3), or an fp16 balanced split with
+                                  at least 256 table blocks per CU.  Its
+                                  waves per
+                                  work-group and residency cap keep about
+                                  32 KiB of K/V loads in flight per CU from
                                   start to end.  A wrong bound changes no
                                   result, only the speed */
     int32_t max_resident_wgs;  /* at most this many decode work-groups per CU

@@ -66,25 +66,31 @@ constexpr int kTwoLoopPartitionBlocks = 32;
 constexpr int kResidentWavesPerCU = 12;
 //  * The streaming shape, for batches whose contexts all fill the table
 //    (pa_options.min_context_hint >= 7/8 of its width) with a whole number u
-//    of units per CU.  A CU streams best with about 32 KiB of K/V loads in
-//    flight: 4 fp16 blocks of one KV head (K and V, 8 KiB each), 8 E4M3
-//    ones.  The shapes above keep 8-24 blocks in flight and over-subscribe
-//    it by 4-6 %.  The streaming shape picks the waves per work-group and a
-//    residency cap from u and from the blocks each wave keeps in flight (1
-//    with the look-ahead off, 2 with the register look-ahead one block
-//    ahead, 3 two blocks ahead), so that every CU holds about that many
-//    from the start to the end of the launch (stream_shape below).
-//    Measured, us (default shape -> streaming shape, look-ahead on):
-//    MHA 32/32, 32 x 2K (llama2_7b-shaped) 159.5 -> 152.6; 8 x 4K 80.2 ->
-//    76.1; 16 x 2K 80.7 -> 76.4; 24 x 2K 120.1 -> 117.2; 48 x 1K 121.8 ->
-//    118.8; 64 x 1K 161.0 -> 158.0; GQA 28/4, 128 x 4K 160.2 -> 158.4;
-//    E4M3 32 x 2K 81.7 -> 78.6.  With the look-ahead off, 32 x 2K: 161.1 ->
-//    149.9.  Other u gained under 2 % or lost: a partial last round leaves
-//    CUs with one work-group and too few loads in flight.  A ragged batch
-//    must not take this shape: its long units then run alone on their CUs
-//    with 1-2 blocks in flight (llama3_8b-shaped, 64 x 512..8K tokens: 181 ->
-//    256 us), hence the hint.
+//    of units per CU and one partition per unit.  A CU streams best with
+//    about 32 KiB of K/V loads in flight: 4 fp16 blocks of one KV head (K
+//    and V, 8 KiB each), 8 E4M3 ones.  The shapes above keep 8-24 blocks in
+//    flight and over-subscribe it by 2-6 %.  The streaming shape picks the
+//    waves per work-group and a residency cap from u and from the blocks
+//    each wave keeps in flight (1 with the look-ahead off, 2 with the
+//    register look-ahead one block ahead, 3 two blocks ahead), so that every
+//    CU holds about that many from the start to the end of the launch
+//    (stream_shape below).  Measured, us (default shape -> streaming shape,
+//    look-ahead on): MHA 32/32, 32 x 2K (llama2_7b-shaped) 159.5 -> 152.8;
+//    8 x 4K 79.9 -> 75.7; 16 x 2K 82.1 -> 79.3; 24 x 2K 120.1 -> 117.2;
+//    32 x 16K 1253 -> 1208; GQA 32/8, 64 x 16K 627 -> 615; GQA 28/4, 128 x
+//    4K 160.2 -> 158.4; GQA 40/8, 128 x 8K 628.6 -> 619.8; E4M3 MHA 32 x 2K
+//    81.7 -> 78.6.  With the look-ahead off, 32 x 2K: 161.1 -> 149.9.  Where
+//    it did not pay it is left out: other u (a partial last round leaves CUs
+//    with one work-group and too few loads in flight; 8 units per CU lost up
+//    to 4 % on GQA batches), GQA tables under kStreamMinBlocksGqa blocks
+//    (their longer prologue and merge: GQA 32/8 32 x 1K 21.5 -> 22.7), and
+//    tables split into partitions.  A ragged batch must not take this
+//    shape: its long units then run alone on their CUs with 1-2 blocks in
+//    flight (llama3_8b-shaped, 64 x 512..8K tokens: 181 -> 256 us), hence
+//    the hint.
 constexpr int kStreamMinBlocks = 64;
+constexpr int kStreamMinBlocksGqa = 256;
+constexpr int kStreamSplitBlocks = 256;
 
 bool valid_device(const pa_device_info* d) {
   return d && d->compute_units >= 1 && d->compute_units <= 65536 &&
@@ -164,7 +170,7 @@ StreamShape stream_shape(int64_t u, bool kv8, int f) {
       case 1: return {4, 0};
       case 2: return {2, 0};
       case 3: return {4, 1};
-      case 4: case 8: return {1, 4};
+      case 4: return {1, 4};
       case 6: return {2, 2};
       default: return {0, 0};
     }
@@ -174,7 +180,7 @@ StreamShape stream_shape(int64_t u, bool kv8, int f) {
       case 1: return {2, 0};
       case 2: return {1, 0};
       case 3: return {2, 1};
-      case 4: case 6: case 8: return {1, 2};
+      case 4: case 6: return {1, 2};
       default: return {0, 0};
     }
   }
@@ -272,11 +278,12 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   // number of units per CU, the look-ahead off or in registers (the
   // measured distances), waves, partitions and residency left to the plan
   const int in_flight = pf == PA_PREFETCH_OFF ? 1 : pf == PA_PREFETCH_REG ? 1 + dist : 0;
-  if (o->min_context_hint > 0 &&
-      (int64_t)o->min_context_hint * 8 >= (int64_t)MB * PA_BLOCK_SIZE * 7 &&
-      MB >= kStreamMinBlocks && !two && in_flight > 0 && o->waves_per_wg == 0 &&
-      o->partition_blocks == 0 && o->max_resident_wgs == 0 && units >= dv.cus &&
-      units % dv.cus == 0) {
+  const bool streaming = o->min_context_hint > 0 &&
+                         (int64_t)o->min_context_hint * 8 >= (int64_t)MB * PA_BLOCK_SIZE * 7 &&
+                         MB >= (g == 1 ? kStreamMinBlocks : kStreamMinBlocksGqa) && !two &&
+                         in_flight > 0 && o->waves_per_wg == 0 && o->partition_blocks == 0 &&
+                         o->max_resident_wgs == 0;
+  if (streaming && units >= dv.cus && units % dv.cus == 0 && MB <= kMaxPartitionBlocks) {
     const StreamShape ss = stream_shape(units / dv.cus, kv8, in_flight);
     if (ss.waves > 0) {
       waves = ss.waves;
@@ -288,6 +295,17 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
       }
     }
   }
+  // Fewer units than CUs, split by the balanced rule into about one
+  // work-group per CU: with at least kStreamSplitBlocks blocks per CU, the
+  // same 4 fp16 blocks in flight (2 waves one block ahead, or 4 without the
+  // look-ahead) beat the 8 waves of the split plans by 0.5-2 % (us, 8 waves
+  // -> 2: GQA 32/8 8 x 32K 164.5 -> 161.6, 16 x 16K 164.9 -> 161.7, 16 x
+  // 8K 83.9 -> 83.4; GQA 5/1 128 x 8K 85.9 -> 84.8); on shorter walks the
+  // 8 waves hide more of the start-up (GQA 32/8 16 x 4K: 45.1 against 45.5).
+  if (streaming && !kv8 && units < dv.cus && o->seq_order == PA_ORDER_AUTO && B >= 2 &&
+      B <= PA_RANK_MAX_SEQS && MB <= kBalancedMaxTable &&
+      (int64_t)MB * units >= (int64_t)kStreamSplitBlocks * dv.cus && in_flight <= 2)
+    waves = in_flight == 1 ? 4 : 2;
   if (waves == 0 && two) waves = 4;
   if (waves == 0) {
     const bool whole = o->partition_blocks == 0 ? units >= dv.cus : o->partition_blocks >= MB;

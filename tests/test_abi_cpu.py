@@ -498,11 +498,10 @@ def hinted(min_ctx, **kw):
     (32, 32, 32, nat.KV_F16, (1, 2)),    # u = 4 (the llama2_7b shape)
     (128, 40, 8, nat.KV_F16, (1, 2)),    # u = 4, GQA 5:1
     (48, 32, 32, nat.KV_F16, (1, 2)),    # u = 6
-    (64, 32, 32, nat.KV_F16, (1, 2)),    # u = 8
     (32, 32, 32, nat.KV_E4M3, (1, 4)),   # u = 4, E4M3
 ])
 def test_streaming_shape_for_uniform_contexts(native_lib, B, Hq, Hkv, kv, want):
-    MB = 128
+    MB = 256
     sh = nat.make_shape(B, Hq, Hkv, MB, 1, kv_dtype=kv)
     p = nat.plan(sh, hinted(MB * 16), device=MI355X)
     assert (p["waves_per_wg"], p["resident_wgs"]) == want
@@ -520,7 +519,8 @@ def test_streaming_shape_for_uniform_contexts(native_lib, B, Hq, Hkv, kv, want):
 
 
 @pytest.mark.parametrize("case", [
-    "no hint", "ragged", "short table", "not a multiple", "u = 5", "u = 16", "e4m3 u = 2",
+    "no hint", "ragged", "short table", "short gqa table", "split table", "not a multiple",
+    "u = 5", "u = 8", "u = 16", "e4m3 u = 2",
     "explicit waves", "l2 touch", "lds ring", "fp16 two blocks ahead", "e4m3 one block ahead",
     "explicit partitions",
     "explicit cap", "two-loop"])
@@ -532,8 +532,14 @@ def test_streaming_shape_needs_every_condition(native_lib, case):
         hint = 128 * 16 * 7 // 8 - 1  # one token under 7/8 of the table
     elif case == "short table":
         MB, hint = 63, 63 * 16
+    elif case == "short gqa table":
+        B, Hq, Hkv, MB, hint = 128, 32, 8, 255, 255 * 16
+    elif case == "split table":
+        MB, hint = 1025, 1025 * 16
     elif case == "not a multiple":
         B = 33
+    elif case == "u = 8":
+        B = 64
     elif case == "u = 5":
         B = 40
     elif case == "u = 16":
@@ -570,7 +576,6 @@ def test_streaming_shape_needs_every_condition(native_lib, case):
     (24, 32, 32, nat.KV_F16, (4, 1)),    # u = 3
     (32, 32, 32, nat.KV_F16, (1, 4)),    # u = 4
     (48, 32, 32, nat.KV_F16, (2, 2)),    # u = 6
-    (64, 32, 32, nat.KV_F16, (1, 4)),    # u = 8
     (8, 32, 32, nat.KV_E4M3, (8, 0)),    # u = 1
     (32, 32, 32, nat.KV_E4M3, (2, 4)),   # u = 4
 ])
@@ -592,6 +597,7 @@ def test_explicit_default_distance_keeps_the_streaming_shape(native_lib, kv, dis
 def test_the_hint_at_exactly_seven_eighths_of_the_table(native_lib):
     sh = nat.make_shape(32, 32, 32, 128, 1)
     assert nat.plan(sh, hinted(128 * 16 * 7 // 8), device=MI355X)["resident_wgs"] == 2
+    assert nat.plan(sh, hinted(128 * 16 * 7 // 8 - 1), device=MI355X)["resident_wgs"] == 0
 
 
 @pytest.mark.parametrize("cap", [1, 2, 3, 4, 5, 8, 16, 64])
@@ -630,3 +636,26 @@ def test_lds_limit_leaves_room_for_the_compilers_lds(native_lib):
     tight = dict(MI355X, lds_bytes_per_cu=163840, lds_bytes_per_workgroup=need + 512)
     with pytest.raises(ValueError, match="unsupported"):
         nat.plan(sh, o, device=tight)
+
+
+# fewer units than CUs, uniform: the balanced split keeps one work-group per
+# CU; from 256 table blocks per CU it takes 2 waves (4 with the look-ahead
+# off) instead of 8
+@pytest.mark.parametrize("B,Hq,Hkv,MB,pf,want", [
+    (4, 32, 32, 512, -1, 2),     # 512 x 128 units = 256 blocks per CU
+    (8, 32, 8, 1024, -1, 2),
+    (128, 5, 1, 512, -1, 2),
+    (4, 32, 32, 512, 0, 4),
+    (16, 32, 8, 256, -1, 8),     # 128 blocks per CU: 8 waves
+    (4, 32, 32, 256, -1, 8),
+    (8, 32, 8, 1024, 1, 8),      # the L2 touch: no streaming shape
+])
+def test_streaming_waves_for_balanced_uniform_batches(native_lib, B, Hq, Hkv, MB, pf, want):
+    sh = nat.make_shape(B, Hq, Hkv, MB, 1)
+    p = nat.plan(sh, hinted(MB * 16, prefetch=pf), device=MI355X)
+    assert p["balanced"] == 1 and p["waves_per_wg"] == want and p["resident_wgs"] == 0
+    q = nat.plan(sh, hinted(0, prefetch=pf), device=MI355X)
+    assert q["balanced"] == 1 and q["waves_per_wg"] == 8
+    e4 = nat.plan(nat.make_shape(B, Hq, Hkv, MB, 1, kv_dtype=nat.KV_E4M3),
+                  hinted(MB * 16, prefetch=pf), device=MI355X)
+    assert e4["waves_per_wg"] == 8

@@ -37,12 +37,11 @@ def cus():
 CASES = [
     (1, 32, 32, 1024, (2, 0)),
     (2, 32, 32, 1024, (1, 0)),
-    (2, 28, 4, 1024, (1, 0)),
+    (2, 28, 4, 4096, (1, 0)),
     (3, 32, 32, 1024, (2, 1)),
     (4, 32, 32, 1024, (1, 2)),
-    (4, 40, 8, 1040, (1, 2)),   # 65 blocks, the last one partial
+    (4, 40, 8, 4112, (1, 2)),   # 257 blocks, the last one partial
     (6, 32, 32, 1024, (1, 2)),
-    (8, 16, 16, 1024, (1, 2)),
 ]
 
 
@@ -116,3 +115,20 @@ def test_streaming_shape_over_an_e4m3_cache():
     assert_close(got, ref, "e4m3 streaming")
     assert np.array_equal(bits(got), bits(dec(**same_plan(plan, max_resident_wgs=0))))
     assert np.array_equal(bits(got), bits(dec(prefetch=0, **same_plan(plan))))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,ctx", [(4, 32, 32, 8192), (128, 5, 1, 8192), (3, 16, 4, 96000)])
+def test_streaming_waves_of_a_balanced_split(B, Hq, Hkv, ctx):
+    """Fewer units than CUs, every context at the table's width: the balanced
+    split on 2-wave work-groups (where the walk per CU is long enough)."""
+    x = gen.make_case(B, Hq, Hkv, [ctx] * B, seed=790 + B, extra_pool_blocks=3, poison=True)
+    dev = to_device(x)
+    plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], min_context_hint=ctx)
+    assert plan["balanced"] == 1
+    if cus() == 256:
+        assert plan["waves_per_wg"] == 2
+    got = run(x, dev, min_context_hint=ctx)
+    assert_close(got, oracle(x), f"balanced streaming {B}x{ctx}")
+    for pf in (0, 1, 3):
+        o = run(x, dev, prefetch=pf, **same_plan(plan))
+        assert np.array_equal(bits(o), bits(got)), f"mode {pf}"
