@@ -397,6 +397,17 @@ def measure_workload(args, name, env, cpu_leg):
     timed_key = (mode, args.prefetch_distance, 0, False)
 
     if args.profile:
+        # Coming out of idle (the host has just built the inputs) the GPU
+        # runs slower for a while; the profilers average every dispatch of a
+        # kernel, so the first mode's would carry that.  Warm up on a kernel
+        # the summaries do not read (a torch sum) for 0.3 s first.
+        warm = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        t_end = time.perf_counter() + 0.3
+        while time.perf_counter() < t_end:
+            for _ in range(20):
+                warm.sum()
+            torch.cuda.synchronize()
+        del warm
         for pf, dist_r, structure in MODE_RUNS:
             if not (fp8 and structure):
                 timed((pf, dist_r, structure, False), args.steps, args.warmup)

@@ -150,19 +150,24 @@ def sweep_timing(jsonl, workload, out_dir, command):
     lines = [f"# Batch x context sweep, timings: {workload}", "", "```", "command:",
              *["    " + c for c in command.split(" ;; ") if c], "```", "",
              "One decode step per point (prepared call, event-timed mean over the steps); "
-             "KV bytes = 2 * Hkv * 128 * 2 B * batch * context.  'on' is the library's "
-             "default look-ahead; parity is the default mode's output on the first and last "
+             "KV bytes = 2 * Hkv * 128 * 2 B * batch * context.  Every context of a point "
+             "is the point's context, which the calls pass as min_context_hint.  'on' is "
+             "the library's default look-ahead and 'off' the look-ahead off, each on its "
+             "own plan; parity is the default mode's output on the first and last "
              "sequence (every head) against the fp64 oracle.  'partitions' is the plan's: "
              "per sequence for a fixed split, the most one sequence may get for a balanced "
-             "one (sized on the device).", "",
-             "| batch | context | KV bytes | split | partitions | us off | us on | GB/s off |"
-             " GB/s on | % of 8 TB/s on | on vs off | parity abs | parity rel |",
-             "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+             "one (sized on the device).  'W / cap' is the default mode's waves per "
+             "work-group and residency cap (- = none).", "",
+             "| batch | context | KV bytes | split | partitions | W / cap | us off | us on |"
+             " GB/s off | GB/s on | % of 8 TB/s on | on vs off | parity abs | parity rel |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for p in points:
         off_gbps = p["kv_bytes"] / p["us_off"] / 1e3
         split = "one" if p["partitions"] == 1 else ("balanced" if p.get("balanced") else "fixed")
+        wc = f"{p.get('waves_per_wg', '?')} / {p.get('resident_wgs') or '-'}"
         lines.append(f"| {p['batch']} | {p['context']} | {p['kv_bytes']} | {split} | "
-                     f"{p['partitions']} | {p['us_off']:.2f} | {p['us_on']:.2f} | {off_gbps:.0f} | "
+                     f"{p['partitions']} | {wc} | {p['us_off']:.2f} | {p['us_on']:.2f} | "
+                     f"{off_gbps:.0f} | "
                      f"{p['GBps_on']:.0f} | {p['pct_hbm_peak_on']:.1f} | "
                      f"{p['speedup_on_vs_off']:.3f} | {p['parity_abs']:.2e} | "
                      f"{p['parity_rel']:.2e} |")
@@ -257,6 +262,36 @@ def request_path_table(dirs, tag, head, out_dir, kernel_us):
     return path
 
 
+# (mode, look-ahead distance, structure) of each profiled mode, as bench.py
+# runs them (0 = the library's default distance)
+MODE_OPTIONS = {0: (0, 1, 0), 1: (1, 1, 0), 2: (2, 1, 0), 3: (3, 1, 0), 4: (2, 2, 0),
+                5: (4, 1, 0), 6: (4, 2, 0), 10: (0, 1, 1), 11: (1, 1, 1), 12: (2, 1, 1),
+                13: (3, 1, 1)}
+
+
+def mode_plans(w, kv8, hint):
+    """Each mode's own plan for workload w on the MI355X figures, with the
+    caller's context hint as bench.py passes it: 'waves W, cap R, P parts'."""
+    from paged_kv_cache_226_amd import _native as nat
+    from paged_kv_cache_226_amd import inputs as gen
+    ctx = gen.workload_context_lens(w)
+    MB = w.max_blocks_per_seq or max(-(-int(c) // 16) for c in ctx)
+    sh = nat.make_shape(w.num_seqs, w.num_q_heads, w.num_kv_heads, MB, w.pool_blocks or 1,
+                        kv_dtype=nat.KV_E4M3 if kv8 else nat.KV_F16)
+    dev = dict(compute_units=256, lds_bytes_per_cu=163840, lds_bytes_per_workgroup=163840)
+    out = {}
+    for m, (pf, dist, structure) in MODE_OPTIONS.items():
+        if kv8 and structure:
+            continue
+        o = nat.default_options()
+        o.prefetch, o.prefetch_distance, o.structure = pf, dist, structure
+        o.min_context_hint = hint
+        p = nat.plan(sh, o, device=dev)
+        out[m] = (f"{p['waves_per_wg']} waves, cap {p['resident_wgs'] or '-'}, "
+                  f"{p['num_partitions']} partition(s)" + (" balanced" if p["balanced"] else ""))
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
@@ -305,6 +340,10 @@ def main(argv=None):
     if a.source_hash:
         head.append(f"kernel_source_hash: {a.source_hash} (bench.py kernel_source_hash of the "
                     "profiled sources)")
+    hint = max(int(min(ctx)), 0)
+    head.append(f"plans (each mode on its own plan, min_context_hint {hint} as bench.py "
+                "passes it; 256 CUs):")
+    head.extend(f"    {MODE_NAMES[m]}: {desc}" for m, desc in mode_plans(w, KV8, hint).items())
 
     if a.kernel_trace:
         lines = ["# pa_decode kernel trace: " + tag, "", "```", *head, "```", "",

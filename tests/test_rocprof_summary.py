@@ -99,10 +99,25 @@ def test_sweep_timing_table(tmp_path):
     import json
     pts = [{"sweep": "w", "batch": 8, "context": 1024, "kv_bytes": 8000000, "partitions": 4,
             "us_off": 10.0, "us_on": 8.0, "GBps_on": 1000.0, "pct_hbm_peak_on": 12.5,
-            "speedup_on_vs_off": 1.25, "parity_abs": 1e-5, "parity_rel": 2e-4}]
+            "speedup_on_vs_off": 1.25, "parity_abs": 1e-5, "parity_rel": 2e-4,
+            "waves_per_wg": 2, "resident_wgs": 0}]
     (tmp_path / "s.jsonl").write_text("noise\n" + "".join(json.dumps(p) + "\n" for p in pts))
     path = rs.sweep_timing(str(tmp_path / "s.jsonl"), "w", str(tmp_path), "cmd a ;; cmd b")
     text = open(path).read()
     assert "    cmd a\n    cmd b\n" in text
     row = [l for l in text.splitlines() if l.startswith("| 8 ")][0].split("|")
-    assert [c.strip() for c in row[4:11]] == ["fixed", "4", "10.00", "8.00", "800", "1000", "12.5"]
+    assert [c.strip() for c in row[4:12]] == ["fixed", "4", "2 / -", "10.00", "8.00", "800",
+                                              "1000", "12.5"]
+
+
+def test_mode_plans_follow_the_library(native_lib):
+    """The per-mode plans the summary header lists are the library's, with the
+    shortest context as the hint: llama2_7b's register look-ahead on 1-wave
+    work-groups capped at 2 per CU, the look-ahead off at 4 per CU."""
+    from paged_kv_cache_226_amd import inputs as gen
+    plans = rs.mode_plans(gen.WORKLOADS["llama2_7b"], False, 2048)
+    assert plans[2] == "1 waves, cap 2, 1 partition(s)"
+    assert plans[0] == "1 waves, cap 4, 1 partition(s)"
+    assert plans[1].startswith("4 waves, cap -")
+    assert 10 in plans and 4 in plans
+    assert 10 not in rs.mode_plans(gen.WORKLOADS["llama2_7b"], True, 2048)
