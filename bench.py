@@ -68,8 +68,9 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def profile_tag(workload: str, kv_dtype: str) -> str:
-    return workload if kv_dtype == "fp16" else f"{workload}_{kv_dtype}"
+def profile_tag(workload: str, kv_dtype: str, hint: bool = True) -> str:
+    return ((workload if kv_dtype == "fp16" else f"{workload}_{kv_dtype}") +
+            ("" if hint else "_nohint"))
 
 
 def _profile_figures(workload: str):
@@ -454,7 +455,7 @@ def measure_workload(args, name, env, cpu_leg):
     # only kernel of a step, and its average duration is the timed region over
     # the steps; otherwise the step also holds the reduce kernel and the
     # figure covers both.
-    tag = profile_tag(name, args.kv_dtype)
+    tag = profile_tag(name, args.kv_dtype, not args.no_context_hint)
     decode_only = plan["num_partitions"] == 1
     achieved = kv_bytes / us / 1e3
     kernel_us_rocprof = read_kernel_us(tag, mode_label)

@@ -296,6 +296,9 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
     ap.add_argument("--kv-dtype", choices=("fp16", "fp8"), default="fp16")
+    ap.add_argument("--no-context-hint", action="store_true",
+                    help="the profiled runs planned without min_context_hint (bench.py "
+                         "--no-context-hint): summaries are tagged _nohint")
     ap.add_argument("--kernel-trace")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
@@ -328,7 +331,7 @@ def main(argv=None):
     if a.sweep_timing:
         print(sweep_timing(a.sweep_timing, a.workload, a.out_dir, a.command))
         return 0
-    tag = a.workload + ("_fp8" if KV8 else "")
+    tag = a.workload + ("_fp8" if KV8 else "") + ("_nohint" if a.no_context_hint else "")
     w = gen.WORKLOADS[a.workload]
     ctx = gen.workload_context_lens(w)
     kv = acc.step_kv_bytes(w.num_kv_heads, 128, ctx, elem_bytes=1 if KV8 else 2)
@@ -340,7 +343,7 @@ def main(argv=None):
     if a.source_hash:
         head.append(f"kernel_source_hash: {a.source_hash} (bench.py kernel_source_hash of the "
                     "profiled sources)")
-    hint = max(int(min(ctx)), 0)
+    hint = 0 if a.no_context_hint else max(int(min(ctx)), 0)
     head.append(f"plans (each mode on its own plan, min_context_hint {hint} as bench.py "
                 "passes it; 256 CUs):")
     head.extend(f"    {MODE_NAMES[m]}: {desc}" for m, desc in mode_plans(w, KV8, hint).items())
