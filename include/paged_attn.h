@@ -369,9 +369,11 @@ int paged_attn_pack_k(const void *k_token_major, void *k_cache, int64_t num_bloc
 
 /* Streaming-read ceiling: reads `bytes` (a multiple of 16, 16-byte aligned)
    from device buffer `buf` once, in 8 KiB chunks per wavefront of the same
-   non-temporal 128-bit loads the decode kernel uses, and writes one 16-byte
-   XOR per work-group into `sink` (device, at least
-   paged_attn_stream_read_sink_bytes(bytes) bytes). */
+   non-temporal 128-bit loads the decode kernel uses, with one 4-wave
+   work-group per CU of the current device (about 32 KiB of loads in flight
+   per CU, the rate-best count), and writes one 16-byte XOR per work-group
+   into `sink` (device, at least paged_attn_stream_read_sink_bytes(bytes)
+   bytes, 16 per CU). */
 int paged_attn_stream_read(const void *buf, size_t bytes, void *sink,
                            void *stream);
 size_t paged_attn_stream_read_sink_bytes(size_t bytes);

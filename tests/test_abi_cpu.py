@@ -217,6 +217,11 @@ def test_explicit_partition_size_and_workspace_size(native_lib):
     assert native_lib.paged_attn_workspace_size(ctypes.byref(bad), None) == 0
 
 
+def test_stream_read_sink_is_one_word_per_cu(native_lib):
+    assert native_lib.paged_attn_stream_read_sink_bytes(1 << 30) == \
+        16 * nat.device_info()["compute_units"]
+
+
 def test_stream_read_validation(native_lib):
     f = native_lib.paged_attn_stream_read
     assert f(None, 1024, ctypes.c_void_p(FAKE), None) == nat.PA_ERR_INVALID_ARG
