@@ -161,6 +161,10 @@ def parse():
                     help="plan without the shortest context as min_context_hint")
     ap.add_argument("--profile", action="store_true",
                     help="short run for rocprofv3: every prefetch mode, no CPU leg")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-work-group timeline of the headline workload's timed plan "
+                         "(debug kernel variant): one JSON line of per-XCD and per-CU "
+                         "finish times")
     ap.add_argument("--sweep", action="store_true",
                     help="batch x context sweep of one workload's head shape: one JSON "
                          "line per point (look-ahead off vs on, sampled parity)")
@@ -278,6 +282,100 @@ def run_sweep(args):
             torch.cuda.empty_cache()
     if args.profile:
         calibrate_counters(torch, ops)
+
+
+def run_timeline(args):
+    """The timed plan of --workload once more with the debug timeline (the
+    checked kernel variant): when each work-group started and ended, on which
+    CU and XCD.  Prints one JSON line: the launch span, the kernel's own
+    event-timed duration, and per XCD the work-groups, the mean work-group
+    duration and when its last work-group ended."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_226_amd import accounting as acc
+    from paged_kv_cache_226_amd import inputs as gen
+    from paged_kv_cache_226_amd import ops
+
+    w = gen.WORKLOADS[args.workload]
+    x = gen.make_inputs(w)
+    fp8 = args.kv_dtype == "fp8"
+    d = {k: torch.from_numpy(getattr(x, k)).cuda() for k in ("q", "block_tables", "context_lens")}
+    if fp8:
+        x8 = gen.to_fp8(x)
+        d["k_cache"] = torch.from_numpy(gen.pack_k_fp8(x8.k8)).cuda()
+        d["v_cache"] = torch.from_numpy(x8.v8).cuda()
+    else:
+        d["k_cache"] = torch.from_numpy(gen.pack_k(x.k_cache)).cuda()
+        d["v_cache"] = torch.from_numpy(x.v_cache).cuda()
+    d["k_cache"], d["v_cache"] = gen.side_by_side(d["k_cache"], d["v_cache"])
+    hint = 0 if args.no_context_hint else max(int(x.context_lens.min()), 0)
+    kw = dict(prefetch=args.prefetch, prefetch_distance=args.prefetch_distance,
+              min_context_hint=hint)
+    plan = ops.plan(d["q"], d["k_cache"], d["block_tables"], **kw)
+    tl = torch.zeros(plan["workgroups"], 4, dtype=torch.int64, device="cuda")
+    out = torch.empty_like(d["q"])
+    extra = (x8.k_scale, x8.v_scale) if fp8 else ()
+    prep = ops.prepare_decode_fp8 if fp8 else ops.prepare_decode
+    plain = prep(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                 x.scale, *extra, out, **kw)
+    traced = prep(d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
+                  x.scale, *extra, out, debug_timeline=tl, **kw)
+    stream = torch.cuda.current_stream()
+
+    def event_us(f, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            f()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    t_end = time.perf_counter() + 0.3  # out of idle first
+    while time.perf_counter() < t_end:
+        event_us(plain, 20)
+    plain_us = event_us(plain, 50)
+    traced_us = event_us(traced, 20)
+    spans = []
+    keep = None
+    for _ in range(5):  # the run whose span is the median is reported
+        traced()
+        torch.cuda.synchronize()
+        t = tl.cpu().numpy().copy()
+        spans.append(((t[:, 1].max() - t[:, 0].min()) / 100.0, t))
+    spans.sort(key=lambda r: r[0])
+    span_us, t = spans[len(spans) // 2]
+    t0 = t[:, 0].min()
+    start = (t[:, 0] - t0) / 100.0
+    end = (t[:, 1] - t0) / 100.0
+    hw, xcc = t[:, 2].astype(np.int64), (t[:, 3].astype(np.int64) & 0xF)
+    cu = [(int(a), (int(h) >> 13) & 7, (int(h) >> 12) & 1, (int(h) >> 8) & 0xF)
+          for a, h in zip(xcc, hw)]
+    last = {}
+    for k, e in zip(cu, end):
+        last[k] = max(last.get(k, 0.0), float(e))
+    cu_ends = np.array(sorted(last.values()))
+    kv_bytes = acc.step_kv_bytes(w.num_kv_heads, 128, x.context_lens, elem_bytes=1 if fp8 else 2)
+    wg = np.arange(len(xcc))
+    per_xcd = []
+    for xi in sorted(set(xcc.tolist())):
+        m = xcc == xi
+        per_xcd.append({"xcd": int(xi), "workgroups": int(m.sum()),
+                        "mean_wg_us": round(float((end[m] - start[m]).mean()), 2),
+                        "last_end_us": round(float(end[m].max()), 2),
+                        "wg_index_mod_8": sorted(set((wg[m] % 8).tolist()))})
+    busy_at = lambda f: float((cu_ends >= f * span_us).mean())
+    print(json.dumps({
+        "timeline": args.workload, "kv_dtype": args.kv_dtype, "min_context_hint": hint,
+        "waves_per_wg": plan["waves_per_wg"], "resident_wgs": plan["resident_wgs"],
+        "workgroups": plan["workgroups"], "cus_seen": len(last),
+        "kernel_us_plain": round(plain_us, 2), "kernel_us_traced": round(traced_us, 2),
+        "span_us": round(float(span_us), 2), "kv_bytes": kv_bytes,
+        "cu_last_end_us": {"min": round(float(cu_ends.min()), 2),
+                           "median": round(float(np.median(cu_ends)), 2),
+                           "max": round(float(cu_ends.max()), 2)},
+        "cus_busy_at_80_90_95_pct_of_span": [round(busy_at(f), 3) for f in (0.8, 0.9, 0.95)],
+        "per_xcd": per_xcd}), flush=True)
 
 
 def mode_name_of(nat, pf: int, dist: int, structure: int = 0) -> str:
@@ -584,6 +682,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.sweep:
         run_sweep(args)
+        return
+    if args.timeline:
+        run_timeline(args)
         return
     stream = torch.cuda.current_stream()
     env = dict(torch=torch, ops=ops, nat=nat, acc=acc, gen=gen, dev=dev, stream=stream)

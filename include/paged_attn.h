@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 6
+#define PA_ABI_VERSION 7
 #define PA_HEAD_DIM 128
 #define PA_BLOCK_SIZE 16
 #define PA_G_MAX 16      /* query heads per KV head */
@@ -221,7 +221,8 @@ typedef struct pa_options {
                                   NULL when the plan has one partition */
     size_t workspace_bytes;
     /* Debug outputs (all NULL in normal use; any non-NULL selects the
-       checked kernel variant, which computes bitwise the same result):
+       checked kernel variant, which computes bitwise the same result; the
+       fourth, debug_timeline, follows after them):
        debug_gather_k  fp16 [B][Hkv][max_blocks_per_seq*16][128]: the K rows
                        each wavefront actually loaded for the compute step;
        debug_trace     int32 [B][Hkv][max_blocks_per_seq][2]: per block, the
@@ -233,6 +234,15 @@ typedef struct pa_options {
     void *debug_gather_k;
     int32_t *debug_trace;
     int32_t *debug_error_word;
+    int64_t *debug_timeline;  /* int64 [workgroups][4] (pa_plan_info.workgroups
+                                 of the decode kernel): per work-group, in
+                                 grid order (x fastest), its start and end on
+                                 the GPU's constant 100 MHz clock
+                                 (s_memrealtime) and the HW_ID and XCC_ID
+                                 registers of the CU it ran on.  Work-groups
+                                 with nothing to do still record both times.
+                                 A debug output like the three above: the
+                                 checked kernel variant runs */
 } pa_options;
 
 /* The plan a call would use, for logging and tests. */

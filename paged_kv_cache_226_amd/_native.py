@@ -43,7 +43,7 @@ class PaOptions(ctypes.Structure):
                 ("min_context_hint", ctypes.c_int32), ("max_resident_wgs", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("debug_gather_k", ctypes.c_void_p), ("debug_trace", ctypes.c_void_p),
-                ("debug_error_word", ctypes.c_void_p)]
+                ("debug_error_word", ctypes.c_void_p), ("debug_timeline", ctypes.c_void_p)]
 
 
 class PaPlanInfo(ctypes.Structure):
@@ -63,7 +63,7 @@ class PaDeviceInfo(ctypes.Structure):
 _lib = None
 
 # the PA_ABI_VERSION whose struct layouts the classes above mirror
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class NativeLibraryMissing(RuntimeError):

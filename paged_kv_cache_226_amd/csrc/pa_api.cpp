@@ -526,7 +526,8 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   }
   if ((o->debug_gather_k && !aligned16(o->debug_gather_k)) ||
       (o->debug_trace && (reinterpret_cast<uintptr_t>(o->debug_trace) & 3u)) ||
-      (o->debug_error_word && (reinterpret_cast<uintptr_t>(o->debug_error_word) & 3u)))
+      (o->debug_error_word && (reinterpret_cast<uintptr_t>(o->debug_error_word) & 3u)) ||
+      (o->debug_timeline && (reinterpret_cast<uintptr_t>(o->debug_timeline) & 7u)))
     return PA_ERR_INVALID_ARG;
 
   const int g = sh->num_q_heads / sh->num_kv_heads;
@@ -541,6 +542,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.dbg_k = static_cast<uint16_t*>(o->debug_gather_k);
   a.dbg_trace = o->debug_trace;
   a.dbg_err = o->debug_error_word;
+  a.dbg_timeline = o->debug_timeline;
   a.sink = nullptr;
   a.sink_enable = 0;
   a.rank_seqs = pl.order == PA_ORDER_LONGEST_FIRST ? 1 : 0;
@@ -564,7 +566,8 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.pb_max = pl.pb_max;
   if (pl.bal) a.k_uniform = pl.nslot / sh->num_seqs < pl.P ? pl.nslot / sh->num_seqs : pl.P;
   a.pf_dist = pl.dist;
-  const bool dbg = o->debug_gather_k || o->debug_trace || o->debug_error_word;
+  const bool dbg =
+      o->debug_gather_k || o->debug_trace || o->debug_error_word || o->debug_timeline;
   if (pl.two && dbg) return PA_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
 

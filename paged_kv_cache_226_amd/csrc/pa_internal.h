@@ -21,6 +21,7 @@ struct DecodeArgs {
   uint16_t* dbg_k;       // see pa_options.debug_gather_k
   int32_t* dbg_trace;    // see pa_options.debug_trace
   int32_t* dbg_err;      // see pa_options.debug_error_word
+  int64_t* dbg_timeline; // see pa_options.debug_timeline
   int32_t* sink;         // never written while sink_enable == 0
   float scale_log2;      // scale * log2(e) (times the K scale for E4M3 caches)
   float v_scale;         // 1, or the V scale of an E4M3 cache

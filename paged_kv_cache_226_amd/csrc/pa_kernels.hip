@@ -1056,6 +1056,31 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
   int32_t* bt_s = reinterpret_cast<int32_t*>(smem_raw);
   float* merge_s = reinterpret_cast<float*>(smem_raw + a.lds_bt_bytes);
 
+  // Debug timeline: the work-group's start and end on the constant 100 MHz
+  // clock, and the HW_ID and XCC_ID registers of its CU (full 32 bits).
+  int64_t* tl = nullptr;
+  if constexpr (DBG) {
+    if (a.dbg_timeline) {
+      const int64_t wg =
+          blockIdx.x + (int64_t)gridDim.x * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+      tl = a.dbg_timeline + wg * 4;
+      if (threadIdx.x == 0) {
+        tl[0] = (int64_t)__builtin_amdgcn_s_memrealtime();
+        tl[2] = (int64_t)(uint32_t)__builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID
+        tl[3] = (int64_t)(uint32_t)__builtin_amdgcn_s_getreg((31 << 11) | 20);  // XCC_ID
+      }
+    }
+  }
+  // every return below is taken by the whole work-group
+  auto stamp_end = [&]() {
+    if constexpr (DBG) {
+      if (tl) {
+        __syncthreads();
+        if (threadIdx.x == 0) tl[1] = (int64_t)__builtin_amdgcn_s_memrealtime();
+      }
+    }
+  };
+
   // Partition index slowest: every sequence's first partition is dispatched
   // before any second one, so the large work-groups of a ragged batch start
   // first and the short tail partitions fill in behind them.
@@ -1068,7 +1093,10 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
   int b, part = p, np_seq = a.P, pb = a.PB, ctx;
   if (a.balanced) {
     const Slot sl = balanced_slot(a, blockIdx.y, tab_tokens);
-    if (sl.b < 0) return;  // a grid row past the last partition
+    if (sl.b < 0) {  // a grid row past the last partition
+      stamp_end();
+      return;
+    }
     b = sl.b;
     part = sl.p;
     np_seq = sl.np;
@@ -1098,6 +1126,7 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
         a.out[((int64_t)b * a.Hq + kvh * G + h) * kD + d] = 0;
       }
     }
+    stamp_end();
     return;
   }
 
@@ -1124,6 +1153,7 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
       a.ws_o[pr * kD + d] = O;
     }
   }
+  stamp_end();
 }
 
 // ---------------------------------------------------------------------------

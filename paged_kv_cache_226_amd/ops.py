@@ -74,6 +74,15 @@ def check_debug_shapes(B: int, Hkv: int, MB: int, debug_gather_k=None, debug_tra
         raise ValueError("debug_error_word must hold at least one int32")
 
 
+def check_debug_timeline(debug_timeline, workgroups: int):
+    """The timeline holds one int64 row of 4 per decode work-group of the plan."""
+    if debug_timeline is None:
+        return
+    if debug_timeline.dtype != torch.int64 or tuple(debug_timeline.shape) != (workgroups, 4):
+        raise ValueError(f"debug_timeline must be int64 [{workgroups}, 4] (the plan's "
+                         f"work-groups), got {debug_timeline.dtype} {list(debug_timeline.shape)}")
+
+
 def shape_of(q: torch.Tensor, k_cache: torch.Tensor, block_tables: torch.Tensor,
              v_cache: Optional[torch.Tensor] = None) -> nat.PaShape:
     """pa_shape of these tensors; K and V may be views into a larger pool
@@ -99,7 +108,8 @@ def options(prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0
             debug_gather_k: Optional[torch.Tensor] = None,
             debug_trace: Optional[torch.Tensor] = None,
             debug_error_word: Optional[torch.Tensor] = None, *,
-            min_context_hint: int = 0, max_resident_wgs: int = 0) -> nat.PaOptions:
+            min_context_hint: int = 0, max_resident_wgs: int = 0,
+            debug_timeline: Optional[torch.Tensor] = None) -> nat.PaOptions:
     """pa_options for these settings (any debug tensor selects the checked
     kernel variant).  min_context_hint: a lower bound on every context length
     (tokens) that the caller knows, 0 = none; it only steers the auto plan."""
@@ -121,6 +131,9 @@ def options(prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0
     if debug_error_word is not None:
         _check(debug_error_word, "debug_error_word", torch.int32, 1)
         o.debug_error_word = debug_error_word.data_ptr()
+    if debug_timeline is not None:
+        _check(debug_timeline, "debug_timeline", torch.int64, 2)
+        o.debug_timeline = debug_timeline.data_ptr()
     return o
 
 
@@ -173,7 +186,8 @@ class DecodeCall:
                  k_scale, v_scale, out, prefetch, partition_blocks, waves_per_wg,
                  prefetch_distance, seq_order, structure, workspace, debug_gather_k,
                  debug_trace, debug_error_word, stream, noalloc: bool = False,
-                 min_context_hint: int = 0, max_resident_wgs: int = 0):
+                 min_context_hint: int = 0, max_resident_wgs: int = 0,
+                 debug_timeline: Optional[torch.Tensor] = None):
         if noalloc and (fp8 or workspace is not None):
             raise ValueError("the no-allocation call takes an fp16 cache and no workspace")
         self.name = ("paged_attn_decode_noalloc" if noalloc else
@@ -197,7 +211,7 @@ class DecodeCall:
         _same_device(self._index, k_cache=k_cache, v_cache=v_cache, block_tables=block_tables,
                      context_lens=context_lens, out=out, workspace=workspace,
                      debug_gather_k=debug_gather_k, debug_trace=debug_trace,
-                     debug_error_word=debug_error_word)
+                     debug_error_word=debug_error_word, debug_timeline=debug_timeline)
         if scale is None:
             scale = D ** -0.5
         if out is None:
@@ -210,7 +224,9 @@ class DecodeCall:
         self._opts = options(prefetch, partition_blocks, waves_per_wg, prefetch_distance,
                              seq_order, structure, debug_gather_k, debug_trace,
                              debug_error_word, min_context_hint=min_context_hint,
-                             max_resident_wgs=max_resident_wgs)
+                             max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline)
+        if debug_timeline is not None:
+            check_debug_timeline(debug_timeline, nat.plan(self._shape, self._opts)["workgroups"])
         L = nat.lib()
         need = int(L.paged_attn_workspace_size(ctypes.byref(self._shape),
                                                ctypes.byref(self._opts)))
@@ -228,7 +244,7 @@ class DecodeCall:
         self.out, self.workspace = out, workspace
         # the tensors whose storage the call reads or writes stay alive with it
         self._keep = (q, k_cache, v_cache, block_tables, context_lens, debug_gather_k,
-                      debug_trace, debug_error_word)
+                      debug_trace, debug_error_word, debug_timeline)
         ptrs = [ctypes.c_void_p(t.data_ptr()) for t in (q, k_cache, v_cache, block_tables,
                                                           context_lens)]
         st = _stream_handle(stream, q.device)
@@ -263,13 +279,14 @@ def prepare_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                    debug_trace: Optional[torch.Tensor] = None,
                    debug_error_word: Optional[torch.Tensor] = None,
                    stream: Optional[torch.cuda.Stream] = None, min_context_hint: int = 0,
-                   max_resident_wgs: int = 0) -> DecodeCall:
+                   max_resident_wgs: int = 0,
+                   debug_timeline: Optional[torch.Tensor] = None) -> DecodeCall:
     """paged_attn_decode prepared for repeated calls on the same tensors."""
     return DecodeCall(False, q, k_cache, v_cache, block_tables, context_lens, scale, 1.0, 1.0,
                       out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
                       seq_order, structure, workspace, debug_gather_k, debug_trace,
                       debug_error_word, stream, min_context_hint=min_context_hint,
-                      max_resident_wgs=max_resident_wgs)
+                      max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline)
 
 
 def prepare_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -281,14 +298,15 @@ def prepare_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                            debug_trace: Optional[torch.Tensor] = None,
                            debug_error_word: Optional[torch.Tensor] = None,
                            stream: Optional[torch.cuda.Stream] = None,
-                           min_context_hint: int = 0, max_resident_wgs: int = 0) -> DecodeCall:
+                           min_context_hint: int = 0, max_resident_wgs: int = 0,
+                           debug_timeline: Optional[torch.Tensor] = None) -> DecodeCall:
     """paged_attn_decode_noalloc prepared for repeated calls; pass `out` to
     keep the calls free of allocation."""
     return DecodeCall(False, q, k_cache, v_cache, block_tables, context_lens, scale, 1.0, 1.0,
                       out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
                       seq_order, structure, None, debug_gather_k, debug_trace,
                       debug_error_word, stream, noalloc=True, min_context_hint=min_context_hint,
-                      max_resident_wgs=max_resident_wgs)
+                      max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline)
 
 
 def paged_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -313,7 +331,8 @@ def prepare_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                        debug_trace: Optional[torch.Tensor] = None,
                        debug_error_word: Optional[torch.Tensor] = None,
                        stream: Optional[torch.cuda.Stream] = None, min_context_hint: int = 0,
-                       max_resident_wgs: int = 0) -> DecodeCall:
+                       max_resident_wgs: int = 0,
+                       debug_timeline: Optional[torch.Tensor] = None) -> DecodeCall:
     """paged_attn_decode_fp8 prepared for repeated calls on the same tensors."""
     if k_cache.dtype == torch.float8_e4m3fn:
         k_cache = k_cache.view(torch.uint8)
@@ -323,7 +342,7 @@ def prepare_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                       v_scale, out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
                       seq_order, structure, workspace, debug_gather_k, debug_trace,
                       debug_error_word, stream, min_context_hint=min_context_hint,
-                      max_resident_wgs=max_resident_wgs)
+                      max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline)
 
 
 def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -336,7 +355,8 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       debug_trace: Optional[torch.Tensor] = None,
                       debug_error_word: Optional[torch.Tensor] = None,
                       stream: Optional[torch.cuda.Stream] = None, min_context_hint: int = 0,
-                      max_resident_wgs: int = 0) -> torch.Tensor:
+                      max_resident_wgs: int = 0,
+                      debug_timeline: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One decode step of paged attention; returns out (fp16 [B, Hq, 128]).
 
     q [B, Hq, 128] fp16; k_cache [NB, Hkv, 16, 16, 8] fp16 (dim group, token, 8
@@ -350,7 +370,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                           debug_gather_k=debug_gather_k, debug_trace=debug_trace,
                           debug_error_word=debug_error_word, stream=stream,
                           min_context_hint=min_context_hint,
-                          max_resident_wgs=max_resident_wgs)()
+                          max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline)()
 
 
 def paged_attn_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -365,7 +385,8 @@ def paged_attn_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                           debug_trace: Optional[torch.Tensor] = None,
                           debug_error_word: Optional[torch.Tensor] = None,
                           stream: Optional[torch.cuda.Stream] = None,
-                          min_context_hint: int = 0, max_resident_wgs: int = 0) -> torch.Tensor:
+                          min_context_hint: int = 0, max_resident_wgs: int = 0,
+                          debug_timeline: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Decode over an OCP E4M3 cache (uint8 or float8_e4m3fn); a cached value
     is decode(byte) * k_scale (K) or * v_scale (V).
 
@@ -381,7 +402,7 @@ def paged_attn_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                               debug_gather_k=debug_gather_k, debug_trace=debug_trace,
                               debug_error_word=debug_error_word, stream=stream,
                               min_context_hint=min_context_hint,
-                              max_resident_wgs=max_resident_wgs)()
+                              max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline)()
 
 
 def pack_k(k_token_major: torch.Tensor, out: Optional[torch.Tensor] = None,

@@ -177,6 +177,42 @@ def sweep_timing(jsonl, workload, out_dir, command):
     return path
 
 
+def timeline_table(jsonl, workload, kv_dtype, out_dir, command):
+    """Per-XCD table of a `bench.py --timeline` run."""
+    r = [json.loads(l) for l in open(jsonl) if l.startswith('{"timeline"')][-1]
+    tag = workload + ("_fp8" if kv_dtype == "fp8" else "") + \
+        ("" if r["min_context_hint"] else "_nohint")
+    c = r["cu_last_end_us"]
+    lines = [f"# pa_decode per-work-group timeline: {tag}", "", "```", "command:",
+             *["    " + x for x in command.split(" ;; ") if x], "```", "",
+             "The timed plan run once more in the checked kernel variant with the debug "
+             "timeline: each work-group's start and end (s_memrealtime, 100 MHz) and the "
+             "HW_ID / XCC_ID of its CU.  Times are from the launch's first start; the run "
+             "whose span is the median of five is shown.", "",
+             f"- plan: {r['waves_per_wg']} waves per work-group, residency cap "
+             f"{r['resident_wgs'] or '-'}, {r['workgroups']} work-groups, "
+             f"min_context_hint {r['min_context_hint']}",
+             f"- kernel (event-timed mean): {r['kernel_us_plain']} us plain, "
+             f"{r['kernel_us_traced']} us with the timeline; span of the shown run: "
+             f"{r['span_us']} us",
+             f"- CUs seen: {r['cus_seen']}; each CU's last work-group ends between "
+             f"{c['min']} and {c['max']} us (median {c['median']})",
+             "- share of CUs still busy at 80 / 90 / 95 % of the span: " +
+             " / ".join(f"{100 * v:.0f} %" for v in r["cus_busy_at_80_90_95_pct_of_span"]),
+             f"- KV bytes {r['kv_bytes']}: {r['kv_bytes'] / r['span_us'] / 1e3:.0f} GB/s over "
+             "the span", "",
+             "| XCD | work-groups | work-group index mod 8 | mean work-group us | last end us |",
+             "|---|---|---|---|---|"]
+    for x in r["per_xcd"]:
+        lines.append(f"| {x['xcd']} | {x['workgroups']} | "
+                     f"{','.join(str(v) for v in x['wg_index_mod_8'])} | {x['mean_wg_us']} | "
+                     f"{x['last_end_us']} |")
+    path = os.path.join(out_dir, f"pa_decode_{tag}_timeline.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return path
+
+
 # Derived figures of the request-path passes, per decode launch.  The SQ
 # clock count GRBM_GUI_ACTIVE is summed over the 8 XCDs; per-CU figures
 # divide by the 256 CUs (one TA and one TCP each).
@@ -312,6 +348,8 @@ def main(argv=None):
                          "means, pa_decode_<tag>_request_path.md")
     ap.add_argument("--sweep-timing", help="JSON lines of `bench.py --sweep`: writes the "
                                            "per-point timing table")
+    ap.add_argument("--timeline", help="JSON line of `bench.py --timeline`: writes "
+                                       "pa_decode_<tag>_timeline.md")
     ap.add_argument("--command", default="", help="the command lines that produced the inputs")
     ap.add_argument("--source-hash", default="")
     ap.add_argument("--out-dir", default="profiles")
@@ -330,6 +368,9 @@ def main(argv=None):
         return 0
     if a.sweep_timing:
         print(sweep_timing(a.sweep_timing, a.workload, a.out_dir, a.command))
+        return 0
+    if a.timeline:
+        print(timeline_table(a.timeline, a.workload, a.kv_dtype, a.out_dir, a.command))
         return 0
     tag = a.workload + ("_fp8" if KV8 else "") + ("_nohint" if a.no_context_hint else "")
     w = gen.WORKLOADS[a.workload]

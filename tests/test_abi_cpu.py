@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function(native_lib):
 
 
 def test_version_and_error_strings(native_lib):
-    assert native_lib.paged_attn_abi_version() == nat.ABI_VERSION == 6
+    assert native_lib.paged_attn_abi_version() == nat.ABI_VERSION == 7
     assert nat.error_string(0) == "ok"
     for code in range(1, 5):
         assert nat.error_string(code) not in ("ok", "unknown status")
@@ -664,3 +664,19 @@ def test_streaming_waves_for_balanced_uniform_batches(native_lib, B, Hq, Hkv, MB
     e4 = nat.plan(nat.make_shape(B, Hq, Hkv, MB, 1, kv_dtype=nat.KV_E4M3),
                   hinted(MB * 16, prefetch=pf), device=MI355X)
     assert e4["waves_per_wg"] == 8
+
+
+def test_debug_timeline_pointer_must_be_8_byte_aligned(native_lib):
+    o = nat.default_options()
+    o.debug_timeline = FAKE + 4
+    assert call(good_shape(max_blocks_per_seq=16), o) == nat.PA_ERR_INVALID_ARG
+
+
+def test_binding_refuses_a_timeline_of_the_wrong_size(native_lib):
+    import torch
+    from paged_kv_cache_226_amd import ops
+    ops.check_debug_timeline(torch.empty(256, 4, dtype=torch.int64), 256)
+    for bad in (torch.empty(255, 4, dtype=torch.int64), torch.empty(256, 3, dtype=torch.int64),
+                torch.empty(256, 4, dtype=torch.int32)):
+        with pytest.raises(ValueError, match="debug_timeline"):
+            ops.check_debug_timeline(bad, 256)

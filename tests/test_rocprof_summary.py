@@ -121,3 +121,20 @@ def test_mode_plans_follow_the_library(native_lib):
     assert plans[1].startswith("4 waves, cap -")
     assert 10 in plans and 4 in plans
     assert 10 not in rs.mode_plans(gen.WORKLOADS["llama2_7b"], True, 2048)
+
+
+def test_timeline_table(tmp_path):
+    import json
+    r = {"timeline": "w", "kv_dtype": "fp16", "min_context_hint": 0, "waves_per_wg": 4,
+         "resident_wgs": 0, "workgroups": 16, "cus_seen": 8, "kernel_us_plain": 10.0,
+         "kernel_us_traced": 11.0, "span_us": 10.5, "kv_bytes": 1000000,
+         "cu_last_end_us": {"min": 9.0, "median": 10.0, "max": 10.5},
+         "cus_busy_at_80_90_95_pct_of_span": [1.0, 0.5, 0.25],
+         "per_xcd": [{"xcd": 0, "workgroups": 2, "mean_wg_us": 9.5, "last_end_us": 10.5,
+                      "wg_index_mod_8": [0]}]}
+    (tmp_path / "t.jsonl").write_text("noise\n" + json.dumps(r) + "\n")
+    path = rs.timeline_table(str(tmp_path / "t.jsonl"), "w", "fp16", str(tmp_path), "cmd")
+    assert path.endswith("pa_decode_w_nohint_timeline.md")
+    text = open(path).read()
+    assert "| 0 | 2 | 0 | 9.5 | 10.5 |" in text and "100 % / 50 % / 25 %" in text
+    assert "95 GB/s" in text
