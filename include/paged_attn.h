@@ -215,7 +215,7 @@ typedef struct pa_options {
                                   start to end.  A wrong bound changes no
                                   result, only the speed */
     int32_t max_resident_wgs;  /* at most this many decode work-groups per CU
-                                  at once (0 = the plan's choice, 1..64): the
+                                  at once (0 = the plan's choice, 1..8): the
                                   launch requests the LDS that enforces it */
     void *workspace;           /* device scratch for partition partials; may be
                                   NULL when the plan has one partition */

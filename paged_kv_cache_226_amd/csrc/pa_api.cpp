@@ -89,6 +89,10 @@ constexpr int kResidentWavesPerCU = 12;
 //    flight (llama3_8b-shaped, 64 x 512..8K tokens: 181 -> 256 us), hence
 //    the hint.
 constexpr int kStreamMinBlocks = 64;
+// The largest residency cap the LDS request enforces on 160 KiB of LDS per
+// CU: beyond about 10 the 1 KiB margin for the compiler's LDS and the
+// allocation granularity is a large part of each work-group's share.
+constexpr int kMaxResidencyCap = 8;
 constexpr int kStreamMinBlocksGqa = 256;
 constexpr int kStreamSplitBlocks = 256;
 
@@ -235,7 +239,8 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   const bool two = o->structure == PA_STRUCTURE_TWO_LOOP;
   const bool kv8 = sh->kv_dtype == PA_KV_E4M3;
   if (two && (o->prefetch_distance > 1 || kv8)) return PA_ERR_UNSUPPORTED;
-  if (o->min_context_hint < 0 || o->max_resident_wgs < 0 || o->max_resident_wgs > 64)
+  if (o->min_context_hint < 0 || o->max_resident_wgs < 0 ||
+      o->max_resident_wgs > kMaxResidencyCap)
     return PA_ERR_INVALID_ARG;
   int order = o->seq_order;
   if (order < PA_ORDER_AUTO || order > PA_ORDER_LONGEST_FIRST) return PA_ERR_INVALID_ARG;

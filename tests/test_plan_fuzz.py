@@ -35,22 +35,28 @@ options = st.tuples(
     st.sampled_from([0, 0, 1, 2, 3, 4, 8, 16]),            # waves_per_wg (3, 16 invalid)
     st.sampled_from([0, 0, 1, 2, 3, 63, 64]),              # prefetch_distance
     st.sampled_from([0, 0, 1, 2]),                         # seq_order
-    st.sampled_from([0, 0, 0, 1]))                         # structure
+    st.sampled_from([0, 0, 0, 1]),                         # structure
+    st.sampled_from(["none", "none", "full", "7/8", "under", "neg"]),  # min_context_hint
+    st.sampled_from([0, 0, 0, 0, 1, 2, 3, 4, 5, 7, 8, 9, -1]))  # max_resident_wgs (9, -1 invalid)
 
 
 @settings(max_examples=600, deadline=None)
 @given(shapes, options)
 def test_every_accepted_plan_is_launchable(shape_t, opt_t):
     B, Hkv, g, MB, kv = shape_t
-    pf, pb, waves, dist, order, structure = opt_t
+    pf, pb, waves, dist, order, structure, hint_kind, cap = opt_t
+    hint = {"none": 0, "full": MB * 16, "7/8": MB * 16 * 7 // 8 + 1,
+            "under": max(MB * 16 * 7 // 8 - 1, 1), "neg": -5}[hint_kind]
     sh = nat.make_shape(B, g * Hkv, Hkv, MB, 10 * MB * B, kv_dtype=kv)
     o = nat.default_options()
     o.prefetch, o.partition_blocks, o.waves_per_wg = pf, pb, waves
     o.prefetch_distance, o.seq_order, o.structure = dist, order, structure
+    o.min_context_hint, o.max_resident_wgs = hint, cap
     rc, p = raw_plan(sh, o)
     assert rc in (nat.PA_OK, nat.PA_ERR_INVALID_ARG, nat.PA_ERR_UNSUPPORTED)
     must_refuse = (g > 16 or pf > 4 or waves in (3, 16) or pb > 1024 or dist > 63
-                   or (order == nat.ORDER_LONGEST_FIRST and B > nat.RANK_MAX_SEQS))
+                   or (order == nat.ORDER_LONGEST_FIRST and B > nat.RANK_MAX_SEQS)
+                   or hint < 0 or cap < 0 or cap > 8)
     if must_refuse:
         assert rc != nat.PA_OK
     if rc != nat.PA_OK:
@@ -93,3 +99,26 @@ def test_every_accepted_plan_is_launchable(shape_t, opt_t):
     assert p["structure"] == structure
     if structure == nat.STRUCTURE_TWO_LOOP:
         assert kv == nat.KV_F16 and p["prefetch_distance"] == 1
+    # LDS: dynamic + the compiler's share within the work-group limit, and a
+    # residency cap enforced (cap + 1 work-groups never fit beside their
+    # compiler LDS)
+    lds, R = p["lds_bytes"], p["resident_wgs"]
+    assert lds + 1024 <= 163840
+    if cap:
+        assert R == cap
+    if R:
+        assert 1 <= R <= 8 and (R + 1) * (lds + 256) > 163840
+    else:
+        assert cap == 0
+    # the hint only picks waves, residency and order: never the mode, the
+    # distance or the structure, and a refused hint-less plan stays refused
+    o0 = nat.default_options()
+    o0.prefetch, o0.partition_blocks, o0.waves_per_wg = pf, pb, waves
+    o0.prefetch_distance, o0.seq_order, o0.structure = dist, order, structure
+    o0.max_resident_wgs = cap
+    rc0, p0 = raw_plan(sh, o0)
+    assert rc0 == nat.PA_OK
+    for k in ("prefetch", "prefetch_distance", "structure"):
+        assert p[k] == p0[k], k
+    if hint_kind in ("none", "under"):
+        assert p == p0
