@@ -72,7 +72,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 7
+#define PA_ABI_VERSION 8
 #define PA_HEAD_DIM 128
 #define PA_BLOCK_SIZE 16
 #define PA_G_MAX 16      /* query heads per KV head */
@@ -273,6 +273,12 @@ typedef struct pa_plan_info {
     size_t lds_bytes;          /* dynamic LDS per decode work-group: what the
                                   walk needs, or more where a residency cap
                                   is enforced */
+    int32_t seqs_per_wg;       /* 1, or 2: each work-group walks two
+                                  sequences in turn (grid row y: ranks y and
+                                  B-1-y), for 1-wave work-groups capped at 2
+                                  per CU whose halved grid fills whole rounds
+                                  of the cap; workgroups counts the halved
+                                  grid */
 } pa_plan_info;
 
 /* What the auto plan takes from the device.  paged_attn_plan,

@@ -52,7 +52,8 @@ class PaPlanInfo(ctypes.Structure):
                 ("workgroups", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t),
                 ("seq_order", ctypes.c_int32), ("structure", ctypes.c_int32),
                 ("prefetch_distance", ctypes.c_int32), ("balanced", ctypes.c_int32),
-                ("resident_wgs", ctypes.c_int32), ("lds_bytes", ctypes.c_size_t)]
+                ("resident_wgs", ctypes.c_int32), ("lds_bytes", ctypes.c_size_t),
+                ("seqs_per_wg", ctypes.c_int32)]
 
 
 class PaDeviceInfo(ctypes.Structure):
@@ -63,7 +64,7 @@ class PaDeviceInfo(ctypes.Structure):
 _lib = None
 
 # the PA_ABI_VERSION whose struct layouts the classes above mirror
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 
 class NativeLibraryMissing(RuntimeError):

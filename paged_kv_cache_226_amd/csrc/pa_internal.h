@@ -46,6 +46,7 @@ struct DecodeArgs {
   int nslot;
   int pb_max;
   int k_uniform;         // min(nslot / B, P): partitions per sequence of a uniform batch
+  int chain;             // 2: grid row y walks sequence ranks y and B-1-y in turn (P == 1)
   int32_t* ws_np;
 };
 

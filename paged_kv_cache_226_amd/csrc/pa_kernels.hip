@@ -1090,6 +1090,38 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
   const int tid = threadIdx.x;
   const int W = blockDim.x / kWave;
   const int tab_tokens = a.MB * kT;
+  if (!a.balanced && a.chain == 2) {
+    // Two sequences in turn, one partition each: grid row y takes ranks y
+    // and B-1-y (B is even).
+    for (int k = 0; k < 2; ++k) {
+      if (k == 1) __syncthreads();  // the first sequence's merge records are read
+      const int r = k == 0 ? (int)blockIdx.y : a.B - 1 - (int)blockIdx.y;
+      const int bk = a.rank_seqs ? ranked_sequence(a, r, tab_tokens, smem_raw) : r;
+      int ck = a.ctx[bk];
+      if (ck > tab_tokens) {
+        if (DBG && tid == 0 && a.dbg_err) atomicOr(a.dbg_err, 2);
+        ck = tab_tokens;
+      }
+      const int nbk = ck > 0 ? (ck + kT - 1) / kT : 0;
+      if (nbk == 0) {  // context <= 0: zeros
+        for (int idx = tid; idx < G * kD; idx += blockDim.x) {
+          const int h = idx / kD, d = idx % kD;
+          a.out[((int64_t)bk * a.Hq + kvh * G + h) * kD + d] = 0;
+        }
+        continue;
+      }
+      if constexpr (!TWO) walk_range<PF, DBG, KV8>(a, bk, kvh, ck, 0, nbk, bt_s, merge_s);
+      for (int idx = tid; idx < G * kD; idx += blockDim.x) {
+        const int h = idx / kD, d = idx % kD;
+        float M, L, O;
+        combine_waves(merge_s, W, G, h, d, M, L, O);
+        a.out[((int64_t)bk * a.Hq + kvh * G + h) * kD + d] =
+            f32_to_f16_bits(O * a.v_scale / L);
+      }
+    }
+    stamp_end();
+    return;
+  }
   int b, part = p, np_seq = a.P, pb = a.PB, ctx;
   if (a.balanced) {
     const Slot sl = balanced_slot(a, blockIdx.y, tab_tokens);
@@ -1309,7 +1341,7 @@ hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int wa
       launch_decode_t<5, false, true>,  launch_decode_t<5, true, true>,
       launch_decode_t<6, false, true>,  launch_decode_t<6, true, true>};
   if (pf < 0 || pf > 6) return hipErrorInvalidValue;
-  const dim3 grid(a.Hkv, a.balanced ? a.nslot : a.B, a.balanced ? 1 : a.P);
+  const dim3 grid(a.Hkv, a.balanced ? a.nslot : a.B / a.chain, a.balanced ? 1 : a.P);
   const dim3 block(kWave * waves);
   // what the walk needs (the LDS ring: depth + 1 slots of one block's K and
   // V per wave); the plan may ask for more, to cap the residency

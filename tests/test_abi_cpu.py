@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function(native_lib):
 
 
 def test_version_and_error_strings(native_lib):
-    assert native_lib.paged_attn_abi_version() == nat.ABI_VERSION == 7
+    assert native_lib.paged_attn_abi_version() == nat.ABI_VERSION == 8
     assert nat.error_string(0) == "ok"
     for code in range(1, 5):
         assert nat.error_string(code) not in ("ok", "unknown status")
@@ -512,6 +512,11 @@ def test_streaming_shape_for_uniform_contexts(native_lib, B, Hq, Hkv, kv, want):
     assert (p["waves_per_wg"], p["resident_wgs"]) == want
     assert p["prefetch"] == nat.PREFETCH_REG and p["num_partitions"] == 1
     assert p["seq_order"] == nat.ORDER_NATURAL
+    # two sequences per work-group where 1-wave work-groups capped at 2 per
+    # CU still fill whole rounds of the cap with the grid halved
+    chained = want == (1, 2) and (B * Hkv) % (2 * 2 * 256) == 0
+    assert p["seqs_per_wg"] == (2 if chained else 1)
+    assert p["workgroups"] == B * Hkv // p["seqs_per_wg"]
     if want[1]:
         # cap work-groups of the LDS fill a CU, cap + 1 do not
         share = 163840 // want[1] // 1024 * 1024 - 1024
@@ -683,3 +688,23 @@ def test_binding_refuses_a_timeline_of_the_wrong_size(native_lib):
                 torch.empty(256, 4, dtype=torch.int32)):
         with pytest.raises(ValueError, match="debug_timeline"):
             ops.check_debug_timeline(bad, 256)
+
+
+@pytest.mark.parametrize("B,Hkv,waves,cap,order,want", [
+    (64, 16, 1, 2, 0, 2),                          # explicit: 1024 units, 512 work-groups
+    (64, 16, 1, 2, nat.ORDER_LONGEST_FIRST, 2),    # ranked pairs y and B-1-y
+    (63, 16, 1, 2, 0, 1),                          # odd batch
+    (32, 16, 1, 2, 0, 1),                          # 512 units: half a round of the cap
+    (64, 16, 2, 2, 0, 1),                          # 2-wave work-groups
+    (64, 16, 1, 3, 0, 1),                          # another cap
+    (64, 16, 1, 0, 0, 1),                          # no cap
+])
+def test_two_sequences_per_work_group(native_lib, B, Hkv, waves, cap, order, want):
+    sh = nat.make_shape(B, 2 * Hkv, Hkv, 64, 64 * B)
+    p = nat.plan(sh, hinted(0, waves_per_wg=waves, max_resident_wgs=cap, seq_order=order,
+                            partition_blocks=64), device=MI355X)
+    assert (p["waves_per_wg"], p["num_partitions"]) == (waves, 1)
+    assert p["seqs_per_wg"] == want
+    assert p["workgroups"] == B * Hkv // want
+    if order:
+        assert p["seq_order"] == order

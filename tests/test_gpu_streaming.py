@@ -132,3 +132,33 @@ def test_streaming_waves_of_a_balanced_split(B, Hq, Hkv, ctx):
     for pf in (0, 1, 3):
         o = run(x, dev, prefetch=pf, **same_plan(plan))
         assert np.array_equal(bits(o), bits(got)), f"mode {pf}"
+
+
+@pytest.mark.parametrize("order", [0, nat.ORDER_LONGEST_FIRST])
+def test_two_sequences_per_work_group_on_a_ragged_batch(order):
+    """1-wave work-groups capped at 2 per CU walk sequence ranks y and B-1-y
+    in turn (under longest-first order a long sequence pairs with a short
+    one); empty sequences on either side of a pair give zeros.  The same
+    waves, order and partitions under another cap (one sequence per
+    work-group) give the same bits."""
+    C = cus()
+    Hkv = 16
+    B = 4 * C // Hkv
+    rng = np.random.default_rng(830)
+    lens = rng.integers(1, 1025, size=B)
+    lens[[0, 3, B - 1, B // 2]] = 0
+    lens[[1, 5]] = 1024
+    x = gen.make_case(B, 2 * Hkv, Hkv, [int(v) for v in lens], seed=831, extra_pool_blocks=3,
+                      poison=True)
+    dev = to_device(x)
+    kw = dict(waves_per_wg=1, partition_blocks=64, seq_order=order)
+    plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], max_resident_wgs=2, **kw)
+    print(f"[chain] order={order} B={B} plan={plan}", flush=True)
+    assert plan["seqs_per_wg"] == 2 and plan["num_partitions"] == 1
+    got = run(x, dev, max_resident_wgs=2, **kw)
+    assert_close(got, oracle(x), f"two per work-group, order {order}")
+    one = run(x, dev, max_resident_wgs=3, **kw)
+    assert np.array_equal(bits(got), bits(one))
+    for pf in (0, 1, 3):
+        o = run(x, dev, prefetch=pf, max_resident_wgs=2, **kw)
+        assert np.array_equal(bits(o), bits(got)), f"mode {pf}"

@@ -75,12 +75,20 @@ def test_every_accepted_plan_is_launchable(shape_t, opt_t):
         pb_max = -(-min(MB, 1024) // W) * W
         assert rows >= B * -(-MB // pb_max) and P <= rows - B + 1
         assert P >= -(-MB // pb_max) and P <= -(-MB // PB)
+        assert p["seqs_per_wg"] == 1
         assert p["seq_order"] == nat.ORDER_NATURAL
         want_ws = (-(-B // 4) * 4 + B * g * Hkv * P * 130) * 4
     else:
         assert 1 <= PB <= min(MB, 1024)
         assert P == -(-MB // PB) and P <= 65535
-        assert p["workgroups"] == P * Hkv * B
+        S = p["seqs_per_wg"]
+        assert S in (1, 2)
+        if S == 2:
+            # two sequences per work-group only for one partition of 1-wave
+            # work-groups capped at 2 per CU, the halved grid whole rounds
+            assert P == 1 and W == 1 and p["resident_wgs"] == 2 and B % 2 == 0
+            assert (B * Hkv) % (2 * 2 * 256) == 0 and structure != nat.STRUCTURE_TWO_LOOP
+        assert p["workgroups"] == P * Hkv * B // S
         if pb:
             assert PB == min(pb, MB)
         want_ws = B * g * Hkv * P * 130 * 4 if P > 1 else 0
