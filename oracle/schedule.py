@@ -5,8 +5,9 @@ TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
 The asynchronous-KV-prefetch review (section 3.4, Algorithm 1) gives each of
 w warps of a thread block a block-index range [s, e): a warp walks its blocks
 with stride w, looks up the current block in the block table and loads it,
-and, when block_idx + w is still below e, looks up that block too and starts
-fetching it into the cache before computing Q*K^T on the current one.  The
+and, when the block w further on still lies inside the range, looks that one
+up too and starts fetching it into the cache before computing Q*K^T on the
+current one.  The
 third page (section 2.2) assigns warp i the blocks i, i + 4, i + 8, ... of a
 4-warp block, so wave i starts at s + i.
 """
