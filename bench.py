@@ -424,9 +424,13 @@ def measure_workload(args, name, env, cpu_leg):
     hint = 0 if args.no_context_hint else max(int(x.context_lens.min()), 0)
     plan = ops.plan(d["q"], d["k_cache"], d["block_tables"], prefetch=args.prefetch,
                     prefetch_distance=args.prefetch_distance, min_context_hint=hint)
-    shape_kw = dict(waves_per_wg=plan["waves_per_wg"], seq_order=plan["seq_order"],
-                    max_resident_wgs=plan["resident_wgs"],
-                    partition_blocks=0 if plan["balanced"] else plan["partition_blocks"])
+    if plan["even_split"]:
+        shape_kw = dict(even_split=nat.EVEN_SPLIT_ON, waves_per_wg=plan["waves_per_wg"],
+                        max_resident_wgs=plan["resident_wgs"])
+    else:
+        shape_kw = dict(waves_per_wg=plan["waves_per_wg"], seq_order=plan["seq_order"],
+                        max_resident_wgs=plan["resident_wgs"], even_split=nat.EVEN_SPLIT_OFF,
+                        partition_blocks=0 if plan["balanced"] else plan["partition_blocks"])
 
     # One prepared call per configuration, each with its own output tensor
     # and its own workspace (sized for its own plan): a step is then one C
@@ -514,7 +518,8 @@ def measure_workload(args, name, env, cpu_leg):
 
     def shape_of_plan(p):
         return {k: p[k] for k in ("waves_per_wg", "partition_blocks", "num_partitions",
-                                  "seq_order", "resident_wgs", "balanced", "workgroups")}
+                                  "seq_order", "resident_wgs", "balanced", "even_split",
+                                  "workgroups")}
 
     us = timed(timed_key, args.steps, args.warmup, min_warm_s=0.25)
     launch_avg, launch_med, launch_p10, launch_p90 = per_launch(timed_key, args.steps)
@@ -585,6 +590,7 @@ def measure_workload(args, name, env, cpu_leg):
                    "waves_per_wg": plan["waves_per_wg"],
                    "partition_blocks": plan["partition_blocks"],
                    "num_partitions": plan["num_partitions"],
+                   "even_split": plan["even_split"],
                    "seq_order": nat.ORDER_NAMES.get(plan["seq_order"], plan["seq_order"]),
                    "parallelism": "single GPU"},
         "us_per_step": round(us, 2),

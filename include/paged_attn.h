@@ -140,6 +140,13 @@ enum pa_structure {
                                   scores are kept in LDS) */
 };
 
+/* pa_options.even_split */
+enum pa_even_split {
+    PA_EVEN_SPLIT_AUTO = 0,   /* the plan's choice */
+    PA_EVEN_SPLIT_OFF = 1,
+    PA_EVEN_SPLIT_ON = 2      /* PA_ERR_UNSUPPORTED where it does not apply */
+};
+
 typedef struct pa_shape {
     int32_t num_seqs;           /* B >= 1 */
     int32_t num_q_heads;        /* Hq >= 1 */
@@ -217,6 +224,22 @@ typedef struct pa_options {
     int32_t max_resident_wgs;  /* at most this many decode work-groups per CU
                                   at once (0 = the plan's choice, 1..8): the
                                   launch requests the LDS that enforces it */
+    int32_t even_split;        /* enum pa_even_split.  The even split gives
+                                  each of S = CUs x residency work-groups an
+                                  equal share of all the batch's (block, KV
+                                  head) pairs, KV head 0's sequences first,
+                                  then head 1's, ...; a work-group walks the
+                                  pieces of the (sequence, KV head) units in
+                                  its share, writes a whole unit's output
+                                  directly and a piece of a unit that
+                                  crosses a share boundary to the workspace,
+                                  and a second kernel merges those.  The
+                                  shares are found on the device from the
+                                  context lengths.  It needs num_seqs <=
+                                  PA_RANK_MAX_SEQS, max_blocks_per_seq <=
+                                  1024, the fused structure and no explicit
+                                  partition size; the sequence order does
+                                  not apply */
     void *workspace;           /* device scratch for partition partials; may be
                                   NULL when the plan has one partition */
     size_t workspace_bytes;
@@ -279,6 +302,11 @@ typedef struct pa_plan_info {
                                   per CU whose halved grid fills whole rounds
                                   of the cap; workgroups counts the halved
                                   grid */
+    int32_t even_split;        /* 1: the even split (pa_options.even_split);
+                                  workgroups = the shares; the workspace
+                                  holds two partial records of Hq / Hkv rows
+                                  per share and one piece record per
+                                  (sequence, KV head) */
 } pa_plan_info;
 
 /* What the auto plan takes from the device.  paged_attn_plan,

@@ -21,6 +21,7 @@ ORDER_AUTO, ORDER_NATURAL, ORDER_LONGEST_FIRST = 0, 1, 2
 ORDER_NAMES = {1: "natural", 2: "longest_first"}
 RANK_MAX_SEQS = 256
 STRUCTURE_FUSED, STRUCTURE_TWO_LOOP = 0, 1
+EVEN_SPLIT_AUTO, EVEN_SPLIT_OFF, EVEN_SPLIT_ON = 0, 1, 2
 KV_F16, KV_E4M3 = 0, 1
 # bytes of the device scratch array behind paged_attn_decode_noalloc
 NOALLOC_SCRATCH_BYTES = 16 << 20
@@ -41,6 +42,7 @@ class PaOptions(ctypes.Structure):
                 ("waves_per_wg", ctypes.c_int32), ("prefetch_distance", ctypes.c_int32),
                 ("seq_order", ctypes.c_int32), ("structure", ctypes.c_int32),
                 ("min_context_hint", ctypes.c_int32), ("max_resident_wgs", ctypes.c_int32),
+                ("even_split", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("debug_gather_k", ctypes.c_void_p), ("debug_trace", ctypes.c_void_p),
                 ("debug_error_word", ctypes.c_void_p), ("debug_timeline", ctypes.c_void_p)]
@@ -53,7 +55,7 @@ class PaPlanInfo(ctypes.Structure):
                 ("seq_order", ctypes.c_int32), ("structure", ctypes.c_int32),
                 ("prefetch_distance", ctypes.c_int32), ("balanced", ctypes.c_int32),
                 ("resident_wgs", ctypes.c_int32), ("lds_bytes", ctypes.c_size_t),
-                ("seqs_per_wg", ctypes.c_int32)]
+                ("seqs_per_wg", ctypes.c_int32), ("even_split", ctypes.c_int32)]
 
 
 class PaDeviceInfo(ctypes.Structure):

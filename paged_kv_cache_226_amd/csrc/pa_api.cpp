@@ -95,6 +95,8 @@ constexpr int kStreamMinBlocks = 64;
 constexpr int kMaxResidencyCap = 8;
 constexpr int kStreamMinBlocksGqa = 256;
 constexpr int kStreamSplitBlocks = 256;
+// The even split's shortest table (blocks) for the auto plan.
+constexpr int kEvenMinBlocks = 256;
 
 bool valid_device(const pa_device_info* d) {
   return d && d->compute_units >= 1 && d->compute_units <= 65536 &&
@@ -155,6 +157,7 @@ struct Plan {
   int cap;                 // residency cap (work-groups per CU), 0 = none
   size_t lds;              // dynamic LDS per decode work-group
   int chain;               // sequences one work-group walks in turn (1 or 2)
+  int even;                // 1: the even split over `wgs` shares
 };
 
 // Waves per work-group and residency cap of the streaming shape for u units
@@ -312,6 +315,48 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
       B <= PA_RANK_MAX_SEQS && MB <= kBalancedMaxTable &&
       (int64_t)MB * units >= (int64_t)kStreamSplitBlocks * dv.cus && in_flight <= 2)
     waves = in_flight == 1 ? 4 : 2;
+  // The even split (pa_options.even_split): one share of the batch's
+  // blocks per work-group, S = CUs x the residency cap (1 unless asked),
+  // with the waves that keep about 4 fp16 (8 E4M3) blocks in flight per
+  // work-group.
+  //
+  // The plan takes it by itself for an fp16 cache with more than C / 2 and
+  // fewer than 2 C units and 256..1024 table blocks, unless the hint says
+  // every context fills the table: the fixed grid then leaves CUs idle
+  // (a second round of fewer units than CUs, or ragged units one per CU),
+  // and the balanced split keeps whole partitions of one size.  Measured
+  // (us, the plan before -> the even split): ragged GQA 32/8, 48 x 1..8K
+  // (1.5 units per CU) 175.5 -> 134.1; 24 x 512..8K 85.5 -> 71.6; llama3_8b
+  // TP2 shard (64 x 512..8K, 4 KV heads) 106.0 -> 96.6; 32 x 512..8K 106.3
+  // -> 95.8; uniform MHA 8 x 4K 80.5 -> 78.3.  It lost on shorter tables
+  // (MHA 8 x 1K +14 %, GQA 32 x 1..2K +17 %), at C / 2 units or fewer (+5
+  // % on two of three ragged batches) and, with these waves, over E4M3.
+  if (o->even_split < PA_EVEN_SPLIT_AUTO || o->even_split > PA_EVEN_SPLIT_ON)
+    return PA_ERR_INVALID_ARG;
+  const bool uniform_hint = o->min_context_hint > 0 && (int64_t)o->min_context_hint * 8 >=
+                                                           (int64_t)MB * PA_BLOCK_SIZE * 7;
+  const bool even_auto =
+      o->even_split == PA_EVEN_SPLIT_AUTO && !kv8 && !two && !uniform_hint && in_flight > 0 &&
+      o->partition_blocks == 0 && o->waves_per_wg == 0 && o->max_resident_wgs == 0 &&
+      o->seq_order == PA_ORDER_AUTO && B >= 2 && B <= PA_RANK_MAX_SEQS &&
+      MB >= kEvenMinBlocks && MB <= kMaxPartitionBlocks && 2 * units > dv.cus &&
+      units < 2 * dv.cus && (int64_t)B * MB * Hkv <= INT32_MAX / 2;
+  const bool even = o->even_split == PA_EVEN_SPLIT_ON || even_auto;
+  if (even) {
+    // positions in the (block, KV head) sequence are int32 on the device
+    if (two || o->partition_blocks != 0 || B > PA_RANK_MAX_SEQS || MB > kMaxPartitionBlocks ||
+        (int64_t)B * MB * Hkv > INT32_MAX / 2)
+      return PA_ERR_UNSUPPORTED;
+    waves = o->waves_per_wg;
+    if (waves == 0) {
+      const int per_wave = in_flight > 0 ? in_flight : 1;
+      const int want = (kv8 ? 8 : 4) / per_wave;
+      waves = want >= 8 ? 8 : want >= 4 ? 4 : want >= 2 ? 2 : 1;
+    }
+    cap = o->max_resident_wgs > 0 ? o->max_resident_wgs : 1;
+    order = PA_ORDER_NATURAL;
+    rank = false;
+  }
   if (waves == 0 && two) waves = 4;
   if (waves == 0) {
     const bool whole = o->partition_blocks == 0 ? units >= dv.cus : o->partition_blocks >= MB;
@@ -329,7 +374,9 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   }
 
   int PB;
-  if (o->partition_blocks > 0) {
+  if (even) {
+    PB = MB;  // a piece is at most one sequence's table
+  } else if (o->partition_blocks > 0) {
     PB = o->partition_blocks < MB ? o->partition_blocks : MB;
   } else if (two) {
     // 512-token partitions, halved until the scores fit in LDS
@@ -355,8 +402,9 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   if (P > 65535) return PA_ERR_UNSUPPORTED;  // grid.z
   // the balanced split replaces the fixed partitions of an auto split plan
   int bal = 0, nslot = 0, pb_max = 0;
-  if (!two && o->partition_blocks == 0 && units < dv.cus && o->seq_order == PA_ORDER_AUTO &&
-      B >= 2 && B <= PA_RANK_MAX_SEQS && MB <= kBalancedMaxTable) {
+  if (!even && !two && o->partition_blocks == 0 && units < dv.cus &&
+      o->seq_order == PA_ORDER_AUTO && B >= 2 && B <= PA_RANK_MAX_SEQS &&
+      MB <= kBalancedMaxTable) {
     const int pb_min = (kMinShortPartition + waves - 1) / waves * waves;
     const int cap = MB < kMaxPartitionBlocks ? MB : kMaxPartitionBlocks;
     pb_max = (cap + waves - 1) / waves * waves;
@@ -397,10 +445,12 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   // where the halved grid still fills whole rounds of the cap (MHA 32/32, 32
   // x 2K: 152.4 -> 150.9 us).
   int chain = 1;
-  if (!two && !bal && P == 1 && waves == 1 && cap == 2 && B % 2 == 0 &&
+  if (!even && !two && !bal && P == 1 && waves == 1 && cap == 2 && B % 2 == 0 &&
       units % ((int64_t)2 * cap * dv.cus) == 0)
     chain = 2;
-  const int64_t wgs = bal ? (int64_t)nslot * Hkv : (int64_t)P * Hkv * B / chain;
+  const int64_t wgs = even  ? (int64_t)dv.cus * cap
+                      : bal ? (int64_t)nslot * Hkv
+                            : (int64_t)P * Hkv * B / chain;
   // a residency cap takes LDS: cap work-groups of it fill a CU
   const size_t cap_lds = cap > 0 ? pa::residency_lds_bytes(dv.lds_per_cu, cap) : 0;
   auto lds_with_cap = [&](bool r) {
@@ -432,6 +482,7 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   pl->pb_max = pb_max;
   pl->cap = cap;
   pl->chain = chain;
+  pl->even = even ? 1 : 0;
   pl->lds = lds;
   // partials [B][Hq][P][128] and [B][Hq][P][2] in fp32; the balanced split
   // adds the sequences' partition counts (B int32, padded to 16 bytes)
@@ -439,6 +490,9 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
                           (size_t)B * sh->num_q_heads * P * (2 + PA_HEAD_DIM)) *
                              sizeof(float)
                        : 0;
+  // the even split: two records of g rows (128 outputs, then m and l) per
+  // share, then (first record, pieces) per (sequence, KV head)
+  if (even) pl->ws_bytes = (pa::even_records(wgs, g) + (size_t)2 * units) * sizeof(float);
   return PA_OK;
 }
 
@@ -478,6 +532,7 @@ static int plan_info(const pa_shape* sh, const pa_options* o, const DeviceInfo& 
   info->resident_wgs = pl.cap;
   info->lds_bytes = pl.lds;
   info->seqs_per_wg = pl.chain;
+  info->even_split = pl.even;
   return PA_OK;
 }
 
@@ -588,6 +643,8 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   if (pl.bal) a.k_uniform = pl.nslot / sh->num_seqs < pl.P ? pl.nslot / sh->num_seqs : pl.P;
   a.pf_dist = pl.dist;
   a.chain = pl.chain;
+  a.even = pl.even;
+  a.shares = pl.even ? (int)pl.wgs : 0;
   const bool dbg =
       o->debug_gather_k || o->debug_trace || o->debug_error_word || o->debug_timeline;
   if (pl.two && dbg) return PA_ERR_UNSUPPORTED;
@@ -603,6 +660,14 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
     a.ws_ml = ws + rows * PA_HEAD_DIM;
     if (pl.bal) a.ws_np = reinterpret_cast<int32_t*>(a.ws_ml + rows * 2);
   }
+  if (pl.even) {
+    // [2 S][g][128] outputs, [2 S][g][2] (m, l), then [B][Hkv][2] int32
+    float* ws = static_cast<float*>(o->workspace);
+    const size_t recs = (size_t)2 * pl.wgs * g;
+    a.ws_o = ws;
+    a.ws_ml = ws + recs * PA_HEAD_DIM;
+    a.ws_np = reinterpret_cast<int32_t*>(ws + pa::even_records(pl.wgs, g));
+  }
   if (pl.two) {
     if (pa::launch_decode_two_loop(a, pl.pf, pl.waves, pl.lds, st) != hipSuccess)
       return PA_ERR_HIP;
@@ -615,7 +680,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
     if (pa::launch_decode(a, variant, dbg, kv8, pl.waves, pl.lds, st) != hipSuccess)
       return PA_ERR_HIP;
   }
-  if (pl.P > 1 && pa::launch_reduce(a, st) != hipSuccess) return PA_ERR_HIP;
+  if ((pl.P > 1 || pl.even) && pa::launch_reduce(a, st) != hipSuccess) return PA_ERR_HIP;
   return PA_OK;
 }
 

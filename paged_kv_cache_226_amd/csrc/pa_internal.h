@@ -47,8 +47,24 @@ struct DecodeArgs {
   int pb_max;
   int k_uniform;         // min(nslot / B, P): partitions per sequence of a uniform batch
   int chain;             // 2: grid row y walks sequence ranks y and B-1-y in turn (P == 1)
+  // Even split (even = 1): grid (S); share c takes blocks [c T / S, (c + 1)
+  // T / S) of the T (block, KV head) pairs of all sequences, KV-head-major
+  // (head 0's sequences in order, then head 1's, ...).  A piece of a unit
+  // that crosses a share boundary goes to record 2c (the share's first
+  // piece) or 2c + 1 (its last) of ws_o / ws_ml, [2 S][G] rows, and the
+  // share holding a unit's block 0 writes ws_np[2 u] = its record and
+  // ws_np[2 u + 1] = the unit's piece count (u = b Hkv + kvh).  Piece j > 0
+  // of a unit is record 2 (c0 + j); a share with no blocks leaves an empty
+  // record (m = -inf, l = 0, o = 0) at 2c.
+  int even;
+  int shares;            // S, the even split's grid
   int32_t* ws_np;
 };
+
+// floats of the even split's records: 2 per share, g rows of 128 + 2
+inline size_t even_records(int64_t shares, int g) {
+  return (size_t)2 * shares * g * (128 + 2);
+}
 
 // Partials the reduce kernel merges with one memory round trip, and the
 // partition size from which the auto plans let a sequence have more of them

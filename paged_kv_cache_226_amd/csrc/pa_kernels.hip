@@ -1049,6 +1049,128 @@ __device__ Slot balanced_slot(const DecodeArgs& a, int slot, int tab_tokens) {
   return r;
 }
 
+// Even split: this work-group's share [X, Y) of the T = Hkv * N (block, KV
+// head) pairs, N the blocks of all sequences, units (KV head, sequence)
+// KV-head-major: head kvh's units fill [kvh N, (kvh + 1) N), its sequences
+// in order.  (Sequence-major order, a sequence's KV heads one after the
+// other, measured 5-7 % slower: the work-groups that run at the same time
+// then read every other KV head's slice of the same blocks instead of all
+// of them.)  Every wave finds the unit holding block X from the block
+// counts of all sequences (lane l holds sequences 4l..4l+3, B <= 256); the
+// work-group then walks the pieces of the units in [X, Y) in order.  A
+// whole unit's output is written here; a piece goes to record 2c (the
+// share's first piece) or 2c + 1 (its last: a unit that starts in the
+// share and runs past its end), and the piece that holds a unit's block 0
+// also records where the unit's pieces are for the merge.  The share of
+// block z is the largest c' with c' T / S <= z, i.e. ((z + 1) S - 1) / T.
+template <int PF, bool DBG, bool KV8>
+__device__ __forceinline__ void even_walk(const DecodeArgs& a, int tab_tokens, int32_t* bt_s,
+                                          float* merge_s) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int W = blockDim.x / kWave;
+  const int G = a.G, Hkv = a.Hkv;
+  int nb[4], cx[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = 4 * lane + i;
+    const int raw = idx < a.B ? a.ctx[idx] : 0;
+    cx[i] = raw < 0 ? 0 : (raw > tab_tokens ? tab_tokens : raw);
+    nb[i] = (cx[i] + kT - 1) / kT;
+    if (DBG && raw > tab_tokens && a.dbg_err) atomicOr(a.dbg_err, 2);
+  }
+  const int mine = nb[0] + nb[1] + nb[2] + nb[3];
+  const int incl = wave_prefix_i32(mine);
+  const int N = __builtin_amdgcn_readlane(incl, kWave - 1);
+  const int T = N * Hkv;
+  const int S = gridDim.x;
+  const int c = blockIdx.x;
+  const int X = (int)((int64_t)c * T / S);
+  const int Y = (int)((int64_t)(c + 1) * T / S);
+  if (X == Y) {
+    // no blocks: an empty record at 2c, for the merge of a unit that
+    // spans this share
+    for (int idx = tid; idx < G * kD; idx += blockDim.x) {
+      const int h = idx / kD, d = idx % kD;
+      const int64_t r = (int64_t)2 * c * G + h;
+      a.ws_o[r * kD + d] = 0.f;
+      if (d == 0) {
+        a.ws_ml[r * 2] = -INFINITY;
+        a.ws_ml[r * 2 + 1] = 0.f;
+      }
+    }
+    return;
+  }
+  int kvh = X / N;
+  const int xr = X - kvh * N;  // X's block among head kvh's
+  int start = incl - mine;
+  int fb = -1, frel = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (xr >= start && xr < start + nb[i]) {
+      fb = 4 * lane + i;
+      frel = xr - start;
+    }
+    start += nb[i];
+  }
+  const int ol = __builtin_ctzll(__builtin_amdgcn_ballot_w64(fb >= 0));
+  int b = __builtin_amdgcn_readlane(fb, ol);
+  int off = __builtin_amdgcn_readlane(frel, ol);
+  auto pick = [&](const int* v, int seq) {  // v[seq % 4] of the lane holding seq
+    const int k = seq & 3;
+    const int x = k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3];
+    return __builtin_amdgcn_readlane(x, seq >> 2);
+  };
+  int nbb = pick(nb, b);
+  int pos = X;
+  bool first = true;
+  while (true) {
+    const int seg = nbb - off < Y - pos ? nbb - off : Y - pos;
+    walk_range<PF, DBG, KV8>(a, b, kvh, pick(cx, b), off, off + seg, bt_s, merge_s);
+    const bool whole = off == 0 && seg == nbb;
+    const int rec = first ? 2 * c : 2 * c + 1;
+    if (off == 0 && tid == 0) {
+      const int64_t last = (int64_t)pos + nbb - 1;  // the unit's last block
+      const int c1 = (int)(((last + 1) * S - 1) / T);
+      a.ws_np[2 * (b * Hkv + kvh)] = rec;
+      a.ws_np[2 * (b * Hkv + kvh) + 1] = c1 - c + 1;
+    }
+    for (int idx = tid; idx < G * kD; idx += blockDim.x) {
+      const int h = idx / kD, d = idx % kD;
+      float M, L, O;
+      combine_waves(merge_s, W, G, h, d, M, L, O);
+      if (whole) {
+        a.out[((int64_t)b * a.Hq + kvh * G + h) * kD + d] = f32_to_f16_bits(O * a.v_scale / L);
+      } else {
+        const int64_t r = (int64_t)rec * G + h;
+        a.ws_o[r * kD + d] = O;
+        if (d == 0) {
+          a.ws_ml[r * 2] = M;
+          a.ws_ml[r * 2 + 1] = L;
+        }
+      }
+    }
+    pos += seg;
+    if (pos >= Y) break;
+    first = false;
+    // the next unit: the next sequence with blocks, else the next KV head's
+    // first one (one exists: pos < Y <= T)
+    off = 0;
+    int n = 0;
+    while (true) {
+      if (++b >= a.B) {
+        b = 0;
+        if (++kvh >= Hkv) break;
+      }
+      n = pick(nb, b);
+      if (n > 0) break;
+    }
+    if (kvh >= Hkv) break;  // not reached
+    nbb = n;
+    __syncthreads();  // the merge records above are read before the next walk
+  }
+}
+
 // TWO selects the two-loop walk (fp16, no debug outputs).
 template <int PF, bool DBG, bool KV8, bool TWO = false>
 __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
@@ -1090,6 +1212,11 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
   const int tid = threadIdx.x;
   const int W = blockDim.x / kWave;
   const int tab_tokens = a.MB * kT;
+  if (a.even) {
+    if constexpr (!TWO) even_walk<PF, DBG, KV8>(a, tab_tokens, bt_s, merge_s);
+    stamp_end();
+    return;
+  }
   if (!a.balanced && a.chain == 2) {
     // Two sequences in turn, one partition each: grid row y takes ranks y
     // and B-1-y (B is even).
@@ -1201,7 +1328,80 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
 // wrote (straight from HBM).  Outputs between spec and the sequence's count
 // are loaded once it is known.  Every branch combines in the same order, so
 // the results are the same bits.
+// Merge of the even split's pieces of one (sequence, head) row, in piece
+// order.  The context length and the unit's record are loaded together;
+// then the (m, l, o) of the first kReduceRegs pieces, together.  More
+// pieces: the maximum first, then the sums, in chunks of kReduceRegs whose
+// loads are issued together (the same order of operations).
+__device__ __forceinline__ void reduce_even(const DecodeArgs& a) {
+  const int row = blockIdx.x;  // b * Hq + h
+  const int b = row / a.Hq, h = row % a.Hq;
+  const int kvh = h / a.G, g = h % a.G;
+  const int d = threadIdx.x;
+  const int rec0 = a.ws_np[2 * (b * a.Hkv + kvh)];
+  int np = a.ws_np[2 * (b * a.Hkv + kvh) + 1];
+  int ctx = a.ctx[b];
+  ctx = min(ctx, a.MB * kT);
+  if (ctx <= 0) {
+    a.out[(int64_t)row * kD + d] = 0;
+    return;
+  }
+  if (rec0 < 0 || rec0 >= 2 * a.shares) {  // not written by the decode kernel: NaN
+    a.out[(int64_t)row * kD + d] = 0x7E00;
+    return;
+  }
+  if (np <= 1) return;  // the decode kernel wrote this row
+  const int c0 = rec0 >> 1;
+  np = np < a.shares - c0 ? np : a.shares - c0;  // the records stay inside the workspace
+  auto rec = [&](int j) { return (int64_t)(j == 0 ? rec0 : 2 * (c0 + j)) * a.G + g; };
+  float mq[kReduceRegs], lq[kReduceRegs], oq[kReduceRegs];
+  auto load = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < kReduceRegs; ++i) {
+      if (j0 + i < np) {
+        const int64_t r = rec(j0 + i);
+        mq[i] = a.ws_ml[r * 2];
+        lq[i] = a.ws_ml[r * 2 + 1];
+        oq[i] = a.ws_o[r * kD + d];
+      }
+    }
+  };
+  float M = -INFINITY;
+  if (np <= kReduceRegs) {
+    load(0);
+#pragma unroll
+    for (int i = 0; i < kReduceRegs; ++i)
+      if (i < np) M = fmaxf(M, mq[i]);
+  } else {
+    for (int j0 = 0; j0 < np; j0 += kReduceRegs) {
+#pragma unroll
+      for (int i = 0; i < kReduceRegs; ++i)
+        if (j0 + i < np) mq[i] = a.ws_ml[rec(j0 + i) * 2];
+#pragma unroll
+      for (int i = 0; i < kReduceRegs; ++i)
+        if (j0 + i < np) M = fmaxf(M, mq[i]);
+    }
+  }
+  float L = 0.f, O = 0.f;
+  for (int j0 = 0; j0 < np; j0 += kReduceRegs) {
+    if (np > kReduceRegs) load(j0);
+#pragma unroll
+    for (int i = 0; i < kReduceRegs; ++i) {
+      if (j0 + i < np) {
+        const float al = fast_exp2(mq[i] - M);
+        L += al * lq[i];
+        O += al * oq[i];
+      }
+    }
+  }
+  a.out[(int64_t)row * kD + d] = f32_to_f16_bits(O * a.v_scale / L);
+}
+
 __global__ void __launch_bounds__(128) pa_reduce_kernel(const DecodeArgs a) {
+  if (a.even) {
+    reduce_even(a);
+    return;
+  }
   const int row = blockIdx.x;  // b * Hq + h
   const int b = row / a.Hq;
   const int d = threadIdx.x;
@@ -1341,7 +1541,9 @@ hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int wa
       launch_decode_t<5, false, true>,  launch_decode_t<5, true, true>,
       launch_decode_t<6, false, true>,  launch_decode_t<6, true, true>};
   if (pf < 0 || pf > 6) return hipErrorInvalidValue;
-  const dim3 grid(a.Hkv, a.balanced ? a.nslot : a.B / a.chain, a.balanced ? 1 : a.P);
+  const dim3 grid = a.even ? dim3(a.shares)
+                           : dim3(a.Hkv, a.balanced ? a.nslot : a.B / a.chain,
+                                  a.balanced ? 1 : a.P);
   const dim3 block(kWave * waves);
   // what the walk needs (the LDS ring: depth + 1 slots of one block's K and
   // V per wave); the plan may ask for more, to cap the residency

@@ -109,7 +109,8 @@ def options(prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0
             debug_trace: Optional[torch.Tensor] = None,
             debug_error_word: Optional[torch.Tensor] = None, *,
             min_context_hint: int = 0, max_resident_wgs: int = 0,
-            debug_timeline: Optional[torch.Tensor] = None) -> nat.PaOptions:
+            debug_timeline: Optional[torch.Tensor] = None,
+            even_split: int = 0) -> nat.PaOptions:
     """pa_options for these settings (any debug tensor selects the checked
     kernel variant).  min_context_hint: a lower bound on every context length
     (tokens) that the caller knows, 0 = none; it only steers the auto plan."""
@@ -122,6 +123,7 @@ def options(prefetch: int = -1, partition_blocks: int = 0, waves_per_wg: int = 0
     o.structure = int(structure)
     o.min_context_hint = int(min_context_hint)
     o.max_resident_wgs = int(max_resident_wgs)
+    o.even_split = int(even_split)
     if debug_gather_k is not None:
         _check(debug_gather_k, "debug_gather_k", torch.float16, 4)
         o.debug_gather_k = debug_gather_k.data_ptr()
@@ -187,7 +189,7 @@ class DecodeCall:
                  prefetch_distance, seq_order, structure, workspace, debug_gather_k,
                  debug_trace, debug_error_word, stream, noalloc: bool = False,
                  min_context_hint: int = 0, max_resident_wgs: int = 0,
-                 debug_timeline: Optional[torch.Tensor] = None):
+                 debug_timeline: Optional[torch.Tensor] = None, even_split: int = 0):
         if noalloc and (fp8 or workspace is not None):
             raise ValueError("the no-allocation call takes an fp16 cache and no workspace")
         self.name = ("paged_attn_decode_noalloc" if noalloc else
@@ -224,7 +226,8 @@ class DecodeCall:
         self._opts = options(prefetch, partition_blocks, waves_per_wg, prefetch_distance,
                              seq_order, structure, debug_gather_k, debug_trace,
                              debug_error_word, min_context_hint=min_context_hint,
-                             max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline)
+                             max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline,
+                      even_split=even_split)
         if debug_timeline is not None:
             check_debug_timeline(debug_timeline, nat.plan(self._shape, self._opts)["workgroups"])
         L = nat.lib()
@@ -280,13 +283,15 @@ def prepare_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                    debug_error_word: Optional[torch.Tensor] = None,
                    stream: Optional[torch.cuda.Stream] = None, min_context_hint: int = 0,
                    max_resident_wgs: int = 0,
-                   debug_timeline: Optional[torch.Tensor] = None) -> DecodeCall:
+                   debug_timeline: Optional[torch.Tensor] = None,
+                   even_split: int = 0) -> DecodeCall:
     """paged_attn_decode prepared for repeated calls on the same tensors."""
     return DecodeCall(False, q, k_cache, v_cache, block_tables, context_lens, scale, 1.0, 1.0,
                       out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
                       seq_order, structure, workspace, debug_gather_k, debug_trace,
                       debug_error_word, stream, min_context_hint=min_context_hint,
-                      max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline)
+                      max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline,
+                      even_split=even_split)
 
 
 def prepare_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -299,14 +304,16 @@ def prepare_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                            debug_error_word: Optional[torch.Tensor] = None,
                            stream: Optional[torch.cuda.Stream] = None,
                            min_context_hint: int = 0, max_resident_wgs: int = 0,
-                           debug_timeline: Optional[torch.Tensor] = None) -> DecodeCall:
+                           debug_timeline: Optional[torch.Tensor] = None,
+                           even_split: int = 0) -> DecodeCall:
     """paged_attn_decode_noalloc prepared for repeated calls; pass `out` to
     keep the calls free of allocation."""
     return DecodeCall(False, q, k_cache, v_cache, block_tables, context_lens, scale, 1.0, 1.0,
                       out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
                       seq_order, structure, None, debug_gather_k, debug_trace,
                       debug_error_word, stream, noalloc=True, min_context_hint=min_context_hint,
-                      max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline)
+                      max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline,
+                      even_split=even_split)
 
 
 def paged_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -332,7 +339,8 @@ def prepare_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                        debug_error_word: Optional[torch.Tensor] = None,
                        stream: Optional[torch.cuda.Stream] = None, min_context_hint: int = 0,
                        max_resident_wgs: int = 0,
-                       debug_timeline: Optional[torch.Tensor] = None) -> DecodeCall:
+                       debug_timeline: Optional[torch.Tensor] = None,
+                       even_split: int = 0) -> DecodeCall:
     """paged_attn_decode_fp8 prepared for repeated calls on the same tensors."""
     if k_cache.dtype == torch.float8_e4m3fn:
         k_cache = k_cache.view(torch.uint8)
@@ -342,7 +350,8 @@ def prepare_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                       v_scale, out, prefetch, partition_blocks, waves_per_wg, prefetch_distance,
                       seq_order, structure, workspace, debug_gather_k, debug_trace,
                       debug_error_word, stream, min_context_hint=min_context_hint,
-                      max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline)
+                      max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline,
+                      even_split=even_split)
 
 
 def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -356,7 +365,8 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       debug_error_word: Optional[torch.Tensor] = None,
                       stream: Optional[torch.cuda.Stream] = None, min_context_hint: int = 0,
                       max_resident_wgs: int = 0,
-                      debug_timeline: Optional[torch.Tensor] = None) -> torch.Tensor:
+                      debug_timeline: Optional[torch.Tensor] = None,
+                      even_split: int = 0) -> torch.Tensor:
     """One decode step of paged attention; returns out (fp16 [B, Hq, 128]).
 
     q [B, Hq, 128] fp16; k_cache [NB, Hkv, 16, 16, 8] fp16 (dim group, token, 8
@@ -370,7 +380,8 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                           debug_gather_k=debug_gather_k, debug_trace=debug_trace,
                           debug_error_word=debug_error_word, stream=stream,
                           min_context_hint=min_context_hint,
-                          max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline)()
+                          max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline,
+                      even_split=even_split)()
 
 
 def paged_attn_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -386,7 +397,8 @@ def paged_attn_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                           debug_error_word: Optional[torch.Tensor] = None,
                           stream: Optional[torch.cuda.Stream] = None,
                           min_context_hint: int = 0, max_resident_wgs: int = 0,
-                          debug_timeline: Optional[torch.Tensor] = None) -> torch.Tensor:
+                          debug_timeline: Optional[torch.Tensor] = None,
+                          even_split: int = 0) -> torch.Tensor:
     """Decode over an OCP E4M3 cache (uint8 or float8_e4m3fn); a cached value
     is decode(byte) * k_scale (K) or * v_scale (V).
 
@@ -402,7 +414,8 @@ def paged_attn_decode_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                               debug_gather_k=debug_gather_k, debug_trace=debug_trace,
                               debug_error_word=debug_error_word, stream=stream,
                               min_context_hint=min_context_hint,
-                              max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline)()
+                              max_resident_wgs=max_resident_wgs, debug_timeline=debug_timeline,
+                      even_split=even_split)()
 
 
 def pack_k(k_token_major: torch.Tensor, out: Optional[torch.Tensor] = None,

@@ -323,8 +323,13 @@ def mode_plans(w, kv8, hint):
         o.prefetch, o.prefetch_distance, o.structure = pf, dist, structure
         o.min_context_hint = hint
         p = nat.plan(sh, o, device=dev)
-        out[m] = (f"{p['waves_per_wg']} waves, cap {p['resident_wgs'] or '-'}, "
-                  f"{p['num_partitions']} partition(s)" + (" balanced" if p["balanced"] else ""))
+        if p["even_split"]:
+            out[m] = (f"{p['waves_per_wg']} waves, cap {p['resident_wgs']}, even split over "
+                      f"{p['workgroups']} shares")
+        else:
+            out[m] = (f"{p['waves_per_wg']} waves, cap {p['resident_wgs'] or '-'}, "
+                      f"{p['num_partitions']} partition(s)" +
+                      (" balanced" if p["balanced"] else ""))
     return out
 
 

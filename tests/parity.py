@@ -13,6 +13,7 @@ import torch
 
 from oracle import oracle as orc
 from paged_kv_cache_226_amd import inputs as gen
+from paged_kv_cache_226_amd import _native as nat
 from paged_kv_cache_226_amd import ops
 
 ABS_TOL = 2e-3
@@ -68,12 +69,16 @@ def same_plan(plan, **extra):
     look-ahead mode: a balanced split is reproduced by asking for it again
     (auto partitions and order with the same waves), a fixed one by its
     partition size and order.  A residency cap is kept (it changes no bits,
-    only how many work-groups share a CU)."""
-    if plan["balanced"]:
-        kw = dict(partition_blocks=0, waves_per_wg=plan["waves_per_wg"], seq_order=0)
+    only how many work-groups share a CU).  An even split is asked for again
+    with the same waves and residency (the shares follow from them)."""
+    if plan["even_split"]:
+        kw = dict(even_split=nat.EVEN_SPLIT_ON, waves_per_wg=plan["waves_per_wg"])
+    elif plan["balanced"]:
+        kw = dict(partition_blocks=0, waves_per_wg=plan["waves_per_wg"], seq_order=0,
+                  even_split=nat.EVEN_SPLIT_OFF)
     else:
         kw = dict(partition_blocks=plan["partition_blocks"], waves_per_wg=plan["waves_per_wg"],
-                  seq_order=plan["seq_order"])
+                  seq_order=plan["seq_order"], even_split=nat.EVEN_SPLIT_OFF)
     kw["max_resident_wgs"] = plan["resident_wgs"]
     kw.update(extra)
     return kw

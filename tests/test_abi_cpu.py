@@ -179,19 +179,27 @@ def test_noalloc_validation_codes(native_lib):
 
 def test_plans_of_the_workloads(native_lib):
     from paged_kv_cache_226_amd import inputs as gen
-    # (partitions, waves) of the auto plan
-    # (partitions, waves, balanced) of the auto plan; under the balanced
-    # split the partitions are the most one sequence can get
-    expect = {"tiny": (1, 8, 0), "llama2_7b": (1, 4, 0), "llama3_8b": (1, 8, 0),
-              "qwen25_7b": (1, 4, 0), "qwen25_14b": (1, 4, 0), "llama3_8b_tp2": (1, 8, 0),
-              "llama3_8b_tp4": (8, 8, 1), "llama3_8b_tp8": (8, 8, 1),
-              "qwen25_14b_tp2": (1, 8, 0), "qwen25_14b_tp4": (1, 8, 0),
-              "qwen25_14b_tp8": (8, 8, 1)}
+    # (partitions, waves, balanced, even split) of the auto plan without a
+    # hint; under the balanced split the partitions are the most one
+    # sequence can get
+    expect = {"tiny": (1, 8, 0, 0), "llama2_7b": (1, 4, 0, 0), "llama3_8b": (1, 8, 0, 0),
+              "qwen25_7b": (1, 4, 0, 0), "qwen25_14b": (1, 4, 0, 0),
+              "llama3_8b_tp2": (1, 2, 0, 1), "llama3_8b_tp4": (8, 8, 1, 0),
+              "llama3_8b_tp8": (8, 8, 1, 0), "qwen25_14b_tp2": (1, 8, 0, 0),
+              "qwen25_14b_tp4": (1, 2, 0, 1), "qwen25_14b_tp8": (8, 8, 1, 0)}
     for name, w in gen.WORKLOADS.items():
         MB = w.max_blocks_per_seq or max(-(-c // 16) for c in w.context_lens)
         nb = w.pool_blocks or 1
         p = nat.plan(nat.make_shape(w.num_seqs, w.num_q_heads, w.num_kv_heads, MB, nb))
-        assert (p["num_partitions"], p["waves_per_wg"], p["balanced"]) == expect[name], name
+        got = (p["num_partitions"], p["waves_per_wg"], p["balanced"], p["even_split"])
+        assert got == expect[name], name
+        if p["even_split"]:
+            # one share per CU, two records of g rows per share and one
+            # piece record per (sequence, KV head)
+            g = w.num_q_heads // w.num_kv_heads
+            assert p["workgroups"] == 256 and p["resident_wgs"] == 1
+            assert p["workspace_bytes"] == (2 * 256 * g * 130 + 2 * w.num_seqs * w.num_kv_heads) * 4
+            continue
         if p["balanced"]:
             # one grid row per CU and KV head (256 CUs), the smallest size 16
             assert p["workgroups"] == 256 // w.num_kv_heads * w.num_kv_heads
@@ -287,7 +295,9 @@ def test_balanced_split_plan(native_lib, B, Hkv, MB, cus, rows, P):
     of the smallest size; at most 8 unless they hold 64 blocks or more; at
     most rows - B + 1), and the workspace (partials, then partition counts)."""
     dev = dict(MI355X, compute_units=cus)
-    p = nat.plan(nat.make_shape(B, 4 * Hkv, Hkv, MB, 1), device=dev)
+    o = nat.default_options()
+    o.even_split = nat.EVEN_SPLIT_OFF  # (200 x 1 x 1024 blocks would take the even split)
+    p = nat.plan(nat.make_shape(B, 4 * Hkv, Hkv, MB, 1), o, device=dev)
     assert p["balanced"] == 1
     assert (p["workgroups"], p["num_partitions"], p["partition_blocks"]) == (rows * Hkv, P, 16)
     assert p["seq_order"] == nat.ORDER_NATURAL and p["waves_per_wg"] == 8
@@ -432,11 +442,18 @@ def test_plan_rules_follow_the_cu_count(native_lib, cus):
     one partition per sequence iff there are at least as many (sequence, KV
     head) units as CUs; 8 waves for such unsplit long tables while there are
     fewer than three units per CU; longest-first order iff the grid holds
-    more work-groups than the CUs keep resident (three 4-wave ones each)."""
+    more work-groups than the CUs keep resident (three 4-wave ones each);
+    the even split (one share per CU, 2 waves) for more than half and fewer
+    than twice as many units as CUs over a long table."""
     dev = dict(MI355X, compute_units=cus)
     for B in (1, 2, 4, 8, 16, 32, 64, 96, 128, 200, 256):
         units = B * 8
         p = nat.plan(nat.make_shape(B, 32, 8, 512, 1), device=dev)
+        even = B >= 2 and cus < 2 * units < 4 * cus
+        assert p["even_split"] == even, (B, p)
+        if even:
+            assert (p["workgroups"], p["waves_per_wg"], p["num_partitions"]) == (cus, 2, 1)
+            continue
         assert (p["num_partitions"] == 1) == (units >= cus), (B, p)
         if units >= cus:
             assert p["waves_per_wg"] == (8 if units < 3 * cus else 4), (B, p)
@@ -524,7 +541,7 @@ def test_streaming_shape_for_uniform_contexts(native_lib, B, Hq, Hkv, kv, want):
         assert want[1] * (share + 1024) <= 163840 < (want[1] + 1) * (share + 256)
     # the hint is the only difference from the default plan
     base = nat.plan(sh, device=MI355X)
-    assert base["resident_wgs"] == 0
+    assert base["resident_wgs"] == 0 or base["even_split"] == 1
     assert (base["waves_per_wg"], base["resident_wgs"]) != want
 
 

@@ -1,0 +1,175 @@
+"""The even split's bookkeeping, modelled on the host: which work-group
+walks which piece of which (sequence, KV head) unit, which workspace record
+each piece goes to, and where the merge looks for them.  The model follows
+the kernel's integer arithmetic step by step (shares c T / S, the unit
+holding a share's first block, the record rule, the piece count from the
+share of the unit's last block).  Checked on random ragged batches: every
+block of every unit is walked exactly once; each record is written at most
+once; the merge of a split unit finds exactly that unit's pieces in order,
+plus only empty records between them; whole units need no merge.  Plans
+that take the even split are checked against the ABI (grid, workspace)."""
+import random
+
+import pytest
+
+from paged_kv_cache_226_amd import _native as nat
+
+MI355X = dict(compute_units=256, lds_bytes_per_cu=163840, lds_bytes_per_workgroup=163840)
+
+
+def shares_walk(nb, Hkv, S):
+    """The pieces each share walks, (c, b, kvh, s, e, record) in order, the
+    empty records, and the per-unit (record, pieces) written.  Units are
+    KV-head-major: head kvh's sequences fill [kvh N, (kvh + 1) N)."""
+    B = len(nb)
+    N = sum(nb)
+    T = N * Hkv
+    starts = []
+    acc = 0
+    for n in nb:
+        starts.append(acc)
+        acc += n
+    pieces, empty, unit_rec = [], [], {}
+    for c in range(S):
+        X, Y = c * T // S, (c + 1) * T // S
+        if X == Y:
+            empty.append(2 * c)
+            continue
+        kvh = X // N
+        xr = X - kvh * N
+        b = max(i for i in range(B) if starts[i] <= xr and nb[i] > 0)
+        off = xr - starts[b]
+        nbb = nb[b]
+        pos, first = X, True
+        while True:
+            seg = min(nbb - off, Y - pos)
+            rec = 2 * c if first else 2 * c + 1
+            whole = off == 0 and seg == nbb
+            if off == 0:
+                last = pos + nbb - 1
+                c1 = ((last + 1) * S - 1) // T
+                unit_rec[(b, kvh)] = (rec, c1 - c + 1)
+            pieces.append((c, b, kvh, off, off + seg, None if whole else rec))
+            pos += seg
+            if pos >= Y:
+                break
+            first = False
+            off = 0
+            n = 0
+            while True:
+                b += 1
+                if b >= B:
+                    b = 0
+                    kvh += 1
+                    if kvh >= Hkv:
+                        break
+                n = nb[b]
+                if n > 0:
+                    break
+            assert kvh < Hkv and n > 0
+            nbb = n
+    return T, pieces, empty, unit_rec
+
+
+def check(nb, Hkv, S):
+    T, pieces, empty, unit_rec = shares_walk(nb, Hkv, S)
+    covered = {}
+    written = {}
+    for c, b, kvh, s, e, rec in pieces:
+        for j in range(s, e):
+            assert (b, kvh, j) not in covered
+            covered[(b, kvh, j)] = c
+        if rec is not None:
+            assert 0 <= rec < 2 * S and rec not in written
+            written[rec] = (b, kvh, s, e)
+    for r in empty:
+        assert r not in written
+        written[r] = None
+    assert len(covered) == T
+    for b, n in enumerate(nb):
+        for kvh in range(Hkv):
+            if n == 0:
+                assert (b, kvh) not in unit_rec
+                continue
+            rec0, npc = unit_rec[(b, kvh)]
+            c0 = rec0 // 2
+            recs = [rec0] + [2 * (c0 + j) for j in range(1, npc)]
+            assert all(0 <= r < 2 * S for r in recs)
+            got = [written.get(r, "missing") for r in recs]
+            if npc == 1:  # walked whole by one share, written directly
+                assert [pc for pc in pieces if pc[1:3] == (b, kvh)] == \
+                    [(covered[(b, kvh, 0)], b, kvh, 0, n, None)]
+                continue
+            assert "missing" not in got
+            real = [g for g in got if g is not None]
+            assert all(g[:2] == (b, kvh) for g in real)
+            # the pieces in order cover [0, n) exactly
+            edge = 0
+            for g in real:
+                assert g[2] == edge
+                edge = g[3]
+            assert edge == n
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_every_block_once_and_the_merge_finds_each_piece(seed):
+    rng = random.Random(seed)
+    B = rng.choice([1, 2, 3, 7, 64, 200, 256])
+    Hkv = rng.choice([1, 2, 8])
+    MB = rng.choice([1, 3, 64, 512, 1024])
+    nb = [rng.choice([0, rng.randint(1, MB), MB]) for _ in range(B)]
+    if not any(nb):
+        nb[rng.randrange(B)] = 1
+    S = rng.choice([1, 7, 256, 512, 2048])
+    check(nb, Hkv, S)
+
+
+def test_fewer_blocks_than_shares_and_one_long_unit():
+    check([3], 1, 256)           # most shares empty
+    check([1024], 1, 256)        # one unit in 256 pieces
+    check([0, 0, 5, 0], 2, 256)  # empty sequences around the only one
+    check([512] * 64, 8, 256)    # whole units, no merge
+
+
+def test_plans_that_take_the_even_split(native_lib):
+    o = nat.default_options()
+    o.even_split = nat.EVEN_SPLIT_ON
+    sh = nat.make_shape(64, 32, 8, 512, 64 * 512)
+    p = nat.plan(sh, o, device=MI355X)
+    assert p["even_split"] == 1 and p["workgroups"] == 256 and p["resident_wgs"] == 1
+    assert p["num_partitions"] == 1 and p["seq_order"] == nat.ORDER_NATURAL
+    assert p["waves_per_wg"] == 2  # the register look-ahead: 2 blocks per wave
+    assert p["workspace_bytes"] == (2 * 256 * 4 * 130 + 2 * 64 * 8) * 4
+    o.max_resident_wgs, o.waves_per_wg, o.prefetch = 2, 1, nat.PREFETCH_OFF
+    p = nat.plan(sh, o, device=MI355X)
+    assert (p["workgroups"], p["waves_per_wg"], p["resident_wgs"]) == (512, 1, 2)
+    o = nat.default_options()
+    o.even_split, o.prefetch = nat.EVEN_SPLIT_ON, nat.PREFETCH_OFF
+    assert nat.plan(sh, o, device=MI355X)["waves_per_wg"] == 4
+    sh8 = nat.make_shape(64, 32, 8, 512, 64 * 512, kv_dtype=nat.KV_E4M3)
+    o.prefetch = -1
+    assert nat.plan(sh8, o, device=MI355X)["waves_per_wg"] == 2  # 3 E4M3 blocks per wave
+    # off and auto keep the other plans
+    o.even_split = nat.EVEN_SPLIT_OFF
+    assert nat.plan(sh, o, device=MI355X)["even_split"] == 0
+
+
+@pytest.mark.parametrize("why", ["two loop", "partition size", "batch", "table"])
+def test_where_the_even_split_does_not_apply(native_lib, why):
+    B, MB = {"batch": 257, "table": 1025}.get(why, 64), 1025 if why == "table" else 64
+    sh = nat.make_shape(B, 8, 8, MB, B * MB)
+    o = nat.default_options()
+    o.even_split = nat.EVEN_SPLIT_ON
+    if why == "two loop":
+        o.structure = nat.STRUCTURE_TWO_LOOP
+    if why == "partition size":
+        o.partition_blocks = 16
+    with pytest.raises(ValueError, match="unsupported"):
+        nat.plan(sh, o, device=MI355X)
+
+
+def test_invalid_even_split_value(native_lib):
+    o = nat.default_options()
+    o.even_split = 3
+    with pytest.raises(ValueError, match="invalid argument"):
+        nat.plan(nat.make_shape(4, 8, 8, 16, 64), o, device=MI355X)

@@ -2,7 +2,9 @@
 device from the context lengths.
 
 Auto partitions of a batch with 2..256 sequences and fewer (sequence, KV
-head) pairs than CUs use it.  Checked here: the output against the fp64
+head) pairs than CUs use it, unless the even split takes the batch (more
+than half as many pairs as CUs over a long table): these tests turn that
+off where their batches would take it.  Checked here: the output against the fp64
 oracle, the ranges each work-group walked against the split model
 (oracle/schedule.py), bitwise equality across look-ahead modes on the same
 plan, the per-sequence partition cap (many empty sequences and one long
@@ -15,6 +17,7 @@ import torch
 
 from oracle import oracle as orc
 from oracle import schedule as sch
+from paged_kv_cache_226_amd import _native as nat
 from paged_kv_cache_226_amd import inputs as gen
 from paged_kv_cache_226_amd import ops
 
@@ -23,6 +26,7 @@ from parity import assert_close, bits, oracle, run, same_plan, to_device
 pytestmark = pytest.mark.gpu
 
 MODES = [0, 1, 2, 3, 4]
+OFF = dict(even_split=nat.EVEN_SPLIT_OFF)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -37,7 +41,7 @@ def check_trace(x, dev, plan, **kw):
     B, MB = x.block_tables.shape
     Hkv = x.k_cache.shape[1]
     trace = torch.full((B, Hkv, MB, 2), -1, dtype=torch.int32, device="cuda")
-    run(x, dev, debug_trace=trace, **kw)
+    run(x, dev, debug_trace=trace, **OFF, **kw)
     tr = trace.cpu().numpy()
     W = plan["waves_per_wg"]
     nbs = [-(-max(int(L), 0) // 16) for L in x.context_lens]
@@ -75,12 +79,12 @@ def test_balanced_split_against_the_oracle_and_the_split_model(case):
     x = gen.make_case(B, Hq, Hkv, [int(c) for c in lens], seed=600 + case, extra_pool_blocks=3,
                       poison=True)
     dev = to_device(x)
-    plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"])
+    plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], **OFF)
     assert plan["balanced"] == 1 and plan["num_partitions"] > 1
     ref = oracle(x)
     outs = {}
     for pf in MODES:
-        p = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], prefetch=pf)
+        p = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], prefetch=pf, **OFF)
         assert p["balanced"] == 1
         outs[pf] = run(x, dev, prefetch=pf, **same_plan(plan))
         assert_close(outs[pf], ref, f"case {case} mode {pf}")
@@ -94,7 +98,7 @@ def test_one_long_sequence_among_empty_ones_stays_within_the_workspace():
     lens = [0] * 199 + [16384]
     x = gen.make_case(200, 8, 1, lens, seed=640, extra_pool_blocks=2, poison=True)
     dev = to_device(x)
-    plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"])
+    plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], **OFF)
     assert plan["balanced"] == 1
     nbs = [-(-c // 16) for c in lens]
     size, parts = sch.balanced_split(nbs, plan["partition_blocks"], 1 << 16,
@@ -103,9 +107,10 @@ def test_one_long_sequence_among_empty_ones_stays_within_the_workspace():
     assert size > plan["partition_blocks"] and len(parts) <= plan["num_partitions"]
     assert -(-1024 // plan["partition_blocks"]) > plan["num_partitions"]
     # fill the workspace with NaN: anything read past what was written shows
-    ws = torch.full((ops.workspace_bytes(dev["q"], dev["k_cache"], dev["block_tables"]) // 4,),
+    ws = torch.full((ops.workspace_bytes(dev["q"], dev["k_cache"], dev["block_tables"],
+                                         **OFF) // 4,),
                     float("nan"), dtype=torch.float32, device="cuda")
-    out = run(x, dev, workspace=ws)
+    out = run(x, dev, workspace=ws, **OFF)
     assert_close(out, oracle(x), "one long sequence")
     check_trace(x, dev, plan)
 

@@ -37,14 +37,15 @@ options = st.tuples(
     st.sampled_from([0, 0, 1, 2]),                         # seq_order
     st.sampled_from([0, 0, 0, 1]),                         # structure
     st.sampled_from(["none", "none", "full", "7/8", "under", "neg"]),  # min_context_hint
-    st.sampled_from([0, 0, 0, 0, 1, 2, 3, 4, 5, 7, 8, 9, -1]))  # max_resident_wgs (9, -1 invalid)
+    st.sampled_from([0, 0, 0, 0, 1, 2, 3, 4, 5, 7, 8, 9, -1]),  # max_resident_wgs (9, -1 invalid)
+    st.sampled_from([0, 0, 0, 1, 2, 3]))    # even_split (3 invalid)
 
 
 @settings(max_examples=600, deadline=None)
 @given(shapes, options)
 def test_every_accepted_plan_is_launchable(shape_t, opt_t):
     B, Hkv, g, MB, kv = shape_t
-    pf, pb, waves, dist, order, structure, hint_kind, cap = opt_t
+    pf, pb, waves, dist, order, structure, hint_kind, cap, even = opt_t
     hint = {"none": 0, "full": MB * 16, "7/8": MB * 16 * 7 // 8 + 1,
             "under": max(MB * 16 * 7 // 8 - 1, 1), "neg": -5}[hint_kind]
     sh = nat.make_shape(B, g * Hkv, Hkv, MB, 10 * MB * B, kv_dtype=kv)
@@ -52,11 +53,14 @@ def test_every_accepted_plan_is_launchable(shape_t, opt_t):
     o.prefetch, o.partition_blocks, o.waves_per_wg = pf, pb, waves
     o.prefetch_distance, o.seq_order, o.structure = dist, order, structure
     o.min_context_hint, o.max_resident_wgs = hint, cap
+    o.even_split = even
     rc, p = raw_plan(sh, o)
     assert rc in (nat.PA_OK, nat.PA_ERR_INVALID_ARG, nat.PA_ERR_UNSUPPORTED)
     must_refuse = (g > 16 or pf > 4 or waves in (3, 16) or pb > 1024 or dist > 63
                    or (order == nat.ORDER_LONGEST_FIRST and B > nat.RANK_MAX_SEQS)
-                   or hint < 0 or cap < 0 or cap > 8)
+                   or hint < 0 or cap < 0 or cap > 8 or even > 2
+                   or (even == nat.EVEN_SPLIT_ON and (structure == nat.STRUCTURE_TWO_LOOP
+                                                      or pb != 0 or B > 256 or MB > 1024)))
     if must_refuse:
         assert rc != nat.PA_OK
     if rc != nat.PA_OK:
@@ -64,6 +68,26 @@ def test_every_accepted_plan_is_launchable(shape_t, opt_t):
     PB, P = p["partition_blocks"], p["num_partitions"]
     W = p["waves_per_wg"]
     assert W in (1, 2, 4, 8)
+    if p["even_split"]:
+        # one share per CU and cap; by itself only for fp16, all-auto
+        # options, no uniform hint, C/2 < units < 2C and 256..1024 blocks
+        assert even != nat.EVEN_SPLIT_OFF
+        if even == nat.EVEN_SPLIT_AUTO:
+            assert kv == nat.KV_F16 and pb == 0 and waves == 0 and cap == 0 and order == 0
+            assert structure == 0 and hint_kind not in ("full", "7/8") and pf in (-1, 0, 2, 3)
+            assert 128 < B * Hkv < 512 and 256 <= MB <= 1024 and 2 <= B <= 256
+        R = p["resident_wgs"]
+        assert R >= 1 and p["workgroups"] == 256 * R and P == 1 and PB == MB
+        assert p["balanced"] == 0 and p["seqs_per_wg"] == 1
+        assert p["seq_order"] == nat.ORDER_NATURAL
+        want = (2 * 256 * R * g * 130 + 2 * B * Hkv) * 4
+        assert p["workspace_bytes"] == want
+        assert nat.lib().paged_attn_workspace_size(ctypes.byref(sh), ctypes.byref(o)) == want
+        assert p["lds_bytes"] + 1024 <= 163840
+        if waves:
+            assert W == waves
+        return
+    assert even != nat.EVEN_SPLIT_ON
     if p["balanced"]:
         # only for auto partitions and order of a split batch of 2..256
         # sequences; rows per KV head cover every sequence's largest-size
@@ -123,7 +147,7 @@ def test_every_accepted_plan_is_launchable(shape_t, opt_t):
     o0 = nat.default_options()
     o0.prefetch, o0.partition_blocks, o0.waves_per_wg = pf, pb, waves
     o0.prefetch_distance, o0.seq_order, o0.structure = dist, order, structure
-    o0.max_resident_wgs = cap
+    o0.max_resident_wgs, o0.even_split = cap, even
     rc0, p0 = raw_plan(sh, o0)
     assert rc0 == nat.PA_OK
     for k in ("prefetch", "prefetch_distance", "structure"):
