@@ -142,7 +142,14 @@ enum pa_structure {
 
 /* pa_options.even_split */
 enum pa_even_split {
-    PA_EVEN_SPLIT_AUTO = 0,   /* the plan's choice */
+    PA_EVEN_SPLIT_AUTO = 0,   /* the plan's choice: the even split for more
+                                 than CUs / 2 and fewer than 2 x CUs
+                                 (sequence, KV head) units over a table of
+                                 256..1024 blocks, with waves, partitions,
+                                 order and residency left to the plan, the
+                                 look-ahead off or in registers, and no
+                                 min_context_hint that says every context
+                                 fills the table */
     PA_EVEN_SPLIT_OFF = 1,
     PA_EVEN_SPLIT_ON = 2      /* PA_ERR_UNSUPPORTED where it does not apply */
 };

@@ -262,7 +262,7 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   // VGPRs, still 3 waves per SIMD, for the registers) measured up to 10 %
   // faster on a ragged batch.
   const bool ring = pf == PA_PREFETCH_REG || pf == PA_PREFETCH_LDS;
-  const int dist = o->prefetch_distance > 0 ? o->prefetch_distance : (kv8 && ring ? 2 : 1);
+  int dist = o->prefetch_distance > 0 ? o->prefetch_distance : (kv8 && ring ? 2 : 1);
   // the register and LDS rings hold at most two blocks ahead
   if (ring && dist > 2) return PA_ERR_UNSUPPORTED;
   if (pf == PA_PREFETCH_LDS && two) return PA_ERR_UNSUPPORTED;
@@ -316,11 +316,9 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
       (int64_t)MB * units >= (int64_t)kStreamSplitBlocks * dv.cus && in_flight <= 2)
     waves = in_flight == 1 ? 4 : 2;
   // The even split (pa_options.even_split): one share of the batch's
-  // blocks per work-group, S = CUs x the residency cap (1 unless asked),
-  // with the waves that keep about 4 fp16 (8 E4M3) blocks in flight per
-  // work-group.
+  // blocks per work-group, S = CUs x the residency cap (1 unless asked).
   //
-  // The plan takes it by itself for an fp16 cache with more than C / 2 and
+  // The plan takes it by itself for a batch with more than C / 2 and
   // fewer than 2 C units and 256..1024 table blocks, unless the hint says
   // every context fills the table: the fixed grid then leaves CUs idle
   // (a second round of fewer units than CUs, or ragged units one per CU),
@@ -328,15 +326,17 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   // (us, the plan before -> the even split): ragged GQA 32/8, 48 x 1..8K
   // (1.5 units per CU) 175.5 -> 134.1; 24 x 512..8K 85.5 -> 71.6; llama3_8b
   // TP2 shard (64 x 512..8K, 4 KV heads) 106.0 -> 96.6; 32 x 512..8K 106.3
-  // -> 95.8; uniform MHA 8 x 4K 80.5 -> 78.3.  It lost on shorter tables
-  // (MHA 8 x 1K +14 %, GQA 32 x 1..2K +17 %), at C / 2 units or fewer (+5
-  // % on two of three ragged batches) and, with these waves, over E4M3.
+  // -> 95.8; uniform MHA 8 x 4K 80.5 -> 78.3.  E4M3: llama3_8b TP2 59.5 ->
+  // 53.9, 48 x 1..8K 96.3 -> 74.8, 24 x 512..8K 51.6 -> 41.7 (a uniform
+  // GQA 40/8 32 x 8K without the hint lost 4 %: 83.0 -> 86.3).  It lost on
+  // shorter tables (MHA 8 x 1K +14 %, GQA 32 x 1..2K +17 %) and at C / 2
+  // units or fewer (+5 % on two of three ragged batches).
   if (o->even_split < PA_EVEN_SPLIT_AUTO || o->even_split > PA_EVEN_SPLIT_ON)
     return PA_ERR_INVALID_ARG;
   const bool uniform_hint = o->min_context_hint > 0 && (int64_t)o->min_context_hint * 8 >=
                                                            (int64_t)MB * PA_BLOCK_SIZE * 7;
   const bool even_auto =
-      o->even_split == PA_EVEN_SPLIT_AUTO && !kv8 && !two && !uniform_hint && in_flight > 0 &&
+      o->even_split == PA_EVEN_SPLIT_AUTO && !two && !uniform_hint && in_flight > 0 &&
       o->partition_blocks == 0 && o->waves_per_wg == 0 && o->max_resident_wgs == 0 &&
       o->seq_order == PA_ORDER_AUTO && B >= 2 && B <= PA_RANK_MAX_SEQS &&
       MB >= kEvenMinBlocks && MB <= kMaxPartitionBlocks && 2 * units > dv.cus &&
@@ -347,12 +347,13 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
     if (two || o->partition_blocks != 0 || B > PA_RANK_MAX_SEQS || MB > kMaxPartitionBlocks ||
         (int64_t)B * MB * Hkv > INT32_MAX / 2)
       return PA_ERR_UNSUPPORTED;
+    // fp16: 2 waves one block ahead, or 4 without the look-ahead (4 blocks
+    // per work-group); E4M3: 8 waves, the register look-ahead one block
+    // ahead unless asked (us, over 2 ahead or 2-4 waves: llama3_8b TP2
+    // 55.5 -> 53.9, 48 x 1..8K 77.4 -> 74.8, 32 x 512..8K 55.9 -> 54.1)
+    if (kv8 && pf == PA_PREFETCH_REG && o->prefetch_distance == 0) dist = 1;
     waves = o->waves_per_wg;
-    if (waves == 0) {
-      const int per_wave = in_flight > 0 ? in_flight : 1;
-      const int want = (kv8 ? 8 : 4) / per_wave;
-      waves = want >= 8 ? 8 : want >= 4 ? 4 : want >= 2 ? 2 : 1;
-    }
+    if (waves == 0) waves = kv8 ? 8 : in_flight == 1 ? 4 : 2;
     cap = o->max_resident_wgs > 0 ? o->max_resident_wgs : 1;
     order = PA_ORDER_NATURAL;
     rank = false;

@@ -146,9 +146,17 @@ def test_plans_that_take_the_even_split(native_lib):
     o = nat.default_options()
     o.even_split, o.prefetch = nat.EVEN_SPLIT_ON, nat.PREFETCH_OFF
     assert nat.plan(sh, o, device=MI355X)["waves_per_wg"] == 4
+    # E4M3: 8 waves, one block ahead unless asked; by itself too
     sh8 = nat.make_shape(64, 32, 8, 512, 64 * 512, kv_dtype=nat.KV_E4M3)
     o.prefetch = -1
-    assert nat.plan(sh8, o, device=MI355X)["waves_per_wg"] == 2  # 3 E4M3 blocks per wave
+    p8 = nat.plan(sh8, o, device=MI355X)
+    assert (p8["waves_per_wg"], p8["prefetch_distance"]) == (8, 1)
+    half = nat.make_shape(32, 32, 8, 512, 32 * 512, kv_dtype=nat.KV_E4M3)  # 256 units
+    assert nat.plan(half, device=MI355X)["even_split"] == 1
+    assert nat.plan(sh8, device=MI355X)["even_split"] == 0  # 512 units: 2 per CU
+    o.prefetch_distance = 2
+    assert nat.plan(sh8, o, device=MI355X)["prefetch_distance"] == 2
+    o.prefetch_distance = 0
     # off and auto keep the other plans
     o.even_split = nat.EVEN_SPLIT_OFF
     assert nat.plan(sh, o, device=MI355X)["even_split"] == 0

@@ -88,18 +88,31 @@ def test_even_split_twice_with_fewer_blocks():
         assert_close(got, oracle(x), "even split, reused workspace")
 
 
-def test_even_split_over_an_e4m3_cache():
-    x8 = gen.to_fp8(gen.make_case(64, 32, 8, None, seed=930, ctx_range=(1, 6000)))
+@pytest.mark.parametrize("B,auto", [(64, False), (24, True)])
+def test_even_split_over_an_e4m3_cache(B, auto):
+    """Asked for (512 units), and taken by the auto plan (192 units over 256
+    table blocks: 8 waves, one block ahead)."""
+    x8 = gen.to_fp8(gen.make_case(B, 32, 8, None, seed=930 + B, ctx_range=(1, 4096),
+                                  max_blocks_per_seq=256))
     d = {k: torch.from_numpy(getattr(x8, k)).cuda() for k in ("q", "block_tables", "context_lens")}
     d["k_cache"] = torch.from_numpy(gen.pack_k_fp8(x8.k8)).cuda()
     d["v_cache"] = torch.from_numpy(x8.v8).cuda()
-    dec = lambda **kw: ops.paged_attn_decode_fp8(
+    kw = {} if auto else dict(even_split=EVEN)
+    plan = ops.plan(d["q"], d["k_cache"], d["block_tables"], **kw)
+    assert plan["even_split"] == 1
+    if auto and nat.device_info()["compute_units"] == 256:
+        assert (plan["waves_per_wg"], plan["prefetch_distance"]) == (8, 1)
+    dec = lambda **k2: ops.paged_attn_decode_fp8(
         d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"], x8.scale,
-        x8.k_scale, x8.v_scale, even_split=EVEN, **kw).cpu().numpy()
+        x8.k_scale, x8.v_scale, **kw, **k2).cpu().numpy()
     got = dec()
     ref = orc.paged_attention_fp8_f64(x8.q, x8.k8, x8.v8, x8.block_tables, x8.context_lens,
                                       x8.scale, x8.k_scale, x8.v_scale)
     assert_close(got, ref, "e4m3 even split")
+    # the look-ahead two blocks ahead on the same shares: the same bits
+    two = dec(prefetch=nat.PREFETCH_REG, prefetch_distance=2, even_split=EVEN,
+              waves_per_wg=plan["waves_per_wg"]) if auto else dec(prefetch_distance=2)
+    assert np.array_equal(bits(two), bits(got))
 
 
 def test_even_split_without_allocation_matches_the_workspace_call():

@@ -73,7 +73,7 @@ def test_every_accepted_plan_is_launchable(shape_t, opt_t):
         # options, no uniform hint, C/2 < units < 2C and 256..1024 blocks
         assert even != nat.EVEN_SPLIT_OFF
         if even == nat.EVEN_SPLIT_AUTO:
-            assert kv == nat.KV_F16 and pb == 0 and waves == 0 and cap == 0 and order == 0
+            assert pb == 0 and waves == 0 and cap == 0 and order == 0
             assert structure == 0 and hint_kind not in ("full", "7/8") and pf in (-1, 0, 2, 3)
             assert 128 < B * Hkv < 512 and 256 <= MB <= 1024 and 2 <= B <= 256
         R = p["resident_wgs"]
@@ -150,7 +150,8 @@ def test_every_accepted_plan_is_launchable(shape_t, opt_t):
     o0.max_resident_wgs, o0.even_split = cap, even
     rc0, p0 = raw_plan(sh, o0)
     assert rc0 == nat.PA_OK
-    for k in ("prefetch", "prefetch_distance", "structure"):
+    # (without the hint an E4M3 batch may take the even split, one block ahead)
+    for k in ("prefetch", "structure") + (() if p0["even_split"] else ("prefetch_distance",)):
         assert p[k] == p0[k], k
     if hint_kind in ("none", "under"):
         assert p == p0
