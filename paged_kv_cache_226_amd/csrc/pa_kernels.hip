@@ -1124,6 +1124,18 @@ __device__ __forceinline__ void even_walk(const DecodeArgs& a, int tab_tokens, i
   int nbb = pick(nb, b);
   int pos = X;
   bool first = true;
+  // the next unit with blocks after (b, kvh), KV-head-major; kvh2 == Hkv if none
+  auto next_unit = [&](int& b2, int& kvh2) {
+    int n = 0;
+    while (true) {
+      if (++b2 >= a.B) {
+        b2 = 0;
+        if (++kvh2 >= Hkv) return 0;
+      }
+      n = pick(nb, b2);
+      if (n > 0) return n;
+    }
+  };
   while (true) {
     const int seg = nbb - off < Y - pos ? nbb - off : Y - pos;
     walk_range<PF, DBG, KV8>(a, b, kvh, pick(cx, b), off, off + seg, bt_s, merge_s);
@@ -1156,23 +1168,17 @@ __device__ __forceinline__ void even_walk(const DecodeArgs& a, int tab_tokens, i
     // the next unit: the next sequence with blocks, else the next KV head's
     // first one (one exists: pos < Y <= T)
     off = 0;
-    int n = 0;
-    while (true) {
-      if (++b >= a.B) {
-        b = 0;
-        if (++kvh >= Hkv) break;
-      }
-      n = pick(nb, b);
-      if (n > 0) break;
-    }
+    const int n = next_unit(b, kvh);
     if (kvh >= Hkv) break;  // not reached
     nbb = n;
     __syncthreads();  // the merge records above are read before the next walk
   }
 }
 
-// TWO selects the two-loop walk (fp16, no debug outputs).
-template <int PF, bool DBG, bool KV8, bool TWO = false>
+// TWO selects the two-loop walk (fp16, no debug outputs), EVEN the even
+// split (its own instances, so that its registers do not count against the
+// other plans' occupancy).
+template <int PF, bool DBG, bool KV8, bool TWO = false, bool EVEN = false>
 __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   int32_t* bt_s = reinterpret_cast<int32_t*>(smem_raw);
@@ -1212,8 +1218,8 @@ __global__ void __launch_bounds__(512) pa_decode_kernel(const DecodeArgs a) {
   const int tid = threadIdx.x;
   const int W = blockDim.x / kWave;
   const int tab_tokens = a.MB * kT;
-  if (a.even) {
-    if constexpr (!TWO) even_walk<PF, DBG, KV8>(a, tab_tokens, bt_s, merge_s);
+  if constexpr (EVEN) {
+    even_walk<PF, DBG, KV8>(a, tab_tokens, bt_s, merge_s);
     stamp_end();
     return;
   }
@@ -1513,11 +1519,17 @@ __global__ void __launch_bounds__(256) stream_read_kernel(const u32x4* __restric
 // ---------------------------------------------------------------------------
 // Launchers.
 
-template <int PF, bool DBG, bool KV8, bool TWO = false>
+template <int PF, bool DBG, bool KV8, bool TWO = false, bool EVEN = false>
 static hipError_t launch_decode_t(const DecodeArgs& a, dim3 grid, dim3 block, size_t lds,
                                   hipStream_t st) {
-  hipLaunchKernelGGL((pa_decode_kernel<PF, DBG, KV8, TWO>), grid, block, lds, st, a);
+  hipLaunchKernelGGL((pa_decode_kernel<PF, DBG, KV8, TWO, EVEN>), grid, block, lds, st, a);
   return hipGetLastError();
+}
+
+template <int PF, bool DBG, bool KV8>
+static hipError_t launch_even_t(const DecodeArgs& a, dim3 grid, dim3 block, size_t lds,
+                                hipStream_t st) {
+  return launch_decode_t<PF, DBG, KV8, false, true>(a, grid, block, lds, st);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int waves,
@@ -1540,6 +1552,21 @@ hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int wa
       launch_decode_t<4, false, true>,  launch_decode_t<4, true, true>,
       launch_decode_t<5, false, true>,  launch_decode_t<5, true, true>,
       launch_decode_t<6, false, true>,  launch_decode_t<6, true, true>};
+  static const fn_t even_table[28] = {
+      launch_even_t<0, false, false>, launch_even_t<0, true, false>,
+      launch_even_t<1, false, false>, launch_even_t<1, true, false>,
+      launch_even_t<2, false, false>, launch_even_t<2, true, false>,
+      launch_even_t<3, false, false>, launch_even_t<3, true, false>,
+      launch_even_t<4, false, false>, launch_even_t<4, true, false>,
+      launch_even_t<5, false, false>, launch_even_t<5, true, false>,
+      launch_even_t<6, false, false>, launch_even_t<6, true, false>,
+      launch_even_t<0, false, true>,  launch_even_t<0, true, true>,
+      launch_even_t<1, false, true>,  launch_even_t<1, true, true>,
+      launch_even_t<2, false, true>,  launch_even_t<2, true, true>,
+      launch_even_t<3, false, true>,  launch_even_t<3, true, true>,
+      launch_even_t<4, false, true>,  launch_even_t<4, true, true>,
+      launch_even_t<5, false, true>,  launch_even_t<5, true, true>,
+      launch_even_t<6, false, true>,  launch_even_t<6, true, true>};
   if (pf < 0 || pf > 6) return hipErrorInvalidValue;
   const dim3 grid = a.even ? dim3(a.shares)
                            : dim3(a.Hkv, a.balanced ? a.nslot : a.B / a.chain,
@@ -1550,8 +1577,8 @@ hipError_t launch_decode(const DecodeArgs& a, int pf, bool dbg, bool kv8, int wa
   const size_t slots = pf >= 5 ? (size_t)waves * (pf - 3) * (kv8 ? 4096 : 8192) : 0;
   const size_t need =
       decode_lds_bytes(a.balanced ? a.pb_max : a.PB, a.G, waves, a.B, a.rank_seqs != 0, slots);
-  return table[(kv8 ? 14 : 0) + pf * 2 + (dbg ? 1 : 0)](a, grid, block, lds > need ? lds : need,
-                                                       st);
+  const int k = (kv8 ? 14 : 0) + pf * 2 + (dbg ? 1 : 0);
+  return (a.even ? even_table : table)[k](a, grid, block, lds > need ? lds : need, st);
 }
 
 hipError_t launch_decode_two_loop(const DecodeArgs& a, int pf, int waves, size_t lds,
