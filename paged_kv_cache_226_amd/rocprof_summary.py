@@ -36,8 +36,10 @@ import sys
 
 MODE_NAMES = {0: "off", 1: "l2", 2: "reg", 3: "both", 4: "reg2", 5: "lds", 6: "lds2",
               10: "two_loop_off", 11: "two_loop_l2", 12: "two_loop_reg", 13: "two_loop_both"}
-# pa_decode_kernel<PF, DBG, KV8, TWO>; the two-loop instances count as modes 10 + PF
-DECODE_RE = re.compile(r"pa_decode_kernel<(\d), (true|false), (true|false)(?:, (true|false))?>")
+# pa_decode_kernel<PF, DBG, KV8, TWO, EVEN>; the two-loop instances count as
+# modes 10 + PF; the even split's instances count as their look-ahead mode
+DECODE_RE = re.compile(r"pa_decode_kernel<(\d), (true|false), (true|false)"
+                       r"(?:, (true|false))?(?:, (true|false))?>")
 KV8 = False  # which cache type's kernels the summary counts (set by main)
 
 

@@ -19,6 +19,14 @@ def test_decode_mode_selects_the_cache_type_and_skips_debug_instances():
             assert rs.decode_mode(f"void pa::pa_decode_kernel<{m}, false, false, true>(x)") \
                 == 10 + m
             assert rs.MODE_NAMES[10 + m].startswith("two_loop_")
+            # with all five template arguments spelled out: fused, two-loop,
+            # even split (its look-ahead mode), and the E4M3 / debug ones skipped
+            five = "void pa::pa_decode_kernel<{}, {}, {}, {}, {}>(pa::DecodeArgs)"
+            assert rs.decode_mode(five.format(m, "false", "false", "false", "false")) == m
+            assert rs.decode_mode(five.format(m, "false", "false", "true", "false")) == 10 + m
+            assert rs.decode_mode(five.format(m, "false", "false", "false", "true")) == m
+            assert rs.decode_mode(five.format(m, "true", "false", "false", "true")) is None
+            assert rs.decode_mode(five.format(m, "false", "true", "false", "true")) is None
     finally:
         rs.KV8 = False
 
