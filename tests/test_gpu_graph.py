@@ -1,6 +1,8 @@
 """The decode call captured in a HIP graph (torch.cuda.CUDAGraph) and
 replayed: every replay must give the eager result's bits, also after the
-inputs are changed in place (MI355X)."""
+inputs are changed in place and with the workspace overwritten between
+replays (MI355X).  Plans: a split batch with the reduce, whole units, E4M3,
+and the even split."""
 import numpy as np
 import pytest
 import torch
@@ -29,11 +31,14 @@ def _call(dev, scale, out, ws, fp8=None, pf=-1):
 
 
 @pytest.mark.parametrize("pf", [-1, 4])  # the default mode and the LDS ring
-@pytest.mark.parametrize("case", ["split", "whole", "fp8"])
+@pytest.mark.parametrize("case", ["split", "whole", "fp8", "even"])
 def test_graph_replays_match_eager(case, pf):
     if case == "whole":  # 256 (sequence, KV head) pairs: one partition, no reduce
         x = gen.make_case(64, 16, 4, list(np.random.default_rng(1).integers(1, 300, 64)),
                           seed=501)
+    elif case == "even":  # 192 pairs over 256 table blocks: the even split (default mode)
+        x = gen.make_case(24, 16, 8, list(np.random.default_rng(2).integers(1, 4097, 24)),
+                          seed=502, max_blocks_per_seq=256)
     else:                # 32 pairs: split contexts and the reduce kernel
         x = gen.make_case(4, 32, 8, [900, 33, 4000, 129], seed=500)
     fp8 = None
@@ -48,7 +53,10 @@ def test_graph_replays_match_eager(case, pf):
     else:
         dev = to_device(x)
     p = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"], prefetch=pf)
-    assert (p["num_partitions"] > 1) == (case != "whole")
+    if case == "even":
+        assert p["even_split"] == (pf == -1)
+    else:
+        assert (p["num_partitions"] > 1) == (case != "whole")
     out = torch.empty_like(dev["q"])
     ws = ops.new_workspace(dev["q"], dev["k_cache"], dev["block_tables"], prefetch=pf)
     eager = _call(dev, x.scale, out, ws, fp8, pf).clone()
