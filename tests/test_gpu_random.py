@@ -5,12 +5,13 @@ with empty and partial-block sequences), a plan (partition size, waves), a
 look-ahead mode and distance, a sequence order, a cache placement and the
 cache type.  Every output element must be within tolerance of the fp64
 oracle, and bitwise equal to the plain walk (no look-ahead) on the same
-plan."""
+plan.  A second set asks for the even split on larger ragged batches."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import oracle as orc
+from paged_kv_cache_226_amd import _native as nat
 from paged_kv_cache_226_amd import inputs as gen
 from paged_kv_cache_226_amd import ops
 
@@ -103,3 +104,64 @@ def test_random_configuration(seed):
     got = got.cpu().numpy()
     assert_close(got, ref, f"seed {7000 + seed} {c}")
     assert np.array_equal(bits(got), bits(plain.cpu().numpy())), f"seed {7000 + seed} {c}"
+
+
+def draw_even(seed):
+    rng = np.random.default_rng(seed)
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 5, 7, 8]))
+    B = int(rng.integers(1, 49))
+    lens = [int(rng.choice([0, 1, int(rng.integers(1, 3000)), 16 * int(rng.integers(1, 120))]))
+            for _ in range(B)]
+    if max(lens) == 0:
+        lens[0] = 17
+    pf = int(rng.choice([0, 1, 2, 3, 4]))
+    return dict(B=B, Hq=Hkv * g, Hkv=Hkv, lens=lens, fp8=bool(rng.random() < 0.3), pf=pf,
+                dist=int(rng.choice([0, 1, 2])) if pf in (2, 4) else 0,
+                waves=int(rng.choice([0, 1, 2, 4, 8])), cap=int(rng.choice([0, 1, 2, 3])),
+                layout=str(rng.choice(["dense", "adjacent", "padded"])),
+                extra=int(rng.integers(0, 4)))
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_random_even_split(seed):
+    """The even split asked for on random ragged batches (empty sequences,
+    one-token ones, tables of 1..120 blocks, 1 to 3 shares per CU): within
+    tolerance of the oracle, and bitwise equal to the walk without the
+    look-ahead over the same shares."""
+    c = draw_even(9000 + seed)
+    print(f"[random even] seed {9000 + seed}: {c}", flush=True)
+    x = gen.make_case(c["B"], c["Hq"], c["Hkv"], c["lens"], seed=9000 + seed,
+                      extra_pool_blocks=c["extra"], poison=True)
+    q = torch.from_numpy(x.q).cuda()
+    bt = torch.from_numpy(x.block_tables).cuda()
+    ctx = torch.from_numpy(x.context_lens).cuda()
+    if c["fp8"]:
+        x8 = gen.to_fp8(x)
+        kc = torch.from_numpy(gen.pack_k_fp8(x8.k8)).cuda()
+        vc = torch.from_numpy(x8.v8).cuda()
+        ref = orc.paged_attention_fp8_f64(x8.q, x8.k8, x8.v8, x8.block_tables, x8.context_lens,
+                                          x8.scale, x8.k_scale, x8.v_scale)
+        dec = lambda k, v, **kw: ops.paged_attn_decode_fp8(q, k, v, bt, ctx, x8.scale,
+                                                           x8.k_scale, x8.v_scale, **kw)
+    else:
+        kc = torch.from_numpy(gen.pack_k(x.k_cache)).cuda()
+        vc = torch.from_numpy(x.v_cache).cuda()
+        ref = orc.paged_attention_f64(x.q, x.k_cache, x.v_cache, x.block_tables,
+                                      x.context_lens, x.scale)
+        dec = lambda k, v, **kw: ops.paged_attn_decode(q, k, v, bt, ctx, x.scale, **kw)
+    k, v = place(kc, vc, c["layout"])
+    kw = dict(even_split=nat.EVEN_SPLIT_ON, waves_per_wg=c["waves"],
+              max_resident_wgs=c["cap"])
+    try:
+        plan = ops.plan(q, k, bt, prefetch=c["pf"], prefetch_distance=c["dist"], **kw)
+    except ValueError as e:  # e.g. LDS ring slots for 8 waves of 16 heads
+        assert "unsupported" in str(e), e
+        return
+    assert plan["even_split"] == 1
+    got = dec(k, v, prefetch=c["pf"], prefetch_distance=c["dist"], **kw).cpu().numpy()
+    plain = dec(k, v, prefetch=0, even_split=nat.EVEN_SPLIT_ON,
+                waves_per_wg=plan["waves_per_wg"], max_resident_wgs=plan["resident_wgs"])
+    torch.cuda.synchronize()
+    assert_close(got, ref, f"seed {9000 + seed} {c}")
+    assert np.array_equal(bits(got), bits(plain.cpu().numpy())), f"seed {9000 + seed} {c}"
