@@ -142,12 +142,12 @@ enum pa_structure {
 
 /* pa_options.even_split */
 enum pa_even_split {
-    PA_EVEN_SPLIT_AUTO = 0,   /* the plan's choice: the even split for more
-                                 than CUs / 2 and fewer than 2 x CUs
-                                 (sequence, KV head) units over a table of
-                                 256..1024 blocks, with waves, partitions,
-                                 order and residency left to the plan, the
-                                 look-ahead off or in registers, and no
+    PA_EVEN_SPLIT_AUTO = 0,   /* the plan's choice: the even split for 2..256
+                                 sequences with at least CUs / 2 (sequence,
+                                 KV head) units over a table of 256..1024
+                                 blocks, with waves, partitions, order and
+                                 residency left to the plan, the look-ahead
+                                 off or in registers, and no
                                  min_context_hint that says every context
                                  fills the table */
     PA_EVEN_SPLIT_OFF = 1,

@@ -97,6 +97,13 @@ constexpr int kStreamMinBlocksGqa = 256;
 constexpr int kStreamSplitBlocks = 256;
 // The even split's shortest table (blocks) for the auto plan.
 constexpr int kEvenMinBlocks = 256;
+// What a piece change costs a share, in blocks read: the shares are cut as
+// if every (sequence, KV head) unit began with this many more blocks, so a
+// share that crosses more unit starts gets fewer blocks.  About 3 us per
+// change on the llama3_8b TP2 shard, where a CU reads a 8 KiB fp16 block
+// (4 KiB E4M3) in about 0.3 us (0.15 us).
+constexpr int kEvenPieceBlocksF16 = 10;
+constexpr int kEvenPieceBlocksE4M3 = 20;
 
 bool valid_device(const pa_device_info* d) {
   return d && d->compute_units >= 1 && d->compute_units <= 65536 &&
@@ -318,19 +325,21 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   // The even split (pa_options.even_split): one share of the batch's
   // blocks per work-group, S = CUs x the residency cap (1 unless asked).
   //
-  // The plan takes it by itself for a batch with more than C / 2 and
-  // fewer than 2 C units and 256..1024 table blocks, unless the hint says
-  // every context fills the table: the fixed grid then leaves CUs idle
-  // (a second round of fewer units than CUs, or ragged units one per CU),
-  // and the balanced split keeps whole partitions of one size.  Measured
-  // (us, the plan before -> the even split): ragged GQA 32/8, 48 x 1..8K
-  // (1.5 units per CU) 175.5 -> 134.1; 24 x 512..8K 85.5 -> 71.6; llama3_8b
-  // TP2 shard (64 x 512..8K, 4 KV heads) 106.0 -> 96.6; 32 x 512..8K 106.3
-  // -> 95.8; uniform MHA 8 x 4K 80.5 -> 78.3.  E4M3: llama3_8b TP2 59.5 ->
-  // 53.9, 48 x 1..8K 96.3 -> 74.8, 24 x 512..8K 51.6 -> 41.7 (a uniform
-  // GQA 40/8 32 x 8K without the hint lost 4 %: 83.0 -> 86.3).  It lost on
-  // shorter tables (MHA 8 x 1K +14 %, GQA 32 x 1..2K +17 %) and at C / 2
-  // units or fewer (+5 % on two of three ragged batches).
+  // The plan takes it by itself for a batch of 2..256 sequences with at
+  // least C / 2 units and 256..1024 table blocks, unless the hint says every
+  // context fills the table (a uniform batch takes the streaming shape,
+  // which is faster).  The fixed grid leaves CUs idle on a ragged batch (a
+  // last round of fewer units than CUs, or long units alone on their CUs)
+  // and the balanced split keeps partitions of one size.  Measured (us, the
+  // plan before -> the even split, with the piece charge): llama3_8b (64 x
+  // 512..8K, 512 units) 181.4 -> 175.3; its TP2 shard 106.0 -> 93.3, TP4
+  // shard 53.3 -> 50.5; GQA 32/8 96 x 512..8K 299.0 -> 260.2, 64 x 1..8K
+  // 199.9 -> 168.7, 48 x 1..8K 175.5 -> 130.8, 256 x 1..4K 347.2 -> 334.2;
+  // E4M3 llama3_8b TP2 59.5 -> 51.0, TP4 32.7 -> 29.1, llama3_8b 96.2 ->
+  // 96.3.  It lost on shorter tables (GQA 32 x 1..2K, 128 blocks: 27.5 ->
+  // 29.7; 64 blocks: 13-16 %), below C / 2 units (the TP8 shard 28.6 ->
+  // 29.4) and on uniform batches planned without the hint (qwen25_7b 158.4
+  // -> 163.5).
   if (o->even_split < PA_EVEN_SPLIT_AUTO || o->even_split > PA_EVEN_SPLIT_ON)
     return PA_ERR_INVALID_ARG;
   const bool uniform_hint = o->min_context_hint > 0 && (int64_t)o->min_context_hint * 8 >=
@@ -339,13 +348,13 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
       o->even_split == PA_EVEN_SPLIT_AUTO && !two && !uniform_hint && in_flight > 0 &&
       o->partition_blocks == 0 && o->waves_per_wg == 0 && o->max_resident_wgs == 0 &&
       o->seq_order == PA_ORDER_AUTO && B >= 2 && B <= PA_RANK_MAX_SEQS &&
-      MB >= kEvenMinBlocks && MB <= kMaxPartitionBlocks && 2 * units > dv.cus &&
-      units < 2 * dv.cus && (int64_t)B * MB * Hkv <= INT32_MAX / 2;
+      MB >= kEvenMinBlocks && MB <= kMaxPartitionBlocks && 2 * units >= dv.cus &&
+      (int64_t)B * (MB + kEvenPieceBlocksE4M3) * Hkv <= INT32_MAX / 2;
   const bool even = o->even_split == PA_EVEN_SPLIT_ON || even_auto;
   if (even) {
     // positions in the (block, KV head) sequence are int32 on the device
     if (two || o->partition_blocks != 0 || B > PA_RANK_MAX_SEQS || MB > kMaxPartitionBlocks ||
-        (int64_t)B * MB * Hkv > INT32_MAX / 2)
+        (int64_t)B * (MB + kEvenPieceBlocksE4M3) * Hkv > INT32_MAX / 2)
       return PA_ERR_UNSUPPORTED;
     // fp16: 2 waves one block ahead, or 4 without the look-ahead (4 blocks
     // per work-group); E4M3: 8 waves, the register look-ahead one block
@@ -646,6 +655,7 @@ int decode_impl(const void* q, const void* k_cache, const void* v_cache,
   a.chain = pl.chain;
   a.even = pl.even;
   a.shares = pl.even ? (int)pl.wgs : 0;
+  a.even_kappa = kv8 ? kEvenPieceBlocksE4M3 : kEvenPieceBlocksF16;
   const bool dbg =
       o->debug_gather_k || o->debug_trace || o->debug_error_word || o->debug_timeline;
   if (pl.two && dbg) return PA_ERR_UNSUPPORTED;

@@ -58,6 +58,7 @@ struct DecodeArgs {
   // record (m = -inf, l = 0, o = 0) at 2c.
   int even;
   int shares;            // S, the even split's grid
+  int even_kappa;        // blocks a piece change is charged in the share sizes
   int32_t* ws_np;
 };
 

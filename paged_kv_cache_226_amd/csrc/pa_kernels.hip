@@ -1049,20 +1049,23 @@ __device__ Slot balanced_slot(const DecodeArgs& a, int slot, int tab_tokens) {
   return r;
 }
 
-// Even split: this work-group's share [X, Y) of the T = Hkv * N (block, KV
-// head) pairs, N the blocks of all sequences, units (KV head, sequence)
-// KV-head-major: head kvh's units fill [kvh N, (kvh + 1) N), its sequences
-// in order.  (Sequence-major order, a sequence's KV heads one after the
-// other, measured 5-7 % slower: the work-groups that run at the same time
-// then read every other KV head's slice of the same blocks instead of all
-// of them.)  Every wave finds the unit holding block X from the block
-// counts of all sequences (lane l holds sequences 4l..4l+3, B <= 256); the
-// work-group then walks the pieces of the units in [X, Y) in order.  A
-// whole unit's output is written here; a piece goes to record 2c (the
-// share's first piece) or 2c + 1 (its last: a unit that starts in the
-// share and runs past its end), and the piece that holds a unit's block 0
-// also records where the unit's pieces are for the merge.  The share of
-// block z is the largest c' with c' T / S <= z, i.e. ((z + 1) S - 1) / T.
+// Even split: this work-group's share [X, Y) of a sequence of positions in
+// which every non-empty (KV head, sequence) unit takes K + nb positions, K
+// the cost of a piece change in blocks (a.even_kappa) and nb its blocks at
+// positions [v + K, v + K + nb) from its start v.  Units are KV-head-major:
+// head kvh's fill [kvh N, (kvh + 1) N), N = sum of (K + nb) over the
+// non-empty sequences, T = Hkv N.  (Sequence-major order, a sequence's KV
+// heads one after the other, measured 5-7 % slower: the work-groups that
+// run at the same time then read every other KV head's slice of the same
+// blocks instead of all of them.)  Every wave finds the unit holding
+// position X from the block counts of all sequences (lane l holds
+// sequences 4l..4l+3, B <= 256); the work-group then walks, unit by unit,
+// the blocks of [X, Y).  A whole unit's output is written here; a piece
+// goes to record 2c (the share's first piece) or 2c + 1 (its last: a unit
+// that starts in the share and runs past its end), and the piece that
+// holds a unit's block 0 also records where the unit's pieces are for the
+// merge.  The share of position z is the largest c' with c' T / S <= z,
+// i.e. ((z + 1) S - 1) / T.
 template <int PF, bool DBG, bool KV8>
 __device__ __forceinline__ void even_walk(const DecodeArgs& a, int tab_tokens, int32_t* bt_s,
                                           float* merge_s) {
@@ -1070,16 +1073,18 @@ __device__ __forceinline__ void even_walk(const DecodeArgs& a, int tab_tokens, i
   const int lane = tid & (kWave - 1);
   const int W = blockDim.x / kWave;
   const int G = a.G, Hkv = a.Hkv;
-  int nb[4], cx[4];
+  const int K = a.even_kappa;
+  int nb[4], cx[4], len[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int idx = 4 * lane + i;
     const int raw = idx < a.B ? a.ctx[idx] : 0;
     cx[i] = raw < 0 ? 0 : (raw > tab_tokens ? tab_tokens : raw);
     nb[i] = (cx[i] + kT - 1) / kT;
+    len[i] = nb[i] > 0 ? nb[i] + K : 0;
     if (DBG && raw > tab_tokens && a.dbg_err) atomicOr(a.dbg_err, 2);
   }
-  const int mine = nb[0] + nb[1] + nb[2] + nb[3];
+  const int mine = len[0] + len[1] + len[2] + len[3];
   const int incl = wave_prefix_i32(mine);
   const int N = __builtin_amdgcn_readlane(incl, kWave - 1);
   const int T = N * Hkv;
@@ -1087,9 +1092,11 @@ __device__ __forceinline__ void even_walk(const DecodeArgs& a, int tab_tokens, i
   const int c = blockIdx.x;
   const int X = (int)((int64_t)c * T / S);
   const int Y = (int)((int64_t)(c + 1) * T / S);
-  if (X == Y) {
-    // no blocks: an empty record at 2c, for the merge of a unit that
-    // spans this share
+  // no blocks: an empty record at 2c, for the merge of a unit that spans
+  // this share (only a share with no positions can lie inside a unit's
+  // span without blocks of it; any other share without blocks is read by
+  // no merge, and gets the same record)
+  auto empty_record = [&]() {
     for (int idx = tid; idx < G * kD; idx += blockDim.x) {
       const int h = idx / kD, d = idx % kD;
       const int64_t r = (int64_t)2 * c * G + h;
@@ -1099,23 +1106,26 @@ __device__ __forceinline__ void even_walk(const DecodeArgs& a, int tab_tokens, i
         a.ws_ml[r * 2 + 1] = 0.f;
       }
     }
+  };
+  if (X == Y) {
+    empty_record();
     return;
   }
   int kvh = X / N;
-  const int xr = X - kvh * N;  // X's block among head kvh's
+  const int xr = X - kvh * N;  // X's position among head kvh's
   int start = incl - mine;
   int fb = -1, frel = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (xr >= start && xr < start + nb[i]) {
+    if (xr >= start && xr < start + len[i]) {
       fb = 4 * lane + i;
       frel = xr - start;
     }
-    start += nb[i];
+    start += len[i];
   }
   const int ol = __builtin_ctzll(__builtin_amdgcn_ballot_w64(fb >= 0));
   int b = __builtin_amdgcn_readlane(fb, ol);
-  int off = __builtin_amdgcn_readlane(frel, ol);
+  int vs = X - __builtin_amdgcn_readlane(frel, ol);  // the unit's first position
   auto pick = [&](const int* v, int seq) {  // v[seq % 4] of the lane holding seq
     const int k = seq & 3;
     const int x = k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3];
@@ -1137,42 +1147,46 @@ __device__ __forceinline__ void even_walk(const DecodeArgs& a, int tab_tokens, i
     }
   };
   while (true) {
-    const int seg = nbb - off < Y - pos ? nbb - off : Y - pos;
-    walk_range<PF, DBG, KV8>(a, b, kvh, pick(cx, b), off, off + seg, bt_s, merge_s);
-    const bool whole = off == 0 && seg == nbb;
-    const int rec = first ? 2 * c : 2 * c + 1;
-    if (off == 0 && tid == 0) {
-      const int64_t last = (int64_t)pos + nbb - 1;  // the unit's last block
-      const int c1 = (int)(((last + 1) * S - 1) / T);
-      a.ws_np[2 * (b * Hkv + kvh)] = rec;
-      a.ws_np[2 * (b * Hkv + kvh) + 1] = c1 - c + 1;
-    }
-    for (int idx = tid; idx < G * kD; idx += blockDim.x) {
-      const int h = idx / kD, d = idx % kD;
-      float M, L, O;
-      combine_waves(merge_s, W, G, h, d, M, L, O);
-      if (whole) {
-        a.out[((int64_t)b * a.Hq + kvh * G + h) * kD + d] = f32_to_f16_bits(O * a.v_scale / L);
-      } else {
-        const int64_t r = (int64_t)rec * G + h;
-        a.ws_o[r * kD + d] = O;
-        if (d == 0) {
-          a.ws_ml[r * 2] = M;
-          a.ws_ml[r * 2 + 1] = L;
+    // this unit's blocks inside [pos, Y)
+    const int r0 = (pos > vs + K ? pos : vs + K) - (vs + K);
+    const int r1 = (Y < vs + K + nbb ? Y : vs + K + nbb) - (vs + K);
+    if (r1 > r0) {
+      walk_range<PF, DBG, KV8>(a, b, kvh, pick(cx, b), r0, r1, bt_s, merge_s);
+      const bool whole = r0 == 0 && r1 == nbb;
+      const int rec = first ? 2 * c : 2 * c + 1;
+      if (r0 == 0 && tid == 0) {
+        const int64_t last = (int64_t)vs + K + nbb - 1;  // the unit's last block
+        const int c1 = (int)(((last + 1) * S - 1) / T);
+        a.ws_np[2 * (b * Hkv + kvh)] = rec;
+        a.ws_np[2 * (b * Hkv + kvh) + 1] = c1 - c + 1;
+      }
+      for (int idx = tid; idx < G * kD; idx += blockDim.x) {
+        const int h = idx / kD, d = idx % kD;
+        float M, L, O;
+        combine_waves(merge_s, W, G, h, d, M, L, O);
+        if (whole) {
+          a.out[((int64_t)b * a.Hq + kvh * G + h) * kD + d] =
+              f32_to_f16_bits(O * a.v_scale / L);
+        } else {
+          const int64_t r = (int64_t)rec * G + h;
+          a.ws_o[r * kD + d] = O;
+          if (d == 0) {
+            a.ws_ml[r * 2] = M;
+            a.ws_ml[r * 2 + 1] = L;
+          }
         }
       }
+      first = false;
     }
-    pos += seg;
+    pos = vs + K + nbb;
     if (pos >= Y) break;
-    first = false;
-    // the next unit: the next sequence with blocks, else the next KV head's
-    // first one (one exists: pos < Y <= T)
-    off = 0;
-    const int n = next_unit(b, kvh);
+    // the next unit (one exists: pos < Y <= T); units are contiguous
+    nbb = next_unit(b, kvh);
     if (kvh >= Hkv) break;  // not reached
-    nbb = n;
+    vs = pos;
     __syncthreads();  // the merge records above are read before the next walk
   }
+  if (first) empty_record();  // no blocks in this share
 }
 
 // TWO selects the two-loop walk (fp16, no debug outputs), EVEN the even

@@ -182,11 +182,11 @@ def test_plans_of_the_workloads(native_lib):
     # (partitions, waves, balanced, even split) of the auto plan without a
     # hint; under the balanced split the partitions are the most one
     # sequence can get
-    expect = {"tiny": (1, 8, 0, 0), "llama2_7b": (1, 4, 0, 0), "llama3_8b": (1, 8, 0, 0),
-              "qwen25_7b": (1, 4, 0, 0), "qwen25_14b": (1, 4, 0, 0),
-              "llama3_8b_tp2": (1, 2, 0, 1), "llama3_8b_tp4": (8, 8, 1, 0),
-              "llama3_8b_tp8": (8, 8, 1, 0), "qwen25_14b_tp2": (1, 8, 0, 0),
-              "qwen25_14b_tp4": (1, 2, 0, 1), "qwen25_14b_tp8": (8, 8, 1, 0)}
+    expect = {"tiny": (1, 8, 0, 0), "llama2_7b": (1, 4, 0, 0), "llama3_8b": (1, 2, 0, 1),
+              "qwen25_7b": (1, 2, 0, 1), "qwen25_14b": (1, 2, 0, 1),
+              "llama3_8b_tp2": (1, 2, 0, 1), "llama3_8b_tp4": (1, 2, 0, 1),
+              "llama3_8b_tp8": (8, 8, 1, 0), "qwen25_14b_tp2": (1, 2, 0, 1),
+              "qwen25_14b_tp4": (1, 2, 0, 1), "qwen25_14b_tp8": (1, 2, 0, 1)}
     for name, w in gen.WORKLOADS.items():
         MB = w.max_blocks_per_seq or max(-(-c // 16) for c in w.context_lens)
         nb = w.pool_blocks or 1
@@ -249,6 +249,7 @@ def test_stream_read_validation(native_lib):
 def test_sequence_order_of_the_plan(native_lib, B, Hkv, MB, order, want):
     o = nat.default_options()
     o.seq_order = order
+    o.even_split = nat.EVEN_SPLIT_OFF  # (64 and 256 x 8 x 512 blocks would take it)
     sh = good_shape(num_seqs=B, num_q_heads=4 * Hkv, num_kv_heads=Hkv, max_blocks_per_seq=MB)
     assert nat.plan(sh, o)["seq_order"] == want
 
@@ -275,6 +276,11 @@ def test_auto_plan_rule(native_lib, B, Hkv, MB, waves, P, PB):
     assert (p["waves_per_wg"], p["num_partitions"], p["partition_blocks"]) == (waves, P, PB)
     assert p["balanced"] == 0
     auto = nat.plan(nat.make_shape(B, Hkv * 4, Hkv, MB, 1000))
+    even = 2 <= B <= 256 and 256 <= MB <= 1024 and 2 * B * Hkv >= 256
+    assert auto["even_split"] == even
+    if even:
+        assert (auto["workgroups"], auto["num_partitions"]) == (256, 1)
+        return
     assert auto["balanced"] == (1 if P > 1 and 2 <= B <= 256 and B * Hkv < 256 else 0)
     if not auto["balanced"]:
         assert (auto["waves_per_wg"], auto["num_partitions"], auto["partition_blocks"]) == \
@@ -443,13 +449,13 @@ def test_plan_rules_follow_the_cu_count(native_lib, cus):
     head) units as CUs; 8 waves for such unsplit long tables while there are
     fewer than three units per CU; longest-first order iff the grid holds
     more work-groups than the CUs keep resident (three 4-wave ones each);
-    the even split (one share per CU, 2 waves) for more than half and fewer
-    than twice as many units as CUs over a long table."""
+    the even split (one share per CU, 2 waves) for at least half as many
+    units as CUs over a long table."""
     dev = dict(MI355X, compute_units=cus)
     for B in (1, 2, 4, 8, 16, 32, 64, 96, 128, 200, 256):
         units = B * 8
         p = nat.plan(nat.make_shape(B, 32, 8, 512, 1), device=dev)
-        even = B >= 2 and cus < 2 * units < 4 * cus
+        even = B >= 2 and 2 * units >= cus
         assert p["even_split"] == even, (B, p)
         if even:
             assert (p["workgroups"], p["waves_per_wg"], p["num_partitions"]) == (cus, 2, 1)
@@ -459,8 +465,9 @@ def test_plan_rules_follow_the_cu_count(native_lib, cus):
             assert p["waves_per_wg"] == (8 if units < 3 * cus else 4), (B, p)
         else:
             assert p["num_partitions"] >= min(-(-cus // units), 2) and p["waves_per_wg"] == 8
-        # short tables: 4 waves, one partition when units >= cus
+        # short tables (no even split): 4 waves, one partition when units >= cus
         q = nat.plan(nat.make_shape(B, 32, 8, 64, 1), device=dev)
+        assert q["even_split"] == 0
         if units >= cus:
             want = nat.ORDER_LONGEST_FIRST if B >= 2 and units > 3 * cus else nat.ORDER_NATURAL
             assert (q["waves_per_wg"], q["num_partitions"], q["seq_order"]) == (4, 1, want), (B, q)
@@ -542,7 +549,7 @@ def test_streaming_shape_for_uniform_contexts(native_lib, B, Hq, Hkv, kv, want):
     # the hint is the only difference from the default plan
     base = nat.plan(sh, device=MI355X)
     assert base["resident_wgs"] == 0 or base["even_split"] == 1
-    assert (base["waves_per_wg"], base["resident_wgs"]) != want
+    assert (base["waves_per_wg"], base["resident_wgs"], base["even_split"]) != want + (0,)
 
 
 @pytest.mark.parametrize("case", [
@@ -684,7 +691,7 @@ def test_streaming_waves_for_balanced_uniform_batches(native_lib, B, Hq, Hkv, MB
     sh = nat.make_shape(B, Hq, Hkv, MB, 1)
     p = nat.plan(sh, hinted(MB * 16, prefetch=pf), device=MI355X)
     assert p["balanced"] == 1 and p["waves_per_wg"] == want and p["resident_wgs"] == 0
-    q = nat.plan(sh, hinted(0, prefetch=pf), device=MI355X)
+    q = nat.plan(sh, hinted(0, prefetch=pf, even_split=nat.EVEN_SPLIT_OFF), device=MI355X)
     assert q["balanced"] == 1 and q["waves_per_wg"] == 8
     e4 = nat.plan(nat.make_shape(B, Hq, Hkv, MB, 1, kv_dtype=nat.KV_E4M3),
                   hinted(MB * 16, prefetch=pf), device=MI355X)

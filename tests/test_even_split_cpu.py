@@ -17,62 +17,63 @@ from paged_kv_cache_226_amd import _native as nat
 MI355X = dict(compute_units=256, lds_bytes_per_cu=163840, lds_bytes_per_workgroup=163840)
 
 
-def shares_walk(nb, Hkv, S):
+def shares_walk(nb, Hkv, S, K=0):
     """The pieces each share walks, (c, b, kvh, s, e, record) in order, the
-    empty records, and the per-unit (record, pieces) written.  Units are
-    KV-head-major: head kvh's sequences fill [kvh N, (kvh + 1) N)."""
+    empty records, and the per-unit (record, pieces) written.  Positions:
+    every non-empty unit takes K + nb of them, its blocks at [v + K, v + K +
+    nb) from its first position v (K charges a piece change); units are
+    KV-head-major, head kvh's at [kvh N, (kvh + 1) N).  Returns the number
+    of blocks (not positions) as T."""
     B = len(nb)
-    N = sum(nb)
+    L = [n + K if n > 0 else 0 for n in nb]
+    N = sum(L)
     T = N * Hkv
     starts = []
     acc = 0
-    for n in nb:
+    for x in L:
         starts.append(acc)
-        acc += n
+        acc += x
     pieces, empty, unit_rec = [], [], {}
     for c in range(S):
         X, Y = c * T // S, (c + 1) * T // S
-        if X == Y:
-            empty.append(2 * c)
-            continue
-        kvh = X // N
-        xr = X - kvh * N
-        b = max(i for i in range(B) if starts[i] <= xr and nb[i] > 0)
-        off = xr - starts[b]
-        nbb = nb[b]
-        pos, first = X, True
-        while True:
-            seg = min(nbb - off, Y - pos)
-            rec = 2 * c if first else 2 * c + 1
-            whole = off == 0 and seg == nbb
-            if off == 0:
-                last = pos + nbb - 1
-                c1 = ((last + 1) * S - 1) // T
-                unit_rec[(b, kvh)] = (rec, c1 - c + 1)
-            pieces.append((c, b, kvh, off, off + seg, None if whole else rec))
-            pos += seg
-            if pos >= Y:
-                break
-            first = False
-            off = 0
-            n = 0
+        first = True
+        if X < Y:
+            kvh = X // N
+            xr = X - kvh * N
+            b = max(i for i in range(B) if starts[i] <= xr and L[i] > 0)
+            vs = kvh * N + starts[b]
+            pos = X
             while True:
-                b += 1
-                if b >= B:
-                    b = 0
-                    kvh += 1
-                    if kvh >= Hkv:
-                        break
                 n = nb[b]
-                if n > 0:
+                r0 = max(pos, vs + K) - (vs + K)
+                r1 = min(Y, vs + K + n) - (vs + K)
+                if r1 > r0:
+                    rec = 2 * c if first else 2 * c + 1
+                    if r0 == 0:
+                        c1 = ((vs + K + n) * S - 1) // T  # the share of the last block
+                        unit_rec[(b, kvh)] = (rec, c1 - c + 1)
+                    whole = r0 == 0 and r1 == n
+                    pieces.append((c, b, kvh, r0, r1, None if whole else rec))
+                    first = False
+                pos = vs + K + n
+                if pos >= Y:
                     break
-            assert kvh < Hkv and n > 0
-            nbb = n
-    return T, pieces, empty, unit_rec
+                while True:  # the next unit with blocks
+                    b += 1
+                    if b >= B:
+                        b = 0
+                        kvh += 1
+                        assert kvh < Hkv
+                    if nb[b] > 0:
+                        break
+                vs = pos
+        if first:
+            empty.append(2 * c)
+    return sum(nb) * Hkv, pieces, empty, unit_rec
 
 
-def check(nb, Hkv, S):
-    T, pieces, empty, unit_rec = shares_walk(nb, Hkv, S)
+def check(nb, Hkv, S, K=0):
+    T, pieces, empty, unit_rec = shares_walk(nb, Hkv, S, K)
     covered = {}
     written = {}
     for c, b, kvh, s, e, rec in pieces:
@@ -111,8 +112,9 @@ def check(nb, Hkv, S):
             assert edge == n
 
 
+@pytest.mark.parametrize("K", [0, 1, 10, 20])  # blocks charged per piece change (10 fp16, 20 E4M3)
 @pytest.mark.parametrize("seed", range(40))
-def test_every_block_once_and_the_merge_finds_each_piece(seed):
+def test_every_block_once_and_the_merge_finds_each_piece(seed, K):
     rng = random.Random(seed)
     B = rng.choice([1, 2, 3, 7, 64, 200, 256])
     Hkv = rng.choice([1, 2, 8])
@@ -121,14 +123,33 @@ def test_every_block_once_and_the_merge_finds_each_piece(seed):
     if not any(nb):
         nb[rng.randrange(B)] = 1
     S = rng.choice([1, 7, 256, 512, 2048])
-    check(nb, Hkv, S)
+    check(nb, Hkv, S, K)
 
 
-def test_fewer_blocks_than_shares_and_one_long_unit():
-    check([3], 1, 256)           # most shares empty
-    check([1024], 1, 256)        # one unit in 256 pieces
-    check([0, 0, 5, 0], 2, 256)  # empty sequences around the only one
-    check([512] * 64, 8, 256)    # whole units, no merge
+@pytest.mark.parametrize("K", [0, 10, 20])
+def test_fewer_blocks_than_shares_and_one_long_unit(K):
+    check([3], 1, 256, K)           # most shares empty
+    check([1024], 1, 256, K)        # one unit in 256 pieces
+    check([0, 0, 5, 0], 2, 256, K)  # empty sequences around the only one
+    check([512] * 64, 8, 256, K)    # whole units, no merge
+
+
+def test_the_piece_charge_evens_out_the_shares_cost():
+    """On the llama3_8b TP2 shard's lengths (64 sequences of 512..8K tokens,
+    4 KV heads, 256 shares): with 10 blocks charged per piece, the costliest
+    share (blocks + 10 per piece) costs no more than the median share."""
+    from paged_kv_cache_226_amd import inputs as gen
+    x = gen.make_inputs("llama3_8b_tp2")
+    nb = [-(-max(int(c), 0) // 16) for c in x.context_lens]
+    worst = {}
+    for K in (0, 10):
+        _, pieces, _, _ = shares_walk(nb, 4, 256, K)
+        cost = {}
+        for c, b, kvh, s, e, rec in pieces:
+            cost[c] = cost.get(c, 0) + (e - s) + 10
+        v = sorted(cost.values())
+        worst[K] = (v[-1], v[len(v) // 2])
+    assert worst[10][0] <= worst[10][1] + 2 < worst[0][0]
 
 
 def test_plans_that_take_the_even_split(native_lib):
@@ -153,7 +174,19 @@ def test_plans_that_take_the_even_split(native_lib):
     assert (p8["waves_per_wg"], p8["prefetch_distance"]) == (8, 1)
     half = nat.make_shape(32, 32, 8, 512, 32 * 512, kv_dtype=nat.KV_E4M3)  # 256 units
     assert nat.plan(half, device=MI355X)["even_split"] == 1
-    assert nat.plan(sh8, device=MI355X)["even_split"] == 0  # 512 units: 2 per CU
+    assert nat.plan(sh8, device=MI355X)["even_split"] == 1  # 512 units: 2 per CU
+    # below half as many units as CUs, on a short table, with a hint that
+    # every context fills the table, or for one sequence: the other plans
+    few = nat.make_shape(15, 32, 8, 512, 15 * 512)  # 120 units
+    assert nat.plan(few, device=MI355X)["even_split"] == 0
+    assert nat.plan(nat.make_shape(16, 32, 8, 512, 1), device=MI355X)["even_split"] == 1
+    assert nat.plan(nat.make_shape(64, 32, 8, 255, 1), device=MI355X)["even_split"] == 0
+    full = nat.default_options()
+    full.min_context_hint = 512 * 16
+    assert nat.plan(sh, full, device=MI355X)["even_split"] == 0
+    full.min_context_hint = 512 * 16 * 7 // 8 - 1
+    assert nat.plan(sh, full, device=MI355X)["even_split"] == 1
+    assert nat.plan(nat.make_shape(1, 8, 1, 1024, 1), device=MI355X)["even_split"] == 0
     o.prefetch_distance = 2
     assert nat.plan(sh8, o, device=MI355X)["prefetch_distance"] == 2
     o.prefetch_distance = 0
