@@ -99,11 +99,13 @@ constexpr int kStreamSplitBlocks = 256;
 constexpr int kEvenMinBlocks = 256;
 // What a piece change costs a share, in blocks read: the shares are cut as
 // if every (sequence, KV head) unit began with this many more blocks, so a
-// share that crosses more unit starts gets fewer blocks.  About 3 us per
-// change on the llama3_8b TP2 shard, where a CU reads a 8 KiB fp16 block
-// (4 KiB E4M3) in about 0.3 us (0.15 us).
-constexpr int kEvenPieceBlocksF16 = 10;
-constexpr int kEvenPieceBlocksE4M3 = 20;
+// share that crosses more unit starts gets fewer blocks.  A share's end time
+// grew about 3 us per piece on the llama3_8b TP2 shard, where a CU reads an
+// 8 KiB fp16 block (4 KiB E4M3) in about 0.3 us (0.15 us); swept over
+// 0..20 (fp16) and 10..30 (E4M3) on five ragged batches, 12 and 20..30 were
+// the fastest (12 against 10: 0.2-0.5 us).
+constexpr int kEvenPieceBlocksF16 = 12;
+constexpr int kEvenPieceBlocksE4M3 = 24;
 
 bool valid_device(const pa_device_info* d) {
   return d && d->compute_units >= 1 && d->compute_units <= 65536 &&
@@ -334,7 +336,8 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   // plan before -> the even split, with the piece charge): llama3_8b (64 x
   // 512..8K, 512 units) 181.4 -> 175.3; its TP2 shard 106.0 -> 93.3, TP4
   // shard 53.3 -> 50.5; GQA 32/8 96 x 512..8K 299.0 -> 260.2, 64 x 1..8K
-  // 199.9 -> 168.7, 48 x 1..8K 175.5 -> 130.8, 256 x 1..4K 347.2 -> 334.2;
+  // 199.9 -> 168.7, 256 x 1..4K 347.2 -> 334.2; GQA 40/8 48 x 1..8K 175.5
+  // -> 130.8;
   // E4M3 llama3_8b TP2 59.5 -> 51.0, TP4 32.7 -> 29.1, llama3_8b 96.2 ->
   // 96.3.  It lost on shorter tables (GQA 32 x 1..2K, 128 blocks: 27.5 ->
   // 29.7; 64 blocks: 13-16 %), below C / 2 units (the TP8 shard 28.6 ->
