@@ -96,7 +96,7 @@ constexpr int kMaxResidencyCap = 8;
 constexpr int kStreamMinBlocksGqa = 256;
 constexpr int kStreamSplitBlocks = 256;
 // The even split's shortest table (blocks) for the auto plan.
-constexpr int kEvenMinBlocks = 256;
+constexpr int kEvenMinBlocks = 160;
 // What a piece change costs a share, in blocks read: the shares are cut as
 // if every (sequence, KV head) unit began with this many more blocks, so a
 // share that crosses more unit starts gets fewer blocks.  A share's end time
@@ -328,7 +328,7 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   // blocks per work-group, S = CUs x the residency cap (1 unless asked).
   //
   // The plan takes it by itself for a batch of 2..256 sequences with at
-  // least C / 2 units and 256..1024 table blocks, unless the hint says every
+  // least C / 2 units and 160..1024 table blocks, unless the hint says every
   // context fills the table (a uniform batch takes the streaming shape,
   // which is faster).  The fixed grid leaves CUs idle on a ragged batch (a
   // last round of fewer units than CUs, or long units alone on their CUs)
@@ -339,8 +339,9 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   // 199.9 -> 168.7, 256 x 1..4K 347.2 -> 334.2; GQA 40/8 48 x 1..8K 175.5
   // -> 130.8;
   // E4M3 llama3_8b TP2 59.5 -> 51.0, TP4 32.7 -> 29.1, llama3_8b 96.2 ->
-  // 96.3.  It lost on shorter tables (GQA 32 x 1..2K, 128 blocks: 27.5 ->
-  // 29.7; 64 blocks: 13-16 %), below C / 2 units (the TP8 shard 28.6 ->
+  // 96.3; tables of 160..223 blocks 0.5-11 % faster (GQA 32/8 64 x 1..3K
+  // 76.8 -> 70.2).  It lost on shorter tables (GQA 32 x 1..2K, 128 blocks:
+  // 27.5 -> 29.7; 64 blocks: 13-16 %), below C / 2 units (the TP8 shard 28.6 ->
   // 29.4) and on uniform batches planned without the hint (qwen25_7b 158.4
   // -> 163.5).
   if (o->even_split < PA_EVEN_SPLIT_AUTO || o->even_split > PA_EVEN_SPLIT_ON)

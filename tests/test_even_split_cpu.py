@@ -180,7 +180,8 @@ def test_plans_that_take_the_even_split(native_lib):
     few = nat.make_shape(15, 32, 8, 512, 15 * 512)  # 120 units
     assert nat.plan(few, device=MI355X)["even_split"] == 0
     assert nat.plan(nat.make_shape(16, 32, 8, 512, 1), device=MI355X)["even_split"] == 1
-    assert nat.plan(nat.make_shape(64, 32, 8, 255, 1), device=MI355X)["even_split"] == 0
+    assert nat.plan(nat.make_shape(64, 32, 8, 159, 1), device=MI355X)["even_split"] == 0
+    assert nat.plan(nat.make_shape(64, 32, 8, 160, 1), device=MI355X)["even_split"] == 1
     full = nat.default_options()
     full.min_context_hint = 512 * 16
     assert nat.plan(sh, full, device=MI355X)["even_split"] == 0

@@ -138,18 +138,19 @@ def test_even_split_timeline_and_checked_variant():
     assert int(err.item()) == 0
 
 
-def test_the_auto_plan_takes_the_even_split_between_half_and_two_units_per_cu():
-    """24 ragged sequences x 8 KV heads (192 units on 256 CUs, 256 table
-    blocks): the auto plan is the even split, against the oracle and
-    against the plan without it (another split of the same work)."""
+@pytest.mark.parametrize("units_per_cu,MB", [(0.75, 256), (1, 160), (2, 200)])
+def test_the_auto_plan_takes_the_even_split(units_per_cu, MB):
+    """Ragged sequences x 8 KV heads from 3/4 to 2 units per CU over tables
+    of 160..256 blocks: the auto plan is the even split, against the oracle
+    and against the plan without it (another split of the same work)."""
     C = nat.device_info()["compute_units"]
-    B = 3 * C // 4 // 8
-    x = gen.make_case(B, 16, 8, None, seed=960, ctx_range=(1, 4096), max_blocks_per_seq=256,
-                      poison=True)
+    B = int(units_per_cu * C) // 8
+    print(f"[even auto] B={B} MB={MB}", flush=True)
+    x = gen.make_case(B, 16, 8, None, seed=960 + MB, ctx_range=(1, MB * 16),
+                      max_blocks_per_seq=MB, poison=True)
     dev = to_device(x)
     plan = ops.plan(dev["q"], dev["k_cache"], dev["block_tables"])
     assert plan["even_split"] == 1 and plan["workgroups"] == C
-    got = run(x, dev)
-    assert_close(got, oracle(x), "auto even split")
-    off = run(x, dev, even_split=nat.EVEN_SPLIT_OFF)
-    assert_close(off, oracle(x), "without the even split")
+    ref = oracle(x)
+    assert_close(run(x, dev), ref, "auto even split")
+    assert_close(run(x, dev, even_split=nat.EVEN_SPLIT_OFF), ref, "without the even split")

@@ -90,8 +90,9 @@ def test_wrong_hint_on_a_ragged_batch_changes_no_result():
 def test_explicit_residency_caps_change_no_bits(cap):
     x = gen.make_case(64, 16, 4, None, seed=770, ctx_range=(1, 3000), extra_pool_blocks=2)
     dev = to_device(x)
-    ref = run(x, dev)
-    got = run(x, dev, max_resident_wgs=cap)
+    off = dict(even_split=nat.EVEN_SPLIT_OFF)  # (the auto plan would take the even split)
+    ref = run(x, dev, **off)
+    got = run(x, dev, max_resident_wgs=cap, **off)
     assert np.array_equal(bits(got), bits(ref))
     assert_close(got, oracle(x), f"cap {cap}")
 
