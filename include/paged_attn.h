@@ -144,8 +144,9 @@ enum pa_structure {
 enum pa_even_split {
     PA_EVEN_SPLIT_AUTO = 0,   /* the plan's choice: the even split for 2..256
                                  sequences with at least CUs / 2 (sequence,
-                                 KV head) units over a table of 160..1024
-                                 blocks, with waves, partitions, order and
+                                 KV head) units (E4M3 with at most 8 query
+                                 heads per KV head: CUs / 4) over a table of
+                                 160..1024 blocks, with waves, partitions, order and
                                  residency left to the plan, the look-ahead
                                  off or in registers, and no
                                  min_context_hint that says every context

@@ -341,9 +341,12 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
   // E4M3 llama3_8b TP2 59.5 -> 51.0, TP4 32.7 -> 29.1, llama3_8b 96.2 ->
   // 96.3; tables of 160..223 blocks 0.5-11 % faster (GQA 32/8 64 x 1..3K
   // 76.8 -> 70.2).  It lost on shorter tables (GQA 32 x 1..2K, 128 blocks:
-  // 27.5 -> 29.7; 64 blocks: 13-16 %), below C / 2 units (the TP8 shard 28.6 ->
-  // 29.4) and on uniform batches planned without the hint (qwen25_7b 158.4
-  // -> 163.5).
+  // 27.5 -> 29.7; 64 blocks: 13-16 %), below C / 2 units in fp16 (the TP8
+  // shard 28.6 -> 29.4) and on uniform batches planned without the hint
+  // (qwen25_7b 158.4 -> 163.5).  E4M3 also takes it from C / 4 units with
+  // groups of at most 8 query heads: 4-8 % faster there (the llama3_8b TP8
+  // shard 19.1 -> 18.3; GQA 4/1 96 x 512..8K 25.4 -> 23.5), but 6 % slower
+  // with 16 (GQA 32/2 32 x 512..8K 21.5 -> 22.9).
   if (o->even_split < PA_EVEN_SPLIT_AUTO || o->even_split > PA_EVEN_SPLIT_ON)
     return PA_ERR_INVALID_ARG;
   const bool uniform_hint = o->min_context_hint > 0 && (int64_t)o->min_context_hint * 8 >=
@@ -352,7 +355,8 @@ int make_plan(const pa_shape* sh, const pa_options* o, const DeviceInfo& dv, Pla
       o->even_split == PA_EVEN_SPLIT_AUTO && !two && !uniform_hint && in_flight > 0 &&
       o->partition_blocks == 0 && o->waves_per_wg == 0 && o->max_resident_wgs == 0 &&
       o->seq_order == PA_ORDER_AUTO && B >= 2 && B <= PA_RANK_MAX_SEQS &&
-      MB >= kEvenMinBlocks && MB <= kMaxPartitionBlocks && 2 * units >= dv.cus &&
+      MB >= kEvenMinBlocks && MB <= kMaxPartitionBlocks &&
+      (2 * units >= dv.cus || (kv8 && g <= 8 && 4 * units >= dv.cus)) &&
       (int64_t)B * (MB + kEvenPieceBlocksE4M3) * Hkv <= INT32_MAX / 2;
   const bool even = o->even_split == PA_EVEN_SPLIT_ON || even_auto;
   if (even) {

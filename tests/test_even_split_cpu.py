@@ -188,6 +188,13 @@ def test_plans_that_take_the_even_split(native_lib):
     full.min_context_hint = 512 * 16 * 7 // 8 - 1
     assert nat.plan(sh, full, device=MI355X)["even_split"] == 1
     assert nat.plan(nat.make_shape(1, 8, 1, 1024, 1), device=MI355X)["even_split"] == 0
+    # E4M3 from C/4 units with groups of at most 8 query heads
+    e4 = lambda B, Hq, Hkv: nat.plan(nat.make_shape(B, Hq, Hkv, 512, 1, kv_dtype=nat.KV_E4M3),
+                                     device=MI355X)["even_split"]
+    assert e4(64, 4, 1) == 1 and e4(16, 64, 8) == 1   # 64 units, g = 4 and 8
+    assert e4(63, 4, 1) == 0                          # 63 units
+    assert e4(32, 32, 2) == 0                         # g = 16
+    assert nat.plan(nat.make_shape(64, 4, 1, 512, 1), device=MI355X)["even_split"] == 0  # fp16
     o.prefetch_distance = 2
     assert nat.plan(sh8, o, device=MI355X)["prefetch_distance"] == 2
     o.prefetch_distance = 0

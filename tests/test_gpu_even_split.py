@@ -88,11 +88,16 @@ def test_even_split_twice_with_fewer_blocks():
         assert_close(got, oracle(x), "even split, reused workspace")
 
 
-@pytest.mark.parametrize("B,auto", [(64, False), (24, True)])
-def test_even_split_over_an_e4m3_cache(B, auto):
+@pytest.mark.parametrize("case", ["asked", "auto", "auto below C/2"])
+def test_even_split_over_an_e4m3_cache(case):
     """Asked for (512 units), and taken by the auto plan (192 units over 256
-    table blocks: 8 waves, one block ahead)."""
-    x8 = gen.to_fp8(gen.make_case(B, 32, 8, None, seed=930 + B, ctx_range=(1, 4096),
+    table blocks; and C/4 units of GQA 4/1, below the fp16 rule's C/2: 8
+    waves, one block ahead)."""
+    auto = case != "asked"
+    B, Hq, Hkv = {"asked": (64, 32, 8), "auto": (24, 32, 8),
+                  "auto below C/2": (nat.device_info()["compute_units"] // 4, 4, 1)}[case]
+    print(f"[even e4m3] {case}: B={B} Hq={Hq} Hkv={Hkv}", flush=True)
+    x8 = gen.to_fp8(gen.make_case(B, Hq, Hkv, None, seed=930 + B, ctx_range=(1, 4096),
                                   max_blocks_per_seq=256))
     d = {k: torch.from_numpy(getattr(x8, k)).cuda() for k in ("q", "block_tables", "context_lens")}
     d["k_cache"] = torch.from_numpy(gen.pack_k_fp8(x8.k8)).cuda()

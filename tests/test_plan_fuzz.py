@@ -70,12 +70,14 @@ def test_every_accepted_plan_is_launchable(shape_t, opt_t):
     assert W in (1, 2, 4, 8)
     if p["even_split"]:
         # one share per CU and cap; by itself only for all-auto options, no
-        # uniform hint, units >= C/2, 2..256 sequences and 160..1024 blocks
+        # uniform hint, units >= C/2 (E4M3 with g <= 8: C/4), 2..256
+        # sequences and 160..1024 blocks
         assert even != nat.EVEN_SPLIT_OFF
         if even == nat.EVEN_SPLIT_AUTO:
             assert pb == 0 and waves == 0 and cap == 0 and order == 0
             assert structure == 0 and hint_kind not in ("full", "7/8") and pf in (-1, 0, 2, 3)
-            assert 128 <= B * Hkv and 160 <= MB <= 1024 and 2 <= B <= 256
+            assert 128 <= B * Hkv or (kv == nat.KV_E4M3 and g <= 8 and 64 <= B * Hkv)
+            assert 160 <= MB <= 1024 and 2 <= B <= 256
         R = p["resident_wgs"]
         assert R >= 1 and p["workgroups"] == 256 * R and P == 1 and PB == MB
         assert p["balanced"] == 0 and p["seqs_per_wg"] == 1
